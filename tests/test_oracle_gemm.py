@@ -1,0 +1,241 @@
+"""Pins for the GEMM oracle and its error bound, plus planted-mistake checks
+that show the pins catch a wrong oracle. Everything here runs on the CPU."""
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+import pytest
+import torch
+
+import datagen
+from oracle import gemm as og
+from oracle import layout as ol
+
+
+def _op(m: datagen.Matrix) -> og.Operand:
+    return og.Operand(m.store, m.shape, m.stride)
+
+
+def _dense(m: datagen.Matrix) -> np.ndarray:
+    return m.view().to(torch.float64).numpy()
+
+
+def _all_points(M, N):
+    return np.array([(i, j) for i in range(M) for j in range(N)], dtype=np.int64)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _built():
+    og.build()
+
+
+def test_identity_a_gives_b():
+    """A = I: the sum has one nonzero term, so S == B exactly and
+    D_ref == alpha*B + beta*C in two roundings."""
+    M = K = 24
+    N = 17
+    A = datagen.place(np.eye(M), torch.float16, "row")
+    B = datagen.matrix(K, N, torch.float16, "col", "uniform", 11)
+    C = datagen.matrix(M, N, torch.float16, "row", "uniform", 12)
+    ij = _all_points(M, N)
+    S, T = og.gemm_points(_op(A), _op(B), ij)
+    b = _dense(B).reshape(-1)
+    assert np.array_equal(S, b) and np.array_equal(T, np.abs(b))
+    Dref, Cabs = og.epilogue(S, _op(C), ij, 2.0, -0.5)
+    c = _dense(C).reshape(-1)
+    assert np.array_equal(Dref, 2.0 * b + -0.5 * c)
+    assert np.array_equal(Cabs, np.abs(-0.5 * c))
+
+
+def test_small_integers_exact_against_python_ints():
+    """Entries in {-2..2}: every partial sum is an exact small integer, so the
+    oracle must equal a brute-force sum over Python ints."""
+    M, N, K = 9, 7, 64
+    A = datagen.matrix(M, K, torch.bfloat16, "row", "smallint", 21)
+    B = datagen.matrix(K, N, torch.bfloat16, "row", "smallint", 22)
+    a = [[int(v) for v in row] for row in _dense(A)]
+    b = [[int(v) for v in row] for row in _dense(B)]
+    S, T = og.gemm_rows(_op(A), _op(B), range(M))
+    for i in range(M):
+        for j in range(N):
+            assert S[i, j] == sum(a[i][k] * b[k][j] for k in range(K))
+            assert T[i, j] == sum(abs(a[i][k] * b[k][j]) for k in range(K))
+
+
+@pytest.mark.parametrize("a_major,b_major", [("row", "col"), ("col", "row"), ("row", "row"), ("col", "col")])
+def test_matches_numpy_matmul_any_layout(a_major, b_major):
+    """Library routine cross-check (float64 matmul) on a non-square shape,
+    with operands stored through different layouts (and padded leading
+    dimensions) — a transposed operand or a dropped term would fail this."""
+    M, N, K = 37, 53, 29
+    A = datagen.matrix(M, K, torch.float16, a_major, "uniform", 31, ld=(K + 3 if a_major == "row" else M + 5))
+    B = datagen.matrix(K, N, torch.float16, b_major, "uniform", 32, ld=(N + 2 if b_major == "row" else K + 7))
+    S, T = og.gemm_rows(_op(A), _op(B), range(M))
+    a, b = _dense(A), _dense(B)
+    assert np.allclose(S, a @ b, rtol=0, atol=1e-12)
+    assert np.allclose(T, np.abs(a) @ np.abs(b), rtol=0, atol=1e-12)
+
+
+def test_points_equal_rows():
+    M, N, K = 16, 12, 40
+    A = datagen.matrix(M, K, torch.bfloat16, "col", "normal", 41)
+    B = datagen.matrix(K, N, torch.bfloat16, "row", "normal", 42)
+    S1, T1 = og.gemm_rows(_op(A), _op(B), range(M))
+    S2, T2 = og.gemm_points(_op(A), _op(B), _all_points(M, N))
+    assert np.array_equal(S1.reshape(-1), S2) and np.array_equal(T1.reshape(-1), T2)
+
+
+def test_beta_zero_never_reads_c():
+    M, N, K = 4, 4, 8
+    A = datagen.matrix(M, K, torch.float16, "row", "uniform", 1)
+    B = datagen.matrix(K, N, torch.float16, "col", "uniform", 2)
+    C = datagen.place(np.full((M, N), np.nan), torch.float16, "row")
+    ij = _all_points(M, N)
+    S, _ = og.gemm_points(_op(A), _op(B), ij)
+    Dref, Cabs = og.epilogue(S, _op(C), ij, 1.0, 0.0)
+    assert np.all(np.isfinite(Dref)) and np.all(Cabs == 0)
+
+
+def test_empty_k_gives_beta_c():
+    M, N = 3, 5
+    A = datagen.place(np.zeros((M, 0)), torch.float16, "row")
+    B = datagen.place(np.zeros((0, N)), torch.float16, "col")
+    C = datagen.matrix(M, N, torch.float16, "row", "uniform", 3)
+    ij = _all_points(M, N)
+    S, T = og.gemm_points(_op(A), _op(B), ij)
+    assert np.all(S == 0) and np.all(T == 0)
+    Dref, _ = og.epilogue(S, _op(C), ij, 1.0, 0.5)
+    assert np.array_equal(Dref, 0.5 * _dense(C).reshape(-1))
+
+
+# ---------------------------------------------------------------------------
+# ulp_out and the bound
+# ---------------------------------------------------------------------------
+
+def test_ulp_out_fp16_matches_numpy_spacing():
+    rng = np.random.default_rng(0)
+    vals = np.concatenate([rng.uniform(-70000, 70000, 2000), rng.uniform(-1e-3, 1e-3, 2000),
+                           [1.0, 2.0, 0.5, 6.1e-5, 6.0e-5, 1e-7, 65504.0, -1.0]])
+    with np.errstate(over="ignore"):
+        v16 = vals.astype(np.float16)
+        v16 = v16[np.isfinite(v16) & (np.abs(v16) < np.float16(65504))]
+        want = np.abs(np.spacing(np.abs(v16))).astype(np.float64)
+    got = og.ulp_out(v16.astype(np.float64), torch.float16)
+    assert np.array_equal(got, want)
+    assert og.ulp_out(np.array([0.0]), torch.float16)[0] == 2.0 ** -24
+
+
+def test_ulp_out_bf16_matches_bit_increment():
+    rng = np.random.default_rng(1)
+    vals = torch.from_numpy(np.concatenate([rng.standard_normal(3000) * 10.0 ** rng.integers(-30, 30, 3000),
+                                            [1.0, 3.0, 2.0 ** -126, 2.0 ** -130]])).to(torch.bfloat16).abs()
+    vals = vals[(vals > 0) & torch.isfinite(vals)]
+    bits = vals.view(torch.int16)
+    nxt = (bits + 1).view(torch.bfloat16)
+    want = (nxt.to(torch.float64) - vals.to(torch.float64)).numpy()
+    ok = np.isfinite(want)
+    got = og.ulp_out(vals.to(torch.float64).numpy(), torch.bfloat16)
+    assert np.array_equal(got[ok], want[ok])
+    assert og.ulp_out(np.array([0.0]), torch.bfloat16)[0] == 2.0 ** -133
+
+
+def test_check_accepts_inside_rejects_outside():
+    Dref = np.array([1.0, -2.0, 0.0, 100.0])
+    T = np.array([10.0, 3.0, 0.0, 50.0])
+    Cabs = np.zeros(4)
+    b = og.bound(T, Cabs, Dref, 1.0, torch.float16)
+    assert og.check(Dref + 0.99 * b, Dref, T, Cabs, 1.0, torch.float16).ok
+    r = og.check(Dref + 1.01 * b, Dref, T, Cabs, 1.0, torch.float16)
+    assert not r.ok and r.n_bad == 4 and r.worst_fraction > 1.0
+    bad = Dref.copy()
+    bad[2] = np.nan
+    assert not og.check(bad, Dref, T, Cabs, 1.0, torch.float16).ok
+
+
+# ---------------------------------------------------------------------------
+# Planted mistakes: each mutant of the oracle must fail a pin above.
+# ---------------------------------------------------------------------------
+
+_C_MUTANTS = {
+    "drop_last_k": ("k < K; ++k", "k < K - 1; ++k"),
+    "wrong_sign": ("s += p;", "s -= p;"),
+    "transposed_b": ("B[k * sb0 + j * sb1]", "B[j * sb0 + k * sb1]"),
+    "abs_missing": ("t += fabs(p);", "t += p;"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(_C_MUTANTS))
+def test_c_mutant_is_caught(name, tmp_path):
+    src = open(os.path.join(os.path.dirname(og.__file__), "gemm_oracle.c")).read()
+    old, new = _C_MUTANTS[name]
+    assert old in src
+    mpath = tmp_path / "mutant.c"
+    mpath.write_text(src.replace(old, new))
+    so = tmp_path / "libmutant.so"
+    subprocess.check_call(["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", "-o", str(so), str(mpath), "-lm"])
+    saved = og._lib
+    try:
+        og._lib = None
+        lib = ctypes.CDLL(str(so))
+        d, i64 = ctypes.POINTER(ctypes.c_double), ctypes.c_int64
+        lib.oracle_gemm_rows.argtypes = [d, i64, i64, d, i64, i64, i64, i64, ctypes.POINTER(i64), i64, d, d]
+        lib.oracle_gemm_points.argtypes = [d, i64, i64, d, i64, i64, i64, ctypes.POINTER(i64), i64, d, d]
+        lib.oracle_epilogue_points.argtypes = [d, d, i64, i64, ctypes.POINTER(i64), i64,
+                                               ctypes.c_double, ctypes.c_double, d, d]
+        og._lib = lib
+        with pytest.raises(AssertionError):
+            test_matches_numpy_matmul_any_layout("row", "col")
+    finally:
+        og._lib = saved
+
+
+def _rowmajor_unravel(shape, x):
+    c = []
+    for s in reversed(ol.flatten(shape)):
+        c.append(x % s)
+        x //= s
+    return list(reversed(c))
+
+
+def _bad_coalesce(L):
+    pairs = [(s, d) for s, d in zip(ol.flatten(L.shape), ol.flatten(L.stride)) if s != 1]
+    out = []
+    for s, d in pairs:
+        if out and d == out[-1][0]:          # forgets the stride factor
+            out[-1] = (out[-1][0] * s, out[-1][1])
+        else:
+            out.append((s, d))
+    return ol._from_leaves(out) if out else ol.Layout(1, 0)
+
+
+def _bad_complement(B, M):
+    pairs = sorted((d, s) for s, d in zip(ol.flatten(B.shape), ol.flatten(B.stride)) if d > 0 and s > 1)
+    out, cur = [], 1
+    for d, s in pairs:
+        out.append((d // cur, cur))
+        cur = s * d
+    return ol.coalesce(ol._from_leaves(out or [(1, 0)]))   # drops the last leaf
+
+
+@pytest.mark.parametrize("target,mutant", [
+    ("unravel", _rowmajor_unravel),
+    ("coalesce", _bad_coalesce),
+    ("complement", _bad_complement),
+])
+def test_layout_mutant_is_caught(monkeypatch, target, mutant):
+    import tests.test_oracle_layout as T
+    monkeypatch.setattr(ol, target, mutant)
+    pins = [T.test_zipped_divide_printed_form_and_modes, T.test_zipped_divide_element_37_44,
+            T.test_composition_worked_example, T.test_unravel_4x3, T.test_packed_panel,
+            T.test_nested_2x4_and_coalesce, T.test_costume_24, T.test_divides,
+            T.test_coalesce_preserves_function_and_is_maximal,
+            T.test_complement_closed_form_equals_greedy_definition]
+    failures = 0
+    for pin in pins:
+        try:
+            pin()
+        except Exception:
+            failures += 1
+    assert failures > 0
