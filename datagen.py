@@ -84,8 +84,8 @@ def matrix(rows: int, cols: int, dtype: torch.dtype, major: str, dist: str, seed
     return place(draw(rows, cols, dist, seed, k_for_scale), dtype, major, ld)
 
 
-def zeros(rows: int, cols: int, dtype: torch.dtype, major: str = "row") -> Matrix:
-    return place(np.zeros((rows, cols)), dtype, major)
+def zeros(rows: int, cols: int, dtype: torch.dtype, major: str = "row", ld: Optional[int] = None) -> Matrix:
+    return place(np.zeros((rows, cols)), dtype, major, ld)
 
 
 @dataclass

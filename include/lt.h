@@ -1,0 +1,309 @@
+/*
+ * lt.h — C ABI of the layout-algebra GEMM library for AMD Instinct MI355X
+ * (gfx950).
+ *
+ * The library has three parts, all behind plain C types:
+ *   1. Host layout algebra: Shape:Stride layouts as values, their evaluation,
+ *      coalesce, composition, complement, logical/zipped divide, local_tile
+ *      and local_partition. Pure integer math, no device, thread-safe.
+ *   2. Device layout maps: evaluate or gather through a layout on the GPU.
+ *   3. The tiled GEMM D = alpha*A*B + beta*C with fp16/bf16 operands and fp32
+ *      accumulation, whose operands, block tiles and thread partitions are
+ *      addressed through those layouts.
+ *
+ * Sources (cited by page title and section):
+ *   [P1] "CUTLASS and CuTe layouts" (Day 84)
+ *   [P2] "3.5 CUTLASS II — CuTe 레이아웃·텐서"
+ *   [P3] "CUTLASS, in depth: the GEMM hierarchy, CuTe layouts, Hopper kernel
+ *        schedules and the Python DSL"
+ *   [P4] "Layouts as Algebra: CUTLASS & CuTe"
+ *
+ * Conventions for every function:
+ *   - The return value is an lt_status; results come back through pointer
+ *     arguments, which the caller owns. On any error nothing is written to
+ *     the outputs and nothing is launched.
+ *   - Layouts are caller-owned values (lt_layout, no heap, no free function).
+ *   - Device pointers are caller-owned device memory; the library never
+ *     allocates or frees device memory on the caller's behalf.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Device functions are asynchronous on that stream; a launch failure is
+ *     reported as LT_ERR_HIP, later faults surface at the caller's next
+ *     synchronisation.
+ */
+#ifndef LT_H_
+#define LT_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ------------------------------------------------------------------------ */
+/* Status                                                                    */
+/* ------------------------------------------------------------------------ */
+
+typedef enum lt_status {
+    LT_OK = 0,
+    LT_ERR_INVALID_ARGUMENT = 1,   /* NULL pointer, bad enum, bad count           */
+    LT_ERR_INVALID_LAYOUT = 2,     /* incongruent tree, extent < 1, stride < 0    */
+    LT_ERR_NOT_ADMISSIBLE = 3,     /* composition/complement has no layout [P4 "Composition, worked by hand"] */
+    LT_ERR_NOT_DIVISIBLE = 4,      /* tiler does not divide the mode [P2 3.5.8]   */
+    LT_ERR_OUT_OF_RANGE = 5,       /* index >= size, coordinate out of its mode, int64 overflow */
+    LT_ERR_MISALIGNED_OPERAND = 6, /* 16-bit operand not 128-bit aligned [P1 "Pitfalls"; P3 "Failure modes"] */
+    LT_ERR_UNSUPPORTED = 7,        /* no kernel for this layout/dtype combination */
+    LT_ERR_ARCH_MISMATCH = 8,      /* device is not gfx950 [P1 "Results", "Pitfalls"] */
+    LT_ERR_LDS_OVERFLOW = 9,       /* tile x stages exceeds LDS [P3 "Failure modes"] */
+    LT_ERR_WORKSPACE = 10,         /* workspace missing or too small              */
+    LT_ERR_HIP = 11,               /* a HIP runtime call failed                   */
+    LT_ERR_CAPACITY = 12           /* result needs more leaves/nodes than lt_layout holds, or text buffer too small */
+} lt_status;
+
+/* Static description of a status code (never NULL). */
+const char* lt_status_string(lt_status s);
+
+/* ------------------------------------------------------------------------ */
+/* Layout value                                                              */
+/* ------------------------------------------------------------------------ */
+
+#define LT_MAX_LEAVES 32
+#define LT_MAX_NODES 64
+
+/*
+ * A Shape:Stride layout [P1 "A layout is a shape and a stride"; P2 3.5.3;
+ * P4 "The formula gets a name"]: a function from coordinates to offsets,
+ * offset = sum over leaves of coordinate * stride. Shape and stride are
+ * congruent trees [P4 "A shape is a tree"; P2 3.5.4]; they share one tree
+ * here, stored in preorder:
+ *   tree[i] == 0 : a leaf; its extent and stride are the next entries of
+ *                  shape[] and stride[] (leaves are numbered left to right);
+ *   tree[i] == k : a tuple of k >= 1 children, which follow in preorder.
+ * nnodes entries of tree[] and nleaves entries of shape[]/stride[] are used.
+ * The root may be a single leaf ("8:1"), else a tuple whose children are the
+ * top-level modes. Extents are >= 1, strides >= 0 (negative strides are
+ * rejected: a reading, the pages use none).
+ */
+typedef struct lt_layout {
+    int32_t nleaves;
+    int32_t nnodes;
+    int64_t shape[LT_MAX_LEAVES];
+    int64_t stride[LT_MAX_LEAVES];
+    int8_t tree[LT_MAX_NODES];
+} lt_layout;
+
+/* Check that L is well formed (tree consistent, extents >= 1, strides >= 0). */
+lt_status lt_layout_validate(const lt_layout* L);
+
+/* Parse the printed form, e.g. "((16,16),(16,8)):((128,1),(2048,16))".
+ * Spaces and the '_' marks of static integers [P1 "Results"] are ignored. */
+lt_status lt_layout_parse(const char* text, lt_layout* out);
+
+/* Print L as shape:stride with no spaces into buf (NUL-terminated). *needed
+ * (optional) receives the length including the NUL; if cap is too small the
+ * call returns LT_ERR_CAPACITY and writes nothing to buf. */
+lt_status lt_layout_format(const lt_layout* L, char* buf, size_t cap, size_t* needed);
+
+/* A flat layout with `rank` leaves as its top-level modes (rank 1 gives a
+ * bare "s:d" root). */
+lt_status lt_make_layout(int32_t rank, const int64_t* shape, const int64_t* stride, lt_layout* out);
+
+/* Compact strides: first mode fastest (the natural, colexicographic default
+ * [P2 3.5.3-3.5.4]) or last mode fastest (row-major [P2 3.5.3]). */
+lt_status lt_make_colmajor(int32_t rank, const int64_t* shape, lt_layout* out);
+lt_status lt_make_rowmajor(int32_t rank, const int64_t* shape, lt_layout* out);
+
+/* Concatenate n layouts as the top-level modes of a new layout. */
+lt_status lt_make_tuple(int32_t n, const lt_layout* modes, lt_layout* out);
+
+/* Top-level mode i of L (a leaf root has one mode, itself). */
+lt_status lt_mode(const lt_layout* L, int32_t i, lt_layout* out);
+
+/* size = product of extents; cosize = largest offset reached + 1, the memory
+ * footprint [P2 3.5.5]; rank = number of top-level modes; depth = tuple
+ * nesting depth (0 for a leaf root). */
+lt_status lt_size(const lt_layout* L, int64_t* out);
+lt_status lt_cosize(const lt_layout* L, int64_t* out);
+lt_status lt_rank(const lt_layout* L, int32_t* out);
+lt_status lt_depth(const lt_layout* L, int32_t* out);
+
+/* Evaluate at a 1-D index, unravelled first-leaf-fastest (colexicographic)
+ * [P4 "The formula gets a name"; P2 3.5.4]. idx must be in [0, size). */
+lt_status lt_eval_index(const lt_layout* L, int64_t idx, int64_t* offset);
+
+/* Evaluate at a coordinate. ncoord == rank: one integer per top-level mode,
+ * each unravelled colexicographically inside its mode. ncoord == nleaves: a
+ * natural coordinate, one integer per leaf. Each entry must lie inside its
+ * (mode's or leaf's) extent. */
+lt_status lt_eval_coord(const lt_layout* L, const int64_t* coord, int32_t ncoord, int64_t* offset);
+
+/* coalesce [P4 "A shape is a tree"; P2 3.5.6]: flatten, drop extent-1 leaves,
+ * merge s0:d0 followed by s1:(s0*d0) into (s0*s1):d0. The result has a leaf
+ * root if one leaf remains, else a flat tuple; an all-extent-1 layout gives
+ * 1:0. */
+lt_status lt_coalesce(const lt_layout* L, lt_layout* out);
+
+/* composition A o B [P4 "Composition, worked by hand"; P1 "A layout is a
+ * shape and a stride"]: the layout R with B's mode tree (each leaf of B may
+ * become a tuple) such that R(x) == A(B(x)) for every x < size(B). Built by
+ * walking each leaf of B through A's coalesced leaves. LT_ERR_NOT_ADMISSIBLE
+ * when no such layout exists, including when B reaches outside [0, size(A))
+ * (a reading: A's last mode is not extended). A leaf of B with extent 1
+ * gives 1:0, a leaf with stride 0 gives s:0. */
+lt_status lt_compose(const lt_layout* A, const lt_layout* B, lt_layout* out);
+
+/* complement of B in [0, M) [P4 "Divide is tiling"]: the layout B* with
+ * strictly increasing values and B*(0) == 0 such that the pair (B, B*) hits
+ * every integer of [0, M) exactly once (a reading of "everything B misses";
+ * stride-0 leaves of B are ignored). Coalesced. LT_ERR_NOT_ADMISSIBLE if no
+ * such layout exists. */
+lt_status lt_complement(const lt_layout* B, int64_t M, lt_layout* out);
+
+/* logical_divide(A, B) = A o (B, complement(B, size(A))) [P4 "Divide is
+ * tiling"; P1 "A layout is a shape and a stride"; P2 3.5.6]. Mode 0 is inside
+ * the tile, mode 1 picks the tile. size(B) must divide size(A)
+ * (LT_ERR_NOT_DIVISIBLE otherwise). */
+lt_status lt_logical_divide(const lt_layout* A, const lt_layout* tiler, lt_layout* out);
+
+/* The same division by a shape tiler applied mode by mode: tiler[i] divides
+ * top-level mode i of A by the layout tiler[i]:1, for i < n (n <= rank);
+ * modes past n are kept whole. Result mode i is (in-tile, tile-index). */
+lt_status lt_logical_divide_shape(const lt_layout* A, int32_t n, const int64_t* tiler, lt_layout* out);
+
+/* zipped_divide [P1 "A layout is a shape and a stride"]: the shape-tiler
+ * division regrouped so that mode 0 gathers all in-tile modes and mode 1 all
+ * tile-index modes (plus untiled modes). E.g. (256,128):(128,1) by (16,16)
+ * gives ((16,16),(16,8)):((128,1),(2048,16)). */
+lt_status lt_zipped_divide(const lt_layout* A, int32_t n, const int64_t* tiler, lt_layout* out);
+
+/* local_tile [P4 "The kernel, in three lines"; P2 3.5.6-3.5.7]: zipped_divide
+ * A by the tiler, then fix the tile-index mode at coord. coord[i] < 0 stands
+ * for CuTe's '_' and keeps that tile-index mode free; free modes follow the
+ * in-tile modes in the result. step (optional, n entries of 0/1, CuTe's Step)
+ * selects which of the n tiler modes apply to A; the selected count must be
+ * rank(A). The tile's elements are at *offset + out(x). */
+lt_status lt_local_tile(const lt_layout* A, int32_t n, const int64_t* tiler, const int64_t* coord,
+                        const uint8_t* step, int64_t* offset, lt_layout* out);
+
+/* local_partition [P4 "The kernel, in three lines"; P2 3.5.6-3.5.7]: thread
+ * t's share of the tile T under the thread layout thr. T is zipped-divided by
+ * the per-mode sizes of thr; the in-tile mode is fixed at thread t's
+ * coordinate (the coordinate that thr maps to t; thr must be a bijection onto
+ * [0, size(thr))) and the tile-index mode is kept. step (optional, rank(thr)
+ * entries) selects which thread modes partition T. The thread's elements are
+ * at *offset + out(x). */
+lt_status lt_local_partition(const lt_layout* T, const lt_layout* thr, int64_t t, const uint8_t* step,
+                             int64_t* offset, lt_layout* out);
+
+/* ------------------------------------------------------------------------ */
+/* Device and architecture                                                  */
+/* ------------------------------------------------------------------------ */
+
+/* Check that the current HIP device is gfx950 and record its properties.
+ * Runs once per device before anything is launched or allocated [P1
+ * "Results": refuse before any allocation]. Returns LT_ERR_ARCH_MISMATCH on
+ * another architecture. `arch_out` (optional, cap bytes) receives the
+ * device's gcnArchName. */
+lt_status lt_device_check(char* arch_out, size_t cap);
+
+/* Test hook: when non-NULL, the library uses this architecture name instead
+ * of querying the device (so the refusal path can be exercised without a
+ * GPU). NULL restores the real query. Not thread-safe; for tests only. */
+lt_status lt_set_arch_override(const char* arch);
+
+/* Device layout maps (the bit-exact layout parity path) [P1 "Two programs:
+ * the algebra, then the GEMM" and "Results": a gather through the same layout
+ * on the device]. For x < n (n <= size(L)):
+ *   lt_layout_eval_device: out[x] = L(x)            (out: n int64 on device)
+ *   lt_gather_device:      dst[x] = src[L(x)]       (elem_bytes in {1,2,4,8};
+ *                          src must hold cosize(L) elements) */
+lt_status lt_layout_eval_device(const lt_layout* L, int64_t* d_out, int64_t n, void* stream);
+lt_status lt_gather_device(const lt_layout* L, const void* d_src, void* d_dst, int32_t elem_bytes,
+                           int64_t n, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* GEMM                                                                      */
+/* ------------------------------------------------------------------------ */
+
+typedef enum lt_dtype { LT_F16 = 1, LT_BF16 = 2 } lt_dtype;
+
+/* A tensor is a pointer plus a layout: a zero-copy view [P2 3.5.7; P3 "CuTe:
+ * layouts as functions"]. For the GEMM, A is (M,K), B is (K,N), C and D are
+ * (M,N): rank-2 layouts in elements whose two modes each coalesce to a single
+ * stride. An operand is named by its stride-1 mode [P4 "One notation, and no
+ * more transposes"]: A K-major or M-major, B K-major or N-major, C/D N-major
+ * or M-major. */
+typedef struct lt_tensor {
+    void* ptr;
+    int32_t dtype;     /* lt_dtype */
+    int32_t reserved;
+    lt_layout layout;
+} lt_tensor;
+
+/* Kernel families the planner can choose. */
+typedef enum lt_kernel {
+    LT_KERNEL_AUTO = 0,
+    LT_KERNEL_WAVE16 = 1,   /* one wave per 16x16 tile, any layout/ragged shape */
+    LT_KERNEL_TILED = 2,    /* 256x256x64 block tile, LDS double buffer, 32x32x16 MFMA */
+    LT_KERNEL_SKINNY = 3    /* M <= 32, K-major B streamed once, split-K */
+} lt_kernel;
+
+/* Optional planner overrides; zero fields mean "choose". */
+typedef struct lt_gemm_options {
+    int32_t kernel;     /* lt_kernel */
+    int32_t tile_m;     /* block tile (kernel-specific allowed values) */
+    int32_t tile_n;
+    int32_t split_k;    /* SKINNY only: number of K slices (>= 1) */
+} lt_gemm_options;
+
+/* What the planner chose, for banners and tests [P1 "Exercise": print the
+ * tile, warp tile and shared-memory figures]. */
+typedef struct lt_gemm_plan_info {
+    int32_t kernel;          /* lt_kernel */
+    int32_t tile_m, tile_n, tile_k;
+    int32_t wave_m, wave_n;  /* tile of one wave */
+    int32_t waves;           /* waves per workgroup */
+    int32_t stages;          /* LDS pipeline depth */
+    int32_t split_k;
+    int32_t a_kmajor, b_kmajor, d_nmajor;
+    int64_t grid;            /* workgroups launched */
+    int64_t lds_bytes;       /* per workgroup */
+    int64_t workspace_bytes; /* caller-provided scratch the run needs */
+    int64_t mfma_per_wave_kstep; /* MFMA instructions per wave per K step */
+} lt_gemm_plan_info;
+
+/* Validate and plan without launching. Checks: dtypes (A, B fp16 or bf16
+ * alike; C and D of one 16-bit type), shapes (A (M,K), B (K,N), C/D (M,N)),
+ * each mode a single stride, a stride-1 mode per operand, 16-byte aligned
+ * bases and other strides a multiple of 8 elements (LT_ERR_MISALIGNED_OPERAND),
+ * D not overlapping A or B (D may equal C). C may be NULL when beta == 0
+ * (pass beta_nonzero = 0). */
+lt_status lt_gemm_plan(const lt_tensor* A, const lt_tensor* B, const lt_tensor* C, const lt_tensor* D,
+                       int32_t beta_nonzero, const lt_gemm_options* opt, lt_gemm_plan_info* info);
+
+/* CUTLASS-style split of the same check [P3 "A complete Hopper GEMM with the
+ * builder API"]: can_implement, then the workspace size the run needs. */
+lt_status lt_gemm_can_implement(const lt_tensor* A, const lt_tensor* B, const lt_tensor* C,
+                                const lt_tensor* D, int32_t beta_nonzero, const lt_gemm_options* opt);
+lt_status lt_gemm_workspace_size(const lt_tensor* A, const lt_tensor* B, const lt_tensor* C,
+                                 const lt_tensor* D, int32_t beta_nonzero, const lt_gemm_options* opt,
+                                 size_t* bytes);
+
+/* D = alpha * A*B + beta * C [P3 "The problem CUTLASS solves"], fp32
+ * accumulation, fp32 epilogue, output rounded to nearest even. beta == 0
+ * never reads C (C may be NULL). M == 0 or N == 0 does nothing; K == 0 gives
+ * D = beta*C. `workspace` is caller-owned device memory of at least the
+ * planned workspace_bytes (may be NULL when that is 0). Asynchronous on
+ * `stream`. */
+lt_status lt_gemm_run(const lt_tensor* A, const lt_tensor* B, const lt_tensor* C, const lt_tensor* D,
+                      float alpha, float beta, const lt_gemm_options* opt, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+/* Library version string. */
+const char* lt_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LT_H_ */

@@ -1,0 +1,387 @@
+// GEMM entry points: operand validation, planning and launch.
+//
+// The host API shape (validate, size the workspace, run, all with status
+// codes) follows "CUTLASS, in depth", "A complete Hopper GEMM with the
+// builder API"; the alignment and architecture refusals follow "CUTLASS and
+// CuTe layouts", "Pitfalls". Operands are tensors (pointer + layout) and are
+// classified by their stride-1 mode ("Layouts as Algebra: CUTLASS & CuTe",
+// "One notation, and no more transposes"). The block tile grid is the
+// tile-index mode of zipped_divide(D, tile) ("CUTLASS and CuTe layouts", "A
+// layout is a shape and a stride").
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstring>
+
+#include "gemm_kernels.hpp"
+#include "layout_host.hpp"
+#include "lt.h"
+
+namespace lt {
+
+lt_status ensure_device();   // device.hip
+
+namespace {
+
+// One rank-2 operand reduced to (extent, stride) per mode.
+struct Mat {
+    const void* ptr = nullptr;
+    int dtype = 0;
+    int64_t e0 = 0, e1 = 0;   // extents
+    int64_t s0 = 0, s1 = 0;   // strides
+    int64_t footprint = 0;    // cosize in elements
+};
+
+// A mode must coalesce to one leaf (or have extent 1).
+lt_status mode_single(const Tree& m, int64_t* ext, int64_t* stride) {
+    int64_t n;
+    lt_status st = tree_size(m, &n);
+    if (st != LT_OK) return st;
+    if (n == 0) {   // an empty mode: its strides are never used
+        *ext = 0;
+        *stride = 0;
+        return LT_OK;
+    }
+    Tree c = coalesce(m);
+    if (c.s.size() != 1) return LT_ERR_UNSUPPORTED;
+    *ext = c.s[0];
+    *stride = c.s[0] == 1 ? 0 : c.d[0];
+    return LT_OK;
+}
+
+lt_status read_mat(const lt_tensor* t, bool need_ptr, Mat* out) {
+    if (!t) return LT_ERR_INVALID_ARGUMENT;
+    if (t->dtype != LT_F16 && t->dtype != LT_BF16) return LT_ERR_UNSUPPORTED;
+    Tree tr;
+    lt_status st = from_pod(&t->layout, &tr);
+    if (st != LT_OK) return st;
+    if (tr.rank() != 2) return LT_ERR_INVALID_ARGUMENT;
+    std::vector<Tree> ms = tr.modes();
+    Mat m;
+    st = mode_single(ms[0], &m.e0, &m.s0);
+    if (st != LT_OK) return st;
+    st = mode_single(ms[1], &m.e1, &m.s1);
+    if (st != LT_OK) return st;
+    st = tree_cosize(tr, &m.footprint);
+    if (st != LT_OK) return st;
+    m.ptr = t->ptr;
+    m.dtype = t->dtype;
+    if (need_ptr && !m.ptr && m.e0 * m.e1 > 0) return LT_ERR_INVALID_ARGUMENT;
+    *out = m;
+    return LT_OK;
+}
+
+// Stride-1 mode of an operand: 0 or 1, or -1 if neither. A mode of extent 1
+// is contiguous trivially.
+int unit_mode(const Mat& m) {
+    if (m.e1 > 1 && m.s1 == 1) return 1;
+    if (m.e0 > 1 && m.s0 == 1) return 0;
+    if (m.e1 <= 1) return 1;
+    if (m.e0 <= 1) return 0;
+    return -1;
+}
+
+// 128-bit access of 16-bit elements: 16-byte aligned base and the non-unit
+// stride a multiple of 8 elements ("CUTLASS and CuTe layouts", "Pitfalls";
+// "CUTLASS, in depth", "Failure modes").
+bool aligned(const Mat& m, int unit) {
+    if (reinterpret_cast<uintptr_t>(m.ptr) % 16 != 0) return false;
+    int64_t other = unit == 1 ? m.s0 : m.s1;
+    int64_t other_ext = unit == 1 ? m.e0 : m.e1;
+    return other_ext <= 1 || other % 8 == 0;
+}
+
+bool overlaps(const Mat& x, const Mat& y) {
+    if (!x.ptr || !y.ptr || x.footprint == 0 || y.footprint == 0) return false;
+    auto a0 = reinterpret_cast<uintptr_t>(x.ptr), a1 = a0 + 2 * x.footprint;
+    auto b0 = reinterpret_cast<uintptr_t>(y.ptr), b1 = b0 + 2 * y.footprint;
+    return a0 < b1 && b0 < a1;
+}
+
+struct Plan {
+    lt_gemm_plan_info info;
+    bool empty = false;          // M == 0 or N == 0
+    bool transposed = false;     // solved as D^T = B^T A^T
+    Mat A, B, C, D;              // after the transposition, if any
+    int64_t M = 0, N = 0, K = 0;
+    bool a_k = false, b_k = false;
+};
+
+void transpose(Mat* m) {
+    std::swap(m->e0, m->e1);
+    std::swap(m->s0, m->s1);
+}
+
+lt_status make_plan(const lt_tensor* tA, const lt_tensor* tB, const lt_tensor* tC, const lt_tensor* tD,
+                    int beta_nonzero, const lt_gemm_options* opt, Plan* plan) {
+    Plan p;
+    std::memset(&p.info, 0, sizeof(p.info));
+    lt_status st;
+    if ((st = read_mat(tA, true, &p.A)) != LT_OK) return st;
+    if ((st = read_mat(tB, true, &p.B)) != LT_OK) return st;
+    if ((st = read_mat(tD, true, &p.D)) != LT_OK) return st;
+    if (beta_nonzero) {
+        if (!tC) return LT_ERR_INVALID_ARGUMENT;
+        if ((st = read_mat(tC, true, &p.C)) != LT_OK) return st;
+    }
+    if (p.A.dtype != p.B.dtype) return LT_ERR_UNSUPPORTED;
+    if (beta_nonzero && p.C.dtype != p.D.dtype) return LT_ERR_UNSUPPORTED;
+    if (p.D.dtype != p.A.dtype) return LT_ERR_UNSUPPORTED;
+    // shapes: A (M,K), B (K,N), C/D (M,N)
+    p.M = p.A.e0;
+    p.K = p.A.e1;
+    p.N = p.B.e1;
+    if (p.B.e0 != p.K || p.D.e0 != p.M || p.D.e1 != p.N) return LT_ERR_INVALID_ARGUMENT;
+    if (beta_nonzero && (p.C.e0 != p.M || p.C.e1 != p.N)) return LT_ERR_INVALID_ARGUMENT;
+    if (p.M > INT32_MAX || p.N > INT32_MAX || p.K > INT32_MAX) return LT_ERR_OUT_OF_RANGE;
+
+    // stride-1 modes and alignment
+    const int ua = unit_mode(p.A), ub = unit_mode(p.B), ud = unit_mode(p.D);
+    const int uc = beta_nonzero ? unit_mode(p.C) : 1;
+    if (ua < 0 || ub < 0 || ud < 0 || uc < 0) return LT_ERR_UNSUPPORTED;
+    if (!aligned(p.A, ua) || !aligned(p.B, ub) || !aligned(p.D, ud) || (beta_nonzero && !aligned(p.C, uc)))
+        return LT_ERR_MISALIGNED_OPERAND;
+    // D may be C exactly, never a partial overlap; never A or B.
+    if (overlaps(p.D, p.A) || overlaps(p.D, p.B)) return LT_ERR_INVALID_ARGUMENT;
+    if (beta_nonzero && overlaps(p.D, p.C) &&
+        !(p.D.ptr == p.C.ptr && p.D.s0 == p.C.s0 && p.D.s1 == p.C.s1))
+        return LT_ERR_INVALID_ARGUMENT;
+
+    if (p.M == 0 || p.N == 0) {
+        p.empty = true;
+        *plan = p;
+        return LT_OK;
+    }
+
+    // An M-major D is solved as D^T = B^T A^T: a transpose is a stride swap,
+    // so the kernels only ever see an N-major output.
+    if (ud == 0 && p.D.e1 != 1) {
+        p.transposed = true;
+        Mat a = p.A, b = p.B;
+        p.A = b;
+        transpose(&p.A);
+        p.B = a;
+        transpose(&p.B);
+        transpose(&p.D);
+        if (beta_nonzero) transpose(&p.C);
+        std::swap(p.M, p.N);
+    }
+    p.a_k = p.A.e1 == 1 || p.A.s1 == 1;   // K-major A
+    p.b_k = p.B.e0 == 1 || p.B.s0 == 1;   // K-major B
+    const bool d_n = p.D.e1 == 1 || p.D.s1 == 1;
+    const bool c_n = !beta_nonzero || p.C.e1 == 1 || p.C.s1 == 1;
+
+    int kernel = opt ? opt->kernel : LT_KERNEL_AUTO;
+    const bool tiled_ok = p.M % 256 == 0 && p.N % 256 == 0 && p.K % 64 == 0 && p.K > 0 && p.a_k && p.b_k &&
+                          d_n && c_n;
+    int split = (opt && opt->split_k > 0) ? opt->split_k : 0;
+    auto skinny_ok_for = [&](int s) {
+        if (!(p.M <= 32 && p.a_k && p.b_k && d_n && c_n && p.N % kSkinnyBN == 0 && s >= 1)) return false;
+        const int64_t per = (int64_t)s * kSkinnyWaves * 64;
+        return p.K > 0 && p.K % per == 0;
+    };
+    if (kernel == LT_KERNEL_AUTO) {
+        if (p.M <= 32 && skinny_ok_for(1)) {
+            kernel = LT_KERNEL_SKINNY;
+        } else if (tiled_ok) {
+            kernel = LT_KERNEL_TILED;
+        } else {
+            kernel = LT_KERNEL_WAVE16;
+        }
+    }
+    lt_gemm_plan_info& in = p.info;
+    in.kernel = kernel;
+    in.a_kmajor = p.a_k;
+    in.b_kmajor = p.b_k;
+    in.d_nmajor = 1;
+    in.split_k = 1;
+    switch (kernel) {
+        case LT_KERNEL_WAVE16: {
+            if (opt && ((opt->tile_m && opt->tile_m != 16) || (opt->tile_n && opt->tile_n != 16)))
+                return LT_ERR_UNSUPPORTED;
+            in.tile_m = in.tile_n = 16;
+            in.tile_k = 32;
+            in.wave_m = in.wave_n = 16;
+            in.waves = 4;
+            in.stages = 0;
+            const int64_t tiles = ((p.M + 15) / 16) * ((p.N + 15) / 16);
+            in.grid = (tiles + 3) / 4;
+            in.lds_bytes = 0;
+            in.mfma_per_wave_kstep = 1;   // one 16x16x32 per 32-deep K step
+            break;
+        }
+        case LT_KERNEL_TILED: {
+            if (!tiled_ok) return p.a_k && p.b_k ? LT_ERR_NOT_DIVISIBLE : LT_ERR_UNSUPPORTED;
+            if (opt && ((opt->tile_m && opt->tile_m != 256) || (opt->tile_n && opt->tile_n != 256)))
+                return LT_ERR_UNSUPPORTED;
+            in.tile_m = in.tile_n = 256;
+            in.tile_k = 64;
+            in.wave_m = in.wave_n = 128;
+            in.waves = 4;
+            in.stages = 2;
+            in.lds_bytes = kTiledLdsBytes;
+            if (in.lds_bytes > 160 * 1024) return LT_ERR_LDS_OVERFLOW;
+            in.grid = (p.M / 256) * (p.N / 256);
+            // (128/32) * (128/32) * (64/16): the analogue of counting mma per
+            // warp per K slice ("CUTLASS and CuTe layouts", "The arch tag is not
+            // one instruction")
+            in.mfma_per_wave_kstep = (128 / 32) * (128 / 32) * (64 / 16);
+            break;
+        }
+        case LT_KERNEL_SKINNY: {
+            if (split == 0) {
+                // enough workgroups to cover the 256 CUs, if K allows
+                split = 1;
+                const int64_t wgs = p.N / kSkinnyBN;
+                while (wgs * split < 256 && skinny_ok_for(split * 2)) split *= 2;
+            }
+            if (!skinny_ok_for(split)) return LT_ERR_NOT_DIVISIBLE;
+            in.tile_m = 32;
+            in.tile_n = kSkinnyBN;
+            in.tile_k = static_cast<int32_t>(p.K / split);
+            in.wave_m = 32;
+            in.wave_n = kSkinnyBN;
+            in.waves = kSkinnyWaves;
+            in.stages = 0;
+            in.split_k = split;
+            in.grid = (p.N / kSkinnyBN) * split;
+            in.lds_bytes = (kSkinnyWaves - 1) * 16 * 64 * 4;
+            in.workspace_bytes = split > 1 ? (int64_t)split * 32 * p.N * 4 : 0;
+            in.mfma_per_wave_kstep = 4;   // one 32x32x16 per 16 of a 64-deep K block
+            break;
+        }
+        default:
+            return LT_ERR_INVALID_ARGUMENT;
+    }
+    *plan = p;
+    return LT_OK;
+}
+
+}  // namespace
+}  // namespace lt
+
+extern "C" {
+
+lt_status lt_gemm_plan(const lt_tensor* A, const lt_tensor* B, const lt_tensor* C, const lt_tensor* D,
+                       int32_t beta_nonzero, const lt_gemm_options* opt, lt_gemm_plan_info* info) {
+    lt::Plan p;
+    lt_status st = lt::make_plan(A, B, C, D, beta_nonzero, opt, &p);
+    if (st != LT_OK) return st;
+    if (info) *info = p.info;
+    return LT_OK;
+}
+
+lt_status lt_gemm_can_implement(const lt_tensor* A, const lt_tensor* B, const lt_tensor* C, const lt_tensor* D,
+                                int32_t beta_nonzero, const lt_gemm_options* opt) {
+    lt::Plan p;
+    return lt::make_plan(A, B, C, D, beta_nonzero, opt, &p);
+}
+
+lt_status lt_gemm_workspace_size(const lt_tensor* A, const lt_tensor* B, const lt_tensor* C, const lt_tensor* D,
+                                 int32_t beta_nonzero, const lt_gemm_options* opt, size_t* bytes) {
+    if (!bytes) return LT_ERR_INVALID_ARGUMENT;
+    lt::Plan p;
+    lt_status st = lt::make_plan(A, B, C, D, beta_nonzero, opt, &p);
+    if (st != LT_OK) return st;
+    *bytes = static_cast<size_t>(p.info.workspace_bytes);
+    return LT_OK;
+}
+
+lt_status lt_gemm_run(const lt_tensor* A, const lt_tensor* B, const lt_tensor* C, const lt_tensor* D, float alpha,
+                      float beta, const lt_gemm_options* opt, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+    lt::Plan p;
+    const int bnz = beta != 0.0f;
+    lt_status st = lt::make_plan(A, B, C, D, bnz, opt, &p);
+    if (st != LT_OK) return st;
+    if (p.empty) return LT_OK;
+    if ((size_t)p.info.workspace_bytes > workspace_bytes || (p.info.workspace_bytes > 0 && !workspace))
+        return LT_ERR_WORKSPACE;
+    st = lt::ensure_device();
+    if (st != LT_OK) return st;
+    const int dt = p.A.dtype;
+    const uint16_t* cptr = bnz ? static_cast<const uint16_t*>(p.C.ptr) : nullptr;
+    int err = 0;
+    switch (p.info.kernel) {
+        case LT_KERNEL_WAVE16: {
+            lt::Wave16Args a;
+            a.A = static_cast<const uint16_t*>(p.A.ptr);
+            a.B = static_cast<const uint16_t*>(p.B.ptr);
+            a.C = cptr;
+            a.D = static_cast<uint16_t*>(const_cast<void*>(p.D.ptr));
+            a.sam = p.A.s0;
+            a.sak = p.A.e1 == 1 ? 1 : p.A.s1;
+            a.sbk = p.B.e0 == 1 ? 1 : p.B.s0;
+            a.sbn = p.B.s1;
+            a.scm = bnz ? p.C.s0 : 0;
+            a.scn = bnz ? (p.C.e1 == 1 ? 1 : p.C.s1) : 0;
+            a.sdm = p.D.s0;
+            a.sdn = p.D.e1 == 1 ? 1 : p.D.s1;
+            a.M = (int)p.M;
+            a.N = (int)p.N;
+            a.K = (int)p.K;
+            a.alpha = alpha;
+            a.beta = beta;
+            a.tiles_m = (int)((p.M + 15) / 16);
+            a.tiles_n = (int)((p.N + 15) / 16);
+            err = lt::launch_wave16(dt, a, stream);
+            break;
+        }
+        case LT_KERNEL_TILED: {
+            lt::TiledArgs a;
+            a.A = static_cast<const uint16_t*>(p.A.ptr);
+            a.B = static_cast<const uint16_t*>(p.B.ptr);
+            a.C = cptr;
+            a.D = static_cast<uint16_t*>(const_cast<void*>(p.D.ptr));
+            a.lda = p.A.s0;
+            a.ldb = p.B.s1;
+            a.ldc = bnz ? p.C.s0 : 0;
+            a.ldd = p.D.s0;
+            a.M = (int)p.M;
+            a.N = (int)p.N;
+            a.K = (int)p.K;
+            a.alpha = alpha;
+            a.beta = beta;
+            // The tile grid: mode 1 of zipped_divide(D, (256,256)).
+            lt::Tree dl = lt::Tree::tuple({lt::Tree::leaf(p.M, p.D.s0), lt::Tree::leaf(p.N, 1)});
+            const int64_t tiler[2] = {256, 256};
+            lt::Tree zd;
+            st = lt::divide_shape(dl, 2, tiler, true, &zd);
+            if (st != LT_OK) return st;
+            lt::Tree grid = zd.mode(1);
+            a.tiles_m = (int)grid.s[0];
+            a.tiles_n = (int)grid.s[1];
+            a.group_m = std::min(a.tiles_m, 8);
+            a.xcd_remap = (a.tiles_m * a.tiles_n) % 8 == 0 ? 1 : 0;
+            err = lt::launch_tiled(dt, p.a_k, p.b_k, a, stream);
+            break;
+        }
+        case LT_KERNEL_SKINNY: {
+            lt::SkinnyArgs a;
+            a.A = static_cast<const uint16_t*>(p.A.ptr);
+            a.B = static_cast<const uint16_t*>(p.B.ptr);
+            a.C = cptr;
+            a.D = static_cast<uint16_t*>(const_cast<void*>(p.D.ptr));
+            a.ws = static_cast<float*>(workspace);
+            a.lda = p.A.e0 == 1 ? 0 : p.A.s0;
+            a.ldb = p.B.s1;
+            a.ldc = bnz ? p.C.s0 : 0;
+            a.ldd = p.D.s0;
+            a.M = (int)p.M;
+            a.N = (int)p.N;
+            a.K = (int)p.K;
+            a.alpha = alpha;
+            a.beta = beta;
+            a.split_k = p.info.split_k;
+            a.k_per_wave = (int)(p.K / ((int64_t)a.split_k * lt::kSkinnyWaves));
+            err = lt::launch_skinny(dt, a, stream);
+            break;
+        }
+        default:
+            return LT_ERR_INVALID_ARGUMENT;
+    }
+    return err == 0 ? LT_OK : LT_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,62 @@
+// Launch interface between the host planner (gemm.cpp) and the HIP kernels
+// (gemm_kernels.hip). Internal; not part of the public ABI.
+#pragma once
+
+#include <cstdint>
+
+namespace lt {
+
+// Generic wave-per-16x16-tile kernel: any strides, ragged M/N/K.
+struct Wave16Args {
+    const uint16_t* A;
+    const uint16_t* B;
+    const uint16_t* C;
+    uint16_t* D;
+    int64_t sam, sak;   // A(m,k) at m*sam + k*sak
+    int64_t sbk, sbn;   // B(k,n) at k*sbk + n*sbn
+    int64_t scm, scn;   // C(m,n)
+    int64_t sdm, sdn;   // D(m,n)
+    int M, N, K;
+    float alpha, beta;
+    int tiles_m, tiles_n;   // tile grid: mode 1 of zipped_divide(D, (16,16)), colex
+};
+
+// 256x256x64 block-tiled kernel. A is K-major or M-major, B is K-major or
+// N-major, D and C are N-major. M, N multiples of 256, K of 64.
+struct TiledArgs {
+    const uint16_t* A;
+    const uint16_t* B;
+    const uint16_t* C;
+    uint16_t* D;
+    int64_t lda, ldb, ldc, ldd;   // the non-unit stride of each operand
+    int M, N, K;
+    float alpha, beta;
+    int tiles_m, tiles_n;
+    int group_m;                  // tile rows per raster group
+    int xcd_remap;                // 1: spread consecutive tiles over one XCD
+};
+
+// Skinny kernel: M <= 32, K-major A and B, N-major D; B streamed once.
+struct SkinnyArgs {
+    const uint16_t* A;
+    const uint16_t* B;
+    const uint16_t* C;
+    uint16_t* D;
+    float* ws;                    // split_k > 1: fp32 partials [split_k][32][N]
+    int64_t lda, ldb, ldc, ldd;
+    int M, N, K;
+    float alpha, beta;
+    int split_k;
+    int k_per_wave;               // K elements per wave (multiple of 64)
+};
+
+constexpr int kSkinnyWaves = 8;
+constexpr int kSkinnyBN = 32;
+constexpr int kTiledLdsBytes = 2 * 2 * 256 * 64 * 2;   // 2 stages x (A + B) x 256x64 x 16 bit
+
+// Each returns 0 on success or the hipError_t of the launch.
+int launch_wave16(int dtype, const Wave16Args& a, void* stream);
+int launch_tiled(int dtype, bool a_kmajor, bool b_kmajor, const TiledArgs& a, void* stream);
+int launch_skinny(int dtype, const SkinnyArgs& a, void* stream);
+
+}  // namespace lt

@@ -1,0 +1,111 @@
+"""GEMM and device layout maps on torch-allocated device memory.
+
+Marshalling only: tensors are turned into (pointer, dtype, layout) and handed
+to the C ABI; every step of the computation runs in the library's kernels.
+PyTorch provides device memory and the current stream.
+"""
+
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Union
+
+import torch
+
+from . import _lib as L
+from .layout import Layout
+
+_DT = {torch.float16: L.LT_F16, torch.bfloat16: L.LT_BF16}
+KERNELS = {"auto": L.LT_KERNEL_AUTO, "wave16": L.LT_KERNEL_WAVE16, "tiled": L.LT_KERNEL_TILED,
+           "skinny": L.LT_KERNEL_SKINNY}
+KERNEL_NAMES = {v: k for k, v in KERNELS.items()}
+
+
+def tensor_desc(t: torch.Tensor, layout: Optional[Layout] = None) -> L.lt_tensor:
+    """(pointer, dtype, layout) of a tensor; the layout defaults to the view's
+    own shape and strides. With an explicit layout, ``t`` is the storage and
+    the layout addresses it from ``t.data_ptr()``."""
+    if t.dtype not in _DT:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    if layout is None:
+        layout = Layout.make(list(t.shape), list(t.stride()))
+    d = L.lt_tensor()
+    d.ptr = t.data_ptr()
+    d.dtype = _DT[t.dtype]
+    d.layout = layout.c
+    return d
+
+
+def _opts(kernel: Union[str, int], tile=None, split_k: int = 0) -> L.lt_gemm_options:
+    o = L.lt_gemm_options()
+    o.kernel = KERNELS[kernel] if isinstance(kernel, str) else int(kernel)
+    o.tile_m, o.tile_n = tile if tile else (0, 0)
+    o.split_k = split_k
+    return o
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def plan(A, B, D, C=None, beta: float = 0.0, kernel="auto", tile=None, split_k=0, layouts=None) -> dict:
+    la = layouts or {}
+    dA, dB, dD = tensor_desc(A, la.get("A")), tensor_desc(B, la.get("B")), tensor_desc(D, la.get("D"))
+    dC = tensor_desc(C, la.get("C")) if C is not None else None
+    info = L.lt_gemm_plan_info()
+    o = _opts(kernel, tile, split_k)
+    L.check(L.lib().lt_gemm_plan(ctypes.byref(dA), ctypes.byref(dB), ctypes.byref(dC) if dC else None,
+                                 ctypes.byref(dD), int(beta != 0.0), ctypes.byref(o), ctypes.byref(info)),
+            "gemm_plan")
+    r = info.as_dict()
+    r["kernel_name"] = KERNEL_NAMES.get(r["kernel"], "?")
+    return r
+
+
+def gemm(A: torch.Tensor, B: torch.Tensor, D: torch.Tensor, C: Optional[torch.Tensor] = None,
+         alpha: float = 1.0, beta: float = 0.0, *, kernel="auto", tile=None, split_k: int = 0,
+         layouts: Optional[dict] = None, workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """D = alpha * A @ B + beta * C (asynchronous on ``stream``)."""
+    la = layouts or {}
+    dA, dB, dD = tensor_desc(A, la.get("A")), tensor_desc(B, la.get("B")), tensor_desc(D, la.get("D"))
+    dC = tensor_desc(C, la.get("C")) if C is not None else None
+    o = _opts(kernel, tile, split_k)
+    ws_ptr, ws_bytes = None, 0
+    need = ctypes.c_size_t(0)
+    L.check(L.lib().lt_gemm_workspace_size(ctypes.byref(dA), ctypes.byref(dB), ctypes.byref(dC) if dC else None,
+                                           ctypes.byref(dD), int(beta != 0.0), ctypes.byref(o),
+                                           ctypes.byref(need)), "gemm_workspace_size")
+    if need.value:
+        if workspace is None:
+            workspace = torch.empty(need.value, dtype=torch.uint8, device=D.device)
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    L.check(L.lib().lt_gemm_run(ctypes.byref(dA), ctypes.byref(dB), ctypes.byref(dC) if dC else None,
+                                ctypes.byref(dD), float(alpha), float(beta), ctypes.byref(o), ws_ptr, ws_bytes,
+                                _stream(stream)), "gemm_run")
+
+
+def layout_eval_device(layout: Layout, out: torch.Tensor, n: Optional[int] = None, stream=None) -> None:
+    """out[x] = layout(x) for x < n (int64 device tensor)."""
+    assert out.dtype == torch.int64 and out.is_contiguous()
+    n = out.numel() if n is None else n
+    L.check(L.lib().lt_layout_eval_device(ctypes.byref(layout.c), out.data_ptr(), n, _stream(stream)),
+            "layout_eval_device")
+
+
+def gather_device(layout: Layout, src: torch.Tensor, dst: torch.Tensor, n: Optional[int] = None,
+                  stream=None) -> None:
+    """dst[x] = src[layout(x)] for x < n."""
+    assert src.dtype == dst.dtype and dst.is_contiguous()
+    n = dst.numel() if n is None else n
+    L.check(L.lib().lt_gather_device(ctypes.byref(layout.c), src.data_ptr(), dst.data_ptr(), src.element_size(),
+                                     n, _stream(stream)), "gather_device")
+
+
+def device_check() -> str:
+    buf = ctypes.create_string_buffer(64)
+    L.check(L.lib().lt_device_check(buf, 64), "device_check")
+    return buf.value.decode()

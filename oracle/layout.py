@@ -95,8 +95,8 @@ class Layout:
         if not congruent(self.shape, self.stride):
             raise ValueError(f"shape {self.shape} and stride {self.stride} are not congruent")
         for s in flatten(self.shape):
-            if not isinstance(s, int) or s < 1:
-                raise ValueError(f"extent {s!r} must be an int >= 1")
+            if not isinstance(s, int) or s < 0:
+                raise ValueError(f"extent {s!r} must be an int >= 0")
         for d in flatten(self.stride):
             if not isinstance(d, int) or d < 0:
                 raise ValueError(f"stride {d!r} must be an int >= 0 (READING: negatives rejected)")
@@ -175,8 +175,18 @@ def enumerate_offsets(L: Layout) -> List[int]:
 
 def cosize(L: Layout) -> int:
     """Largest offset reached, plus one: the memory footprint (3.5 CUTLASS II,
-    3.5.5). Computed by enumeration, the definition itself."""
-    return max(enumerate_offsets(L)) + 1
+    3.5.5). Computed by enumeration, the definition itself. READING: a layout
+    with an extent of 0 has no coordinates, size 0 and cosize 0."""
+    offs = enumerate_offsets(L)
+    return max(offs) + 1 if offs else 0
+
+
+def _nonempty(*Ls: Layout):
+    """READING: the algebra (coalesce, composition, complement, divides) is
+    defined here for layouts with at least one coordinate."""
+    for L in Ls:
+        if size(L) == 0:
+            raise ValueError("empty layout")
 
 
 # --------------------------------------------------------------------------
@@ -273,6 +283,7 @@ def coalesce(L: Layout) -> Layout:
     neighbour s0:d0 whenever d1 == s0*d0 ("Layouts as Algebra", "A shape is a
     tree"; 3.5 CUTLASS II, 3.5.6). READING: if nothing is left the result is
     1:0."""
+    _nonempty(L)
     pairs = [(s, d) for s, d in zip(flatten(L.shape), flatten(L.stride)) if s != 1]
     out: List[Tuple[int, int]] = []
     for s, d in pairs:
@@ -349,6 +360,7 @@ def _compose_leaf(a_leaves: List[Tuple[int, int]], s: int, d: int) -> List[Tuple
 def compose(A: Layout, B: Layout) -> Layout:
     """A o B as a layout with B's mode tree: each leaf of B becomes a mode of
     the result (a tuple if the walk crossed a boundary of A)."""
+    _nonempty(A, B)
     ac = coalesce(A)
     a_leaves = list(zip(flatten(ac.shape), flatten(ac.stride)))
 
@@ -385,6 +397,9 @@ def complement_translates(B: Layout, M: int) -> List[int]:
     T[0] = 0 such that {t + B(x)} covers [0, M) exactly once. Built greedily:
     take the smallest integer not yet covered. Raises NotAdmissible if no such
     tiling exists. Stride-0 leaves of B are ignored (they add no new image)."""
+    _nonempty(B)
+    if M < 1:
+        raise ValueError("complement needs M >= 1")
     kept = [(s, d) for s, d in zip(flatten(B.shape), flatten(B.stride)) if d > 0]
     image = sorted(enumerate_offsets(_from_leaves(kept))) if kept else [0]
     if len(set(image)) != len(image):
@@ -411,6 +426,9 @@ def complement(B: Layout, M: int) -> Layout:
     stride > 0 and extent > 1 sorted by stride; the gaps between consecutive
     strides become the complement's leaves, and a last leaf runs to M. The
     result is coalesced. Agrees with complement_translates (tested)."""
+    _nonempty(B)
+    if M < 1:
+        raise ValueError("complement needs M >= 1")
     pairs = sorted((d, s) for s, d in zip(flatten(B.shape), flatten(B.stride)) if d > 0 and s > 1)
     out: List[Tuple[int, int]] = []
     cur = 1
@@ -452,6 +470,7 @@ def logical_divide(A: Layout, tiler: Tiler) -> Layout:
         parts += [A.mode(i) for i in range(len(tiler), A.rank)]
         return make_tuple_layout(*parts)
     B = _tiler_layout(tiler)
+    _nonempty(A, B)
     n = size(A)
     if n % size(B) != 0:
         raise NotDivisible(f"tile of size {size(B)} does not divide {n}")

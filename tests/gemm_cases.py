@@ -1,0 +1,74 @@
+"""Shared helpers of the GEMM parity tests and the smoke check: build a seeded
+case, run it through the C-ABI library on the GPU, and compare with the
+oracle element by element (all outputs, or sampled outputs at full size)."""
+
+from __future__ import annotations
+
+import sys
+from typing import Optional
+
+import numpy as np
+import torch
+
+import datagen
+from oracle import gemm as og
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def op(m: datagen.Matrix) -> og.Operand:
+    return og.Operand(m.store, m.shape, m.stride)
+
+
+def sample_points(M: int, N: int, n: int, seed: int) -> np.ndarray:
+    """Corner and edge outputs plus n uniform random ones."""
+    rng = np.random.default_rng(seed)
+    pts = [(0, 0), (0, N - 1), (M - 1, 0), (M - 1, N - 1)]
+    pts += [(i, j) for i in (0, M - 1) for j in range(0, N, max(1, N // 64))]
+    pts += [(i, j) for j in (0, N - 1) for i in range(0, M, max(1, M // 64))]
+    r = np.stack([rng.integers(0, M, n), rng.integers(0, N, n)], axis=1)
+    return np.concatenate([np.array(pts, dtype=np.int64), r.astype(np.int64)])
+
+
+def all_points(M: int, N: int) -> np.ndarray:
+    i, j = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
+    return np.stack([i.reshape(-1), j.reshape(-1)], axis=1).astype(np.int64)
+
+
+def run_and_check(A: datagen.Matrix, B: datagen.Matrix, C: Optional[datagen.Matrix], D: datagen.Matrix,
+                  alpha: float, beta: float, points: Optional[np.ndarray] = None, kernel="auto",
+                  split_k: int = 0, expect_kernel: Optional[str] = None, label: str = ""):
+    """Run D = alpha*A*B + beta*C on cuda:0 through the library and check the
+    result against the oracle. Returns (CheckResult, plan dict)."""
+    from layout_algebra_tiled_amd import gemm as g
+    from layout_algebra_tiled_amd.layout import Layout
+
+    M, N = D.shape
+    say(f"[gemm] {label} M={M} N={N} K={A.shape[1]} {A.dtype} A{A.stride} B{B.stride} D{D.stride} "
+        f"alpha={alpha} beta={beta} kernel={kernel}")
+    dev = torch.device("cuda:0")
+    dA, dB, dD = A.to(dev), B.to(dev), D.to(dev)
+    dC = C.to(dev) if C is not None else None
+    dD.store.fill_(float("nan"))   # an output the kernel never writes fails the check
+    lay = {"A": Layout.make(list(A.shape), list(A.stride)), "B": Layout.make(list(B.shape), list(B.stride)),
+           "D": Layout.make(list(D.shape), list(D.stride))}
+    if C is not None:
+        lay["C"] = Layout.make(list(C.shape), list(C.stride))
+    plan = g.plan(dA.store, dB.store, dD.store, dC.store if dC is not None else None, beta, kernel=kernel,
+                  split_k=split_k, layouts=lay)
+    if expect_kernel:
+        assert plan["kernel_name"] == expect_kernel, plan
+    g.gemm(dA.store, dB.store, dD.store, dC.store if dC is not None else None, alpha, beta, kernel=kernel,
+           split_k=split_k, layouts=lay)
+    torch.cuda.synchronize()
+    out = datagen.Matrix(dD.store.cpu(), D.shape, D.stride)
+    if points is None:
+        points = all_points(M, N)
+    S, T = og.gemm_points(op(A), op(B), points)
+    Dref, Cabs = og.epilogue(S, op(C) if C is not None else None, points, alpha, beta)
+    got = og.read_points(op(out), points)
+    res = og.check(got, Dref, T, Cabs, alpha, A.dtype)
+    say(f"[gemm] {label} {plan['kernel_name']} grid={plan['grid']} split_k={plan['split_k']}: {res}")
+    return res, plan, out

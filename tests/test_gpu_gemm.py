@@ -1,0 +1,188 @@
+"""GEMM parity on the GPU: the library's kernels against the fp64 oracle,
+element by element, within |D - D_ref| <= 2e-3 (|alpha| sum|a b| + |beta c|)
++ one output ulp. Small cases check every output; the full-size workloads
+check sampled outputs (corners, edges and random points) in the launch
+configuration the benchmark times."""
+
+import numpy as np
+import pytest
+import torch
+
+import datagen
+from tests.gemm_cases import all_points, op, run_and_check, sample_points, say
+from oracle import gemm as og
+
+pytestmark = pytest.mark.gpu
+
+F16, BF16 = torch.float16, torch.bfloat16
+
+
+def _pad8(x):
+    return (x + 7) // 8 * 8
+
+
+def _case(M, N, K, dtype, a_major, b_major, d_major, alpha, beta, dist="uniform", seed=0, lds=None):
+    """Leading dimensions default to the extent rounded up to 8 elements (the
+    128-bit alignment rule); padding holds NaN."""
+    if lds is None:
+        lds = (_pad8(K if a_major == "row" else M), _pad8(N if b_major == "row" else K),
+               _pad8(N if d_major == "row" else M))
+    A = datagen.matrix(M, K, dtype, a_major, dist, seed + 0, ld=lds[0], k_for_scale=K)
+    B = datagen.matrix(K, N, dtype, b_major, dist, seed + 1, ld=lds[1], k_for_scale=K)
+    C = datagen.matrix(M, N, dtype, d_major, "uniform", seed + 2, ld=lds[2]) if beta != 0 else None
+    D = datagen.zeros(M, N, dtype, d_major, ld=lds[2])
+    return A, B, C, D
+
+
+def _ok(res):
+    assert res.ok, str(res)
+
+
+# ---------------------------------------------------------------------------
+# the small workload: 256x128x64 fp16 tiled 16x16 by zipped_divide
+# ---------------------------------------------------------------------------
+
+def test_workload_256x128x64_all_outputs():
+    c = datagen.config(1)
+    A, B, C, D = c.make()
+    res, plan, _ = run_and_check(A, B, None, D, c.alpha, c.beta, expect_kernel="wave16", label="cfg1")
+    _ok(res)
+    assert res.n == 256 * 128 and (plan["tile_m"], plan["tile_n"]) == (16, 16)
+
+
+# ---------------------------------------------------------------------------
+# the 256x256 tiled kernel, every output checked
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("M,N,K,dtype,beta,dist", [
+    (512, 512, 512, F16, 0.5, "uniform"),
+    (512, 768, 1024, BF16, 0.0, "normal_over_sqrtk"),
+    (256, 256, 64, BF16, 1.0, "uniform"),
+    (768, 512, 192, F16, -1.0, "uniform"),
+])
+def test_tiled_all_outputs(M, N, K, dtype, beta, dist):
+    A, B, C, D = _case(M, N, K, dtype, "row", "col", "row", 1.0, beta, dist, seed=100 + K)
+    res, _, _ = run_and_check(A, B, C, D, 1.0, beta, expect_kernel="tiled", label="tiled")
+    _ok(res)
+
+
+def test_tiled_padded_leading_dimensions():
+    """Leading dimensions larger than the extents (padding holds NaN)."""
+    M, N, K = 512, 256, 128
+    A, B, C, D = _case(M, N, K, BF16, "row", "col", "row", 1.0, 0.5, seed=7, lds=(K + 64, K + 8, N + 16))
+    res, _, _ = run_and_check(A, B, C, D, 1.0, 0.5, expect_kernel="tiled", label="tiled-padded")
+    _ok(res)
+
+
+# ---------------------------------------------------------------------------
+# layout variants, ragged shapes, degenerate cases (wave-per-tile kernel)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("a_major,b_major", [("row", "col"), ("col", "row"), ("row", "row"), ("col", "col")])
+@pytest.mark.parametrize("dtype", [F16, BF16])
+def test_any_major_ragged(a_major, b_major, dtype):
+    M, N, K = 250, 130, 72
+    A, B, C, D = _case(M, N, K, dtype, a_major, b_major, "row", 2.0, -1.0, seed=11)
+    res, _, _ = run_and_check(A, B, C, D, 2.0, -1.0, label=f"ragged {a_major}/{b_major}")
+    _ok(res)
+
+
+def test_mn_major_operands_all_outputs():
+    """M-major A and N-major B, alpha=2, beta=-1 (the layout-driven staging case)."""
+    M, N, K = 512, 256, 384
+    A, B, C, D = _case(M, N, K, F16, "col", "row", "row", 2.0, -1.0, seed=21)
+    res, _, _ = run_and_check(A, B, C, D, 2.0, -1.0, label="mn-major")
+    _ok(res)
+
+
+def test_k_tail_not_multiple_of_chunk():
+    """K = 70: the last 8-wide chunk is partial; A's padding columns hold NaN."""
+    M, N, K = 64, 48, 70
+    A, B, C, D = _case(M, N, K, BF16, "row", "col", "row", 1.0, 0.0, seed=31, lds=(72, 72, 48))
+    res, _, _ = run_and_check(A, B, None, D, 1.0, 0.0, label="k-tail")
+    _ok(res)
+
+
+def test_m_major_output_is_solved_transposed():
+    M, N, K = 512, 256, 128
+    A, B, C, D = _case(M, N, K, BF16, "row", "col", "col", 1.0, 0.5, seed=41)
+    res, plan, _ = run_and_check(A, B, C, D, 1.0, 0.5, expect_kernel="tiled", label="d-col-major")
+    _ok(res)
+
+
+def test_in_place_d_is_c():
+    from layout_algebra_tiled_amd import gemm as g
+    M, N, K = 256, 256, 128
+    A, B, C, _ = _case(M, N, K, F16, "row", "col", "row", 1.0, 0.5, seed=51)
+    dA, dB, dC = A.to("cuda"), B.to("cuda"), C.to("cuda")
+    g.gemm(dA.view(), dB.view(), dC.view(), dC.view(), 1.0, 0.5)
+    torch.cuda.synchronize()
+    pts = all_points(M, N)
+    S, T = og.gemm_points(op(A), op(B), pts)
+    Dref, Cabs = og.epilogue(S, op(C), pts, 1.0, 0.5)
+    got = og.read_points(og.Operand(dC.store.cpu(), C.shape, C.stride), pts)
+    _ok(og.check(got, Dref, T, Cabs, 1.0, F16))
+
+
+def test_k_zero_gives_beta_c_and_m_zero_is_noop():
+    from layout_algebra_tiled_amd import gemm as g
+    from layout_algebra_tiled_amd.layout import Layout
+    M, N = 64, 32
+    C = datagen.matrix(M, N, F16, "row", "uniform", 61).to("cuda")
+    D = torch.full((M, N), float("nan"), dtype=F16, device="cuda")
+    a = torch.empty(64, dtype=F16, device="cuda")
+    b = torch.empty(64, dtype=F16, device="cuda")
+    g.gemm(a, b, D, C.view(), 1.0, 0.5,
+           layouts={"A": Layout.make([M, 0], [8, 1]), "B": Layout.make([0, N], [1, 8])})
+    torch.cuda.synchronize()
+    want = (0.5 * C.view().float()).to(F16)
+    assert torch.equal(D.cpu(), want.cpu())
+    E = torch.full((8,), 7.0, dtype=F16, device="cuda")
+    g.gemm(a, b, E, None, 1.0, 0.0, layouts={"A": Layout.make([0, 8], [8, 1]), "B": Layout.make([8, 1], [1, 8]),
+                                           "D": Layout.make([0, 1], [8, 1])})
+    torch.cuda.synchronize()
+    assert torch.all(E.cpu() == 7.0)
+
+
+def test_two_calls_in_a_row_different_sizes():
+    for (M, N, K) in ((512, 512, 256), (256, 256, 64)):
+        A, B, C, D = _case(M, N, K, BF16, "row", "col", "row", 1.0, 0.0, seed=M + K)
+        res, _, _ = run_and_check(A, B, None, D, 1.0, 0.0, label="repeat")
+        _ok(res)
+
+
+# ---------------------------------------------------------------------------
+# skinny (M <= 32) kernel
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("M,N,K,split", [(32, 1024, 4096, 0), (17, 512, 4096, 1), (17, 512, 4096, 2),
+                                         (32, 256, 2048, 4), (1, 64, 512, 1)])
+def test_skinny_all_outputs(M, N, K, split):
+    A, B, C, D = _case(M, N, K, BF16, "row", "col", "row", 1.0, 0.0, dist="normal", seed=71)
+    res, plan, _ = run_and_check(A, B, None, D, 1.0, 0.0, split_k=split, expect_kernel="skinny", label="skinny")
+    _ok(res)
+    if split:
+        assert plan["split_k"] == split
+
+
+def test_skinny_with_beta():
+    A, B, C, D = _case(32, 512, 1024, F16, "row", "col", "row", 0.5, 2.0, seed=81)
+    res, _, _ = run_and_check(A, B, C, D, 0.5, 2.0, expect_kernel="skinny", label="skinny-beta")
+    _ok(res)
+
+
+# ---------------------------------------------------------------------------
+# the full-size workloads, sampled outputs, benchmark launch configuration
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("cfg,kernel", [(2, "tiled"), (3, "tiled"), (4, None), (5, "skinny")])
+def test_full_size_workloads_sampled(cfg, kernel):
+    c = datagen.config(cfg)
+    say(f"[gemm] generating inputs of workload {cfg}: {c.name}")
+    A, B, C, D = c.make()
+    pts = sample_points(c.M, c.N, 4000, seed=cfg)
+    res, plan, out = run_and_check(A, B, C if c.beta != 0 else None, D, c.alpha, c.beta, points=pts,
+                                   expect_kernel=kernel, label=f"cfg{cfg}")
+    _ok(res)
+    # every output finite (cheap full scan)
+    assert torch.isfinite(out.view().float()).all()

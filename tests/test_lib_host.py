@@ -1,0 +1,398 @@
+"""CPU tests of the C-ABI library: it loads and exports every declared
+symbol, its host layout algebra agrees bit-exactly with the oracle, and the
+GEMM planner validates and plans without touching a device."""
+
+import ctypes
+import itertools
+import json
+import os
+import random
+import re
+
+import pytest
+
+from layout_algebra_tiled_amd import Layout, LtError
+from layout_algebra_tiled_amd import _lib as L
+from oracle import layout as ol
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+GOLD = json.load(open(os.path.join(ROOT, "tests", "golden", "layout_pins.json")))
+TILE = json.load(open(os.path.join(ROOT, "tests", "golden", "tile_arithmetic.json")))
+
+
+def O(lay: Layout) -> ol.Layout:
+    """The library's layout as an oracle layout value (same tree, same leaves)."""
+    return ol.Layout(lay.shape, lay.stride)
+
+
+def Lb(x: ol.Layout) -> Layout:
+    return Layout.parse(str(x))
+
+
+def status_of(fn, *a):
+    try:
+        return fn(*a), None
+    except LtError as e:
+        return None, e.name
+    except (ol.NotAdmissible, ol.NotDivisible, IndexError, ValueError) as e:
+        return None, type(e).__name__
+
+
+# ---------------------------------------------------------------------------
+# the library loads and exports the header's functions
+# ---------------------------------------------------------------------------
+
+def test_exports_every_declared_symbol():
+    header = open(os.path.join(ROOT, "include", "lt.h")).read()
+    declared = set(re.findall(r"\b(lt_[a-z_0-9]+)\s*\(", header))
+    assert declared, "no declarations found"
+    lib = L.lib()
+    for name in declared:
+        assert hasattr(lib, name), f"{name} not exported"
+    assert declared == set(L.SIGNATURES), "binding and header disagree"
+    assert b"gfx950" in lib.lt_version()
+
+
+def test_status_strings():
+    for code in L.STATUS_NAMES:
+        assert L.lib().lt_status_string(code)
+
+
+# ---------------------------------------------------------------------------
+# pins through the library
+# ---------------------------------------------------------------------------
+
+def test_pins_through_library():
+    g = GOLD["zipped_divide_256x128"]
+    zd = Layout.parse(g["layout"]).zipped_divide(g["tiler"])
+    assert str(zd) == g["result"]
+    assert str(zd.mode(0)) == g["mode0"] and str(zd.mode(1)) == g["mode1"]
+    (ri, ci), (tr, tc) = g["element_in_tile"], g["element_tile"]
+    assert zd([ri, ci, tr, tc]) == g["element_offset"]          # natural coordinate
+    assert zd([ri + 16 * ci, tr + 16 * tc]) == g["element_offset"]  # per-mode coordinate
+    assert Layout.parse(g["printed_with_static_markers"]) == zd
+    g = GOLD["composition_6x2_4x3"]
+    R = Layout.parse(g["A"]).compose(Layout.parse(g["B"]))
+    assert str(R) == g["R"] and [R(x) for x in range(12)] == g["R_values"]
+    g = GOLD["walkthrough_4x2"]
+    W = Layout.parse(g["layout"])
+    assert W(g["coord"]) == g["offset"] and W.size() == g["size"] and W.cosize() == g["cosize"]
+    g = GOLD["shape_4x3_unravel"]
+    assert Layout.parse(g["layout"])(g["index"]) == g["offset"]
+    g = GOLD["packed_panel"]
+    P = Layout.parse(g["layout"])
+    assert [P(x) for x in range(16)] == g["walk"]
+    for r, c in itertools.product(range(4), range(4)):
+        assert P([r % 2, c % 2, r // 2, c // 2]) == g["matrix"][r][c]
+        assert Layout.parse(g["per_axis_layout"])([r, c]) == g["matrix"][r][c]
+    assert str(Layout.parse(GOLD["costume_24"]["layout"]).coalesce()) == "24:1"
+    assert str(Layout.parse("(2,4):(1,2)").coalesce()) == "8:1"
+    assert str(Layout.parse("(2,4):(4,1)").coalesce()) == "(2,4):(4,1)"
+    assert str(Layout.parse("8:1").logical_divide(4)) == "(4,2):(1,4)"
+    assert str(Layout.parse("(6,4):(1,6)").zipped_divide((3, 2))) == "((3,2),(2,2)):((1,6),(3,12))"
+    assert Layout.parse("(4,4):(5,1)").cosize() == 19
+    assert Layout.parse("(128,32):(33,1)").cosize() == 4223
+    assert str(Layout.colmajor([4, 6])) == "(4,6):(1,4)" and str(Layout.rowmajor([4, 6])) == "(4,6):(6,1)"
+
+
+# ---------------------------------------------------------------------------
+# random layouts: library == oracle
+# ---------------------------------------------------------------------------
+
+def _rand(rng, max_depth=2, max_modes=3, max_extent=4, max_stride=16):
+    def node(depth):
+        if depth < max_depth and rng.random() < 0.35:
+            k = rng.randint(1, 3)
+            parts = [node(depth + 1) for _ in range(k)]
+            return tuple(p[0] for p in parts), tuple(p[1] for p in parts)
+        return rng.randint(1, max_extent), rng.randint(0, max_stride)
+    k = rng.randint(1, max_modes)
+    parts = [node(1) for _ in range(k)]
+    if k == 1 and rng.random() < 0.5:
+        return ol.Layout(parts[0][0], parts[0][1])
+    return ol.Layout(tuple(p[0] for p in parts), tuple(p[1] for p in parts))
+
+
+def test_eval_size_cosize_coalesce_match_oracle():
+    rng = random.Random(10)
+    for _ in range(400):
+        x = _rand(rng)
+        y = Lb(x)
+        assert str(y) == str(x)
+        assert y.shape == x.shape and y.stride == x.stride
+        assert y.size() == ol.size(x) and y.cosize() == ol.cosize(x)
+        assert [y(i) for i in range(ol.size(x))] == ol.enumerate_offsets(x)
+        assert str(y.coalesce()) == str(ol.coalesce(x))
+        for i in range(x.rank):
+            assert str(y.mode(i)) == str(x.mode(i))
+
+
+def test_compose_matches_oracle_including_refusals():
+    rng = random.Random(11)
+    agree = admitted = 0
+    for _ in range(3000):
+        a, b = _rand(rng, max_stride=8), _rand(rng, max_extent=3, max_stride=6)
+        lib_r, lib_e = status_of(lambda: Lb(a).compose(Lb(b)))
+        or_r, or_e = status_of(lambda: ol.compose(a, b))
+        assert (lib_e is None) == (or_e is None), (str(a), str(b), lib_e, or_e)
+        if lib_e is None:
+            admitted += 1
+            assert str(lib_r) == str(or_r), (str(a), str(b))
+        else:
+            assert lib_e == "LT_ERR_NOT_ADMISSIBLE" and or_e == "NotAdmissible"
+        agree += 1
+    assert admitted > 300
+
+
+def test_complement_matches_oracle():
+    for s0, s1 in itertools.product(range(1, 5), repeat=2):
+        for d0, d1 in itertools.product(range(0, 9), repeat=2):
+            b = ol.Layout((s0, s1), (d0, d1))
+            for M in (1, 4, 6, 8, 12, 16, 24, 32):
+                lib_r, lib_e = status_of(lambda: Lb(b).complement(M))
+                or_r, or_e = status_of(lambda: ol.complement(b, M))
+                assert (lib_e is None) == (or_e is None), (str(b), M)
+                if lib_e is None:
+                    assert str(lib_r) == str(or_r)
+
+
+def test_divides_and_tiles_match_oracle():
+    rng = random.Random(12)
+    shapes = [(8, 12), (12, 8), (16, 6), (6, 16), (4, 4), (24, 8)]
+    for _ in range(200):
+        m, n = rng.choice(shapes)
+        major = rng.choice(["row", "col", "pad"])
+        stride = {"row": (n, 1), "col": (1, m), "pad": (n + 3, 1)}[major]
+        a = ol.Layout((m, n), stride)
+        bm = rng.choice([d for d in range(1, m + 1) if m % d == 0])
+        bn = rng.choice([d for d in range(1, n + 1) if n % d == 0])
+        assert str(Lb(a).zipped_divide((bm, bn))) == str(ol.zipped_divide(a, (bm, bn)))
+        assert str(Lb(a).logical_divide((bm, bn))) == str(ol.logical_divide(a, (bm, bn)))
+        tm, tn = rng.randrange(m // bm), rng.randrange(n // bn)
+        off, t = Lb(a).local_tile((bm, bn), (tm, tn))
+        ooff, ot = ol.local_tile(a, (bm, bn), (tm, tn))
+        assert off == ooff and str(t) == str(ot)
+        off, t = Lb(a).local_tile((bm, bn), (tm, None))
+        ooff, ot = ol.local_tile(a, (bm, bn), (tm, None))
+        assert off == ooff and str(t) == str(ot)
+
+
+def test_local_tile_step_projection_matches_oracle():
+    M, N, K = 256, 384, 128
+    mA, mB, mC = ol.make_colmajor((M, K)), ol.make_colmajor((N, K)), ol.make_colmajor((M, N))
+    tiler, coord = (128, 128, 8), (1, 2, None)
+    for lay, step in ((mA, (1, 0, 1)), (mB, (0, 1, 1)), (mC, (1, 1, 0))):
+        off, t = Lb(lay).local_tile(tiler, coord, step)
+        ooff, ot = ol.local_tile(lay, tiler, coord, step)
+        assert off == ooff and str(t) == str(ot)
+
+
+@pytest.mark.parametrize("tile,thr", [("(8,8):(8,1)", "(4,2):(1,4)"), ("(8,8):(8,1)", "(4,2):(2,1)"),
+                                      ("(128,32):(33,1)", "(16,16):(1,16)"), ("(16,8):(1,16)", "(2,4):(1,2)")])
+def test_local_partition_matches_oracle(tile, thr):
+    T, th = ol.parse_layout(tile), ol.parse_layout(thr)
+    for t in range(ol.size(th)):
+        off, lay = Lb(T).local_partition(Lb(th), t)
+        ooff, olay = ol.local_partition(T, th, t)
+        assert off == ooff and str(lay) == str(olay)
+
+
+def test_local_partition_with_step_matches_oracle():
+    sA = ol.Layout((64, 8), (1, 64))       # (BLK_M, BLK_K)
+    tC = ol.Layout((16, 16), (1, 16))      # thread grid (THR_M x THR_N)
+    for t in (0, 1, 17, 255):
+        off, lay = Lb(sA).local_partition(Lb(tC), t, step=(1, 0))
+        ooff, olay = ol.local_partition(sA, tC, t, step=(1, 0))
+        assert off == ooff and str(lay) == str(olay)
+
+
+# ---------------------------------------------------------------------------
+# error statuses
+# ---------------------------------------------------------------------------
+
+def test_error_statuses():
+    def err(fn):
+        with pytest.raises(LtError) as e:
+            fn()
+        return e.value.name
+    assert err(lambda: Layout.parse("(2,3):(1)")) == "LT_ERR_INVALID_LAYOUT"
+    assert err(lambda: Layout.parse("(2,x):(1,2)")) == "LT_ERR_INVALID_ARGUMENT"
+    assert Layout.parse("(2,0):(1,2)").size() == 0   # empty, but valid
+    assert err(lambda: Layout.parse("(4,3):(3,1)")(12)) == "LT_ERR_OUT_OF_RANGE"
+    assert err(lambda: Layout.parse("(4,3):(3,1)")([4, 0])) == "LT_ERR_OUT_OF_RANGE"
+    assert err(lambda: Layout.parse("(10,8):(8,1)").zipped_divide((4, 4))) == "LT_ERR_NOT_DIVISIBLE"
+    assert err(lambda: Layout.parse("(2,2):(1,1)").complement(8)) == "LT_ERR_NOT_ADMISSIBLE"
+    assert err(lambda: Layout.parse("(2,3):(3,1)").compose(Layout.parse("3:1"))) == "LT_ERR_NOT_ADMISSIBLE"
+    assert err(lambda: Layout.parse("(65536,65536,65536,65536):(1,1,1,1)").size()) == "LT_ERR_OUT_OF_RANGE"
+    big = "(" + ",".join(["2"] * 40) + "):(" + ",".join(["1"] * 40) + ")"
+    assert err(lambda: Layout.parse(big)) == "LT_ERR_CAPACITY"
+
+
+# ---------------------------------------------------------------------------
+# capability gate and GEMM planner (no device needed)
+# ---------------------------------------------------------------------------
+
+def _desc(ptr, dtype, shape, stride):
+    d = L.lt_tensor()
+    d.ptr = ptr
+    d.dtype = dtype
+    d.layout = Layout.make(shape, stride).c
+    return d
+
+
+def _plan(A, B, C, D, bnz=0, kernel=0, split=0):
+    o = L.lt_gemm_options()
+    o.kernel, o.split_k = kernel, split
+    info = L.lt_gemm_plan_info()
+    st = L.lib().lt_gemm_plan(ctypes.byref(A), ctypes.byref(B), ctypes.byref(C) if C else None, ctypes.byref(D),
+                              bnz, ctypes.byref(o), ctypes.byref(info))
+    return L.STATUS_NAMES[st], info
+
+
+BASE = 1 << 40   # fake, 256-byte aligned, never dereferenced
+
+
+def _gemm_descs(M, N, K, dt=L.LT_BF16, a="k", b="k", d="n", off=(0, 0, 0, 0)):
+    sz = 2 * (M * K + K * N + 2 * M * N) + 4096
+    A = _desc(BASE + off[0], dt, [M, K], [K, 1] if a == "k" else [1, M])
+    B = _desc(BASE + sz + off[1], dt, [K, N], [1, K] if b == "k" else [N, 1])
+    C = _desc(BASE + 2 * sz + off[2], dt, [M, N], [N, 1] if d == "n" else [1, M])
+    D = _desc(BASE + 3 * sz + off[3], dt, [M, N], [N, 1] if d == "n" else [1, M])
+    return A, B, C, D
+
+
+def test_arch_gate_refuses_before_launch():
+    lib = L.lib()
+    A, B, C, D = _gemm_descs(256, 256, 64)
+    try:
+        lib.lt_set_arch_override(b"gfx942")
+        buf = ctypes.create_string_buffer(32)
+        assert L.STATUS_NAMES[lib.lt_device_check(buf, 32)] == "LT_ERR_ARCH_MISMATCH"
+        assert buf.value == b"gfx942"
+        st = lib.lt_gemm_run(ctypes.byref(A), ctypes.byref(B), None, ctypes.byref(D), 1.0, 0.0, None, None, 0, None)
+        assert L.STATUS_NAMES[st] == "LT_ERR_ARCH_MISMATCH"
+        lay = Layout.parse("(4,4):(4,1)")
+        st = lib.lt_layout_eval_device(ctypes.byref(lay.c), 0x1000, 16, None)
+        assert L.STATUS_NAMES[st] == "LT_ERR_ARCH_MISMATCH"
+        lib.lt_set_arch_override(b"gfx950")
+        assert L.STATUS_NAMES[lib.lt_device_check(buf, 32)] == "LT_OK"
+    finally:
+        lib.lt_set_arch_override(None)
+
+
+def test_plan_kernel_choice_for_the_workloads():
+    st, i = _plan(*_gemm_descs(256, 128, 64, L.LT_F16))
+    assert st == "LT_OK" and i.kernel == L.LT_KERNEL_WAVE16 and i.grid == (16 * 8) // 4
+    st, i = _plan(*_gemm_descs(4096, 4096, 4096, L.LT_F16), bnz=1)
+    assert st == "LT_OK" and i.kernel == L.LT_KERNEL_TILED and i.grid == 256
+    st, i = _plan(*_gemm_descs(8192, 8192, 8192))
+    assert st == "LT_OK" and i.kernel == L.LT_KERNEL_TILED and i.grid == 1024
+    assert (i.tile_m, i.tile_n, i.tile_k, i.waves, i.stages) == (256, 256, 64, 4, 2)
+    st, i = _plan(*_gemm_descs(32, 8192, 8192))
+    assert st == "LT_OK" and i.kernel == L.LT_KERNEL_SKINNY and i.split_k == 1 and i.grid == 256
+    st, i = _plan(*_gemm_descs(32, 1024, 8192))
+    assert st == "LT_OK" and i.kernel == L.LT_KERNEL_SKINNY and i.split_k == 8
+    assert i.workspace_bytes == 8 * 32 * 1024 * 4
+
+
+def test_plan_closed_forms_reproduce_page_arithmetic():
+    """The closed forms behind the plan's LDS bill and MFMA count reproduce the
+    pages' printed tile arithmetic, then give the plan's own figures."""
+    def stage_bytes(bm, bn, bk, elem):
+        return (bm * bk + bk * bn) * elem
+
+    def instr_per_wave(wm, wn, wk, im, in_, ik):
+        return (wm // im) * (wn // in_) * (wk // ik)
+
+    s = TILE["smem_bill"]
+    assert stage_bytes(128, 128, 32, 2) == s["tile_128x128x32_fp16_bytes_per_stage"]
+    assert 2 * stage_bytes(128, 128, 32, 2) == s["two_stages"]
+    assert 3 * stage_bytes(128, 128, 32, 2) == s["three_stages"]
+    assert 3 * stage_bytes(128, 256, 64, 2) == s["tile_128x256x64_three_stages"]
+    assert stage_bytes(128, 64, 32, 2) == s["tile_128x64x32_fp16_bytes_per_stage"]
+    m = TILE["mma_count"]
+    assert instr_per_wave(64, 64, 32, 16, 8, 8) == m["instr_16x8x8"]
+    assert instr_per_wave(64, 64, 32, 16, 8, 16) == m["instr_16x8x16"]
+    t = TILE["tile_intensity"]
+    assert stage_bytes(128, 128, 64, 2) == t["bytes_per_step"]
+    assert 2 * 128 * 128 * 64 == t["flops_per_step"] and t["flops_per_step"] // t["bytes_per_step"] == 64
+    w = TILE["wave_quantisation"]
+    assert (4096 // 128) ** 2 == w["tiles_128x128"] and round(w["tiles_128x128"] / w["sms"], 2) == w["waves_128x128"]
+    assert round(w["tiles_128x256"] / w["sms"], 2) == w["waves_128x256"]
+    _, i = _plan(*_gemm_descs(8192, 8192, 8192))
+    assert i.lds_bytes == i.stages * stage_bytes(i.tile_m, i.tile_n, i.tile_k, 2)
+    assert i.mfma_per_wave_kstep == instr_per_wave(i.wave_m, i.wave_n, i.tile_k, 32, 32, 16)
+    assert i.grid / 256 == 4.0   # 1,024 tiles on 256 CUs: whole waves
+
+
+def test_plan_validation_statuses():
+    # misaligned base
+    A, B, C, D = _gemm_descs(256, 256, 64, off=(2, 0, 0, 0))
+    assert _plan(A, B, C, D)[0] == "LT_ERR_MISALIGNED_OPERAND"
+    # leading dimension not a multiple of 8 elements
+    A = _desc(BASE, L.LT_F16, [256, 60], [60, 1])
+    _, B, C, D = _gemm_descs(256, 256, 60, L.LT_F16)
+    assert _plan(A, B, C, D)[0] == "LT_ERR_MISALIGNED_OPERAND"
+    # no unit stride
+    A = _desc(BASE, L.LT_F16, [64, 64], [128, 2])
+    _, B, C, D = _gemm_descs(64, 64, 64, L.LT_F16)
+    assert _plan(A, B, C, D)[0] == "LT_ERR_UNSUPPORTED"
+    # shape mismatch
+    A, _, C, D = _gemm_descs(256, 256, 64)
+    B = _desc(BASE + (1 << 30), L.LT_BF16, [128, 256], [1, 128])
+    assert _plan(A, B, C, D)[0] == "LT_ERR_INVALID_ARGUMENT"
+    # dtype mix
+    A, B, C, D = _gemm_descs(256, 256, 64)
+    A.dtype = L.LT_F16
+    assert _plan(A, B, C, D)[0] == "LT_ERR_UNSUPPORTED"
+    # forcing the tiled kernel on a ragged shape
+    A, B, C, D = _gemm_descs(250, 256, 64)
+    assert _plan(A, B, C, D, kernel=L.LT_KERNEL_TILED)[0] == "LT_ERR_NOT_DIVISIBLE"
+    assert _plan(A, B, C, D)[1].kernel == L.LT_KERNEL_WAVE16
+    # D overlapping A
+    A, B, C, D = _gemm_descs(256, 256, 64)
+    D.ptr = A.ptr + 64
+    assert _plan(A, B, C, D)[0] == "LT_ERR_INVALID_ARGUMENT"
+    # D == C exactly is allowed
+    A, B, C, D = _gemm_descs(256, 256, 64)
+    C.ptr = D.ptr
+    assert _plan(A, B, C, D, bnz=1)[0] == "LT_OK"
+    # beta != 0 needs C
+    assert _plan(A, B, None, D, bnz=1)[0] == "LT_ERR_INVALID_ARGUMENT"
+    # workspace check before the device is touched
+    A, B, C, D = _gemm_descs(32, 1024, 8192)
+    st = L.lib().lt_gemm_run(ctypes.byref(A), ctypes.byref(B), None, ctypes.byref(D), 1.0, 0.0, None, None, 0, None)
+    assert L.STATUS_NAMES[st] == "LT_ERR_WORKSPACE"
+
+
+def test_plan_m_major_output_is_transposed():
+    st, i = _plan(*_gemm_descs(512, 256, 128, d="m"))
+    assert st == "LT_OK" and i.kernel == L.LT_KERNEL_TILED   # solved as D^T = B^T A^T
+
+
+def test_empty_problem_is_a_no_op():
+    A, B, C, D = _gemm_descs(0, 256, 64)
+    st = L.lib().lt_gemm_run(ctypes.byref(A), ctypes.byref(B), None, ctypes.byref(D), 1.0, 0.0, None, None, 0, None)
+    assert L.STATUS_NAMES[st] == "LT_OK"
+
+
+def test_empty_layout_matches_oracle():
+    E = Layout.parse("(4,0):(1,4)")
+    assert E.size() == 0 and E.cosize() == 0
+    with pytest.raises(LtError):
+        E(0)
+    for op in (lambda: E.coalesce(), lambda: E.compose(Layout.parse("2:1")), lambda: E.complement(8),
+               lambda: E.zipped_divide((2, 2))):
+        with pytest.raises(LtError) as e:
+            op()
+        assert e.value.name == "LT_ERR_INVALID_LAYOUT"
+
+
+def test_plan_unit_mode_prefers_a_real_unit_stride():
+    """An (8,1) operand stored (1,8): the stride-1 mode is mode 0, so the
+    extent-1 mode's stride does not need to be a multiple of 8."""
+    A = _desc(BASE, L.LT_F16, [16, 8], [8, 1])
+    B = _desc(BASE + 4096, L.LT_F16, [8, 1], [1, 8])
+    D = _desc(BASE + 8192, L.LT_F16, [16, 1], [8, 1])
+    st, i = _plan(A, B, None, D)
+    assert st == "LT_OK"

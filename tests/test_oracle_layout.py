@@ -384,8 +384,19 @@ def test_rejects_bad_layouts():
     with pytest.raises(ValueError):
         Layout((2, 3), (1,))
     with pytest.raises(ValueError):
-        Layout((2, 0), (1, 2))
+        Layout((2, -1), (1, 2))
     with pytest.raises(ValueError):
         Layout((2, 3), (1, -2))
     with pytest.raises(IndexError):
         Layout((2, 3), (1, 2))(6)
+
+
+def test_empty_layout():
+    E = Layout((4, 0), (1, 4))
+    assert ol.size(E) == 0 and ol.cosize(E) == 0 and ol.enumerate_offsets(E) == []
+    with pytest.raises(IndexError):
+        E(0)
+    for op in (lambda: ol.coalesce(E), lambda: ol.compose(E, Layout(2, 1)), lambda: ol.complement(E, 8),
+               lambda: ol.zipped_divide(E, (2, 2))):
+        with pytest.raises(ValueError):
+            op()
