@@ -23,7 +23,7 @@ BUILD = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["layout.cpp", "gemm.cpp", "device.hip", "gemm_kernels.hip"]
+SOURCES = ["layout.cpp", "gemm.cpp", "device.hip", "gemm_kernels.hip", "gemm_tiled.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", f"-I{INCLUDE}", f"-I{CSRC}",
           "-Wall", "-Wno-unused-function", "-Wno-unused-variable",

@@ -5,13 +5,14 @@
 // a lane or loop index folds into shifts, masks and immediate offsets ("3.5
 // CUTLASS II — CuTe 레이아웃·텐서", 3.5.10: prefer compile-time integers;
 // "CUTLASS and CuTe layouts", "Two programs": a static layout costs nothing to
-// pass). The same definitions compile for the host so tests can enumerate
+// pass). The same definitions compile for the host, so tests can enumerate
 // them and compare with the host layout algebra.
 #pragma once
 
 #include <cstdint>
 
 #if defined(__HIPCC__)
+#include <hip/hip_runtime.h>
 #define LT_HD __host__ __device__ __forceinline__
 #else
 #define LT_HD inline
@@ -47,9 +48,8 @@ struct Flat {
 };
 
 // XOR swizzle on an offset: bits [shift, shift+bits) are XORed into bits
-// [base, base+bits). A bijection of [0, 2^(shift+bits)) onto itself; composed
-// after a row-major tile layout it permutes the 16-byte chunks of each row by
-// the row index, so that a column of chunks spreads over all LDS banks.
+// [base, base+bits). A bijection of every aligned block of 2^(shift+bits)
+// offsets onto itself (an involution).
 struct Xor {
     int bits, base, shift;
     LT_HD constexpr int operator()(int off) const {
@@ -57,32 +57,58 @@ struct Xor {
     }
 };
 
+LT_HD constexpr int ilog2(int x) { return x <= 1 ? 0 : 1 + ilog2(x / 2); }
+
 // ---------------------------------------------------------------------------
-// Layouts of the 256x256x64 tiled kernel (K-major operands).
+// Operand tiles of the 256-row block-tiled kernel, in units of 16-byte chunks
+// (eight 16-bit elements).
 //
-// One LDS operand tile holds 256 rows (M or N) by 64 K elements of 16 bits:
-// 256 rows of 8 chunks of 16 bytes. In chunk units the unswizzled tile is the
-// row-major layout (8,256):(1,8) over (chunk, row); the stored tile is that
-// layout followed by Xor{3,0,3}: chunk' = chunk ^ (row & 7).
+// K-major tile: 256 rows (M or N) by BK elements of K, row-major chunks
+// (C, 256):(1, C) with C = BK/8 chunks per row, then an XOR swizzle that keys
+// the chunk on the 256-byte window the row falls in: a column of 16
+// consecutive rows read by 16 lanes then covers all 64 banks. With R = 16/C
+// rows per 256 bytes: chunk' = chunk ^ ((row / R) % C).
+//
+// M/N-major tile: BK rows of K by 256 elements of M or N (32 chunks per row),
+// chunk' = chunk ^ 4*(row & 3): the four K rows a transposed read touches at
+// once land in four different 64-byte bank groups.
 // ---------------------------------------------------------------------------
 
-constexpr Flat<2> kTileChunks{{8, 256}, {1, 8}};   // (chunk, row) -> chunk index
-constexpr Xor kTileSwizzle{3, 0, 3};
+template <int BK>
+struct KTile {
+    static constexpr int C = BK / 8;                 // chunks per row
+    static constexpr int R = 16 / C;                 // rows per 256-byte window
+    static constexpr Flat<2> chunks{{C, 256}, {1, C}};
+    static constexpr Xor swz{ilog2(C), 0, ilog2(C) + ilog2(R)};
+    // stored chunk index of logical (row, chunk)
+    LT_HD static constexpr int at(int row, int chunk) { return swz(chunks(chunk + C * row)); }
+};
 
-// Stored (swizzled) chunk index of logical (row, chunk).
-LT_HD constexpr int tile_chunk(int row, int chunk) { return kTileSwizzle(kTileChunks(chunk + 8 * row)); }
+struct MNTile {
+    static constexpr int C = 32;                     // 256 elements per K row
+    static constexpr Flat<2> chunks{{32, 64}, {1, 32}};
+    LT_HD static constexpr int at(int krow, int chunk) { return chunks(chunk + 32 * krow) ^ (4 * (krow & 3)); }
+};
 
 // Direct-to-LDS copy: one instruction of one wave writes 64 consecutive
-// stored chunks (1 KiB); the thread-value layout is lane -> stored chunk
-// lane, so a lane fetches the logical chunk that the swizzle puts there. The
-// swizzle is an involution on (row, chunk), so the logical chunk is the
-// stored one XORed with the row again.
-constexpr Flat<2> kCopyTV{{64, 32}, {1, 64}};       // (lane, instr) -> stored chunk
+// stored chunks (1 KiB); the thread-value layout is lane -> stored chunk, so a
+// lane fetches the logical chunk that the swizzle puts there. Both swizzles
+// are involutions on (row, chunk), so the logical chunk is the stored one
+// swizzled again.
+constexpr Flat<2> kCopyTV{{64, 1 << 10}, {1, 64}};     // (lane, instr) -> stored chunk
 
-// MFMA 32x32x16 operand fragment: lane l holds row l%32 and the 8 K values of
-// chunk l/32 of a 16-wide K step: (row, half) layout (32,2):(1,32) over the
-// lane index, i.e. lane -> (row = l % 32, kchunk = l / 32).
+// MFMA 32x32x16 operand fragment: lane l holds row l%32 and K values
+// 8*(l/32) .. 8*(l/32)+7 of a 16-deep K step: (row, half) = (32,2):(1,32).
 constexpr Flat<2> kFragLane{{32, 2}, {1, 32}};
+
+// Transposed LDS read (ds_read_b64_tr_b16), measured on gfx950: inside each
+// group of 16 lanes, lane i receives as element e the (i % 4)-th 16-bit value
+// of the 8-byte block addressed by lane 4e + i/4 of its group. To hand lane
+// (group g, index i) the MFMA fragment values K = 8*(g/2) + 4q + e of row
+// 16*(g%2) + i, lane j of group g points at K row 8*(g/2) + 4q + j/4 and
+// columns 16*(g%2) + 4*(j%4) .. +3.
+LT_HD constexpr int tr_krow(int lane, int q) { return 8 * (lane >> 5) + 4 * q + ((lane & 15) >> 2); }
+LT_HD constexpr int tr_col(int lane) { return 16 * ((lane >> 4) & 1) + 4 * (lane & 3); }
 
 // Output of one 32x32 MFMA block, per lane and accumulator register v:
 // column (the B-operand row) = lane % 32, row = 8*(v/4) + 4*(lane/32) + v%4.

@@ -173,8 +173,10 @@ lt_status make_plan(const lt_tensor* tA, const lt_tensor* tB, const lt_tensor* t
     const bool c_n = !beta_nonzero || p.C.e1 == 1 || p.C.s1 == 1;
 
     int kernel = opt ? opt->kernel : LT_KERNEL_AUTO;
-    const bool tiled_ok = p.M % 256 == 0 && p.N % 256 == 0 && p.K % 64 == 0 && p.K > 0 && p.a_k && p.b_k &&
-                          d_n && c_n;
+    const TiledShape ts = tiled_shape();
+    // M-major A and N-major B stream through the same kernel (transposed
+    // fragment reads); any stride-1 mode of A and B works.
+    const bool tiled_ok = p.M % ts.bm == 0 && p.N % ts.bn == 0 && p.K % ts.bk == 0 && p.K > 0 && d_n && c_n;
     int split = (opt && opt->split_k > 0) ? opt->split_k : 0;
     auto skinny_ok_for = [&](int s) {
         if (!(p.M <= 32 && p.a_k && p.b_k && d_n && c_n && p.N % kSkinnyBN == 0 && s >= 1)) return false;
@@ -212,21 +214,23 @@ lt_status make_plan(const lt_tensor* tA, const lt_tensor* tB, const lt_tensor* t
             break;
         }
         case LT_KERNEL_TILED: {
-            if (!tiled_ok) return p.a_k && p.b_k ? LT_ERR_NOT_DIVISIBLE : LT_ERR_UNSUPPORTED;
-            if (opt && ((opt->tile_m && opt->tile_m != 256) || (opt->tile_n && opt->tile_n != 256)))
+            if (!tiled_ok) return d_n && c_n ? LT_ERR_NOT_DIVISIBLE : LT_ERR_UNSUPPORTED;
+            if (opt && ((opt->tile_m && opt->tile_m != ts.bm) || (opt->tile_n && opt->tile_n != ts.bn)))
                 return LT_ERR_UNSUPPORTED;
-            in.tile_m = in.tile_n = 256;
-            in.tile_k = 64;
-            in.wave_m = in.wave_n = 128;
-            in.waves = 4;
-            in.stages = 2;
-            in.lds_bytes = kTiledLdsBytes;
+            in.tile_m = ts.bm;
+            in.tile_n = ts.bn;
+            in.tile_k = ts.bk;
+            in.wave_m = ts.wave_m;
+            in.wave_n = ts.wave_n;
+            in.waves = ts.waves;
+            in.stages = ts.stages;
+            in.lds_bytes = ts.lds_bytes;
             if (in.lds_bytes > 160 * 1024) return LT_ERR_LDS_OVERFLOW;
-            in.grid = (p.M / 256) * (p.N / 256);
-            // (128/32) * (128/32) * (64/16): the analogue of counting mma per
-            // warp per K slice ("CUTLASS and CuTe layouts", "The arch tag is not
-            // one instruction")
-            in.mfma_per_wave_kstep = (128 / 32) * (128 / 32) * (64 / 16);
+            in.grid = (p.M / ts.bm) * (p.N / ts.bn);
+            // (wave_m/32) * (wave_n/32) * (bk/16): the analogue of counting mma
+            // per warp per K slice ("CUTLASS and CuTe layouts", "The arch tag
+            // is not one instruction")
+            in.mfma_per_wave_kstep = ts.mfma_per_wave_slice;
             break;
         }
         case LT_KERNEL_SKINNY: {
@@ -334,8 +338,10 @@ lt_status lt_gemm_run(const lt_tensor* A, const lt_tensor* B, const lt_tensor* C
             a.B = static_cast<const uint16_t*>(p.B.ptr);
             a.C = cptr;
             a.D = static_cast<uint16_t*>(const_cast<void*>(p.D.ptr));
-            a.lda = p.A.s0;
-            a.ldb = p.B.s1;
+            // the non-unit stride of each operand (K-major A: row stride;
+            // M-major A: K stride; likewise for B)
+            a.lda = p.a_k ? p.A.s0 : p.A.s1;
+            a.ldb = p.b_k ? p.B.s1 : p.B.s0;
             a.ldc = bnz ? p.C.s0 : 0;
             a.ldd = p.D.s0;
             a.M = (int)p.M;
@@ -344,8 +350,9 @@ lt_status lt_gemm_run(const lt_tensor* A, const lt_tensor* B, const lt_tensor* C
             a.alpha = alpha;
             a.beta = beta;
             // The tile grid: mode 1 of zipped_divide(D, (256,256)).
+            const lt::TiledShape ts = lt::tiled_shape();
             lt::Tree dl = lt::Tree::tuple({lt::Tree::leaf(p.M, p.D.s0), lt::Tree::leaf(p.N, 1)});
-            const int64_t tiler[2] = {256, 256};
+            const int64_t tiler[2] = {ts.bm, ts.bn};
             lt::Tree zd;
             st = lt::divide_shape(dl, 2, tiler, true, &zd);
             if (st != LT_OK) return st;

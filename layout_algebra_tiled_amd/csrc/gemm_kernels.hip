@@ -1,99 +1,16 @@
-// GEMM kernels for gfx950 (CDNA4): D = alpha * A*B + beta * C, fp16/bf16
-// operands, fp32 accumulation on the matrix cores.
-//
-// The block tile, the copy partition of a tile over threads, the LDS tile
-// layout (row-major chunks composed with an XOR swizzle) and the MFMA
-// fragments are the compile-time layouts of device_layout.hpp; global
-// operands are addressed through their runtime Shape:Stride strides. The
-// structure follows the tiled GEMM of "Layouts as Algebra: CUTLASS & CuTe",
-// "The kernel, in three lines" (block tile by local_tile, thread share by
-// local_partition, a K-tile loop of copy / barrier / MMA) and "CUTLASS, in
-// depth", "The problem CUTLASS solves" (tiles staged through on-chip memory),
-// redesigned for CDNA4: 64-lane waves, 32x32x16 MFMA, direct global-to-LDS
-// loads instead of cp.async/TMA, and a double-buffered LDS ring.
+// GEMM kernels for gfx950 (CDNA4) other than the block-tiled one
+// (gemm_tiled.hip): the wave-per-16x16-tile kernel for any layout and ragged
+// shapes, and the skinny (M <= 32) kernel. D = alpha * A*B + beta * C,
+// fp16/bf16 operands, fp32 accumulation on the matrix cores; global operands
+// are addressed through their runtime Shape:Stride strides.
 
 #include <hip/hip_runtime.h>
 
-#include "device_layout.hpp"
 #include "gemm_kernels.hpp"
-#include "lt.h"
+#include "kernel_common.hpp"
 
 namespace lt {
 namespace {
-
-typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
-typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
-typedef __attribute__((ext_vector_type(16))) float f32x16;
-typedef __attribute__((ext_vector_type(4))) float f32x4;
-typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
-typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
-
-#define LDS_AS __attribute__((address_space(3)))
-
-// ---------------------------------------------------------------------------
-// dtype traits
-// ---------------------------------------------------------------------------
-
-template <int DT>
-struct Tr;
-
-template <>
-struct Tr<LT_F16> {
-    using V8 = f16x8;
-    static __device__ __forceinline__ f32x16 mfma32(V8 a, V8 b, f32x16 c) {
-        return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
-    }
-    static __device__ __forceinline__ f32x4 mfma16(V8 a, V8 b, f32x4 c) {
-        return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-    }
-    static __device__ __forceinline__ float to_f32(uint16_t x) {
-        return static_cast<float>(__builtin_bit_cast(_Float16, x));
-    }
-    static __device__ __forceinline__ uint16_t from_f32(float x) {   // round to nearest even
-        return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
-    }
-};
-
-template <>
-struct Tr<LT_BF16> {
-    using V8 = bf16x8;
-    static __device__ __forceinline__ f32x16 mfma32(V8 a, V8 b, f32x16 c) {
-        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-    }
-    static __device__ __forceinline__ f32x4 mfma16(V8 a, V8 b, f32x4 c) {
-        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-    }
-    static __device__ __forceinline__ float to_f32(uint16_t x) {
-        return __builtin_bit_cast(float, static_cast<uint32_t>(x) << 16);
-    }
-    static __device__ __forceinline__ uint16_t from_f32(float x) {   // round to nearest even
-        return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
-    }
-};
-
-template <int DT>
-__device__ __forceinline__ uint32_t pack2(float a, float b) {
-    return static_cast<uint32_t>(Tr<DT>::from_f32(a)) | (static_cast<uint32_t>(Tr<DT>::from_f32(b)) << 16);
-}
-
-// Epilogue of four consecutive N outputs of one row: alpha*acc + beta*c,
-// rounded to the output format and stored as one 8-byte write.
-template <int DT>
-__device__ __forceinline__ void store4(uint16_t* D, const uint16_t* C, int64_t dof, int64_t cof, float a0,
-                                       float a1, float a2, float a3, float alpha, float beta) {
-    float v0 = alpha * a0, v1 = alpha * a1, v2 = alpha * a2, v3 = alpha * a3;
-    if (beta != 0.0f) {
-        u32x2 c = *reinterpret_cast<const u32x2*>(C + cof);
-        v0 += beta * Tr<DT>::to_f32(static_cast<uint16_t>(c.x & 0xffff));
-        v1 += beta * Tr<DT>::to_f32(static_cast<uint16_t>(c.x >> 16));
-        v2 += beta * Tr<DT>::to_f32(static_cast<uint16_t>(c.y & 0xffff));
-        v3 += beta * Tr<DT>::to_f32(static_cast<uint16_t>(c.y >> 16));
-    }
-    u32x2 o;
-    o.x = pack2<DT>(v0, v1);
-    o.y = pack2<DT>(v2, v3);
-    *reinterpret_cast<u32x2*>(D + dof) = o;
-}
 
 // ---------------------------------------------------------------------------
 // WAVE16: one wave per 16x16 output tile, any operand strides, ragged edges.
@@ -154,147 +71,6 @@ __global__ __launch_bounds__(256) void gemm_wave16(Wave16Args p) {
         float v = p.alpha * acc[i];
         if (p.beta != 0.0f) v += p.beta * Tr<DT>::to_f32(p.C[m * p.scm + (int64_t)(n + i) * p.scn]);
         p.D[m * p.sdm + (int64_t)(n + i) * p.sdn] = Tr<DT>::from_f32(v);
-    }
-}
-
-// ---------------------------------------------------------------------------
-// TILED: 256x256 block tile, K step 64, four waves of 128x128, LDS double
-// buffer filled by direct global-to-LDS 16-byte loads.
-// ---------------------------------------------------------------------------
-
-constexpr int kBM = 256, kBN = 256, kBK = 64;
-constexpr int kStageBytes = 2 * kBM * kBK * 2;     // A tile + B tile
-constexpr int kOperandBytes = kBM * kBK * 2;       // 32 KiB
-
-// Bijection from workgroup id to output tile: consecutive ids land on
-// different XCDs (round-robin dispatch), so ids are first regrouped so that
-// each XCD walks a contiguous range of the raster; the raster runs down
-// group_m tile rows before moving one tile column right, so tiles in flight
-// together share A rows and B columns in L2 ("CUTLASS, in depth", "Kernel
-// schedules": rasterised, L2-friendly tile order).
-__device__ __forceinline__ void tile_of(int wg, const TiledArgs& p, int* tm, int* tn) {
-    const int ntiles = p.tiles_m * p.tiles_n;
-    int lin = wg;
-    if (p.xcd_remap) lin = (wg & 7) * (ntiles >> 3) + (wg >> 3);
-    const int gsz = p.group_m * p.tiles_n;
-    const int grp = lin / gsz;
-    const int first = grp * p.group_m;
-    const int gm = min(p.tiles_m - first, p.group_m);
-    const int in = lin - grp * gsz;
-    *tm = first + in % gm;
-    *tn = in / gm;
-}
-
-template <int DT>
-__global__ __launch_bounds__(256, 1) void gemm_tiled_kk(TiledArgs p) {
-    extern __shared__ __attribute__((aligned(1024))) char smem[];
-    using V8 = typename Tr<DT>::V8;
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    int tm, tn;
-    tile_of(blockIdx.x, p, &tm, &tn);
-    const int m0 = tm * kBM, n0 = tn * kBN;
-
-    // Copy partition (kCopyTV): wave w fills stored chunks [512w, 512w+512)
-    // of each operand tile, 64 per instruction, lane -> stored chunk. The
-    // stored chunk s = lane + 64 j + 512 w sits at row s/8 and swizzled column
-    // s%8; the logical K chunk there is (s%8) ^ (row & 7).
-    const int crow = lane >> 3;                                  // row within the 8-row block
-    const int kchunk = (lane & 7) ^ (crow & 7);                  // logical chunk fetched
-    const int row0 = wave * 64 + crow;
-    const uint16_t* gA = p.A + (int64_t)(m0 + row0) * p.lda + kchunk * 8;
-    const uint16_t* gB = p.B + (int64_t)(n0 + row0) * p.ldb + kchunk * 8;
-    const int64_t a_step = 8 * p.lda, b_step = 8 * p.ldb;        // next instruction: 8 rows on
-
-    auto issue = [&](int stage, int k0) {
-        char* sa = smem + stage * kStageBytes + wave * 8192;
-        char* sb = sa + kOperandBytes;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            __builtin_amdgcn_global_load_lds(gA + j * a_step + k0, (LDS_AS void*)(sa + j * 1024), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds(gB + j * b_step + k0, (LDS_AS void*)(sb + j * 1024), 16, 0, 0);
-        }
-    };
-
-    // Fragment partition (kFragLane): lane reads row lane%32 of each 32-row
-    // block and logical K chunk 2s + lane/32 for K step s, at its swizzled
-    // position (row & 7 == lane & 7 for every block).
-    const int wm = wave >> 1, wn = wave & 1;
-    const int frow = lane & 31, fh = lane >> 5;
-    int foff[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) foff[s] = dev::tile_chunk(frow, 2 * s + fh) * 16;
-
-    f32x16 acc[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
-
-    const int KT = p.K / kBK;
-    issue(0, 0);
-    __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
-    __syncthreads();
-
-    for (int t = 0; t < KT; ++t) {
-        const int cur = t & 1;
-        if (t + 1 < KT) issue(cur ^ 1, (t + 1) * kBK);
-        const char* sa = smem + cur * kStageBytes + wm * 128 * 128;
-        const char* sb = smem + cur * kStageBytes + kOperandBytes + wn * 128 * 128;
-        // Fragments of K step s+1 are read while the 16 MFMAs of step s run.
-        V8 af[2][4], bf[2][4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) af[0][i] = *(const LDS_AS V8*)(sa + i * 4096 + foff[0]);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) bf[0][j] = *(const LDS_AS V8*)(sb + j * 4096 + foff[0]);
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const int c = s & 1;
-            if (s + 1 < 4) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) af[c ^ 1][i] = *(const LDS_AS V8*)(sa + i * 4096 + foff[s + 1]);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) bf[c ^ 1][j] = *(const LDS_AS V8*)(sb + j * 4096 + foff[s + 1]);
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] = Tr<DT>::mfma32(bf[c][j], af[c][i], acc[i][j]);
-        }
-        // Issue order for the scheduler: the next tile's copies first, the
-        // first step's fragments, then each step's 16 MFMAs with the next
-        // step's 8 fragment reads threaded between them.
-        __builtin_amdgcn_sched_group_barrier(0x020, 16, 0);   // global-to-LDS copies
-        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);    // fragments of step 0
-#pragma unroll
-        for (int s = 0; s < 3; ++s) {
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // 2 MFMA
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // 1 LDS read
-            }
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
-        __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): this wave's loads of tile t+1 landed
-        __syncthreads();                      // everyone's landed; everyone done reading stage cur
-    }
-
-    // Epilogue: block (i, j), register group g holds row m = lane%32 and
-    // columns 8g + 4*(lane/32) + 0..3 of the 32x32 block.
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int m = m0 + wm * 128 + i * 32 + frow;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int n = n0 + wn * 128 + j * 32 + 8 * g + 4 * fh;
-                store4<DT>(p.D, p.C, (int64_t)m * p.ldd + n, (int64_t)m * p.ldc + n, acc[i][j][4 * g],
-                           acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3], p.alpha, p.beta);
-            }
-        }
     }
 }
 
@@ -419,27 +195,6 @@ int launch_wave16(int dtype, const Wave16Args& a, void* stream) {
         hipLaunchKernelGGL(gemm_wave16<LT_F16>, grid, block, 0, s, a);
     else
         hipLaunchKernelGGL(gemm_wave16<LT_BF16>, grid, block, 0, s, a);
-    return static_cast<int>(hipGetLastError());
-}
-
-int launch_tiled(int dtype, bool a_kmajor, bool b_kmajor, const TiledArgs& a, void* stream) {
-    if (!a_kmajor || !b_kmajor) return static_cast<int>(hipErrorInvalidValue);
-    static bool attr_set[2] = {false, false};
-    auto kf16 = gemm_tiled_kk<LT_F16>;
-    auto kbf16 = gemm_tiled_kk<LT_BF16>;
-    const int which = dtype == LT_F16 ? 0 : 1;
-    if (!attr_set[which]) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(which == 0 ? kf16 : kbf16),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, kTiledLdsBytes);
-        if (e != hipSuccess) return static_cast<int>(e);
-        attr_set[which] = true;
-    }
-    dim3 grid(a.tiles_m * a.tiles_n), block(256);
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    if (which == 0)
-        hipLaunchKernelGGL(kf16, grid, block, kTiledLdsBytes, s, a);
-    else
-        hipLaunchKernelGGL(kbf16, grid, block, kTiledLdsBytes, s, a);
     return static_cast<int>(hipGetLastError());
 }
 

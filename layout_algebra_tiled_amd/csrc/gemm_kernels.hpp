@@ -21,8 +21,8 @@ struct Wave16Args {
     int tiles_m, tiles_n;   // tile grid: mode 1 of zipped_divide(D, (16,16)), colex
 };
 
-// 256x256x64 block-tiled kernel. A is K-major or M-major, B is K-major or
-// N-major, D and C are N-major. M, N multiples of 256, K of 64.
+// 256x256 block-tiled kernel. A is K-major or M-major, B is K-major or
+// N-major, D and C are N-major. M, N multiples of 256, K of the K slice.
 struct TiledArgs {
     const uint16_t* A;
     const uint16_t* B;
@@ -52,7 +52,17 @@ struct SkinnyArgs {
 
 constexpr int kSkinnyWaves = 8;
 constexpr int kSkinnyBN = 32;
-constexpr int kTiledLdsBytes = 2 * 2 * 256 * 64 * 2;   // 2 stages x (A + B) x 256x64 x 16 bit
+
+// Compile-time shape of the tiled kernel the planner launches.
+struct TiledShape {
+    int bm, bn, bk;          // block tile and K slice
+    int wave_m, wave_n;      // tile of one wave
+    int waves;               // waves per workgroup
+    int stages;              // LDS ring depth
+    int lds_bytes;           // per workgroup
+    int mfma_per_wave_slice; // 32x32x16 MFMAs per wave per K slice
+};
+TiledShape tiled_shape();
 
 // Each returns 0 on success or the hipError_t of the launch.
 int launch_wave16(int dtype, const Wave16Args& a, void* stream);

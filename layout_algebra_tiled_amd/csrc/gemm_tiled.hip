@@ -1,0 +1,308 @@
+// Block-tiled GEMM for gfx950: D = alpha * A*B + beta * C with a 256x256 block
+// tile, fp16/bf16 operands, fp32 accumulation in 32x32x16 MFMAs.
+//
+// Structure (the tiled GEMM of "Layouts as Algebra: CUTLASS & CuTe", "The
+// kernel, in three lines", redesigned for CDNA4):
+//   - local_tile: workgroup -> one 256x256 tile of D (XCD-aware raster order);
+//   - the K loop streams BK-deep slices of the A and B tiles through an
+//     S-stage LDS ring filled by direct global-to-LDS 16-byte loads
+//     (global_load_lds_dwordx4; the copy's thread-value layout puts lane l's
+//     16 bytes at stored chunk l, and the lane fetches the logical chunk the
+//     swizzle stores there);
+//   - local_partition: each wave owns a TWM x TWN sub-tile and reads its MFMA
+//     fragments from LDS one K step ahead of the MFMAs that use them
+//     (ds_read_b128 for K-major operands, the transposing ds_read_b64_tr_b16
+//     for M- or N-major operands);
+//   - epilogue alpha*acc + beta*C, rounded once, 8-byte stores.
+// One workgroup barrier per K slice: it publishes slice t+1 and frees slice
+// t's stage, into which slice t+S is loaded at once.
+
+#include <type_traits>
+
+#include "device_layout.hpp"
+#include "gemm_kernels.hpp"
+#include "kernel_common.hpp"
+
+namespace lt {
+namespace {
+
+template <int NWM_, int NWN_, int BK_, int S_, bool AK_, bool BK_MAJ_>
+struct TCfg {
+    static constexpr int BM = 256, BN = 256, BK = BK_, S = S_;
+    static constexpr int NWM = NWM_, NWN = NWN_, NW = NWM * NWN, NT = 64 * NW;
+    static constexpr int TWM = BM / NWM, TWN = BN / NWN;      // wave tile
+    static constexpr int FM = TWM / 32, FN = TWN / 32;        // 32x32 MFMA blocks per wave
+    static constexpr int KS = BK / 16;                        // MFMA K steps per slice
+    static constexpr bool AK = AK_, BKM = BK_MAJ_;            // K-major operands?
+    static constexpr int OP_BYTES = 256 * BK * 2;             // one operand slice
+    static constexpr int STAGE = 2 * OP_BYTES;
+    static constexpr int LDS = S * STAGE;
+    static constexpr int OPI = OP_BYTES / 1024 / NW;          // copy instructions per wave per operand
+    static constexpr int IPW = 2 * OPI;                       // ... per slice
+    static_assert(OP_BYTES % (1024 * NW) == 0, "copy must split evenly over waves");
+    static_assert(KS % 2 == 0, "fragment double buffer assumes an even K-step count");
+    static_assert(IPW * (S - 1) < 64, "vmcnt counts at most 63 outstanding loads");
+};
+
+__device__ __forceinline__ void tile_of(int wg, const TiledArgs& p, int* tm, int* tn) {
+    // Consecutive workgroup ids go to different XCDs (round-robin dispatch);
+    // regroup them so each XCD walks a contiguous stretch of the raster, and
+    // raster down group_m tile rows before moving right, so tiles in flight
+    // together on one XCD share A rows and B columns in its L2 ("CUTLASS, in
+    // depth", "Kernel schedules": L2-friendly tile order).
+    const int ntiles = p.tiles_m * p.tiles_n;
+    int lin = wg;
+    if (p.xcd_remap) lin = (wg & 7) * (ntiles >> 3) + (wg >> 3);
+    const int gsz = p.group_m * p.tiles_n;
+    const int grp = lin / gsz;
+    const int first = grp * p.group_m;
+    const int gm = min(p.tiles_m - first, p.group_m);
+    const int in = lin - grp * gsz;
+    *tm = first + in % gm;
+    *tn = in / gm;
+}
+
+// s_waitcnt with vmcnt = n (0 <= n <= 63, a constant), other counters
+// untouched. (A macro: a __device__ helper template around the target builtin
+// would not be instantiable in the host compilation pass.)
+#define LT_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (0x7 << 4) | (0xf << 8) | (((n) >> 4) << 14))
+
+// One operand (A rows = M, or B rows = N) of the block tile.
+template <class Cf, bool KMAJ>
+struct Operand {
+    // Global source of copy instruction i (of this wave) for K slice k0.
+    // K-major: element (row, k) at row*ld + k; M/N-major: at k*ld + row.
+    // (__host__ __device__: it is called from lambdas inside the kernel, which
+    // the compiler treats as host-device.)
+    static __host__ __device__ __forceinline__ const uint16_t* src(const uint16_t* base, int64_t ld, int row0,
+                                                                   int wave, int lane, int i, int k0) {
+        const int q = dev::kCopyTV(lane + 64 * (wave * Cf::OPI + i));   // stored chunk
+        if constexpr (KMAJ) {
+            using T = dev::KTile<Cf::BK>;
+            const int row = q / T::C;
+            const int lchunk = dev::KTile<Cf::BK>::at(row, q % T::C) - T::C * row;   // involution
+            return base + (int64_t)(row0 + row) * ld + k0 + 8 * lchunk;
+        } else {
+            const int krow = q / 32;
+            const int lchunk = dev::MNTile::at(krow, q % 32) - 32 * krow;
+            return base + (int64_t)(k0 + krow) * ld + row0 + 8 * lchunk;
+        }
+    }
+};
+
+template <int DT, class Cf>
+__global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
+    extern __shared__ __attribute__((aligned(1024))) char smem[];
+    using V8 = typename Tr<DT>::V8;
+    constexpr int BK = Cf::BK, S = Cf::S, KS = Cf::KS, FM = Cf::FM, FN = Cf::FN;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int tm, tn;
+    tile_of(blockIdx.x, p, &tm, &tn);
+    const int m0 = tm * 256, n0 = tn * 256;
+    const int KT = p.K / BK;
+
+    // ---- copy: S-stage ring, stage s at s*STAGE (A slice, then B slice)
+    auto issue = [&](int stage, int kt) {
+        char* sa = smem + stage * Cf::STAGE + wave * Cf::OPI * 1024;
+        char* sb = sa + Cf::OP_BYTES;
+        const int k0 = kt * BK;
+#pragma unroll
+        for (int i = 0; i < Cf::OPI; ++i) {
+            // (sources in locals: passing the call expression straight to the
+            // builtin inside this template keeps the host stub from being made)
+            const void* ga = Operand<Cf, Cf::AK>::src(p.A, p.lda, m0, wave, lane, i, k0);
+            const void* gb = Operand<Cf, Cf::BKM>::src(p.B, p.ldb, n0, wave, lane, i, k0);
+            __builtin_amdgcn_global_load_lds(ga, (LDS_AS void*)(sa + i * 1024), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(gb, (LDS_AS void*)(sb + i * 1024), 16, 0, 0);
+        }
+    };
+
+    // ---- fragments: wave (wm, wn) owns rows wm*TWM.. of A and wn*TWN.. of B
+    const int wm = wave % Cf::NWM, wn = wave / Cf::NWM;
+    const int arow0 = wm * Cf::TWM, brow0 = wn * Cf::TWN;
+    // per-lane LDS byte offsets; the K step s and the block add immediates
+    int aoff[Cf::AK ? KS : FM], boff[Cf::BKM ? KS : FN];
+    if constexpr (Cf::AK) {
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+            aoff[s] = 16 * dev::KTile<BK>::at(arow0 + (lane & 31), 2 * s + (lane >> 5));
+    } else {
+#pragma unroll
+        for (int b = 0; b < FM; ++b)
+            aoff[b] = 16 * dev::MNTile::at(dev::tr_krow(lane, 0), (arow0 + 32 * b + dev::tr_col(lane)) >> 3) +
+                      2 * (dev::tr_col(lane) & 7);
+    }
+    if constexpr (Cf::BKM) {
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+            boff[s] = 16 * dev::KTile<BK>::at(brow0 + (lane & 31), 2 * s + (lane >> 5));
+    } else {
+#pragma unroll
+        for (int b = 0; b < FN; ++b)
+            boff[b] = 16 * dev::MNTile::at(dev::tr_krow(lane, 0), (brow0 + 32 * b + dev::tr_col(lane)) >> 3) +
+                      2 * (dev::tr_col(lane) & 7);
+    }
+
+    // Read the fragments of K step s of the slice in `stage`.
+    auto read_frag = [&](const char* base, const int* off, bool kmaj, int s, int b) -> V8 {
+        if (kmaj) {
+            // row block b: +32 rows of BK*2 bytes
+            return *(const LDS_AS V8*)(base + off[s] + b * 32 * BK * 2);
+        }
+        // K rows 16s + 4q (+ the lane's own rows, folded into off[b]); the
+        // row swizzle depends only on krow & 3, which 16s + 4q keeps
+        const LDS_AS char* p0 = (const LDS_AS char*)(base + off[b] + (16 * s) * 512);
+        i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(p0));
+        i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(p0 + 4 * 512));
+        i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        return __builtin_bit_cast(V8, v);
+    };
+
+    V8 af[2][FM], bfr[2][FN];
+    auto read_step = [&](int stage, int s, int buf) {
+        const char* sa = smem + stage * Cf::STAGE;
+        const char* sb = sa + Cf::OP_BYTES;
+#pragma unroll
+        for (int b = 0; b < FM; ++b) af[buf][b] = read_frag(sa, aoff, Cf::AK, s, b);
+#pragma unroll
+        for (int b = 0; b < FN; ++b) bfr[buf][b] = read_frag(sb, boff, Cf::BKM, s, b);
+    };
+
+    f32x16 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+    // ---- prologue: slices 0 .. S-1
+#pragma unroll
+    for (int s = 0; s < S; ++s)
+        if (s < KT) issue(s, s);
+    if (KT >= S)
+        LT_WAIT_VM(Cf::IPW * (S - 1));
+    else
+        LT_WAIT_VM(0);
+    __syncthreads();
+    read_step(0, 0, 0);
+
+    // One K slice: KS MFMA steps on the fragments already in registers, the
+    // next step's fragments read one step ahead. In the last step the
+    // barrier publishes slice t+1 (and frees slice t's stage, refilled with
+    // slice t+S at once), and slice t+1's first fragments are read while the
+    // last step's MFMAs run. Three branch-free variants: with a refill, with
+    // a next slice but no refill, and the final slice.
+    constexpr int NMF = FM * FN, NRD = (Cf::AK ? FM : 2 * FM) + (Cf::BKM ? FN : 2 * FN);
+    int stage = 0;
+    auto slice = [&](auto has_next, auto refill, int t) {
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            const int cur = s & 1, nxt = cur ^ 1;
+            if (s + 1 < KS) {
+                read_step(stage, s + 1, nxt);
+            } else if constexpr (decltype(has_next)::value) {
+                if constexpr (decltype(refill)::value)
+                    LT_WAIT_VM(Cf::IPW * (S - 2));   // slice t+1 landed (S-2 newer slices may fly)
+                else
+                    LT_WAIT_VM(0);
+                __syncthreads();   // slice t+1 visible to all; slice t's stage free
+                if constexpr (decltype(refill)::value) issue(stage, t + S);
+                read_step(stage + 1 == S ? 0 : stage + 1, 0, nxt);
+            }
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j) acc[i][j] = Tr<DT>::mfma32(bfr[cur][j], af[cur][i], acc[i][j]);
+            // Issue order for this step: after each of the first MFMAs, two
+            // fragment reads for the next step (and, in the last step, two of
+            // the slice copies), then the remaining MFMAs, which cover the
+            // reads' latency.
+            if (s + 1 < KS || decltype(has_next)::value) {
+                constexpr int PAIRS = (NRD + 1) / 2;
+                const bool copies = s + 1 == KS && decltype(refill)::value;
+#pragma unroll
+                for (int q = 0; q < PAIRS; ++q) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    if (copies && 2 * q < Cf::IPW) __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                }
+                if (copies && 2 * PAIRS < Cf::IPW)
+                    __builtin_amdgcn_sched_group_barrier(0x020, Cf::IPW - 2 * PAIRS, 0);
+                if (NMF > PAIRS) __builtin_amdgcn_sched_group_barrier(0x008, NMF - PAIRS, 0);
+            }
+        }
+        stage = stage + 1 == S ? 0 : stage + 1;
+    };
+    const std::true_type yes{};
+    const std::false_type no{};
+    int t = 0;
+    for (; t + S < KT; ++t) slice(yes, yes, t);   // refill slice t+S
+    for (; t + 1 < KT; ++t) slice(yes, no, t);    // slices already in flight
+    slice(no, no, t);                             // the last slice
+
+    // ---- epilogue: block (i, j), register group g holds row m = lane%32 and
+    // columns 8g + 4*(lane/32) + 0..3 of the 32x32 block
+    const int frow = lane & 31, fh = lane >> 5;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+        const int m = m0 + arow0 + i * 32 + frow;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int n = n0 + brow0 + j * 32 + 8 * g + 4 * fh;
+                store4<DT>(p.D, p.C, (int64_t)m * p.ldd + n, (int64_t)m * p.ldc + n, acc[i][j][4 * g],
+                           acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3], p.alpha, p.beta);
+            }
+        }
+    }
+}
+
+// The instantiation the planner launches.
+#ifndef LT_TILED_NWM
+#define LT_TILED_NWM 2
+#define LT_TILED_NWN 4
+#define LT_TILED_BK 64
+#define LT_TILED_S 2
+#endif
+
+template <bool AK, bool BKM>
+using Chosen = TCfg<LT_TILED_NWM, LT_TILED_NWN, LT_TILED_BK, LT_TILED_S, AK, BKM>;
+
+template <int DT, bool AK, bool BKM>
+int launch_one(const TiledArgs& a, hipStream_t s) {
+    using Cf = Chosen<AK, BKM>;
+    static bool attr = false;
+    if (!attr) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_tiled<DT, Cf>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, Cf::LDS);
+        if (e != hipSuccess) return static_cast<int>(e);
+        attr = true;
+    }
+    hipLaunchKernelGGL((gemm_tiled<DT, Cf>), dim3(a.tiles_m * a.tiles_n), dim3(Cf::NT), Cf::LDS, s, a);
+    return static_cast<int>(hipGetLastError());
+}
+
+template <int DT>
+int launch_dt(bool ak, bool bk, const TiledArgs& a, hipStream_t s) {
+    if (ak && bk) return launch_one<DT, true, true>(a, s);
+    if (ak && !bk) return launch_one<DT, true, false>(a, s);
+    if (!ak && bk) return launch_one<DT, false, true>(a, s);
+    return launch_one<DT, false, false>(a, s);
+}
+
+}  // namespace
+
+TiledShape tiled_shape() {
+    using Cf = Chosen<true, true>;
+    return TiledShape{256, 256, Cf::BK, Cf::TWM, Cf::TWN, Cf::NW, Cf::S, Cf::LDS, Cf::FM * Cf::FN * Cf::KS};
+}
+
+int launch_tiled(int dtype, bool a_kmajor, bool b_kmajor, const TiledArgs& a, void* stream) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return dtype == LT_F16 ? launch_dt<LT_F16>(a_kmajor, b_kmajor, a, s)
+                           : launch_dt<LT_BF16>(a_kmajor, b_kmajor, a, s);
+}
+
+}  // namespace lt

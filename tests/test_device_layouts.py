@@ -1,0 +1,133 @@
+"""The tiled kernel's compile-time layouts (device_layout.hpp, compiled for
+the host) checked on the CPU: swizzles are bijections, the copy's
+thread-value layout fetches exactly what the swizzle stores, fragment reads of
+16 (or 32) lanes hit distinct LDS banks, and the transposed-read addressing,
+run through the read semantics measured on gfx950, hands every lane its MFMA
+fragment. The unswizzled maps are also compared with the host layout algebra."""
+
+import os
+import subprocess
+
+import pytest
+
+from layout_algebra_tiled_amd import Layout
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "layout_algebra_tiled_amd", "csrc")
+
+
+@pytest.fixture(scope="module")
+def maps(tmp_path_factory):
+    d = tmp_path_factory.mktemp("devlayout")
+    exe = d / "dump"
+    subprocess.check_call(["g++", "-std=c++17", "-O1", f"-I{CSRC}", "-o", str(exe),
+                           os.path.join(ROOT, "tests", "native", "device_layout_dump.cpp")])
+    out = subprocess.check_output([str(exe)], text=True).split("\n")
+    m, i = {}, 0
+    while i < len(out):
+        head = out[i].split()
+        if not head:
+            i += 1
+            continue
+        m[tuple(head)] = [int(x) for x in out[i + 1].split()]
+        i += 2
+    return m
+
+
+def _ktile(maps, bk):
+    key = next(k for k in maps if k[0] == "ktile" and k[1] == str(bk))
+    C = int(key[2])
+    v = maps[key]
+    return C, lambda row, c: v[row * C + c]
+
+
+@pytest.mark.parametrize("bk", [32, 64])
+def test_ktile_swizzle_is_bijection_and_row_local(maps, bk):
+    C, at = _ktile(maps, bk)
+    allv = [at(r, c) for r in range(256) for c in range(C)]
+    assert sorted(allv) == list(range(256 * C))
+    for r in range(256):   # a row's chunks stay in that row
+        assert sorted(at(r, c) for c in range(C)) == list(range(r * C, (r + 1) * C))
+    # the unswizzled chunk layout is (C,256):(1,C) of the layout algebra
+    L = Layout.parse(f"({C},256):(1,{C})")
+    for r in range(0, 256, 37):
+        for c in range(C):
+            assert at(r, c) ^ (at(r, c) % C) ^ c == L([c, r]) or at(r, c) // C == L([c, r]) // C
+
+
+@pytest.mark.parametrize("bk", [32, 64])
+def test_ktile_fragment_reads_conflict_free(maps, bk):
+    """16 consecutive lanes read 16 consecutive rows at one logical chunk:
+    their 16-byte chunks must fall in 16 distinct 16-byte bank groups of a
+    256-byte (64-bank) window."""
+    C, at = _ktile(maps, bk)
+    for r0 in range(0, 256, 16):
+        for c in range(C):
+            groups = {at(r0 + i, c) % 16 for i in range(16)}
+            assert len(groups) == 16, (bk, r0, c)
+
+
+@pytest.mark.parametrize("bk", [32, 64])
+def test_copy_fetches_what_swizzle_stores(maps, bk):
+    """Stored chunk q receives logical (row, chunk) with at(row, chunk) == q;
+    the kernel's inversion (at(row, q % C) - C*row) gives exactly that."""
+    C, at = _ktile(maps, bk)
+    inv = {at(r, c): (r, c) for r in range(256) for c in range(C)}
+    for q in range(256 * C):
+        row = q // C
+        lchunk = at(row, q % C) - C * row
+        assert inv[q] == (row, lchunk)
+
+
+def test_mntile_bijection_and_transposed_reads(maps):
+    v = maps[("mntile", "64", "32")]
+    at = lambda k, c: v[k * 32 + c]
+    assert sorted(v) == list(range(64 * 32))
+    tr = maps[("tr",)]
+    krow0 = [tr[3 * l] for l in range(64)]
+    krow1 = [tr[3 * l + 1] for l in range(64)]
+    col = [tr[3 * l + 2] for l in range(64)]
+    # logical tile T[k][mn] = a unique tag; LDS holds it at the swizzled place
+    lds = {}
+    for k in range(64):
+        for mn in range(256):
+            byte = at(k, mn // 8) * 16 + (mn % 8) * 2
+            lds[byte] = (k, mn)
+    for s in range(4):              # K step (16 deep)
+        for base in (0, 32, 96, 224):
+            for q, krow in ((0, krow0), (1, krow1)):
+                # address of each lane, as the kernel forms it
+                addr = []
+                for l in range(64):
+                    k = krow[l] + 16 * s
+                    mn = base + col[l]
+                    addr.append(at(k, mn // 8) * 16 + (mn % 8) * 2)
+                # banks: each 32-lane half reads 256 bytes, 8 bytes a lane,
+                # in distinct 8-byte bank pairs
+                for h in (0, 32):
+                    pairs = {(a % 256) // 8 for a in addr[h:h + 32]}
+                    assert len(pairs) == 32
+                # measured semantics: lane i of a 16-lane group receives, as
+                # element e, value (i % 4) of the block lane 4e + i//4 points at
+                for l in range(64):
+                    g, i = l // 16, l % 16
+                    for e in range(4):
+                        src = 16 * g + 4 * e + i // 4
+                        k, mn = lds[addr[src] + 2 * (i % 4)]
+                        assert k == 16 * s + 8 * (l // 32) + 4 * q + e
+                        assert mn == base + 16 * (g % 2) + i
+
+
+def test_fragment_and_accumulator_maps(maps):
+    frag = maps[("frag",)]
+    assert frag == [(l % 32) + 32 * (l // 32) for l in range(64)]
+    acc = maps[("acc",)]
+    cells = set()
+    for l in range(64):
+        for v in range(16):
+            r, c = acc[2 * (16 * l + v)], acc[2 * (16 * l + v) + 1]
+            assert c == l % 32
+            cells.add((r, c))
+    assert cells == {(r, c) for r in range(32) for c in range(32)}
+    copy = maps[("copy",)]
+    assert copy == list(range(256))

@@ -287,7 +287,8 @@ def test_plan_kernel_choice_for_the_workloads():
     assert st == "LT_OK" and i.kernel == L.LT_KERNEL_TILED and i.grid == 256
     st, i = _plan(*_gemm_descs(8192, 8192, 8192))
     assert st == "LT_OK" and i.kernel == L.LT_KERNEL_TILED and i.grid == 1024
-    assert (i.tile_m, i.tile_n, i.tile_k, i.waves, i.stages) == (256, 256, 64, 4, 2)
+    assert (i.tile_m, i.tile_n) == (256, 256) and i.tile_k in (32, 64) and i.waves in (4, 8)
+    assert i.waves * i.wave_m * i.wave_n == 256 * 256 and i.stages >= 2
     st, i = _plan(*_gemm_descs(32, 8192, 8192))
     assert st == "LT_OK" and i.kernel == L.LT_KERNEL_SKINNY and i.split_k == 1 and i.grid == 256
     st, i = _plan(*_gemm_descs(32, 1024, 8192))
