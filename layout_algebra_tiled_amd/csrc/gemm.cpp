@@ -180,7 +180,7 @@ lt_status make_plan(const lt_tensor* tA, const lt_tensor* tB, const lt_tensor* t
     int split = (opt && opt->split_k > 0) ? opt->split_k : 0;
     auto skinny_ok_for = [&](int s) {
         if (!(p.M <= 32 && p.a_k && p.b_k && d_n && c_n && p.N % kSkinnyBN == 0 && s >= 1)) return false;
-        const int64_t per = (int64_t)s * kSkinnyWaves * 64;
+        const int64_t per = (int64_t)s * kSkinnyKQuantum;
         return p.K > 0 && p.K % per == 0;
     };
     if (kernel == LT_KERNEL_AUTO) {
@@ -247,10 +247,10 @@ lt_status make_plan(const lt_tensor* tA, const lt_tensor* tB, const lt_tensor* t
             in.wave_m = 32;
             in.wave_n = kSkinnyBN;
             in.waves = kSkinnyWaves;
-            in.stages = 0;
             in.split_k = split;
             in.grid = (p.N / kSkinnyBN) * split;
-            in.lds_bytes = (kSkinnyWaves - 1) * 16 * 64 * 4;
+            in.lds_bytes = kSkinnyLdsBytes;
+            in.stages = kSkinnyStages;
             in.workspace_bytes = split > 1 ? (int64_t)split * 32 * p.N * 4 : 0;
             in.mfma_per_wave_kstep = 4;   // one 32x32x16 per 16 of a 64-deep K block
             break;

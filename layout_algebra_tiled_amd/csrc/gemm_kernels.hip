@@ -6,6 +6,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include "device_layout.hpp"
 #include "gemm_kernels.hpp"
 #include "kernel_common.hpp"
 
@@ -75,77 +76,113 @@ __global__ __launch_bounds__(256) void gemm_wave16(Wave16Args p) {
 }
 
 // ---------------------------------------------------------------------------
-// SKINNY: M <= 32. B (K-major) is streamed once from HBM straight into MFMA
-// fragments; each workgroup owns 32 columns of N and splits its K range over
-// eight waves; partial sums meet in LDS. With split_k > 1 the K range is
-// further split over workgroups and fp32 partials go to a workspace that a
-// second kernel reduces ("CUTLASS, in depth", "Worked example: tile choice
-// and wave quantisation": narrow N tile and split-K for decode-like shapes).
-//
-// K order inside a 64-wide K block: lane half h holds K values
-// 32h + 8s .. 32h + 8s + 7 for MFMA step s, the same for the A and the B
-// fragment, so each lane streams 64 contiguous bytes of its B column.
+// SKINNY: M <= 32, K-major A and B. The job is to stream B (K x N) from HBM
+// exactly once at full bandwidth ("CUTLASS, in depth", "Worked example: tile
+// choice and wave quantisation": narrow N tile plus split-K for decode-like
+// shapes, or treat the product as memory-bound). Each workgroup owns 32
+// columns of N; its four waves split the workgroup's K range. Every wave owns
+// a private ring of kSkinnyStages LDS slots; a slot holds a 64-deep K slice of
+// the 32 A rows and of the 32 B columns (4 KiB each), filled by direct
+// global-to-LDS loads in which 8 lanes cover one row's 128 contiguous bytes,
+// so every load instruction reads 8 whole cache lines. One explicit vmcnt
+// wait per slot and no barriers; the four waves' partial sums meet in LDS at
+// the end. With split_k > 1 the K range is split over workgroups too and fp32
+// partials go to a workspace that skinny_reduce sums.
 // ---------------------------------------------------------------------------
 
-constexpr int kSkU = 4;   // K blocks of 64 in flight per batch
-
 template <int DT>
-__global__ __launch_bounds__(512, 1) void gemm_skinny(SkinnyArgs p) {
-    __shared__ float red[kSkinnyWaves - 1][16][64];
+__global__ __launch_bounds__(64 * kSkinnyWaves, 1) void gemm_skinny(SkinnyArgs p) {
+    extern __shared__ __attribute__((aligned(1024))) char smem[];
     using V8 = typename Tr<DT>::V8;
+    constexpr int R = kSkinnyStages;
+    constexpr int HALF = 32 * 64 * 2;                 // 32 rows x 64 K x 16 bit
+    constexpr int SLOT = 2 * HALF;                    // A rows, then B columns
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int nb = blockIdx.x, sk = blockIdx.y;
-    const int n0 = nb * kSkinnyBN;
-    const int frow = lane & 31, fh = lane >> 5;
+    const int n0 = blockIdx.x * kSkinnyBN, sk = blockIdx.y;
     const int kbeg = (sk * kSkinnyWaves + wave) * p.k_per_wave;
-    const uint16_t* gB = p.B + (int64_t)(n0 + frow) * p.ldb + kbeg + 32 * fh;
-    const bool arow = frow < p.M;
-    const uint16_t* gA = p.A + (int64_t)(arow ? frow : 0) * p.lda + kbeg + 32 * fh;
-    const u32x4 zero = {0u, 0u, 0u, 0u};
+    const int nst = p.k_per_wave / 64;                // slots to stream
+    char* ring = smem + wave * R * SLOT;
+
+    // Copy: instruction j fills rows 8j .. 8j+7 of each half-slot, 8 lanes
+    // per row; both halves use the K-major tile layout (128-byte rows of 8
+    // chunks, chunk ^ ((row >> 1) & 7)), so each lane fetches the logical
+    // chunk stored at its position. Rows of A past M repeat row M-1 (their
+    // outputs are never stored).
+    const uint16_t* ga[4];
+    const uint16_t* gb[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int row = 8 * j + (lane >> 3);
+        const int lchunk = dev::KTile<64>::at(row, lane & 7) - 8 * row;
+        ga[j] = p.A + (int64_t)min(row, p.M - 1) * p.lda + kbeg + 8 * lchunk;
+        gb[j] = p.B + (int64_t)(n0 + row) * p.ldb + kbeg + 8 * lchunk;
+    }
+    // Fragment offsets inside a half-slot: row lane%32, K chunk 2s + lane/32
+    const int frow = lane & 31, fh = lane >> 5;
+    int foff[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) foff[s] = 16 * dev::KTile<64>::at(frow, 2 * s + fh);
+
+    // Each wave starts its walk over its K range at a slot picked by a small
+    // hash of (workgroup, wave) and wraps around. B's columns are 2^k bytes
+    // apart for power-of-two K, so without the rotation every wave of the GPU
+    // streams addresses with the same low bits at the same time and piles
+    // onto a few DRAM channels (measured: 36.6 us unrotated vs 31.0 us on the
+    // 32x8192x8192 workload). The K sum is order-free.
+    const int rot = (blockIdx.x * 13 + wave * 7 + (blockIdx.x >> 3)) % nst;
+    auto issue = [&](int slot, int st) {
+        char* dst = ring + slot * SLOT;
+        int sr = st + rot;
+        sr = sr >= nst ? sr - nst : sr;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const void* a = ga[j] + sr * 64;
+            const void* b = gb[j] + sr * 64;
+            __builtin_amdgcn_global_load_lds(a, (LDS_AS void*)(dst + j * 1024), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(b, (LDS_AS void*)(dst + HALF + j * 1024), 16, 0, 0);
+        }
+    };
 
     f32x16 acc;
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
 
-    const int nkb = p.k_per_wave / 64;
-    int kb = 0;
-    for (; kb + kSkU <= nkb; kb += kSkU) {
-        u32x4 bv[kSkU][4], av[kSkU][4];
-#pragma unroll
-        for (int u = 0; u < kSkU; ++u)
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-                bv[u][s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(gB + (kb + u) * 64 + 8 * s));
-#pragma unroll
-        for (int u = 0; u < kSkU; ++u)
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-                av[u][s] = arow ? *reinterpret_cast<const u32x4*>(gA + (kb + u) * 64 + 8 * s) : zero;
-#pragma unroll
-        for (int u = 0; u < kSkU; ++u)
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-                acc = Tr<DT>::mfma32(__builtin_bit_cast(V8, bv[u][s]), __builtin_bit_cast(V8, av[u][s]), acc);
-    }
-    for (; kb < nkb; ++kb) {
+    for (int r = 0; r < R - 1 && r < nst; ++r) issue(r, r);
+    int slot = 0;
+    for (int t = 0; t < nst; ++t) {
+        if (t + R - 1 < nst) {
+            issue(slot == 0 ? R - 1 : slot - 1, t + R - 1);
+            // slot t landed: 8 loads per slot, R-1 newer slots may fly
+            __builtin_amdgcn_s_waitcnt(((8 * (R - 1)) & 15) | (0x7 << 4) | (0xf << 8) | (((8 * (R - 1)) >> 4) << 14));
+        } else {
+            __builtin_amdgcn_s_waitcnt(0 | (0x7 << 4) | (0xf << 8));
+        }
+        const char* sl = ring + slot * SLOT;
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-            u32x4 b = *reinterpret_cast<const u32x4*>(gB + kb * 64 + 8 * s);
-            u32x4 a = arow ? *reinterpret_cast<const u32x4*>(gA + kb * 64 + 8 * s) : zero;
-            acc = Tr<DT>::mfma32(__builtin_bit_cast(V8, b), __builtin_bit_cast(V8, a), acc);
+            V8 a = *(const LDS_AS V8*)(sl + foff[s]);
+            V8 b = *(const LDS_AS V8*)(sl + HALF + foff[s]);
+            // B as the row operand: each lane ends with four consecutive N
+            acc = Tr<DT>::mfma32(b, a, acc);
         }
+        slot = slot + 1 == R ? 0 : slot + 1;
     }
 
+    // Partial sums of the four waves meet in LDS (each wave's own ring).
+    __builtin_amdgcn_s_waitcnt(0 | (0x7 << 4) | (0xf << 8));
+    float* red = reinterpret_cast<float*>(ring);
     if (wave > 0) {
 #pragma unroll
-        for (int v = 0; v < 16; ++v) red[wave - 1][v][lane] = acc[v];
+        for (int v = 0; v < 16; ++v) red[v * 64 + lane] = acc[v];
     }
     __syncthreads();
     if (wave != 0) return;
 #pragma unroll
-    for (int w = 0; w < kSkinnyWaves - 1; ++w)
+    for (int w = 1; w < kSkinnyWaves; ++w) {
+        const float* o = reinterpret_cast<const float*>(smem + w * R * SLOT);
 #pragma unroll
-        for (int v = 0; v < 16; ++v) acc[v] += red[w][v][lane];
+        for (int v = 0; v < 16; ++v) acc[v] += o[v * 64 + lane];
+    }
 
     // lane holds m = lane % 32 and n = n0 + 8g + 4*(lane/32) + 0..3
     const int m = frow;
@@ -201,10 +238,19 @@ int launch_wave16(int dtype, const Wave16Args& a, void* stream) {
 int launch_skinny(int dtype, const SkinnyArgs& a, void* stream) {
     dim3 grid(a.N / kSkinnyBN, a.split_k), block(64 * kSkinnyWaves);
     hipStream_t s = static_cast<hipStream_t>(stream);
+    static bool attr[2] = {false, false};
+    const int which = dtype == LT_F16 ? 0 : 1;
+    if (!attr[which]) {
+        const void* k = which == 0 ? reinterpret_cast<const void*>(&gemm_skinny<LT_F16>)
+                                   : reinterpret_cast<const void*>(&gemm_skinny<LT_BF16>);
+        hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, kSkinnyLdsBytes);
+        if (e != hipSuccess) return static_cast<int>(e);
+        attr[which] = true;
+    }
     if (dtype == LT_F16)
-        hipLaunchKernelGGL(gemm_skinny<LT_F16>, grid, block, 0, s, a);
+        hipLaunchKernelGGL(gemm_skinny<LT_F16>, grid, block, kSkinnyLdsBytes, s, a);
     else
-        hipLaunchKernelGGL(gemm_skinny<LT_BF16>, grid, block, 0, s, a);
+        hipLaunchKernelGGL(gemm_skinny<LT_BF16>, grid, block, kSkinnyLdsBytes, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.split_k == 1) return static_cast<int>(e);
     const int64_t quads = (int64_t)a.M * (a.N / 4);

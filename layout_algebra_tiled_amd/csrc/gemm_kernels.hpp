@@ -47,11 +47,15 @@ struct SkinnyArgs {
     int M, N, K;
     float alpha, beta;
     int split_k;
-    int k_per_wave;               // K elements per wave (multiple of 64)
+    int k_per_wave;               // K elements per wave (a multiple of 64)
 };
 
-constexpr int kSkinnyWaves = 8;
-constexpr int kSkinnyBN = 32;
+constexpr int kSkinnyWaves = 4;     // waves per workgroup (split the K range)
+constexpr int kSkinnyBN = 32;       // columns of N per workgroup
+constexpr int kSkinnyStages = 5;    // LDS ring slots per wave (64 K of A and B each)
+constexpr int kSkinnyLdsBytes = kSkinnyWaves * kSkinnyStages * 2 * 32 * 64 * 2;   // 160 KiB
+// K per wave must be a whole number of 64-deep slots
+constexpr int kSkinnyKQuantum = kSkinnyWaves * 64;
 
 // Compile-time shape of the tiled kernel the planner launches.
 struct TiledShape {

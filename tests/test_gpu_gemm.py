@@ -156,7 +156,8 @@ def test_two_calls_in_a_row_different_sizes():
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("M,N,K,split", [(32, 1024, 4096, 0), (17, 512, 4096, 1), (17, 512, 4096, 2),
-                                         (32, 256, 2048, 4), (1, 64, 512, 1)])
+                                         (32, 256, 2048, 4), (1, 64, 512, 1), (32, 64, 256, 1),
+                                         (8, 128, 3072, 3)])
 def test_skinny_all_outputs(M, N, K, split):
     A, B, C, D = _case(M, N, K, BF16, "row", "col", "row", 1.0, 0.0, dist="normal", seed=71)
     res, plan, _ = run_and_check(A, B, None, D, 1.0, 0.0, split_k=split, expect_kernel="skinny", label="skinny")
