@@ -269,7 +269,8 @@ typedef struct lt_gemm_plan_info {
     int64_t grid;            /* workgroups launched */
     int64_t lds_bytes;       /* per workgroup */
     int64_t workspace_bytes; /* caller-provided scratch the run needs */
-    int64_t mfma_per_wave_kstep; /* MFMA instructions per wave per K step */
+    int64_t mfma_per_wave_kstep; /* MFMA instructions per wave per K step (tile_k) */
+    int32_t mfma_m, mfma_n, mfma_k; /* shape of the MFMA instruction the kernel issues */
 } lt_gemm_plan_info;
 
 /* Validate and plan without launching. Checks: dtypes (A, B fp16 or bf16

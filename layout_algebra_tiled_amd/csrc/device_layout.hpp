@@ -70,8 +70,10 @@ LT_HD constexpr int ilog2(int x) { return x <= 1 ? 0 : 1 + ilog2(x / 2); }
 // rows per 256 bytes: chunk' = chunk ^ ((row / R) % C).
 //
 // M/N-major tile: BK rows of K by 256 elements of M or N (32 chunks per row),
-// chunk' = chunk ^ 4*(row & 3): the four K rows a transposed read touches at
-// once land in four different 64-byte bank groups.
+// chunk' = chunk ^ (4*(row & 3) + 2*((row >> 3) & 1)). A transposed read
+// covers, per 32 lanes, either four K rows by 64 bytes (32x32x16 fragments)
+// or eight K rows (two sets of four, 8 apart) by 32 bytes (16x16x32); with
+// the XOR both land in 16 distinct 16-byte bank groups of a 256-byte window.
 // ---------------------------------------------------------------------------
 
 template <int BK>
@@ -87,7 +89,9 @@ struct KTile {
 struct MNTile {
     static constexpr int C = 32;                     // 256 elements per K row
     static constexpr Flat<2> chunks{{32, 64}, {1, 32}};
-    LT_HD static constexpr int at(int krow, int chunk) { return chunks(chunk + 32 * krow) ^ (4 * (krow & 3)); }
+    LT_HD static constexpr int at(int krow, int chunk) {
+        return chunks(chunk + 32 * krow) ^ (4 * (krow & 3) + 2 * ((krow >> 3) & 1));
+    }
 };
 
 // Direct-to-LDS copy: one instruction of one wave writes 64 consecutive
@@ -114,5 +118,28 @@ LT_HD constexpr int tr_col(int lane) { return 16 * ((lane >> 4) & 1) + 4 * (lane
 // column (the B-operand row) = lane % 32, row = 8*(v/4) + 4*(lane/32) + v%4.
 LT_HD constexpr int acc_row(int lane, int v) { return 8 * (v / 4) + 4 * (lane / 32) + (v % 4); }
 LT_HD constexpr int acc_col(int lane) { return lane % 32; }
+
+// The same maps for either MFMA shape the block-tiled kernel uses, MF x MF
+// outputs per instruction: 32x32x16 (K step 16) or 16x16x32 (K step 32).
+//   operand: lane l holds row l % MF and the 8 K values of chunk l / MF of
+//            the K step ((MF, 64/MF):(1, MF));
+//   transposed read: lane j of 16-lane group g points at K row
+//            8*(l/MF) + 4q + (j/4), columns 16*((l/16) % (MF/16)) + 4*(j%4);
+//   output:  register v of lane l is row 8*(v/4) + 4*(l/MF) + v%4 (the B
+//            operand's row) and column l % MF; MF*MF/64 registers per lane.
+template <int MF>
+struct Mfma {
+    static_assert(MF == 32 || MF == 16, "MFMA shape 32x32x16 or 16x16x32");
+    static constexpr int KSTEP = 512 / MF;         // K per instruction
+    static constexpr int CHUNKS = KSTEP / 8;       // 16-byte K chunks per step
+    static constexpr int NACC = MF * MF / 64;      // accumulator registers per lane
+    static constexpr Flat<2> frag{{MF, 64 / MF}, {1, MF}};
+    LT_HD static constexpr int frag_row(int lane) { return lane % MF; }
+    LT_HD static constexpr int frag_chunk(int lane) { return lane / MF; }
+    LT_HD static constexpr int tr_krow(int lane, int q) { return 8 * (lane / MF) + 4 * q + ((lane & 15) >> 2); }
+    LT_HD static constexpr int tr_col(int lane) { return 16 * ((lane >> 4) % (MF / 16)) + 4 * (lane & 3); }
+    LT_HD static constexpr int out_row(int lane, int v) { return 8 * (v / 4) + 4 * (lane / MF) + (v % 4); }
+    LT_HD static constexpr int out_col(int lane) { return lane % MF; }
+};
 
 }  // namespace lt::dev

@@ -176,7 +176,15 @@ lt_status make_plan(const lt_tensor* tA, const lt_tensor* tB, const lt_tensor* t
     const TiledShape ts = tiled_shape();
     // M-major A and N-major B stream through the same kernel (transposed
     // fragment reads); any stride-1 mode of A and B works.
-    const bool tiled_ok = p.M % ts.bm == 0 && p.N % ts.bn == 0 && p.K % ts.bk == 0 && p.K > 0 && d_n && c_n;
+    // The tiled kernel addresses a K slice as a uniform base plus a per-lane
+    // 32-bit byte offset: the largest such offset must stay below 4 GiB.
+    auto offsets_fit = [&](bool kmaj, int64_t ld, int64_t rows) {
+        const int64_t top = kmaj ? (rows - 1) * ld + ts.bk : (int64_t)(ts.bk - 1) * ld + rows;
+        return top * 2 < (int64_t(1) << 32);
+    };
+    const bool tiled_ok = p.M % ts.bm == 0 && p.N % ts.bn == 0 && p.K % ts.bk == 0 && p.K > 0 && d_n && c_n &&
+                          offsets_fit(p.a_k, p.a_k ? p.A.s0 : p.A.s1, p.M) &&
+                          offsets_fit(p.b_k, p.b_k ? p.B.s1 : p.B.s0, p.N);
     int split = (opt && opt->split_k > 0) ? opt->split_k : 0;
     auto skinny_ok_for = [&](int s) {
         if (!(p.M <= 32 && p.a_k && p.b_k && d_n && c_n && p.N % kSkinnyBN == 0 && s >= 1)) return false;
@@ -211,6 +219,8 @@ lt_status make_plan(const lt_tensor* tA, const lt_tensor* tB, const lt_tensor* t
             in.grid = (tiles + 3) / 4;
             in.lds_bytes = 0;
             in.mfma_per_wave_kstep = 1;   // one 16x16x32 per 32-deep K step
+            in.mfma_m = in.mfma_n = 16;
+            in.mfma_k = 32;
             break;
         }
         case LT_KERNEL_TILED: {
@@ -227,10 +237,12 @@ lt_status make_plan(const lt_tensor* tA, const lt_tensor* tB, const lt_tensor* t
             in.lds_bytes = ts.lds_bytes;
             if (in.lds_bytes > 160 * 1024) return LT_ERR_LDS_OVERFLOW;
             in.grid = (p.M / ts.bm) * (p.N / ts.bn);
-            // (wave_m/32) * (wave_n/32) * (bk/16): the analogue of counting mma
+            // (wave_m/mf) * (wave_n/mf) * (bk/mfma_k): the analogue of counting mma
             // per warp per K slice ("CUTLASS and CuTe layouts", "The arch tag
             // is not one instruction")
             in.mfma_per_wave_kstep = ts.mfma_per_wave_slice;
+            in.mfma_m = in.mfma_n = ts.mfma_mn;
+            in.mfma_k = ts.mfma_k;
             break;
         }
         case LT_KERNEL_SKINNY: {
@@ -253,6 +265,8 @@ lt_status make_plan(const lt_tensor* tA, const lt_tensor* tB, const lt_tensor* t
             in.stages = kSkinnyStages;
             in.workspace_bytes = split > 1 ? (int64_t)split * 32 * p.N * 4 : 0;
             in.mfma_per_wave_kstep = 4;   // one 32x32x16 per 16 of a 64-deep K block
+            in.mfma_m = in.mfma_n = 32;
+            in.mfma_k = 16;
             break;
         }
         default:

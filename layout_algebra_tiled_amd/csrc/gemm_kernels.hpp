@@ -64,7 +64,8 @@ struct TiledShape {
     int waves;               // waves per workgroup
     int stages;              // LDS ring depth
     int lds_bytes;           // per workgroup
-    int mfma_per_wave_slice; // 32x32x16 MFMAs per wave per K slice
+    int mfma_per_wave_slice; // MFMAs per wave per K slice
+    int mfma_mn, mfma_k;     // MFMA instruction: mfma_mn x mfma_mn outputs, K depth
 };
 TiledShape tiled_shape();
 

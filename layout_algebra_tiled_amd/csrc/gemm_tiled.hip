@@ -26,13 +26,15 @@
 namespace lt {
 namespace {
 
-template <int NWM_, int NWN_, int BK_, int S_, bool AK_, bool BK_MAJ_>
+template <int NWM_, int NWN_, int BK_, int S_, int MF_, bool AK_, bool BK_MAJ_>
 struct TCfg {
     static constexpr int BM = 256, BN = 256, BK = BK_, S = S_;
     static constexpr int NWM = NWM_, NWN = NWN_, NW = NWM * NWN, NT = 64 * NW;
     static constexpr int TWM = BM / NWM, TWN = BN / NWN;      // wave tile
-    static constexpr int FM = TWM / 32, FN = TWN / 32;        // 32x32 MFMA blocks per wave
-    static constexpr int KS = BK / 16;                        // MFMA K steps per slice
+    using MFMA = dev::Mfma<MF_>;                              // MF x MF outputs per instruction
+    static constexpr int MF = MF_;
+    static constexpr int FM = TWM / MF, FN = TWN / MF;        // MFMA blocks per wave
+    static constexpr int KS = BK / MFMA::KSTEP;               // MFMA K steps per slice
     static constexpr bool AK = AK_, BKM = BK_MAJ_;            // K-major operands?
     static constexpr int OP_BYTES = 256 * BK * 2;             // one operand slice
     static constexpr int STAGE = 2 * OP_BYTES;
@@ -42,6 +44,7 @@ struct TCfg {
     static_assert(OP_BYTES % (1024 * NW) == 0, "copy must split evenly over waves");
     static_assert(KS % 2 == 0, "fragment double buffer assumes an even K-step count");
     static_assert(IPW * (S - 1) < 64, "vmcnt counts at most 63 outstanding loads");
+    static_assert((OPI - 1) * 1024 <= 4095, "copy offsets must fit the 13-bit instruction offset");
 };
 
 __device__ __forceinline__ void tile_of(int wg, const TiledArgs& p, int* tm, int* tn) {
@@ -67,26 +70,38 @@ __device__ __forceinline__ void tile_of(int wg, const TiledArgs& p, int* tm, int
 // would not be instantiable in the host compilation pass.)
 #define LT_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (0x7 << 4) | (0xf << 8) | (((n) >> 4) << 14))
 
+// Compile-time loop: f(integral_constant<int, I>) for I in [B, E).
+template <int B, int E, class F>
+__host__ __device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
 // One operand (A rows = M, or B rows = N) of the block tile.
 template <class Cf, bool KMAJ>
 struct Operand {
-    // Global source of copy instruction i (of this wave) for K slice k0.
+    // Byte offset of the source of copy instruction i (of this wave) for
+    // K slice 0, relative to the operand's base; a K slice adds kslice_bytes.
     // K-major: element (row, k) at row*ld + k; M/N-major: at k*ld + row.
     // (__host__ __device__: it is called from lambdas inside the kernel, which
     // the compiler treats as host-device.)
-    static __host__ __device__ __forceinline__ const uint16_t* src(const uint16_t* base, int64_t ld, int row0,
-                                                                   int wave, int lane, int i, int k0) {
+    static __host__ __device__ __forceinline__ uint32_t offset(int64_t ld, int row0, int wave, int lane, int i) {
         const int q = dev::kCopyTV(lane + 64 * (wave * Cf::OPI + i));   // stored chunk
         if constexpr (KMAJ) {
             using T = dev::KTile<Cf::BK>;
             const int row = q / T::C;
             const int lchunk = dev::KTile<Cf::BK>::at(row, q % T::C) - T::C * row;   // involution
-            return base + (int64_t)(row0 + row) * ld + k0 + 8 * lchunk;
+            return (uint32_t)(((int64_t)(row0 + row) * ld + 8 * lchunk) * 2);
         } else {
             const int krow = q / 32;
             const int lchunk = dev::MNTile::at(krow, q % 32) - 32 * krow;
-            return base + (int64_t)(k0 + krow) * ld + row0 + 8 * lchunk;
+            return (uint32_t)(((int64_t)krow * ld + row0 + 8 * lchunk) * 2);
         }
+    }
+    static __host__ __device__ __forceinline__ int64_t kslice_bytes(int64_t ld) {
+        return KMAJ ? (int64_t)Cf::BK * 2 : (int64_t)Cf::BK * ld * 2;
     }
 };
 
@@ -101,57 +116,73 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
     const int m0 = tm * 256, n0 = tn * 256;
     const int KT = p.K / BK;
 
-    // ---- copy: S-stage ring, stage s at s*STAGE (A slice, then B slice)
+    // ---- copy: S-stage ring, stage s at s*STAGE (A slice, then B slice).
+    // Every copy instruction of one operand writes LDS through the same base
+    // (M0 is set once per operand) and reaches its own 1 KiB through the
+    // instruction offset, which the hardware adds to both the global and the
+    // LDS address; the global source is a uniform slice base plus a per-lane
+    // 32-bit offset, minus that same instruction offset.
+    uint32_t aoffg[Cf::OPI], boffg[Cf::OPI];
+#pragma unroll
+    for (int i = 0; i < Cf::OPI; ++i) {
+        aoffg[i] = Operand<Cf, Cf::AK>::offset(p.lda, m0, wave, lane, i);
+        boffg[i] = Operand<Cf, Cf::BKM>::offset(p.ldb, n0, wave, lane, i);
+    }
+    const int64_t a_ks = Operand<Cf, Cf::AK>::kslice_bytes(p.lda);
+    const int64_t b_ks = Operand<Cf, Cf::BKM>::kslice_bytes(p.ldb);
     auto issue = [&](int stage, int kt) {
         char* sa = smem + stage * Cf::STAGE + wave * Cf::OPI * 1024;
         char* sb = sa + Cf::OP_BYTES;
-        const int k0 = kt * BK;
-#pragma unroll
-        for (int i = 0; i < Cf::OPI; ++i) {
-            // (sources in locals: passing the call expression straight to the
-            // builtin inside this template keeps the host stub from being made)
-            const void* ga = Operand<Cf, Cf::AK>::src(p.A, p.lda, m0, wave, lane, i, k0);
-            const void* gb = Operand<Cf, Cf::BKM>::src(p.B, p.ldb, n0, wave, lane, i, k0);
-            __builtin_amdgcn_global_load_lds(ga, (LDS_AS void*)(sa + i * 1024), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds(gb, (LDS_AS void*)(sb + i * 1024), 16, 0, 0);
-        }
+        const char* ga = reinterpret_cast<const char*>(p.A) + kt * a_ks;
+        const char* gb = reinterpret_cast<const char*>(p.B) + kt * b_ks;
+        static_for<0, Cf::OPI>([&](auto ic) {
+            constexpr int i = decltype(ic)::value;
+            const void* src = (ga - i * 1024) + aoffg[i];
+            __builtin_amdgcn_global_load_lds(src, (LDS_AS void*)sa, 16, i * 1024, 0);
+        });
+        static_for<0, Cf::OPI>([&](auto ic) {
+            constexpr int i = decltype(ic)::value;
+            const void* src = (gb - i * 1024) + boffg[i];
+            __builtin_amdgcn_global_load_lds(src, (LDS_AS void*)sb, 16, i * 1024, 0);
+        });
     };
 
     // ---- fragments: wave (wm, wn) owns rows wm*TWM.. of A and wn*TWN.. of B
     const int wm = wave % Cf::NWM, wn = wave / Cf::NWM;
     const int arow0 = wm * Cf::TWM, brow0 = wn * Cf::TWN;
     // per-lane LDS byte offsets; the K step s and the block add immediates
+    using Mf = typename Cf::MFMA;
     int aoff[Cf::AK ? KS : FM], boff[Cf::BKM ? KS : FN];
     if constexpr (Cf::AK) {
 #pragma unroll
         for (int s = 0; s < KS; ++s)
-            aoff[s] = 16 * dev::KTile<BK>::at(arow0 + (lane & 31), 2 * s + (lane >> 5));
+            aoff[s] = 16 * dev::KTile<BK>::at(arow0 + Mf::frag_row(lane), Mf::CHUNKS * s + Mf::frag_chunk(lane));
     } else {
 #pragma unroll
         for (int b = 0; b < FM; ++b)
-            aoff[b] = 16 * dev::MNTile::at(dev::tr_krow(lane, 0), (arow0 + 32 * b + dev::tr_col(lane)) >> 3) +
-                      2 * (dev::tr_col(lane) & 7);
+            aoff[b] = 16 * dev::MNTile::at(Mf::tr_krow(lane, 0), (arow0 + Cf::MF * b + Mf::tr_col(lane)) >> 3) +
+                      2 * (Mf::tr_col(lane) & 7);
     }
     if constexpr (Cf::BKM) {
 #pragma unroll
         for (int s = 0; s < KS; ++s)
-            boff[s] = 16 * dev::KTile<BK>::at(brow0 + (lane & 31), 2 * s + (lane >> 5));
+            boff[s] = 16 * dev::KTile<BK>::at(brow0 + Mf::frag_row(lane), Mf::CHUNKS * s + Mf::frag_chunk(lane));
     } else {
 #pragma unroll
         for (int b = 0; b < FN; ++b)
-            boff[b] = 16 * dev::MNTile::at(dev::tr_krow(lane, 0), (brow0 + 32 * b + dev::tr_col(lane)) >> 3) +
-                      2 * (dev::tr_col(lane) & 7);
+            boff[b] = 16 * dev::MNTile::at(Mf::tr_krow(lane, 0), (brow0 + Cf::MF * b + Mf::tr_col(lane)) >> 3) +
+                      2 * (Mf::tr_col(lane) & 7);
     }
 
     // Read the fragments of K step s of the slice in `stage`.
     auto read_frag = [&](const char* base, const int* off, bool kmaj, int s, int b) -> V8 {
         if (kmaj) {
-            // row block b: +32 rows of BK*2 bytes
-            return *(const LDS_AS V8*)(base + off[s] + b * 32 * BK * 2);
+            // row block b: +MF rows of BK*2 bytes
+            return *(const LDS_AS V8*)(base + off[s] + b * Cf::MF * BK * 2);
         }
-        // K rows 16s + 4q (+ the lane's own rows, folded into off[b]); the
-        // row swizzle depends only on krow & 3, which 16s + 4q keeps
-        const LDS_AS char* p0 = (const LDS_AS char*)(base + off[b] + (16 * s) * 512);
+        // K rows KSTEP*s + 4q (+ the lane's own rows, folded into off[b]);
+        // the row swizzle depends only on krow & 3, which KSTEP*s + 4q keeps
+        const LDS_AS char* p0 = (const LDS_AS char*)(base + off[b] + (Mf::KSTEP * s) * 512);
         i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(p0));
         i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(p0 + 4 * 512));
         i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -168,13 +199,14 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
         for (int b = 0; b < FN; ++b) bfr[buf][b] = read_frag(sb, boff, Cf::BKM, s, b);
     };
 
-    f32x16 acc[FM][FN];
+    using Acc = std::conditional_t<Cf::MF == 32, f32x16, f32x4>;
+    Acc acc[FM][FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+            for (int v = 0; v < Mf::NACC; ++v) acc[i][j][v] = 0.0f;
 
     // ---- prologue: slices 0 .. S-1
 #pragma unroll
@@ -213,7 +245,12 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
-                for (int j = 0; j < FN; ++j) acc[i][j] = Tr<DT>::mfma32(bfr[cur][j], af[cur][i], acc[i][j]);
+                for (int j = 0; j < FN; ++j) {
+                    if constexpr (Cf::MF == 32)
+                        acc[i][j] = Tr<DT>::mfma32(bfr[cur][j], af[cur][i], acc[i][j]);
+                    else
+                        acc[i][j] = Tr<DT>::mfma16(bfr[cur][j], af[cur][i], acc[i][j]);
+                }
             // Issue order for this step: after each of the first MFMAs, two
             // fragment reads for the next step (and, in the last step, two of
             // the slice copies), then the remaining MFMAs, which cover the
@@ -241,17 +278,16 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
     for (; t + 1 < KT; ++t) slice(yes, no, t);    // slices already in flight
     slice(no, no, t);                             // the last slice
 
-    // ---- epilogue: block (i, j), register group g holds row m = lane%32 and
-    // columns 8g + 4*(lane/32) + 0..3 of the 32x32 block
-    const int frow = lane & 31, fh = lane >> 5;
+    // ---- epilogue: block (i, j), registers 4g..4g+3 hold row m = lane % MF
+    // and four consecutive columns of the MF x MF block
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
-        const int m = m0 + arow0 + i * 32 + frow;
+        const int m = m0 + arow0 + i * Cf::MF + Mf::out_col(lane);
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int n = n0 + brow0 + j * 32 + 8 * g + 4 * fh;
+            for (int g = 0; g < Mf::NACC / 4; ++g) {
+                const int n = n0 + brow0 + j * Cf::MF + Mf::out_row(lane, 4 * g);
                 store4<DT>(p.D, p.C, (int64_t)m * p.ldd + n, (int64_t)m * p.ldc + n, acc[i][j][4 * g],
                            acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3], p.alpha, p.beta);
             }
@@ -266,9 +302,12 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
 #define LT_TILED_BK 64
 #define LT_TILED_S 2
 #endif
+#ifndef LT_TILED_MF
+#define LT_TILED_MF 16
+#endif
 
 template <bool AK, bool BKM>
-using Chosen = TCfg<LT_TILED_NWM, LT_TILED_NWN, LT_TILED_BK, LT_TILED_S, AK, BKM>;
+using Chosen = TCfg<LT_TILED_NWM, LT_TILED_NWN, LT_TILED_BK, LT_TILED_S, LT_TILED_MF, AK, BKM>;
 
 template <int DT, bool AK, bool BKM>
 int launch_one(const TiledArgs& a, hipStream_t s) {
@@ -296,7 +335,8 @@ int launch_dt(bool ak, bool bk, const TiledArgs& a, hipStream_t s) {
 
 TiledShape tiled_shape() {
     using Cf = Chosen<true, true>;
-    return TiledShape{256, 256, Cf::BK, Cf::TWM, Cf::TWN, Cf::NW, Cf::S, Cf::LDS, Cf::FM * Cf::FN * Cf::KS};
+    return TiledShape{256, 256, Cf::BK, Cf::TWM, Cf::TWN, Cf::NW, Cf::S, Cf::LDS, Cf::FM * Cf::FN * Cf::KS,
+                      Cf::MF, Cf::MFMA::KSTEP};
 }
 
 int launch_tiled(int dtype, bool a_kmajor, bool b_kmajor, const TiledArgs& a, void* stream) {

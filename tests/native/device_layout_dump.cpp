@@ -15,6 +15,21 @@ void dump_ktile() {
     std::printf("\n");
 }
 
+// Per MFMA shape: operand (row, chunk), transposed-read (krow q=0, krow q=1,
+// col) and output (row, col) for every lane.
+template <int MF>
+void dump_mfma() {
+    using M = Mfma<MF>;
+    std::printf("mfrag %d %d %d\n", MF, M::KSTEP, M::NACC);
+    for (int l = 0; l < 64; ++l) std::printf("%d %d %d ", M::frag_row(l), M::frag_chunk(l), M::frag(l));
+    std::printf("\nmtr %d\n", MF);
+    for (int l = 0; l < 64; ++l) std::printf("%d %d %d ", M::tr_krow(l, 0), M::tr_krow(l, 1), M::tr_col(l));
+    std::printf("\nmout %d\n", MF);
+    for (int l = 0; l < 64; ++l)
+        for (int v = 0; v < M::NACC; ++v) std::printf("%d %d ", M::out_row(l, v), M::out_col(l));
+    std::printf("\n");
+}
+
 int main() {
     dump_ktile<32>();
     dump_ktile<64>();
@@ -32,5 +47,7 @@ int main() {
     for (int l = 0; l < 64; ++l)
         for (int v = 0; v < 16; ++v) std::printf("%d %d ", acc_row(l, v), acc_col(l));
     std::printf("\n");
+    dump_mfma<32>();
+    dump_mfma<16>();
     return 0;
 }

@@ -48,11 +48,14 @@ def test_ktile_swizzle_is_bijection_and_row_local(maps, bk):
     assert sorted(allv) == list(range(256 * C))
     for r in range(256):   # a row's chunks stay in that row
         assert sorted(at(r, c) for c in range(C)) == list(range(r * C, (r + 1) * C))
-    # the unswizzled chunk layout is (C,256):(1,C) of the layout algebra
+    # the unswizzled chunk layout is (C,256):(1,C) of the layout algebra, and
+    # the swizzle XORs the chunk with the row's 256-byte window index mod C
     L = Layout.parse(f"({C},256):(1,{C})")
-    for r in range(0, 256, 37):
+    R = 16 // C
+    for r in range(256):
         for c in range(C):
-            assert at(r, c) ^ (at(r, c) % C) ^ c == L([c, r]) or at(r, c) // C == L([c, r]) // C
+            assert L([c, r]) == C * r + c
+            assert at(r, c) == C * r + (c ^ ((r // R) % C))
 
 
 @pytest.mark.parametrize("bk", [32, 64])
@@ -79,43 +82,81 @@ def test_copy_fetches_what_swizzle_stores(maps, bk):
         assert inv[q] == (row, lchunk)
 
 
-def test_mntile_bijection_and_transposed_reads(maps):
+def _mntile(maps):
     v = maps[("mntile", "64", "32")]
-    at = lambda k, c: v[k * 32 + c]
+    return v, (lambda k, c: v[k * 32 + c])
+
+
+def test_mntile_bijection(maps):
+    v, at = _mntile(maps)
     assert sorted(v) == list(range(64 * 32))
-    tr = maps[("tr",)]
+    for k in range(64):   # each K row keeps its own 32 chunks
+        assert sorted(at(k, c) for c in range(32)) == list(range(32 * k, 32 * (k + 1)))
+        for c in range(32):   # an involution inside the row
+            assert at(k, at(k, c) - 32 * k) - 32 * k == c
+
+
+@pytest.mark.parametrize("mf", [32, 16])
+def test_transposed_reads_hand_each_lane_its_fragment(maps, mf):
+    """The M/N-major operand path: lanes address the LDS tile as the kernel
+    does, the read semantics measured on gfx950 are applied, and every lane
+    must receive the MFMA fragment of its row and K values; each 32-lane half
+    must touch 32 distinct 8-byte bank pairs (no LDS bank conflict)."""
+    _, at = _mntile(maps)
+    kstep = 512 // mf
+    tr = maps[("mtr", str(mf))]
     krow0 = [tr[3 * l] for l in range(64)]
     krow1 = [tr[3 * l + 1] for l in range(64)]
     col = [tr[3 * l + 2] for l in range(64)]
-    # logical tile T[k][mn] = a unique tag; LDS holds it at the swizzled place
     lds = {}
     for k in range(64):
         for mn in range(256):
-            byte = at(k, mn // 8) * 16 + (mn % 8) * 2
-            lds[byte] = (k, mn)
-    for s in range(4):              # K step (16 deep)
-        for base in (0, 32, 96, 224):
+            lds[at(k, mn // 8) * 16 + (mn % 8) * 2] = (k, mn)
+    for s in range(64 // kstep):          # K step
+        for base in (0, 32, 96, 224) if mf == 32 else (0, 16, 112, 240):
             for q, krow in ((0, krow0), (1, krow1)):
-                # address of each lane, as the kernel forms it
                 addr = []
                 for l in range(64):
-                    k = krow[l] + 16 * s
+                    k = krow[l] + kstep * s
                     mn = base + col[l]
                     addr.append(at(k, mn // 8) * 16 + (mn % 8) * 2)
-                # banks: each 32-lane half reads 256 bytes, 8 bytes a lane,
-                # in distinct 8-byte bank pairs
                 for h in (0, 32):
                     pairs = {(a % 256) // 8 for a in addr[h:h + 32]}
-                    assert len(pairs) == 32
-                # measured semantics: lane i of a 16-lane group receives, as
-                # element e, value (i % 4) of the block lane 4e + i//4 points at
+                    assert len(pairs) == 32, (mf, s, base, q, h)
                 for l in range(64):
                     g, i = l // 16, l % 16
                     for e in range(4):
                         src = 16 * g + 4 * e + i // 4
                         k, mn = lds[addr[src] + 2 * (i % 4)]
-                        assert k == 16 * s + 8 * (l // 32) + 4 * q + e
-                        assert mn == base + 16 * (g % 2) + i
+                        assert k == kstep * s + 8 * (l // mf) + 4 * q + e
+                        assert mn == base + 16 * (g % (mf // 16)) + i
+
+
+@pytest.mark.parametrize("mf", [32, 16])
+def test_mfma_operand_and_output_maps(maps, mf):
+    """Operand: lane l reads row l % MF, K chunk l // MF of the step (the
+    layout (MF, 64/MF):(1, MF)); output: the lanes' registers cover the MF x MF
+    block once, column = lane % MF, and registers 4g..4g+3 of a lane are four
+    consecutive rows (the epilogue's 8-byte stores)."""
+    key = next(k for k in maps if k[0] == "mfrag" and k[1] == str(mf))
+    kstep, nacc = int(key[2]), int(key[3])
+    assert kstep == 512 // mf and nacc == mf * mf // 64
+    fr = maps[key]
+    L = Layout.parse(f"({mf},{64 // mf}):(1,{mf})")
+    for l in range(64):
+        row, chunk, flat = fr[3 * l], fr[3 * l + 1], fr[3 * l + 2]
+        assert (row, chunk) == (l % mf, l // mf)
+        assert flat == L(l) == row + mf * chunk
+    out = maps[("mout", str(mf))]
+    cells = set()
+    for l in range(64):
+        rows = [out[2 * (nacc * l + v)] for v in range(nacc)]
+        for v in range(nacc):
+            assert out[2 * (nacc * l + v) + 1] == l % mf
+            cells.add((rows[v], l % mf))
+        for g in range(nacc // 4):
+            assert rows[4 * g:4 * g + 4] == list(range(rows[4 * g], rows[4 * g] + 4))
+    assert cells == {(r, c) for r in range(mf) for c in range(mf)}
 
 
 def test_fragment_and_accumulator_maps(maps):

@@ -296,6 +296,28 @@ def test_plan_kernel_choice_for_the_workloads():
     assert i.workspace_bytes == 8 * 32 * 1024 * 4
 
 
+def test_plan_tiled_needs_32bit_copy_offsets():
+    """The 256x256 kernel addresses a K slice as a uniform base plus per-lane
+    32-bit byte offsets; a leading dimension that pushes the last row past
+    4 GiB goes to the 16x16 kernel instead (still a valid plan)."""
+    M = N = K = 256
+    ok = ((1 << 31) - 64) // (M - 1)   # ((M-1)*lda + BK)*2 just under 4 GiB
+    for lda, expect in ((K, L.LT_KERNEL_TILED), (ok - 64, L.LT_KERNEL_TILED), (ok + 64, L.LT_KERNEL_WAVE16)):
+        A = _desc(BASE, L.LT_BF16, [M, K], [lda, 1])
+        B = _desc(BASE + (1 << 36), L.LT_BF16, [K, N], [1, K])
+        D = _desc(BASE + (2 << 36), L.LT_BF16, [M, N], [N, 1])
+        st, i = _plan(A, B, None, D)
+        assert st == "LT_OK" and i.kernel == expect, (lda, st, i.kernel)
+    # the same limit on an N-major B: (BK-1)*ldb + N elements
+    B = _desc(BASE + (1 << 36), L.LT_BF16, [K, N], [1 << 26, 1])
+    A = _desc(BASE, L.LT_BF16, [M, K], [K, 1])
+    D = _desc(BASE + (2 << 36), L.LT_BF16, [M, N], [N, 1])
+    st, i = _plan(A, B, None, D)
+    assert st == "LT_OK" and i.kernel == L.LT_KERNEL_WAVE16
+    st, i = _plan(A, B, None, D, kernel=L.LT_KERNEL_TILED)
+    assert st == "LT_ERR_NOT_DIVISIBLE" or st == "LT_ERR_UNSUPPORTED"
+
+
 def test_plan_closed_forms_reproduce_page_arithmetic():
     """The closed forms behind the plan's LDS bill and MFMA count reproduce the
     pages' printed tile arithmetic, then give the plan's own figures."""
@@ -322,7 +344,8 @@ def test_plan_closed_forms_reproduce_page_arithmetic():
     assert round(w["tiles_128x256"] / w["sms"], 2) == w["waves_128x256"]
     _, i = _plan(*_gemm_descs(8192, 8192, 8192))
     assert i.lds_bytes == i.stages * stage_bytes(i.tile_m, i.tile_n, i.tile_k, 2)
-    assert i.mfma_per_wave_kstep == instr_per_wave(i.wave_m, i.wave_n, i.tile_k, 32, 32, 16)
+    assert (i.mfma_m, i.mfma_n, i.mfma_k) in ((32, 32, 16), (16, 16, 32))
+    assert i.mfma_per_wave_kstep == instr_per_wave(i.wave_m, i.wave_n, i.tile_k, i.mfma_m, i.mfma_n, i.mfma_k)
     assert i.grid / 256 == 4.0   # 1,024 tiles on 256 CUs: whole waves
 
 
