@@ -94,12 +94,20 @@ class Workload:
                self.C.store if self.C is not None else None, self.c.alpha, self.c.beta, layouts=self.lay,
                workspace=workspace)
 
-    def time(self, steps: int, warmup: int):
+    def time(self, steps: int, warmup: int, warmup_s: float = 0.0):
         """Wall time per step (barrier + synchronize around the timed steps)
-        and the average kernel duration from HIP events on the launch stream."""
+        and the average kernel duration from HIP events on the launch stream.
+        Warm-up runs at least `warmup` steps and at least `warmup_s` seconds:
+        under sustained MFMA load the GPU's clocks settle only after some
+        tens of milliseconds, and the timed steps should see steady state."""
         import torch
-        for i in range(warmup):
+        t_end = time.perf_counter() + warmup_s
+        i = 0
+        while i < warmup or time.perf_counter() < t_end:
             self.run(i)
+            i += 1
+            if i % 16 == 0:
+                torch.cuda.synchronize()
         torch.cuda.synchronize()
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
         torch.cuda.synchronize()
@@ -110,7 +118,8 @@ class Workload:
             ev[i][1].record()
         torch.cuda.synchronize()
         wall = (time.perf_counter() - t0) / steps
-        kern = sum(a.elapsed_time(b) for a, b in ev) / steps / 1e3
+        self.kernel_times = sorted(a.elapsed_time(b) / 1e3 for a, b in ev)
+        kern = sum(self.kernel_times) / steps
         return wall, kern
 
     def check(self, npts: int = 256):
@@ -198,6 +207,8 @@ def main():
     ap.add_argument("--only-headline", action="store_true", help="skip the other workloads (profiling runs)")
     ap.add_argument("--workload", type=int, default=3, help="headline workload (default: bf16 8192^3)")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--warmup-seconds", type=float, default=2.0,
+                    help="warm up for at least this long as well as --warmup steps (clocks settle)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a 1 GiB identity-layout copy (HBM byte-counter calibration)")
     args = ap.parse_args()
@@ -223,7 +234,7 @@ def main():
         f"wave tile {plan['wave_m']}x{plan['wave_n']}, {plan['waves']} waves, {plan['stages']} LDS stages "
         f"({plan['lds_bytes']} B), grid {plan['grid']}, {plan['mfma_per_wave_kstep']} "
         f"MFMA {plan['mfma_m']}x{plan['mfma_n']}x{plan['mfma_k']} per wave per K step")
-    wall, kern = w.time(args.steps, args.warmup)
+    wall, kern = w.time(args.steps, args.warmup, args.warmup_seconds)
     flops = w.c.flops()
     value = flops / wall / 1e12
     achieved = flops / kern / 1e12
@@ -249,6 +260,10 @@ def main():
                                f"fp32 accumulate", "M": w.c.M, "N": w.c.N, "K": w.c.K,
                    "kernel": plan["kernel_name"], "tile": [plan["tile_m"], plan["tile_n"], plan["tile_k"]],
                    "grid": plan["grid"], "pct_of_peak": round(100 * value / PEAK_TFLOPS, 2),
+                   "kernel_us": {"mean": round(kern * 1e6, 1),
+                                 "median": round(w.kernel_times[len(w.kernel_times) // 2] * 1e6, 1),
+                                 "min": round(w.kernel_times[0] * 1e6, 1)},
+                   "warmup_s": args.warmup_seconds,
                    "parity": f"{chk.n - chk.n_bad}/{chk.n} sampled outputs in bound, worst "
                              f"{chk.worst_fraction:.3f} of budget"},
         "roofline": roofline(w, plan, kern, traffic_for(tkey)),
@@ -262,7 +277,7 @@ def main():
             if p["workspace_bytes"]:
                 ws = torch.empty(p["workspace_bytes"], dtype=torch.uint8, device="cuda:0")
             x.run(0, ws)
-            xw, xk = x.time(max(10, args.steps // 2), 5)
+            xw, xk = x.time(max(10, args.steps // 2), 5, args.warmup_seconds / 2)
             xc = x.check(128)
             rec = {"kernel": p["kernel_name"], "ms_per_step": round(xw * 1e3, 4), "kernel_us": round(xk * 1e6, 2),
                    "TFLOP/s": round(x.c.flops() / xw / 1e12, 2), "parity_ok": bool(xc.ok),

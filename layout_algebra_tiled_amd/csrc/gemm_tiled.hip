@@ -44,7 +44,6 @@ struct TCfg {
     static_assert(OP_BYTES % (1024 * NW) == 0, "copy must split evenly over waves");
     static_assert(KS % 2 == 0, "fragment double buffer assumes an even K-step count");
     static_assert(IPW * (S - 1) < 64, "vmcnt counts at most 63 outstanding loads");
-    static_assert((OPI - 1) * 1024 <= 4095, "copy offsets must fit the 13-bit instruction offset");
 };
 
 __device__ __forceinline__ void tile_of(int wg, const TiledArgs& p, int* tm, int* tn) {
@@ -117,11 +116,11 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
     const int KT = p.K / BK;
 
     // ---- copy: S-stage ring, stage s at s*STAGE (A slice, then B slice).
-    // Every copy instruction of one operand writes LDS through the same base
-    // (M0 is set once per operand) and reaches its own 1 KiB through the
-    // instruction offset, which the hardware adds to both the global and the
-    // LDS address; the global source is a uniform slice base plus a per-lane
-    // 32-bit offset, minus that same instruction offset.
+    // Up to four copy instructions of one operand write LDS through the same
+    // base (M0) and reach their own 1 KiB through the instruction offset,
+    // which the hardware adds to both the global and the LDS address; the
+    // global source is a uniform slice base plus a per-lane 32-bit offset,
+    // minus that same instruction offset.
     uint32_t aoffg[Cf::OPI], boffg[Cf::OPI];
 #pragma unroll
     for (int i = 0; i < Cf::OPI; ++i) {
@@ -135,15 +134,16 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
         char* sb = sa + Cf::OP_BYTES;
         const char* ga = reinterpret_cast<const char*>(p.A) + kt * a_ks;
         const char* gb = reinterpret_cast<const char*>(p.B) + kt * b_ks;
+        // (groups of four: the instruction offset is at most 4095 bytes)
         static_for<0, Cf::OPI>([&](auto ic) {
-            constexpr int i = decltype(ic)::value;
-            const void* src = (ga - i * 1024) + aoffg[i];
-            __builtin_amdgcn_global_load_lds(src, (LDS_AS void*)sa, 16, i * 1024, 0);
+            constexpr int i = decltype(ic)::value, g = i / 4, o = (i % 4) * 1024;
+            const void* src = (ga - o) + aoffg[i];
+            __builtin_amdgcn_global_load_lds(src, (LDS_AS void*)(sa + g * 4096), 16, o, 0);
         });
         static_for<0, Cf::OPI>([&](auto ic) {
-            constexpr int i = decltype(ic)::value;
-            const void* src = (gb - i * 1024) + boffg[i];
-            __builtin_amdgcn_global_load_lds(src, (LDS_AS void*)sb, 16, i * 1024, 0);
+            constexpr int i = decltype(ic)::value, g = i / 4, o = (i % 4) * 1024;
+            const void* src = (gb - o) + boffg[i];
+            __builtin_amdgcn_global_load_lds(src, (LDS_AS void*)(sb + g * 4096), 16, o, 0);
         });
     };
 
@@ -251,22 +251,23 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
                     else
                         acc[i][j] = Tr<DT>::mfma16(bfr[cur][j], af[cur][i], acc[i][j]);
                 }
-            // Issue order for this step: after each of the first MFMAs, two
-            // fragment reads for the next step (and, in the last step, two of
-            // the slice copies), then the remaining MFMAs, which cover the
-            // reads' latency.
+            // Issue order for this step: groups of two MFMAs, then two of the
+            // slice copies (last step only), then two fragment reads for the
+            // next step, until the reads are out; the remaining MFMAs cover
+            // the reads' latency.
             if (s + 1 < KS || decltype(has_next)::value) {
-                constexpr int PAIRS = (NRD + 1) / 2;
+                constexpr int MPG = 2, VPG = 2, RPG = 2;
+                constexpr int GROUPS = (NRD + RPG - 1) / RPG;
                 const bool copies = s + 1 == KS && decltype(refill)::value;
 #pragma unroll
-                for (int q = 0; q < PAIRS; ++q) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                    if (copies && 2 * q < Cf::IPW) __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                for (int q = 0; q < GROUPS; ++q) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, MPG, 0);
+                    if (copies && VPG * q < Cf::IPW) __builtin_amdgcn_sched_group_barrier(0x020, VPG, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, RPG, 0);
                 }
-                if (copies && 2 * PAIRS < Cf::IPW)
-                    __builtin_amdgcn_sched_group_barrier(0x020, Cf::IPW - 2 * PAIRS, 0);
-                if (NMF > PAIRS) __builtin_amdgcn_sched_group_barrier(0x008, NMF - PAIRS, 0);
+                if (copies && VPG * GROUPS < Cf::IPW)
+                    __builtin_amdgcn_sched_group_barrier(0x020, Cf::IPW - VPG * GROUPS, 0);
+                if (NMF > MPG * GROUPS) __builtin_amdgcn_sched_group_barrier(0x008, NMF - MPG * GROUPS, 0);
             }
         }
         stage = stage + 1 == S ? 0 : stage + 1;
@@ -297,9 +298,15 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
 
 // The instantiation the planner launches.
 #ifndef LT_TILED_NWM
-#define LT_TILED_NWM 2
-#define LT_TILED_NWN 4
+#define LT_TILED_NWM 4
+#endif
+#ifndef LT_TILED_NWN
+#define LT_TILED_NWN 2
+#endif
+#ifndef LT_TILED_BK
 #define LT_TILED_BK 64
+#endif
+#ifndef LT_TILED_S
 #define LT_TILED_S 2
 #endif
 #ifndef LT_TILED_MF
