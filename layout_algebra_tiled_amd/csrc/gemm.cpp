@@ -182,9 +182,20 @@ lt_status make_plan(const lt_tensor* tA, const lt_tensor* tB, const lt_tensor* t
         const int64_t top = kmaj ? (rows - 1) * ld + ts.bk : (int64_t)(ts.bk - 1) * ld + rows;
         return top * 2 < (int64_t(1) << 32);
     };
-    const bool tiled_ok = p.M % ts.bm == 0 && p.N % ts.bn == 0 && p.K % ts.bk == 0 && p.K > 0 && d_n && c_n &&
-                          offsets_fit(p.a_k, p.a_k ? p.A.s0 : p.A.s1, p.M) &&
+    // Ragged M, N, K run on the tiled kernel too (edge tiles clamp their copy
+    // rows and predicate their stores, a partial K slice is zero-filled), as
+    // long as every copy moves whole 16-byte chunks: K a multiple of 8 for a
+    // K-major operand, the M (N) extent a multiple of 8 for an M-major A
+    // (N-major B).
+    const bool chunks_ok = (p.a_k ? p.K % 8 == 0 : p.M % 8 == 0) && (p.b_k ? p.K % 8 == 0 : p.N % 8 == 0);
+    const bool tiled_ok = p.K > 0 && d_n && c_n && chunks_ok && offsets_fit(p.a_k, p.a_k ? p.A.s0 : p.A.s1, p.M) &&
                           offsets_fit(p.b_k, p.b_k ? p.B.s1 : p.B.s0, p.N);
+    // Automatic choice: the 256x256 kernel when the problem holds at least
+    // one tile's worth of outputs and padding it to whole tiles adds at most
+    // half again; the 16x16 kernel otherwise.
+    const int64_t tm_ = (p.M + ts.bm - 1) / ts.bm, tn_ = (p.N + ts.bn - 1) / ts.bn;
+    const bool tiled_pays = p.M * p.N >= (int64_t)ts.bm * ts.bn &&
+                            2 * tm_ * ts.bm * tn_ * ts.bn <= 3 * p.M * p.N;
     int split = (opt && opt->split_k > 0) ? opt->split_k : 0;
     auto skinny_ok_for = [&](int s) {
         if (!(p.M <= 32 && p.a_k && p.b_k && d_n && c_n && p.N % kSkinnyBN == 0 && s >= 1)) return false;
@@ -194,7 +205,7 @@ lt_status make_plan(const lt_tensor* tA, const lt_tensor* tB, const lt_tensor* t
     if (kernel == LT_KERNEL_AUTO) {
         if (p.M <= 32 && skinny_ok_for(1)) {
             kernel = LT_KERNEL_SKINNY;
-        } else if (tiled_ok) {
+        } else if (tiled_ok && tiled_pays) {
             kernel = LT_KERNEL_TILED;
         } else {
             kernel = LT_KERNEL_WAVE16;
@@ -236,7 +247,7 @@ lt_status make_plan(const lt_tensor* tA, const lt_tensor* tB, const lt_tensor* t
             in.stages = ts.stages;
             in.lds_bytes = ts.lds_bytes;
             if (in.lds_bytes > 160 * 1024) return LT_ERR_LDS_OVERFLOW;
-            in.grid = (p.M / ts.bm) * (p.N / ts.bn);
+            in.grid = tm_ * tn_;
             // (wave_m/mf) * (wave_n/mf) * (bk/mfma_k): the analogue of counting mma
             // per warp per K slice ("CUTLASS and CuTe layouts", "The arch tag
             // is not one instruction")
@@ -363,9 +374,12 @@ lt_status lt_gemm_run(const lt_tensor* A, const lt_tensor* B, const lt_tensor* C
             a.K = (int)p.K;
             a.alpha = alpha;
             a.beta = beta;
-            // The tile grid: mode 1 of zipped_divide(D, (256,256)).
+            // The tile grid: mode 1 of zipped_divide(D', (256,256)), where D'
+            // is D's layout with M and N rounded up to whole tiles (the
+            // outputs past (M, N) are predicated off in the epilogue).
             const lt::TiledShape ts = lt::tiled_shape();
-            lt::Tree dl = lt::Tree::tuple({lt::Tree::leaf(p.M, p.D.s0), lt::Tree::leaf(p.N, 1)});
+            const int64_t mp = (p.M + ts.bm - 1) / ts.bm * ts.bm, np = (p.N + ts.bn - 1) / ts.bn * ts.bn;
+            lt::Tree dl = lt::Tree::tuple({lt::Tree::leaf(mp, p.D.s0), lt::Tree::leaf(np, 1)});
             const int64_t tiler[2] = {ts.bm, ts.bn};
             lt::Tree zd;
             st = lt::divide_shape(dl, 2, tiler, true, &zd);
@@ -373,6 +387,9 @@ lt_status lt_gemm_run(const lt_tensor* A, const lt_tensor* B, const lt_tensor* C
             lt::Tree grid = zd.mode(1);
             a.tiles_m = (int)grid.s[0];
             a.tiles_n = (int)grid.s[1];
+            const int64_t kt = (p.K + ts.bk - 1) / ts.bk, kbase = p.K - kt * ts.bk;
+            a.A0 = static_cast<const char*>(p.A.ptr) + kbase * (p.a_k ? 2 : 2 * a.lda);
+            a.B0 = static_cast<const char*>(p.B.ptr) + kbase * (p.b_k ? 2 : 2 * a.ldb);
             a.group_m = std::min(a.tiles_m, 8);
             a.xcd_remap = (a.tiles_m * a.tiles_n) % 8 == 0 ? 1 : 0;
             err = lt::launch_tiled(dt, p.a_k, p.b_k, a, stream);

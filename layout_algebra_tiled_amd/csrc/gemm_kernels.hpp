@@ -22,7 +22,9 @@ struct Wave16Args {
 };
 
 // 256x256 block-tiled kernel. A is K-major or M-major, B is K-major or
-// N-major, D and C are N-major. M, N multiples of 256, K of the K slice.
+// N-major, D and C are N-major. Any M, N, K >= 1, with copies in whole 16-byte
+// chunks: K a multiple of 8 for a K-major operand, M (N) a multiple of 8 for
+// an M-major A (N-major B). tiles_m/tiles_n = ceil(M/256)/ceil(N/256).
 struct TiledArgs {
     const uint16_t* A;
     const uint16_t* B;
@@ -34,6 +36,10 @@ struct TiledArgs {
     int tiles_m, tiles_n;
     int group_m;                  // tile rows per raster group
     int xcd_remap;                // 1: spread consecutive tiles over one XCD
+    // A and B moved to the start of K slice 0, k = kbase = K - ceil(K/BK)*BK
+    // (<= 0): a pointer offset only, never dereferenced below k = 0
+    const void* A0;
+    const void* B0;
 };
 
 // Skinny kernel: M <= 32, K-major A and B, N-major D; B streamed once.

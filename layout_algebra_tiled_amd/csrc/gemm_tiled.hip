@@ -1,5 +1,8 @@
 // Block-tiled GEMM for gfx950: D = alpha * A*B + beta * C with a 256x256 block
-// tile, fp16/bf16 operands, fp32 accumulation in 32x32x16 MFMAs.
+// tile, fp16/bf16 operands, fp32 accumulation in MFMAs (16x16x32 by default).
+// M, N and K need not be multiples of the tile: edge tiles clamp their copy
+// rows and store only the outputs inside (M, N); a partial K slice is zero-
+// filled in LDS.
 //
 // Structure (the tiled GEMM of "Layouts as Algebra: CUTLASS & CuTe", "The
 // kernel, in three lines", redesigned for CDNA4):
@@ -82,21 +85,39 @@ __host__ __device__ __forceinline__ void static_for(F&& f) {
 template <class Cf, bool KMAJ>
 struct Operand {
     // Byte offset of the source of copy instruction i (of this wave) for
-    // K slice 0, relative to the operand's base; a K slice adds kslice_bytes.
-    // K-major: element (row, k) at row*ld + k; M/N-major: at k*ld + row.
+    // the K slice that starts at k = 0, relative to the operand's base; a K
+    // slice adds kslice_bytes. K-major: element (row, k) at row*ld + k;
+    // M/N-major: at k*ld + row. Rows past the operand's extent `rows` (a
+    // ragged edge tile) are clamped to its last row (last 8-element chunk):
+    // valid memory whose products land only in outputs that are not stored.
     // (__host__ __device__: it is called from lambdas inside the kernel, which
     // the compiler treats as host-device.)
-    static __host__ __device__ __forceinline__ uint32_t offset(int64_t ld, int row0, int wave, int lane, int i) {
+    static __host__ __device__ __forceinline__ uint32_t offset(int64_t ld, int row0, int rows, int wave, int lane,
+                                                               int i) {
         const int q = dev::kCopyTV(lane + 64 * (wave * Cf::OPI + i));   // stored chunk
         if constexpr (KMAJ) {
             using T = dev::KTile<Cf::BK>;
             const int row = q / T::C;
             const int lchunk = dev::KTile<Cf::BK>::at(row, q % T::C) - T::C * row;   // involution
-            return (uint32_t)(((int64_t)(row0 + row) * ld + 8 * lchunk) * 2);
+            const int r = min(row0 + row, rows - 1);
+            return (uint32_t)(((int64_t)r * ld + 8 * lchunk) * 2);
         } else {
             const int krow = q / 32;
             const int lchunk = dev::MNTile::at(krow, q % 32) - 32 * krow;
-            return (uint32_t)(((int64_t)krow * ld + row0 + 8 * lchunk) * 2);
+            const int c = min(row0 + 8 * lchunk, rows - 8);
+            return (uint32_t)(((int64_t)krow * ld + c) * 2);
+        }
+    }
+    // K offset, within its slice, of the chunk copy instruction i of this
+    // lane fetches (K-major: the chunk's first K; M/N-major: its K row).
+    static __host__ __device__ __forceinline__ int kpos(int wave, int lane, int i) {
+        const int q = dev::kCopyTV(lane + 64 * (wave * Cf::OPI + i));
+        if constexpr (KMAJ) {
+            using T = dev::KTile<Cf::BK>;
+            const int row = q / T::C;
+            return 8 * (dev::KTile<Cf::BK>::at(row, q % T::C) - T::C * row);
+        } else {
+            return q / 32;
         }
     }
     static __host__ __device__ __forceinline__ int64_t kslice_bytes(int64_t ld) {
@@ -113,7 +134,12 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
     int tm, tn;
     tile_of(blockIdx.x, p, &tm, &tn);
     const int m0 = tm * 256, n0 = tn * 256;
-    const int KT = p.K / BK;
+    // K slices: KT = ceil(K / BK). When BK does not divide K, the K range is
+    // shifted to start at kbase = K - KT*BK < 0, so that only slice 0 is
+    // partial: its first -kbase K positions are zero-filled in LDS, and every
+    // later slice is a full, unpredicated copy.
+    const int KT = (p.K + BK - 1) / BK;
+    const int kbase = p.K - KT * BK;
 
     // ---- copy: S-stage ring, stage s at s*STAGE (A slice, then B slice).
     // Up to four copy instructions of one operand write LDS through the same
@@ -124,16 +150,21 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
     uint32_t aoffg[Cf::OPI], boffg[Cf::OPI];
 #pragma unroll
     for (int i = 0; i < Cf::OPI; ++i) {
-        aoffg[i] = Operand<Cf, Cf::AK>::offset(p.lda, m0, wave, lane, i);
-        boffg[i] = Operand<Cf, Cf::BKM>::offset(p.ldb, n0, wave, lane, i);
+        aoffg[i] = Operand<Cf, Cf::AK>::offset(p.lda, m0, p.M, wave, lane, i);
+        boffg[i] = Operand<Cf, Cf::BKM>::offset(p.ldb, n0, p.N, wave, lane, i);
     }
     const int64_t a_ks = Operand<Cf, Cf::AK>::kslice_bytes(p.lda);
     const int64_t b_ks = Operand<Cf, Cf::BKM>::kslice_bytes(p.ldb);
+    // slice 0 sources: the operands' bases moved by kbase (the host does
+    // that, so the slice address stays a kernel argument plus a multiple of
+    // the slice stride); lanes whose chunk lies below K = 0 never load
+    const char* a_k0 = reinterpret_cast<const char*>(p.A0);
+    const char* b_k0 = reinterpret_cast<const char*>(p.B0);
     auto issue = [&](int stage, int kt) {
         char* sa = smem + stage * Cf::STAGE + wave * Cf::OPI * 1024;
         char* sb = sa + Cf::OP_BYTES;
-        const char* ga = reinterpret_cast<const char*>(p.A) + kt * a_ks;
-        const char* gb = reinterpret_cast<const char*>(p.B) + kt * b_ks;
+        const char* ga = a_k0 + kt * a_ks;
+        const char* gb = b_k0 + kt * b_ks;
         // (groups of four: the instruction offset is at most 4095 bytes)
         static_for<0, Cf::OPI>([&](auto ic) {
             constexpr int i = decltype(ic)::value, g = i / 4, o = (i % 4) * 1024;
@@ -144,6 +175,32 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
             constexpr int i = decltype(ic)::value, g = i / 4, o = (i % 4) * 1024;
             const void* src = (gb - o) + boffg[i];
             __builtin_amdgcn_global_load_lds(src, (LDS_AS void*)(sb + g * 4096), 16, o, 0);
+        });
+    };
+
+    // Slice 0 when it is partial: a lane whose chunk lies below K = 0 writes
+    // zeros where the copy would have put it (the copy's lane-linear LDS
+    // position) instead of loading.
+    auto issue_first_partial = [&]() {
+        char* sa = smem + wave * Cf::OPI * 1024;
+        char* sb = sa + Cf::OP_BYTES;
+        static_for<0, Cf::OPI>([&](auto ic) {
+            constexpr int i = decltype(ic)::value, g = i / 4, o = (i % 4) * 1024;
+            if (kbase + Operand<Cf, Cf::AK>::kpos(wave, lane, i) >= 0) {
+                const void* src = (a_k0 - o) + aoffg[i];
+                __builtin_amdgcn_global_load_lds(src, (LDS_AS void*)(sa + g * 4096), 16, o, 0);
+            } else {
+                *(LDS_AS u32x4*)(sa + g * 4096 + o + 16 * lane) = u32x4{0u, 0u, 0u, 0u};
+            }
+        });
+        static_for<0, Cf::OPI>([&](auto ic) {
+            constexpr int i = decltype(ic)::value, g = i / 4, o = (i % 4) * 1024;
+            if (kbase + Operand<Cf, Cf::BKM>::kpos(wave, lane, i) >= 0) {
+                const void* src = (b_k0 - o) + boffg[i];
+                __builtin_amdgcn_global_load_lds(src, (LDS_AS void*)(sb + g * 4096), 16, o, 0);
+            } else {
+                *(LDS_AS u32x4*)(sb + g * 4096 + o + 16 * lane) = u32x4{0u, 0u, 0u, 0u};
+            }
         });
     };
 
@@ -209,8 +266,12 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
             for (int v = 0; v < Mf::NACC; ++v) acc[i][j][v] = 0.0f;
 
     // ---- prologue: slices 0 .. S-1
+    if (kbase < 0)
+        issue_first_partial();
+    else
+        issue(0, 0);
 #pragma unroll
-    for (int s = 0; s < S; ++s)
+    for (int s = 1; s < S; ++s)
         if (s < KT) issue(s, s);
     if (KT >= S)
         LT_WAIT_VM(Cf::IPW * (S - 1));
@@ -280,20 +341,40 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
     slice(no, no, t);                             // the last slice
 
     // ---- epilogue: block (i, j), registers 4g..4g+3 hold row m = lane % MF
-    // and four consecutive columns of the MF x MF block
+    // and four consecutive columns of the MF x MF block. A tile on a ragged
+    // edge stores only the outputs inside (M, N).
+    auto epilogue = [&](auto edge) {
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
-        const int m = m0 + arow0 + i * Cf::MF + Mf::out_col(lane);
+        for (int i = 0; i < FM; ++i) {
+            const int m = m0 + arow0 + i * Cf::MF + Mf::out_col(lane);
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
+            for (int j = 0; j < FN; ++j) {
 #pragma unroll
-            for (int g = 0; g < Mf::NACC / 4; ++g) {
-                const int n = n0 + brow0 + j * Cf::MF + Mf::out_row(lane, 4 * g);
-                store4<DT>(p.D, p.C, (int64_t)m * p.ldd + n, (int64_t)m * p.ldc + n, acc[i][j][4 * g],
-                           acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3], p.alpha, p.beta);
+                for (int g = 0; g < Mf::NACC / 4; ++g) {
+                    const int n = n0 + brow0 + j * Cf::MF + Mf::out_row(lane, 4 * g);
+                    const float v[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                                        acc[i][j][4 * g + 3]};
+                    if constexpr (decltype(edge)::value) {
+                        if (m < p.M && n < p.N) {
+                            if (n + 4 <= p.N)
+                                store4<DT>(p.D, p.C, (int64_t)m * p.ldd + n, (int64_t)m * p.ldc + n, v[0], v[1],
+                                           v[2], v[3], p.alpha, p.beta);
+                            else
+                                store_n<DT>(p.D, p.C, (int64_t)m * p.ldd + n, (int64_t)m * p.ldc + n, v,
+                                            p.N - n, p.alpha, p.beta);
+                        }
+                    } else {
+                        store4<DT>(p.D, p.C, (int64_t)m * p.ldd + n, (int64_t)m * p.ldc + n, v[0], v[1], v[2],
+                                   v[3], p.alpha, p.beta);
+                    }
+                }
             }
         }
-    }
+    };
+    if (m0 + 256 > p.M || n0 + 256 > p.N)
+        epilogue(std::true_type{});
+    else
+        epilogue(std::false_type{});
 }
 
 // The instantiation the planner launches.

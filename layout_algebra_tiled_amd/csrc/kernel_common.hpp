@@ -82,4 +82,16 @@ __device__ __forceinline__ void store4(uint16_t* D, const uint16_t* C, int64_t d
     *reinterpret_cast<u32x2*>(D + dof) = o;
 }
 
+// The same for the first cnt (1..3) of four outputs, one 2-byte store each:
+// the last, partial group of a row that ends inside a tile.
+template <int DT>
+__device__ __forceinline__ void store_n(uint16_t* D, const uint16_t* C, int64_t dof, int64_t cof, const float* a,
+                                        int cnt, float alpha, float beta) {
+    for (int e = 0; e < cnt; ++e) {
+        float v = alpha * a[e];
+        if (beta != 0.0f) v += beta * Tr<DT>::to_f32(C[cof + e]);
+        D[dof + e] = Tr<DT>::from_f32(v);
+    }
+}
+
 }  // namespace lt

@@ -75,6 +75,37 @@ def test_tiled_padded_leading_dimensions():
 
 
 # ---------------------------------------------------------------------------
+# ragged shapes on the 256x256 kernel: edge tiles clamp their copy rows and
+# predicate their stores; a partial K slice is zero-filled (every output)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("M,N,K,dtype,a_major,b_major,alpha,beta,lds", [
+    (300, 520, 200, BF16, "row", "col", 1.0, 0.5, None),           # ragged M and N, K = 3*64 + 8
+    (257, 258, 136, F16, "row", "col", 1.0, -1.0, (136, 136, 264)),  # N % 4 = 2: partial 4-output groups
+    (512, 256, 8, BF16, "row", "col", 1.0, 0.0, None),             # a single, partial K slice
+    (264, 392, 77, F16, "col", "row", 2.0, -1.0, None),            # M-/N-major operands, any K
+    (520, 264, 1000, BF16, "col", "col", 1.0, 0.0, None),          # M-major A, K-major B
+    (1, 300, 64, F16, "row", "col", 1.0, 0.0, None),               # one row
+    (700, 9, 328, BF16, "row", "col", 1.0, 1.0, (328, 328, 16)),   # nine columns, padded D and C
+])
+def test_tiled_ragged_all_outputs(M, N, K, dtype, a_major, b_major, alpha, beta, lds):
+    A, B, C, D = _case(M, N, K, dtype, a_major, b_major, "row", alpha, beta, seed=M + N + K, lds=lds)
+    res, plan, _ = run_and_check(A, B, C, D, alpha, beta, kernel="tiled", expect_kernel="tiled",
+                                 label="tiled-ragged")
+    _ok(res)
+    assert plan["grid"] == ((M + 255) // 256) * ((N + 255) // 256)
+
+
+def test_tiled_ragged_large_auto():
+    """A ragged shape large enough for the automatic choice to take the 256x256 kernel."""
+    M, N, K = 1000, 1304, 1000
+    A, B, C, D = _case(M, N, K, BF16, "row", "col", "row", 1.0, 0.25, dist="normal_over_sqrtk", seed=5)
+    pts = sample_points(M, N, 3000, seed=5)
+    res, plan, _ = run_and_check(A, B, C, D, 1.0, 0.25, points=pts, expect_kernel="tiled", label="ragged-auto")
+    _ok(res)
+
+
+# ---------------------------------------------------------------------------
 # layout variants, ragged shapes, degenerate cases (wave-per-tile kernel)
 # ---------------------------------------------------------------------------
 

@@ -369,10 +369,19 @@ def test_plan_validation_statuses():
     A, B, C, D = _gemm_descs(256, 256, 64)
     A.dtype = L.LT_F16
     assert _plan(A, B, C, D)[0] == "LT_ERR_UNSUPPORTED"
-    # forcing the tiled kernel on a ragged shape
+    # a ragged shape: the tiled kernel takes it when forced (edge tiles are
+    # predicated); the automatic choice keeps a problem smaller than one tile
+    # on the 16x16 kernel
     A, B, C, D = _gemm_descs(250, 256, 64)
-    assert _plan(A, B, C, D, kernel=L.LT_KERNEL_TILED)[0] == "LT_ERR_NOT_DIVISIBLE"
+    st, i = _plan(A, B, C, D, kernel=L.LT_KERNEL_TILED)
+    assert st == "LT_OK" and i.kernel == L.LT_KERNEL_TILED and i.grid == 1
     assert _plan(A, B, C, D)[1].kernel == L.LT_KERNEL_WAVE16
+    # K-major operands copy whole 16-byte chunks of K: K % 8 != 0 is refused
+    A = _desc(BASE, L.LT_BF16, [256, 60], [64, 1])
+    B = _desc(BASE + (1 << 30), L.LT_BF16, [60, 256], [1, 64])
+    D = _desc(BASE + (2 << 30), L.LT_BF16, [256, 256], [256, 1])
+    assert _plan(A, B, None, D, kernel=L.LT_KERNEL_TILED)[0] == "LT_ERR_NOT_DIVISIBLE"
+    assert _plan(A, B, None, D)[1].kernel == L.LT_KERNEL_WAVE16
     # D overlapping A
     A, B, C, D = _gemm_descs(256, 256, 64)
     D.ptr = A.ptr + 64
@@ -387,6 +396,17 @@ def test_plan_validation_statuses():
     A, B, C, D = _gemm_descs(32, 1024, 8192)
     st = L.lib().lt_gemm_run(ctypes.byref(A), ctypes.byref(B), None, ctypes.byref(D), 1.0, 0.0, None, None, 0, None)
     assert L.STATUS_NAMES[st] == "LT_ERR_WORKSPACE"
+
+
+def test_plan_ragged_shapes_on_the_tiled_kernel():
+    """Ragged M, N and K plan onto the 256x256 kernel with a ceil-divided tile
+    grid when padding to whole tiles adds at most half again."""
+    for (M, N, K), expect in (((1000, 1304, 1000), L.LT_KERNEL_TILED), ((4000, 4000, 4000), L.LT_KERNEL_TILED),
+                              ((296, 296, 296), L.LT_KERNEL_WAVE16), ((8192, 8200, 8192), L.LT_KERNEL_TILED)):
+        st, i = _plan(*_gemm_descs(M, N, K))
+        assert st == "LT_OK" and i.kernel == expect, (M, N, K, st, i.kernel)
+        if expect == L.LT_KERNEL_TILED:
+            assert i.grid == -(-M // 256) * -(-N // 256)
 
 
 def test_plan_m_major_output_is_transposed():
