@@ -170,6 +170,27 @@ lt_status lt_logical_divide(const lt_layout* A, const lt_layout* tiler, lt_layou
  * modes past n are kept whole. Result mode i is (in-tile, tile-index). */
 lt_status lt_logical_divide_shape(const lt_layout* A, int32_t n, const int64_t* tiler, lt_layout* out);
 
+/* logical_product(A, B) = (A, complement(A, size(A)*cosize(B)) o B) [P4
+ * "Divide is tiling": the mirror of the divide, which lays copies of a tile
+ * out in a pattern of repetition; the formula is a reading that mirrors the
+ * divide's A o (B, B*)]. Mode 0 is A; mode 1 places copy j of A at offset
+ * A*(B(j)), in the room A leaves free. E.g. (2,2):(1,2) by 3:1 gives
+ * ((2,2),3):((1,2),4). LT_ERR_NOT_ADMISSIBLE when A's complement in
+ * [0, size(A)*cosize(B)) does not exist (A's footprint must divide it). */
+lt_status lt_logical_product(const lt_layout* A, const lt_layout* B, lt_layout* out);
+
+/* Thread-value layout [P4 "The threads are a layout too"]: for a
+ * column-major tile whose mode i has extent thr[i]*val[i], the layout
+ * ((T_0..T_n-1),(V_0..V_n-1)) -> offset in the tile (for n == 1 simply
+ * (T,V)). Per mode, blocked[i] == 0 interleaves the threads (thread t takes
+ * t, t+T, t+2T, ...: logical_product(T:1, V:1) = (T,V):(1,T)); blocked[i] != 0
+ * gives each thread a run of V (logical_product(V:1, T:1) with its modes
+ * swapped = (T,V):(V,1)). The page's two examples for 8 threads and 32 values
+ * are (8,4):(1,8) and (8,4):(4,1). blocked may be NULL (all interleaved).
+ * 1 <= n <= 8. */
+lt_status lt_make_tv_layout(int32_t n, const int64_t* thr, const int64_t* val, const uint8_t* blocked,
+                            lt_layout* out);
+
 /* zipped_divide [P1 "A layout is a shape and a stride"]: the shape-tiler
  * division regrouped so that mode 0 gathers all in-tile modes and mode 1 all
  * tile-index modes (plus untiled modes). E.g. (256,128):(128,1) by (16,16)

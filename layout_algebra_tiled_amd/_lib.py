@@ -81,6 +81,8 @@ SIGNATURES = {
     "lt_compose": ([_L, _L, _L], ctypes.c_int),
     "lt_complement": ([_L, _i64, _L], ctypes.c_int),
     "lt_logical_divide": ([_L, _L, _L], ctypes.c_int),
+    "lt_logical_product": ([_L, _L, _L], ctypes.c_int),
+    "lt_make_tv_layout": ([_i32, _P(_i64), _P(_i64), _P(ctypes.c_uint8), _L], ctypes.c_int),
     "lt_logical_divide_shape": ([_L, _i32, _P(_i64), _L], ctypes.c_int),
     "lt_zipped_divide": ([_L, _i32, _P(_i64), _L], ctypes.c_int),
     "lt_local_tile": ([_L, _i32, _P(_i64), _P(_i64), _P(ctypes.c_uint8), _P(_i64), _L], ctypes.c_int),

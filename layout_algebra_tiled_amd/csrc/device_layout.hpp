@@ -94,16 +94,31 @@ struct MNTile {
     }
 };
 
+// Thread-value layouts of one mode, as logical products of compact 1-D
+// layouts ("Layouts as Algebra", "The threads are a layout too"): with T
+// threads and V values per thread,
+//   interleaved = logical_product(T:1, V:1) = (T,V):(1,T) -- on one step the
+//                 threads take T consecutive offsets (a coalesced access);
+//   blocked     = logical_product(V:1, T:1), modes swapped, = (T,V):(V,1) --
+//                 each thread owns a run of V.
+// For compact inputs the complement inside the product is the single leaf
+// (V):(T) (resp. (T):(V)), which gives these closed forms; the host library
+// builds the same layouts through its complement and composition
+// (lt_make_tv_layout), and the tests compare the two.
+LT_HD constexpr Flat<2> tv_interleaved(int T, int V) { return Flat<2>{{T, V}, {1, T}}; }
+LT_HD constexpr Flat<2> tv_blocked(int T, int V) { return Flat<2>{{T, V}, {V, 1}}; }
+
 // Direct-to-LDS copy: one instruction of one wave writes 64 consecutive
 // stored chunks (1 KiB); the thread-value layout is lane -> stored chunk, so a
 // lane fetches the logical chunk that the swizzle puts there. Both swizzles
 // are involutions on (row, chunk), so the logical chunk is the stored one
-// swizzled again.
-constexpr Flat<2> kCopyTV{{64, 1 << 10}, {1, 64}};     // (lane, instr) -> stored chunk
+// swizzled again. 64 lanes interleaved over the copy instructions (values).
+constexpr Flat<2> kCopyTV = tv_interleaved(64, 1 << 10);   // (lane, instr) -> stored chunk
 
 // MFMA 32x32x16 operand fragment: lane l holds row l%32 and K values
-// 8*(l/32) .. 8*(l/32)+7 of a 16-deep K step: (row, half) = (32,2):(1,32).
-constexpr Flat<2> kFragLane{{32, 2}, {1, 32}};
+// 8*(l/32) .. 8*(l/32)+7 of a 16-deep K step: (row, half) = (32,2):(1,32),
+// the interleaved split of the 64 lanes over the 32 rows.
+constexpr Flat<2> kFragLane = tv_interleaved(32, 2);
 
 // Transposed LDS read (ds_read_b64_tr_b16), measured on gfx950: inside each
 // group of 16 lanes, lane i receives as element e the (i % 4)-th 16-bit value
@@ -133,7 +148,7 @@ struct Mfma {
     static constexpr int KSTEP = 512 / MF;         // K per instruction
     static constexpr int CHUNKS = KSTEP / 8;       // 16-byte K chunks per step
     static constexpr int NACC = MF * MF / 64;      // accumulator registers per lane
-    static constexpr Flat<2> frag{{MF, 64 / MF}, {1, MF}};
+    static constexpr Flat<2> frag = tv_interleaved(MF, 64 / MF);   // lane -> (row, K chunk)
     LT_HD static constexpr int frag_row(int lane) { return lane % MF; }
     LT_HD static constexpr int frag_chunk(int lane) { return lane / MF; }
     LT_HD static constexpr int tr_krow(int lane, int q) { return 8 * (lane / MF) + 4 * q + ((lane & 15) >> 2); }

@@ -399,6 +399,68 @@ lt_status divide_shape(const Tree& A, int n, const int64_t* tiler, bool zipped, 
 }
 
 // ---------------------------------------------------------------------------
+// products and thread-value layouts
+// ---------------------------------------------------------------------------
+
+// logical_product(A, B) = (A, complement(A, size(A) * cosize(B)) o B): mode 0
+// is the tile A, mode 1 lays copies of it out in the pattern B, each copy in
+// the room A leaves free ("Layouts as Algebra", "Divide is tiling": the
+// mirror of logical_divide = A o (B, B*)).
+lt_status logical_product(const Tree& A, const Tree& B, Tree* out) {
+    if (empty(A) || empty(B)) return LT_ERR_INVALID_LAYOUT;
+    int64_t na, cb, M;
+    lt_status st = tree_size(A, &na);
+    if (st != LT_OK) return st;
+    st = tree_cosize(B, &cb);
+    if (st != LT_OK) return st;
+    if (!mul_ok(na, cb, &M)) return LT_ERR_OUT_OF_RANGE;
+    Tree ac, rep;
+    st = complement(A, M, &ac);
+    if (st != LT_OK) return st;
+    st = compose(ac, B, &rep);
+    if (st != LT_OK) return st;
+    Tree res = Tree::tuple({A, rep});
+    if (res.s.size() > LT_MAX_LEAVES || res.code.size() > LT_MAX_NODES) return LT_ERR_CAPACITY;
+    *out = std::move(res);
+    return LT_OK;
+}
+
+// Thread-value layout of a column-major tile with extent thr[i]*val[i] in
+// mode i ("Layouts as Algebra", "The threads are a layout too"). Per mode:
+// interleaved, logical_product(T:1, V:1) = (T,V):(1,T) (on one step the
+// threads take consecutive offsets); blocked, logical_product(V:1, T:1) with
+// its two modes swapped = (T,V):(V,1) (each thread owns a run of V). Each
+// mode's pair is composed with the tile's mode layout E_i:S_i (S_i the
+// product of the earlier extents), and the modes are zipped into
+// ((T_0,...),(V_0,...)).
+lt_status make_tv(int n, const int64_t* thr, const int64_t* val, const uint8_t* blocked, Tree* out) {
+    if (n < 1 || n > 8 || !thr || !val) return LT_ERR_INVALID_ARGUMENT;
+    std::vector<Tree> tm, vm;
+    int64_t stride = 1;
+    for (int i = 0; i < n; ++i) {
+        if (thr[i] < 1 || val[i] < 1) return LT_ERR_INVALID_LAYOUT;
+        const bool blk = blocked && blocked[i];
+        Tree p;
+        lt_status st = blk ? logical_product(Tree::leaf(val[i], 1), Tree::leaf(thr[i], 1), &p)
+                           : logical_product(Tree::leaf(thr[i], 1), Tree::leaf(val[i], 1), &p);
+        if (st != LT_OK) return st;
+        if (blk) p = Tree::tuple({p.mode(1), p.mode(0)});
+        int64_t ext;
+        if (!mul_ok(thr[i], val[i], &ext)) return LT_ERR_OUT_OF_RANGE;
+        Tree scaled;
+        st = compose(Tree::leaf(ext, stride), p, &scaled);
+        if (st != LT_OK) return st;
+        tm.push_back(scaled.mode(0));
+        vm.push_back(scaled.mode(1));
+        if (!mul_ok(stride, ext, &stride)) return LT_ERR_OUT_OF_RANGE;
+    }
+    Tree res = n == 1 ? Tree::tuple({tm[0], vm[0]}) : Tree::tuple({Tree::tuple(tm), Tree::tuple(vm)});
+    if (res.s.size() > LT_MAX_LEAVES || res.code.size() > LT_MAX_NODES) return LT_ERR_CAPACITY;
+    *out = std::move(res);
+    return LT_OK;
+}
+
+// ---------------------------------------------------------------------------
 // text
 // ---------------------------------------------------------------------------
 
@@ -742,6 +804,27 @@ lt_status lt_logical_divide(const lt_layout* A, const lt_layout* tiler, lt_layou
     st = lt::complement(b, na, &bc);
     if (st != LT_OK) return st;
     st = lt::compose(a, Tree::tuple({b, bc}), &r);
+    if (st != LT_OK) return st;
+    return lt::to_pod(r, out);
+}
+
+lt_status lt_logical_product(const lt_layout* A, const lt_layout* B, lt_layout* out) {
+    Tree a, b, r;
+    lt_status st = lt::from_pod(A, &a);
+    if (st != LT_OK) return st;
+    st = lt::from_pod(B, &b);
+    if (st != LT_OK) return st;
+    if (!out) return LT_ERR_INVALID_ARGUMENT;
+    st = lt::logical_product(a, b, &r);
+    if (st != LT_OK) return st;
+    return lt::to_pod(r, out);
+}
+
+lt_status lt_make_tv_layout(int32_t n, const int64_t* thr, const int64_t* val, const uint8_t* blocked,
+                            lt_layout* out) {
+    if (!out) return LT_ERR_INVALID_ARGUMENT;
+    Tree r;
+    lt_status st = lt::make_tv(n, thr, val, blocked, &r);
     if (st != LT_OK) return st;
     return lt::to_pod(r, out);
 }

@@ -38,6 +38,8 @@ Tree coalesce(const Tree& t);
 lt_status compose(const Tree& A, const Tree& B, Tree* out);
 lt_status complement(const Tree& B, int64_t M, Tree* out);
 lt_status divide_shape(const Tree& A, int n, const int64_t* tiler, bool zipped, Tree* out);
+lt_status logical_product(const Tree& A, const Tree& B, Tree* out);
+lt_status make_tv(int n, const int64_t* thr, const int64_t* val, const uint8_t* blocked, Tree* out);
 std::string format(const Tree& t);
 
 }  // namespace lt

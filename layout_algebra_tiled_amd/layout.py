@@ -176,6 +176,24 @@ class Layout:
                   "logical_divide")
         return Layout(c)
 
+    def logical_product(self, B: "Layout") -> "Layout":
+        c = lt_layout()
+        check(lib().lt_logical_product(ctypes.byref(self._c), ctypes.byref(B._c), ctypes.byref(c)),
+              "logical_product")
+        return Layout(c)
+
+    @staticmethod
+    def tv(thr: Sequence[int], val: Sequence[int], blocked: Optional[Sequence[int]] = None) -> "Layout":
+        """Thread-value layout of a column-major tile of extents thr[i]*val[i]
+        (lt_make_tv_layout): ((threads), (values)) -> offset."""
+        n = len(thr)
+        t = (ctypes.c_int64 * n)(*thr)
+        v = (ctypes.c_int64 * n)(*val)
+        b = (ctypes.c_uint8 * n)(*blocked) if blocked is not None else None
+        c = lt_layout()
+        check(lib().lt_make_tv_layout(n, t, v, b, ctypes.byref(c)), "make_tv_layout")
+        return Layout(c)
+
     def zipped_divide(self, tiler: Sequence[int]) -> "Layout":
         t = tuple(tiler)
         arr = (ctypes.c_int64 * len(t))(*t)

@@ -558,3 +558,42 @@ def local_partition(T: Layout, thr: Layout, t: int, step=None) -> Tuple[int, Lay
     tile, rest = zd.mode(0), zd.mode(1)
     offset = evaluate(tile, tuple(tcoord))
     return offset, rest
+
+
+# --------------------------------------------------------------------------
+# products and thread-value layouts
+# --------------------------------------------------------------------------
+
+def logical_product(A: Layout, B: Layout) -> Layout:
+    """READING of "Layouts as Algebra", "Divide is tiling": the product lays
+    copies of the tile A out in the pattern B and mirrors the divide
+    A o (B, B*). Mode 0 is A itself; mode 1 is B read through the complement
+    of A in [0, size(A) * cosize(B)), so copy j of the tile starts where the
+    complement puts B(j): (A, complement(A, size(A)*cosize(B)) o B)."""
+    _nonempty(A, B)
+    return make_tuple_layout(A, compose(complement(A, size(A) * cosize(B)), B))
+
+
+def product_copies(A: Layout, B: Layout) -> List[List[int]]:
+    """The definition of the product spelled out as sets: the translates T of
+    A in [0, size(A)*cosize(B)) (complement_translates, the greedy tiling),
+    and copy j of A placed at translate T[B(j)]. Returns, per copy j, the
+    offsets A(i) + T[B(j)] in i order."""
+    T = complement_translates(A, size(A) * cosize(B))
+    return [[evaluate(A, i) + T[evaluate(B, j)] for i in range(size(A))] for j in range(size(B))]
+
+
+def tv_offset(thr: Sequence[int], val: Sequence[int], blocked: Sequence[int], t: Sequence[int],
+              v: Sequence[int]) -> int:
+    """Offset, in the column-major tile of extents thr[i]*val[i], of value v
+    of thread t ("Layouts as Algebra", "The threads are a layout too"). Per
+    mode: interleaved, thread t's values are t, t + T, t + 2T, ... (on any
+    one step the threads take consecutive offsets); blocked, thread t owns
+    the run t*V .. t*V + V - 1. Written out directly, mode by mode."""
+    off, scale = 0, 1
+    for i in range(len(thr)):
+        T, V = thr[i], val[i]
+        pos = t[i] * V + v[i] if blocked[i] else t[i] + T * v[i]
+        off += pos * scale
+        scale *= T * V
+    return off

@@ -172,3 +172,29 @@ def test_fragment_and_accumulator_maps(maps):
     assert cells == {(r, c) for r in range(32) for c in range(32)}
     copy = maps[("copy",)]
     assert copy == list(range(256))
+
+
+def test_kernel_thread_value_maps_are_the_library_products(maps):
+    """The copy's (lane, instruction) -> stored chunk map and the MFMA operand
+    fragments (lane -> (row, K chunk)) are built in device code by the
+    interleaved thread-value builder; the host library builds the same
+    layouts through complement and composition (lt_make_tv_layout)."""
+    copy = maps[("copy",)]
+    tv = Layout.tv([64], [4])
+    assert copy == [tv(l + 64 * i) for i in range(4) for l in range(64)]
+    frag = maps[("frag",)]
+    tv32 = Layout.tv([32], [2])
+    assert frag == [tv32(l) for l in range(64)]
+    for mf in (16, 32):
+        key = next(k for k in maps if k[0] == "mfrag" and k[1] == str(mf))
+        fr = maps[key]
+        tvm = Layout.tv([mf], [64 // mf])
+        assert [fr[3 * l + 2] for l in range(64)] == [tvm(l) for l in range(64)]
+        # the same fragment in element space of the column-major (MF, KSTEP)
+        # operand atom: lanes (MF rows, 64/MF K groups) x 8 values along K,
+        # blocked in the K mode
+        el = Layout.tv([mf, 64 // mf], [1, 8], [0, 1])
+        for l in range(64):
+            for v in range(8):
+                row, kk = l % mf, 8 * (l // mf) + v
+                assert el([l, v]) == row + mf * kk

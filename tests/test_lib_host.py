@@ -9,6 +9,7 @@ import os
 import random
 import re
 
+import numpy as np
 import pytest
 
 from layout_algebra_tiled_amd import Layout, LtError
@@ -154,6 +155,44 @@ def test_complement_matches_oracle():
                 assert (lib_e is None) == (or_e is None), (str(b), M)
                 if lib_e is None:
                     assert str(lib_r) == str(or_r)
+
+
+def test_logical_product_matches_oracle_including_refusals():
+    rng = random.Random(14)
+    admitted = 0
+    for _ in range(2000):
+        a, b = _rand(rng, max_extent=3, max_stride=6), _rand(rng, max_extent=3, max_stride=4)
+        lib_r, lib_e = status_of(lambda: Lb(a).logical_product(Lb(b)))
+        or_r, or_e = status_of(lambda: ol.logical_product(a, b))
+        assert (lib_e is None) == (or_e is None), (str(a), str(b), lib_e, or_e)
+        if lib_e is None:
+            admitted += 1
+            assert str(lib_r) == str(or_r), (str(a), str(b))
+        else:
+            assert lib_e in ("LT_ERR_NOT_ADMISSIBLE", "LT_ERR_CAPACITY") and or_e == "NotAdmissible"
+    assert admitted > 200
+
+
+def test_tv_layouts_match_oracle_definition():
+    """lt_make_tv_layout against the oracle's direct per-mode definition, and
+    the page's two 8-thread layouts through the library."""
+    g = GOLD["tv_layouts"]
+    assert str(Layout.tv([8], [4])) == g["coalesced"]
+    assert str(Layout.tv([8], [4], [1])) == g["strided"]
+    rng = random.Random(15)
+    for _ in range(200):
+        k = rng.randint(1, 3)
+        thr = [rng.randint(1, 5) for _ in range(k)]
+        val = [rng.randint(1, 5) for _ in range(k)]
+        blk = [rng.randint(0, 1) for _ in range(k)]
+        tv = Layout.tv(thr, val, blk)
+        for t in itertools.product(*[range(x) for x in thr]):
+            for v in itertools.product(*[range(x) for x in val]):
+                # one integer per top-level mode, unravelled colexicographically
+                ti = sum(t[i] * int(np.prod(thr[:i])) for i in range(k))
+                vi = sum(v[i] * int(np.prod(val[:i])) for i in range(k))
+                got = tv([ti, vi])
+                assert got == ol.tv_offset(thr, val, blk, t, v), (thr, val, blk, t, v)
 
 
 def test_divides_and_tiles_match_oracle():

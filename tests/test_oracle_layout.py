@@ -400,3 +400,126 @@ def test_empty_layout():
                lambda: ol.zipped_divide(E, (2, 2))):
         with pytest.raises(ValueError):
             op()
+
+
+# ---------------------------------------------------------------------------
+# logical_product and thread-value layouts ("Layouts as Algebra", "Divide is
+# tiling" and "The threads are a layout too")
+# ---------------------------------------------------------------------------
+
+def _compact_layout(rng, max_modes=3, max_extent=4):
+    """A compact layout: the extents in a random order, strides the running
+    products in that order (a bijection onto [0, size))."""
+    k = rng.randint(1, max_modes)
+    shape = [rng.randint(1, max_extent) for _ in range(k)]
+    order = list(range(k))
+    rng.shuffle(order)
+    stride, run = [0] * k, 1
+    for i in order:
+        stride[i] = run
+        run *= shape[i]
+    return Layout(tuple(shape), tuple(stride)) if k > 1 else Layout(shape[0], stride[0])
+
+
+def test_tv_builders_reproduce_the_pages_two_layouts():
+    """The page's two thread-value layouts for 8 threads and 32 values: the
+    interleaved builder gives thread t the values t, t+8, t+16, t+24 and the
+    blocked builder the run 4t .. 4t+3 -- value for value the printed
+    (8,4):(1,8) and (8,4):(4,1)."""
+    g = GOLD["tv_layouts"]
+    good, bad = P(g["coalesced"]), P(g["strided"])
+    for t in range(8):
+        for v in range(4):
+            assert ol.tv_offset([8], [4], [0], [t], [v]) == good((t, v))
+            assert ol.tv_offset([8], [4], [1], [t], [v]) == bad((t, v))
+    # and the product construction yields exactly those printed layouts
+    assert str(ol.logical_product(P("8:1"), P("4:1"))) == g["coalesced"]
+    swapped = ol.logical_product(P("4:1"), P("8:1"))
+    assert str(Layout((swapped.shape[1], swapped.shape[0]), (swapped.stride[1], swapped.stride[0]))) == g["strided"]
+
+
+def test_logical_product_closed_form_for_compact_tiles():
+    """For a compact tile A (a bijection onto [0, size(A))) the copies are
+    whole shifted blocks: product(i, j) = A(i) + size(A) * B(j). Mode 0 is A
+    itself."""
+    rng = random.Random(17)
+    checked = 0
+    for _ in range(600):
+        A = _compact_layout(rng)
+        B = _compact_layout(rng) if rng.random() < 0.5 else _random_layout(rng, max_stride=5)
+        try:
+            R = ol.logical_product(A, B)
+        except ol.NotAdmissible:
+            # the composition with B needs exact cuts (the composition
+            # reading); a compact B always has them
+            assert sorted(ol.enumerate_offsets(B)) != list(range(ol.size(B)))
+            continue
+        checked += 1
+        assert R.mode(0) == A
+        n = ol.size(A)
+        for j in range(ol.size(B)):
+            for i in range(n):
+                assert R(i + n * j) == A(i) + n * B(j)
+    assert checked > 300
+
+
+def test_logical_product_matches_the_tiling_definition():
+    """Any admissible A: copy j of the tile sits at the B(j)-th translate of
+    the greedy tiling of [0, size(A)*cosize(B)) by A (complement_translates,
+    pinned against the closed complement elsewhere)."""
+    rng = random.Random(23)
+    checked = 0
+    for _ in range(600):
+        A = _random_layout(rng, max_modes=2, max_extent=3, max_stride=6)
+        B = _random_layout(rng, max_modes=2, max_extent=3, max_stride=4)
+        try:
+            R = ol.logical_product(A, B)
+        except ol.NotAdmissible:
+            continue   # no complement, or a composition without exact cuts
+        copies = ol.product_copies(A, B)
+        n = ol.size(A)
+        for j in range(ol.size(B)):
+            assert [R(i + n * j) for i in range(n)] == copies[j]
+        checked += 1
+    assert checked > 100
+
+
+def test_logical_product_fills_the_holes_of_a_strided_tile():
+    """A tile with gaps (2:2 covers 0 and 2): the copies go into the gaps."""
+    R = ol.logical_product(P("2:2"), P("2:1"))
+    assert str(R) == "(2,2):(2,1)"
+    assert ol.product_copies(P("2:2"), P("2:1")) == [[0, 2], [1, 3]]
+
+
+def test_product_and_divide_are_mirrors():
+    """Dividing a product of compact layouts by the tile's size gives back a
+    layout with the same values: (tile, which copy)."""
+    rng = random.Random(29)
+    for _ in range(200):
+        A = _compact_layout(rng)
+        B = _compact_layout(rng)
+        R = ol.logical_product(A, B)
+        D = ol.logical_divide(ol.coalesce(R), ol.size(A))
+        assert ol.enumerate_offsets(D) == ol.enumerate_offsets(R)
+        assert sorted(ol.enumerate_offsets(R)) == list(range(ol.size(A) * ol.size(B)))
+
+
+def test_product_without_complement_is_caught():
+    """Planted mistake: (A, B) without the complement places copies on top of
+    each other; the compact closed form catches it."""
+    A, B = P("(2,2):(1,2)"), P("3:1")
+    wrong = ol.make_tuple_layout(A, B)
+    n = ol.size(A)
+    assert any(wrong(i + n * j) != A(i) + n * B(j) for j in range(3) for i in range(n))
+
+
+def test_tv_offset_multi_mode_is_a_bijection_of_the_tile():
+    rng = random.Random(31)
+    for _ in range(100):
+        k = rng.randint(1, 3)
+        thr = [rng.randint(1, 4) for _ in range(k)]
+        val = [rng.randint(1, 4) for _ in range(k)]
+        blk = [rng.randint(0, 1) for _ in range(k)]
+        offs = [ol.tv_offset(thr, val, blk, t, v) for t in itertools.product(*[range(x) for x in thr])
+                for v in itertools.product(*[range(x) for x in val])]
+        assert sorted(offs) == list(range(int(np.prod([a * b for a, b in zip(thr, val)]))))
