@@ -265,7 +265,7 @@ typedef struct lt_tensor {
 typedef enum lt_kernel {
     LT_KERNEL_AUTO = 0,
     LT_KERNEL_WAVE16 = 1,   /* one wave per 16x16 tile, any layout/ragged shape */
-    LT_KERNEL_TILED = 2,    /* 256x256x64 block tile, LDS double buffer, 32x32x16 MFMA */
+    LT_KERNEL_TILED = 2,    /* 256x256x64 block tile, LDS double buffer, 16x16x32 MFMA, ragged edges predicated */
     LT_KERNEL_SKINNY = 3    /* M <= 32, K-major B streamed once, split-K */
 } lt_kernel;
 
@@ -320,6 +320,36 @@ lt_status lt_gemm_workspace_size(const lt_tensor* A, const lt_tensor* B, const l
 lt_status lt_gemm_run(const lt_tensor* A, const lt_tensor* B, const lt_tensor* C, const lt_tensor* D,
                       float alpha, float beta, const lt_gemm_options* opt, void* workspace,
                       size_t workspace_bytes, void* stream);
+
+/* Fused epilogue [P3 "Epilogue fusion": bias, activation and an absolute
+ * maximum computed on the accumulators while they are in registers, instead
+ * of a second pass over D through HBM]:
+ *   D = act(alpha * A*B + beta * C + bias), in fp32, rounded once.
+ * bias: device pointer or NULL, values of D's dtype; bias[n * bias_stride] is
+ * added to column n (bias_per_row == 0) or bias[m * bias_stride] to row m
+ * (bias_per_row != 0); bias_stride 0 means 1. Caller-owned, N (or M) values.
+ * activation: LT_ACT_NONE, LT_ACT_RELU (x > 0 ? x : 0) or LT_ACT_GELU
+ * (x * Phi(x) = 0.5 x (1 + erf(x / sqrt(2))), the standard normal CDF form;
+ * the pages name GELU without a formula).
+ * amax: device pointer or NULL; receives max |D| over the stored (rounded)
+ * outputs, NaN outputs ignored. The library clears it on the stream first, so
+ * concurrent runs must not share it. */
+typedef enum lt_activation { LT_ACT_NONE = 0, LT_ACT_RELU = 1, LT_ACT_GELU = 2 } lt_activation;
+
+typedef struct lt_epilogue {
+    const void* bias;
+    int64_t bias_stride;
+    int32_t bias_per_row;
+    int32_t activation;      /* lt_activation */
+    float* amax;
+} lt_epilogue;
+
+/* lt_gemm_run with a fused epilogue (epi may be NULL: exactly lt_gemm_run).
+ * LT_ERR_INVALID_ARGUMENT for an unknown activation or a negative
+ * bias_stride. Every kernel family takes it; the same plan as lt_gemm_run. */
+lt_status lt_gemm_run_ex(const lt_tensor* A, const lt_tensor* B, const lt_tensor* C, const lt_tensor* D,
+                         float alpha, float beta, const lt_gemm_options* opt, const lt_epilogue* epi,
+                         void* workspace, size_t workspace_bytes, void* stream);
 
 /* Library version string. */
 const char* lt_version(void);

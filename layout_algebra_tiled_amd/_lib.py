@@ -41,6 +41,14 @@ class lt_gemm_options(ctypes.Structure):
                 ("split_k", ctypes.c_int32)]
 
 
+class lt_epilogue(ctypes.Structure):
+    _fields_ = [("bias", ctypes.c_void_p), ("bias_stride", ctypes.c_int64), ("bias_per_row", ctypes.c_int32),
+                ("activation", ctypes.c_int32), ("amax", ctypes.c_void_p)]
+
+
+LT_ACT_NONE, LT_ACT_RELU, LT_ACT_GELU = 0, 1, 2
+
+
 class lt_gemm_plan_info(ctypes.Structure):
     _fields_ = [("kernel", ctypes.c_int32), ("tile_m", ctypes.c_int32), ("tile_n", ctypes.c_int32),
                 ("tile_k", ctypes.c_int32), ("wave_m", ctypes.c_int32), ("wave_n", ctypes.c_int32),
@@ -96,6 +104,8 @@ SIGNATURES = {
     "lt_gemm_workspace_size": ([_T, _T, _T, _T, _i32, _P(lt_gemm_options), _P(_sz)], ctypes.c_int),
     "lt_gemm_run": ([_T, _T, _T, _T, ctypes.c_float, ctypes.c_float, _P(lt_gemm_options), _vp, _sz, _vp],
                     ctypes.c_int),
+    "lt_gemm_run_ex": ([_T, _T, _T, _T, ctypes.c_float, ctypes.c_float, _P(lt_gemm_options), _P(lt_epilogue),
+                        _vp, _sz, _vp], ctypes.c_int),
     "lt_version": ([], ctypes.c_char_p),
 }
 

@@ -320,18 +320,42 @@ lt_status lt_gemm_workspace_size(const lt_tensor* A, const lt_tensor* B, const l
 lt_status lt_gemm_run(const lt_tensor* A, const lt_tensor* B, const lt_tensor* C, const lt_tensor* D, float alpha,
                       float beta, const lt_gemm_options* opt, void* workspace, size_t workspace_bytes,
                       void* stream) {
+    return lt_gemm_run_ex(A, B, C, D, alpha, beta, opt, nullptr, workspace, workspace_bytes, stream);
+}
+
+lt_status lt_gemm_run_ex(const lt_tensor* A, const lt_tensor* B, const lt_tensor* C, const lt_tensor* D,
+                         float alpha, float beta, const lt_gemm_options* opt, const lt_epilogue* epi,
+                         void* workspace, size_t workspace_bytes, void* stream) {
     lt::Plan p;
     const int bnz = beta != 0.0f;
+    if (epi && (epi->activation < LT_ACT_NONE || epi->activation > LT_ACT_GELU || epi->bias_stride < 0))
+        return LT_ERR_INVALID_ARGUMENT;
     lt_status st = lt::make_plan(A, B, C, D, bnz, opt, &p);
     if (st != LT_OK) return st;
-    if (p.empty) return LT_OK;
     if ((size_t)p.info.workspace_bytes > workspace_bytes || (p.info.workspace_bytes > 0 && !workspace))
         return LT_ERR_WORKSPACE;
+    lt::EpiArgs ea;
+    if (epi && (epi->bias || epi->activation != LT_ACT_NONE || epi->amax)) {
+        ea.fused = 1;
+        ea.bias = static_cast<const uint16_t*>(epi->bias);
+        ea.bias_stride = epi->bias_stride == 0 ? 1 : epi->bias_stride;
+        // a transposed plan solves D^T: D's rows are its columns
+        ea.bias_on_rows = (epi->bias_per_row != 0) != p.transposed ? 1 : 0;
+        ea.act = epi->activation;
+        ea.amax = epi->amax;
+    }
+    if (p.empty) {
+        if (!ea.amax) return LT_OK;
+        st = lt::ensure_device();
+        if (st != LT_OK) return st;
+        return lt::launch_zero_f32(ea.amax, stream) == 0 ? LT_OK : LT_ERR_HIP;   // max over no outputs
+    }
     st = lt::ensure_device();
     if (st != LT_OK) return st;
     const int dt = p.A.dtype;
     const uint16_t* cptr = bnz ? static_cast<const uint16_t*>(p.C.ptr) : nullptr;
     int err = 0;
+    if (ea.amax && (err = lt::launch_zero_f32(ea.amax, stream)) != 0) return LT_ERR_HIP;
     switch (p.info.kernel) {
         case LT_KERNEL_WAVE16: {
             lt::Wave16Args a;
@@ -354,6 +378,7 @@ lt_status lt_gemm_run(const lt_tensor* A, const lt_tensor* B, const lt_tensor* C
             a.beta = beta;
             a.tiles_m = (int)((p.M + 15) / 16);
             a.tiles_n = (int)((p.N + 15) / 16);
+            a.epi = ea;
             err = lt::launch_wave16(dt, a, stream);
             break;
         }
@@ -392,6 +417,7 @@ lt_status lt_gemm_run(const lt_tensor* A, const lt_tensor* B, const lt_tensor* C
             a.B0 = static_cast<const char*>(p.B.ptr) + kbase * (p.b_k ? 2 : 2 * a.ldb);
             a.group_m = std::min(a.tiles_m, 8);
             a.xcd_remap = (a.tiles_m * a.tiles_n) % 8 == 0 ? 1 : 0;
+            a.epi = ea;
             err = lt::launch_tiled(dt, p.a_k, p.b_k, a, stream);
             break;
         }
@@ -413,6 +439,7 @@ lt_status lt_gemm_run(const lt_tensor* A, const lt_tensor* B, const lt_tensor* C
             a.beta = beta;
             a.split_k = p.info.split_k;
             a.k_per_wave = (int)(p.K / ((int64_t)a.split_k * lt::kSkinnyWaves));
+            a.epi = ea;
             err = lt::launch_skinny(dt, a, stream);
             break;
         }

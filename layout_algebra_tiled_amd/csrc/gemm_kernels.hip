@@ -61,6 +61,22 @@ __global__ __launch_bounds__(256) void gemm_wave16(Wave16Args p) {
     }
     const int m = m0 + r;
     const int n = n0 + 4 * h;
+    if (p.epi.fused) {
+        float amax = 0.0f;
+        if (m < p.M) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if (n + i >= p.N) break;
+                const float v = fused_value<DT>(acc[i], p.alpha, p.beta, p.C, m * p.scm + (int64_t)(n + i) * p.scn,
+                                                p.epi, m, n + i);
+                const uint16_t o = Tr<DT>::from_f32(v);
+                p.D[m * p.sdm + (int64_t)(n + i) * p.sdn] = o;
+                amax = fmaxf(amax, fabsf(Tr<DT>::to_f32(o)));
+            }
+        }
+        if (p.epi.amax) amax_commit(p.epi.amax, amax);   // every lane of the wave takes part
+        return;
+    }
     if (m >= p.M) return;
     if (p.sdn == 1 && (p.beta == 0.0f || p.scn == 1) && n + 4 <= p.N) {
         store4<DT>(p.D, p.C, m * p.sdm + n, m * p.scm + n, acc[0], acc[1], acc[2], acc[3], p.alpha, p.beta);
@@ -186,6 +202,20 @@ __global__ __launch_bounds__(64 * kSkinnyWaves, 1) void gemm_skinny(SkinnyArgs p
 
     // lane holds m = lane % 32 and n = n0 + 8g + 4*(lane/32) + 0..3
     const int m = frow;
+    if (p.split_k == 1 && p.epi.fused) {
+        float amax = 0.0f;
+        if (m < p.M) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int n = n0 + 8 * g + 4 * fh;
+                const float v[4] = {acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]};
+                store4_fused<DT>(p.D, p.C, (int64_t)m * p.ldd + n, (int64_t)m * p.ldc + n, v, 4, p.alpha, p.beta,
+                                 p.epi, m, n, &amax);
+            }
+        }
+        if (p.epi.amax) amax_commit(p.epi.amax, amax);
+        return;
+    }
     if (m >= p.M) return;
     if (p.split_k == 1) {
 #pragma unroll
@@ -210,13 +240,27 @@ template <int DT>
 __global__ __launch_bounds__(256) void skinny_reduce(SkinnyArgs p) {
     const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // quad index
     const int64_t quads_per_row = p.N / 4;
-    if (q >= (int64_t)p.M * quads_per_row) return;
-    const int m = (int)(q / quads_per_row);
-    const int n = (int)(q % quads_per_row) * 4;
+    const bool in = q < (int64_t)p.M * quads_per_row;
+    if (!in && !(p.epi.fused && p.epi.amax)) return;
+    const int m = in ? (int)(q / quads_per_row) : 0;
+    const int n = in ? (int)(q % quads_per_row) * 4 : 0;
     f32x4 s = {0.f, 0.f, 0.f, 0.f};
-    for (int k = 0; k < p.split_k; ++k) s += *reinterpret_cast<const f32x4*>(p.ws + ((int64_t)k * 32 + m) * p.N + n);
+    if (in)
+        for (int k = 0; k < p.split_k; ++k)
+            s += *reinterpret_cast<const f32x4*>(p.ws + ((int64_t)k * 32 + m) * p.N + n);
+    if (p.epi.fused) {
+        float amax = 0.0f;
+        const float v[4] = {s[0], s[1], s[2], s[3]};
+        if (in)
+            store4_fused<DT>(p.D, p.C, (int64_t)m * p.ldd + n, (int64_t)m * p.ldc + n, v, 4, p.alpha, p.beta, p.epi,
+                             m, n, &amax);
+        if (p.epi.amax) amax_commit(p.epi.amax, amax);   // every lane of the wave takes part
+        return;
+    }
     store4<DT>(p.D, p.C, (int64_t)m * p.ldd + n, (int64_t)m * p.ldc + n, s[0], s[1], s[2], s[3], p.alpha, p.beta);
 }
+
+__global__ void zero_f32(float* p) { *p = 0.0f; }
 
 }  // namespace
 
@@ -232,6 +276,11 @@ int launch_wave16(int dtype, const Wave16Args& a, void* stream) {
         hipLaunchKernelGGL(gemm_wave16<LT_F16>, grid, block, 0, s, a);
     else
         hipLaunchKernelGGL(gemm_wave16<LT_BF16>, grid, block, 0, s, a);
+    return static_cast<int>(hipGetLastError());
+}
+
+int launch_zero_f32(float* p, void* stream) {
+    hipLaunchKernelGGL(zero_f32, dim3(1), dim3(1), 0, static_cast<hipStream_t>(stream), p);
     return static_cast<int>(hipGetLastError());
 }
 

@@ -6,6 +6,18 @@
 
 namespace lt {
 
+// Fused epilogue ("CUTLASS, in depth", "Epilogue fusion"): after
+// alpha*acc + beta*C, add a bias vector and apply an activation while the
+// accumulators are in registers, and reduce max |D| for output scaling.
+struct EpiArgs {
+    int fused = 0;                 // 0: plain alpha/beta epilogue (the rest unused)
+    const uint16_t* bias = nullptr;  // D's dtype; nullptr: no bias
+    int64_t bias_stride = 1;       // elements between consecutive bias values
+    int bias_on_rows = 0;          // 1: bias[m] for row m; 0: bias[n] for column n
+    int act = 0;                   // lt_activation
+    float* amax = nullptr;         // max |stored D| (as float bits, atomic max); nullptr: none
+};
+
 // Generic wave-per-16x16-tile kernel: any strides, ragged M/N/K.
 struct Wave16Args {
     const uint16_t* A;
@@ -19,6 +31,7 @@ struct Wave16Args {
     int M, N, K;
     float alpha, beta;
     int tiles_m, tiles_n;   // tile grid: mode 1 of zipped_divide(D, (16,16)), colex
+    EpiArgs epi;
 };
 
 // 256x256 block-tiled kernel. A is K-major or M-major, B is K-major or
@@ -40,6 +53,7 @@ struct TiledArgs {
     // (<= 0): a pointer offset only, never dereferenced below k = 0
     const void* A0;
     const void* B0;
+    EpiArgs epi;
 };
 
 // Skinny kernel: M <= 32, K-major A and B, N-major D; B streamed once.
@@ -54,6 +68,7 @@ struct SkinnyArgs {
     float alpha, beta;
     int split_k;
     int k_per_wave;               // K elements per wave (a multiple of 64)
+    EpiArgs epi;
 };
 
 constexpr int kSkinnyWaves = 4;     // waves per workgroup (split the K range)
@@ -79,5 +94,7 @@ TiledShape tiled_shape();
 int launch_wave16(int dtype, const Wave16Args& a, void* stream);
 int launch_tiled(int dtype, bool a_kmajor, bool b_kmajor, const TiledArgs& a, void* stream);
 int launch_skinny(int dtype, const SkinnyArgs& a, void* stream);
+// *p = 0.0f on the stream (a one-thread kernel: no memset node in a captured graph)
+int launch_zero_f32(float* p, void* stream);
 
 }  // namespace lt

@@ -371,7 +371,30 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
             }
         }
     };
-    if (m0 + 256 > p.M || n0 + 256 > p.N)
+    // The fused epilogue (bias, activation, max |D|), for any tile.
+    auto epilogue_fused = [&]() {
+        float amax = 0.0f;
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const int m = m0 + arow0 + i * Cf::MF + Mf::out_col(lane);
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+#pragma unroll
+                for (int g = 0; g < Mf::NACC / 4; ++g) {
+                    const int n = n0 + brow0 + j * Cf::MF + Mf::out_row(lane, 4 * g);
+                    const float v[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                                        acc[i][j][4 * g + 3]};
+                    if (m < p.M && n < p.N)
+                        store4_fused<DT>(p.D, p.C, (int64_t)m * p.ldd + n, (int64_t)m * p.ldc + n, v,
+                                         min(4, p.N - n), p.alpha, p.beta, p.epi, m, n, &amax);
+                }
+            }
+        }
+        if (p.epi.amax) amax_commit(p.epi.amax, amax);
+    };
+    if (p.epi.fused)
+        epilogue_fused();
+    else if (m0 + 256 > p.M || n0 + 256 > p.N)
         epilogue(std::true_type{});
     else
         epilogue(std::false_type{});

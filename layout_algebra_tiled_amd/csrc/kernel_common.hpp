@@ -6,6 +6,7 @@
 
 #include <cstdint>
 
+#include "gemm_kernels.hpp"
 #include "lt.h"
 
 namespace lt {
@@ -80,6 +81,55 @@ __device__ __forceinline__ void store4(uint16_t* D, const uint16_t* C, int64_t d
     o.x = pack2<DT>(v0, v1);
     o.y = pack2<DT>(v2, v3);
     *reinterpret_cast<u32x2*>(D + dof) = o;
+}
+
+// One fused output: alpha*acc + beta*c + bias, then the activation (ReLU:
+// x > 0 ? x : 0; GELU: x * Phi(x) = 0.5 x (1 + erf(x / sqrt 2))), in fp32.
+template <int DT>
+__device__ __forceinline__ float fused_value(float acc, float alpha, float beta, const uint16_t* C, int64_t cof,
+                                             const EpiArgs& e, int m, int n) {
+    float v = alpha * acc;
+    if (beta != 0.0f) v += beta * Tr<DT>::to_f32(C[cof]);
+    if (e.bias) v += Tr<DT>::to_f32(e.bias[(int64_t)(e.bias_on_rows ? m : n) * e.bias_stride]);
+    if (e.act == LT_ACT_RELU)
+        v = v > 0.0f ? v : 0.0f;
+    else if (e.act == LT_ACT_GELU)
+        v = 0.5f * v * (1.0f + erff(v * 0.70710678118654752f));
+    return v;
+}
+
+// Fused epilogue of the first cnt (1..4) of four consecutive N outputs of row
+// m (C and D N-major): one 8-byte store when all four are in, else 2-byte
+// stores. Updates the lane's running max of |stored value|.
+template <int DT>
+__device__ __forceinline__ void store4_fused(uint16_t* D, const uint16_t* C, int64_t dof, int64_t cof,
+                                             const float* a, int cnt, float alpha, float beta,
+                                             const EpiArgs& e, int m, int n, float* amax) {
+    uint16_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        if (i < cnt) {
+            o[i] = Tr<DT>::from_f32(fused_value<DT>(a[i], alpha, beta, C, cof + i, e, m, n + i));
+            *amax = fmaxf(*amax, fabsf(Tr<DT>::to_f32(o[i])));
+        }
+    }
+    if (cnt == 4) {
+        u32x2 w;
+        w.x = (uint32_t)o[0] | ((uint32_t)o[1] << 16);
+        w.y = (uint32_t)o[2] | ((uint32_t)o[3] << 16);
+        *reinterpret_cast<u32x2*>(D + dof) = w;
+    } else {
+        for (int i = 0; i < cnt; ++i) D[dof + i] = o[i];
+    }
+}
+
+// Max of the lanes' values over the wave, then one atomic max per wave on the
+// float's bits (the values are >= 0, so their bit patterns order as
+// unsigned integers).
+__device__ __forceinline__ void amax_commit(float* amax_out, float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+    if ((threadIdx.x & 63) == 0) atomicMax(reinterpret_cast<unsigned int*>(amax_out), __float_as_uint(v));
 }
 
 // The same for the first cnt (1..3) of four outputs, one 2-byte store each:

@@ -66,10 +66,18 @@ def plan(A, B, D, C=None, beta: float = 0.0, kernel="auto", tile=None, split_k=0
     return r
 
 
+ACTIVATIONS = {None: L.LT_ACT_NONE, "none": L.LT_ACT_NONE, "relu": L.LT_ACT_RELU, "gelu": L.LT_ACT_GELU}
+
+
 def gemm(A: torch.Tensor, B: torch.Tensor, D: torch.Tensor, C: Optional[torch.Tensor] = None,
          alpha: float = 1.0, beta: float = 0.0, *, kernel="auto", tile=None, split_k: int = 0,
-         layouts: Optional[dict] = None, workspace: Optional[torch.Tensor] = None, stream=None) -> None:
-    """D = alpha * A @ B + beta * C (asynchronous on ``stream``)."""
+         layouts: Optional[dict] = None, workspace: Optional[torch.Tensor] = None, stream=None,
+         bias: Optional[torch.Tensor] = None, bias_stride: int = 1, bias_per_row: bool = False,
+         activation: Optional[str] = None, amax: Optional[torch.Tensor] = None) -> None:
+    """D = act(alpha * A @ B + beta * C + bias) (asynchronous on ``stream``).
+    ``bias`` (D's dtype, one value per column, or per row with
+    ``bias_per_row``), ``activation`` ("relu", "gelu") and ``amax`` (a float32
+    device scalar receiving max |D|) select the fused epilogue."""
     la = layouts or {}
     dA, dB, dD = tensor_desc(A, la.get("A")), tensor_desc(B, la.get("B")), tensor_desc(D, la.get("D"))
     dC = tensor_desc(C, la.get("C")) if C is not None else None
@@ -83,9 +91,18 @@ def gemm(A: torch.Tensor, B: torch.Tensor, D: torch.Tensor, C: Optional[torch.Te
         if workspace is None:
             workspace = torch.empty(need.value, dtype=torch.uint8, device=D.device)
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
-    L.check(L.lib().lt_gemm_run(ctypes.byref(dA), ctypes.byref(dB), ctypes.byref(dC) if dC else None,
-                                ctypes.byref(dD), float(alpha), float(beta), ctypes.byref(o), ws_ptr, ws_bytes,
-                                _stream(stream)), "gemm_run")
+    epi = None
+    if bias is not None or activation not in (None, "none") or amax is not None:
+        if activation not in ACTIVATIONS:
+            raise ValueError(f"unknown activation {activation!r}")
+        if amax is not None and amax.dtype != torch.float32:
+            raise ValueError("amax must be a float32 device tensor")
+        epi = L.lt_epilogue(bias.data_ptr() if bias is not None else None, int(bias_stride), int(bool(bias_per_row)),
+                            ACTIVATIONS[activation], amax.data_ptr() if amax is not None else None)
+    L.check(L.lib().lt_gemm_run_ex(ctypes.byref(dA), ctypes.byref(dB), ctypes.byref(dC) if dC else None,
+                                   ctypes.byref(dD), float(alpha), float(beta), ctypes.byref(o),
+                                   ctypes.byref(epi) if epi is not None else None, ws_ptr, ws_bytes,
+                                   _stream(stream)), "gemm_run")
 
 
 def layout_eval_device(layout: Layout, out: torch.Tensor, n: Optional[int] = None, stream=None) -> None:

@@ -198,3 +198,63 @@ def read_points(D: Operand, ij: np.ndarray) -> np.ndarray:
     Dw = D.widened()
     ij = np.asarray(ij, dtype=np.int64).reshape(-1, 2)
     return Dw[ij[:, 0] * D.stride[0] + ij[:, 1] * D.stride[1]]
+
+
+# ---------------------------------------------------------------------------
+# Fused epilogue: bias and activation ("CUTLASS, in depth", "Epilogue fusion")
+# ---------------------------------------------------------------------------
+
+def _erf(x: np.ndarray) -> np.ndarray:
+    from scipy.special import erf   # a library primitive used as one step
+    return erf(x)
+
+
+def activation(x: np.ndarray, act: Optional[str]) -> np.ndarray:
+    """READING: the page names ReLU-style activation and GELU without a
+    formula. ReLU(x) = x if x > 0 else 0; GELU(x) = x * Phi(x), Phi the
+    standard normal CDF, Phi(x) = (1 + erf(x / sqrt 2)) / 2 (exact, not the
+    tanh approximation)."""
+    x = np.asarray(x, dtype=np.float64)
+    if act in (None, "none"):
+        return x
+    if act == "relu":
+        return np.where(x > 0, x, 0.0)
+    if act == "gelu":
+        return x * 0.5 * (1.0 + _erf(x / np.sqrt(2.0)))
+    raise ValueError(f"unknown activation {act!r}")
+
+
+# |act(x) - act(y)| <= L |x - y|: ReLU 1; GELU's slope Phi(x) + x phi(x) peaks
+# at x = sqrt 2, Phi(sqrt 2) + sqrt(2) phi(sqrt 2) = 1.1289..., bounded by 1.13.
+LIPSCHITZ = {None: 1.0, "none": 1.0, "relu": 1.0, "gelu": 1.13}
+
+
+def fused_epilogue(Dpre: np.ndarray, Cabs: np.ndarray, ij: np.ndarray, bias: Optional[torch.Tensor],
+                   bias_stride: int, bias_per_row: bool, act: Optional[str]):
+    """D_ref = act(alpha*S + beta*c + bias) from D_pre = alpha*S + beta*c at the
+    points, and the magnitude |beta c| + |bias| that enters the bound."""
+    ij = np.asarray(ij, dtype=np.int64).reshape(-1, 2)
+    b = np.zeros(len(ij))
+    if bias is not None:
+        bw = bias.detach().to("cpu").reshape(-1).to(torch.float64).numpy()
+        idx = ij[:, 0] if bias_per_row else ij[:, 1]
+        b = bw[idx * bias_stride]
+    x = Dpre.reshape(-1) + b
+    return activation(x, act), Cabs.reshape(-1) + np.abs(b)
+
+
+def check_fused(D: np.ndarray, Dref: np.ndarray, T: np.ndarray, mag: np.ndarray, alpha: float,
+                dtype: torch.dtype, act: Optional[str]) -> CheckResult:
+    """The GEMM bound carried through the activation's Lipschitz constant:
+    |D - D_ref| <= L * 2e-3 * (|alpha| T + |beta c| + |bias|) + ulp_out(D_ref)."""
+    D = np.asarray(D, dtype=np.float64).reshape(-1)
+    Dref = Dref.reshape(-1)
+    b = LIPSCHITZ[act] * 2e-3 * (abs(alpha) * T.reshape(-1) + mag) + ulp_out(Dref, dtype)
+    finite = np.isfinite(D)
+    err = np.where(finite, np.abs(D - Dref), np.inf)
+    frac = err / b
+    bad = ~(err <= b)
+    wi = int(np.argmax(frac)) if len(frac) else -1
+    return CheckResult(ok=not bad.any(), n=len(D), n_bad=int(bad.sum()),
+                       worst_fraction=float(frac[wi]) if len(frac) else 0.0,
+                       worst_index=wi, nonfinite=int((~finite).sum()))

@@ -72,3 +72,46 @@ def run_and_check(A: datagen.Matrix, B: datagen.Matrix, C: Optional[datagen.Matr
     res = og.check(got, Dref, T, Cabs, alpha, A.dtype)
     say(f"[gemm] {label} {plan['kernel_name']} grid={plan['grid']} split_k={plan['split_k']}: {res}")
     return res, plan, out
+
+
+def run_and_check_fused(A: datagen.Matrix, B: datagen.Matrix, C: Optional[datagen.Matrix], D: datagen.Matrix,
+                        alpha: float, beta: float, bias: Optional[torch.Tensor], bias_per_row: bool,
+                        act: Optional[str], kernel="auto", split_k: int = 0, bias_stride: int = 1,
+                        expect_kernel: Optional[str] = None, label: str = ""):
+    """The fused epilogue D = act(alpha*A*B + beta*C + bias) through
+    lt_gemm_run_ex, every output checked against the oracle; also returns the
+    kernel's max |D| and the max over the output it wrote."""
+    from layout_algebra_tiled_amd import gemm as g
+    from layout_algebra_tiled_amd.layout import Layout
+
+    M, N = D.shape
+    say(f"[gemm-fused] {label} M={M} N={N} K={A.shape[1]} {A.dtype} bias={'row' if bias_per_row else 'col'}"
+        f"{'' if bias is not None else '(none)'} act={act} kernel={kernel} split_k={split_k}")
+    dev = torch.device("cuda:0")
+    dA, dB, dD = A.to(dev), B.to(dev), D.to(dev)
+    dC = C.to(dev) if C is not None else None
+    dD.store.fill_(float("nan"))
+    lay = {"A": Layout.make(list(A.shape), list(A.stride)), "B": Layout.make(list(B.shape), list(B.stride)),
+           "D": Layout.make(list(D.shape), list(D.stride))}
+    if C is not None:
+        lay["C"] = Layout.make(list(C.shape), list(C.stride))
+    plan = g.plan(dA.store, dB.store, dD.store, dC.store if dC is not None else None, beta, kernel=kernel,
+                  split_k=split_k, layouts=lay)
+    if expect_kernel:
+        assert plan["kernel_name"] == expect_kernel, plan
+    amax = torch.full((1,), -1.0, dtype=torch.float32, device=dev)   # the library must clear it
+    dbias = bias.to(dev) if bias is not None else None
+    g.gemm(dA.store, dB.store, dD.store, dC.store if dC is not None else None, alpha, beta, kernel=kernel,
+           split_k=split_k, layouts=lay, bias=dbias, bias_stride=bias_stride, bias_per_row=bias_per_row,
+           activation=act, amax=amax)
+    torch.cuda.synchronize()
+    out = datagen.Matrix(dD.store.cpu(), D.shape, D.stride)
+    points = all_points(M, N)
+    S, T = og.gemm_points(op(A), op(B), points)
+    Dpre, Cabs = og.epilogue(S, op(C) if C is not None else None, points, alpha, beta)
+    Dref, mag = og.fused_epilogue(Dpre, Cabs, points, bias, bias_stride, bias_per_row, act)
+    got = og.read_points(op(out), points)
+    res = og.check_fused(got, Dref, T, mag, alpha, A.dtype, act)
+    written_max = float(np.nanmax(np.abs(got))) if got.size else 0.0
+    say(f"[gemm-fused] {label} {plan['kernel_name']}: {res}; amax {amax.item()} vs max|D| {written_max}")
+    return res, plan, float(amax.item()), written_max

@@ -479,3 +479,15 @@ def test_plan_unit_mode_prefers_a_real_unit_stride():
     D = _desc(BASE + 8192, L.LT_F16, [16, 1], [8, 1])
     st, i = _plan(A, B, None, D)
     assert st == "LT_OK"
+
+
+def test_fused_epilogue_argument_checks_before_the_device():
+    A, B, C, D = _gemm_descs(256, 256, 64)
+    bad = L.lt_epilogue(None, 1, 0, 7, None)
+    st = L.lib().lt_gemm_run_ex(ctypes.byref(A), ctypes.byref(B), None, ctypes.byref(D), 1.0, 0.0, None,
+                                ctypes.byref(bad), None, 0, None)
+    assert L.STATUS_NAMES[st] == "LT_ERR_INVALID_ARGUMENT"
+    neg = L.lt_epilogue(None, -2, 0, L.LT_ACT_RELU, None)
+    st = L.lib().lt_gemm_run_ex(ctypes.byref(A), ctypes.byref(B), None, ctypes.byref(D), 1.0, 0.0, None,
+                                ctypes.byref(neg), None, 0, None)
+    assert L.STATUS_NAMES[st] == "LT_ERR_INVALID_ARGUMENT"

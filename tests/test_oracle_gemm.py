@@ -239,3 +239,59 @@ def test_layout_mutant_is_caught(monkeypatch, target, mutant):
         except Exception:
             failures += 1
     assert failures > 0
+
+
+# ---------------------------------------------------------------------------
+# Fused epilogue: activation definitions pinned to values they must take
+# ---------------------------------------------------------------------------
+
+# The standard normal CDF at 1, 2 and -0.5, as printed in normal tables
+# (a source other than the oracle's erf): GELU(x) = x Phi(x).
+_PHI = {1.0: 0.8413447460685429, 2.0: 0.9772498680518208, -0.5: 0.3085375387259869}
+
+
+def test_gelu_matches_normal_table_values():
+    for x, phi in _PHI.items():
+        assert abs(og.activation(np.array([x]), "gelu")[0] - x * phi) < 1e-15
+
+
+def test_gelu_odd_part_is_identity_and_limits():
+    """Phi(x) + Phi(-x) = 1 gives GELU(x) - GELU(-x) = x; GELU(0) = 0; far
+    out GELU(x) is x on the right and 0 on the left."""
+    x = np.random.default_rng(3).uniform(-6, 6, 1000)
+    assert np.allclose(og.activation(x, "gelu") - og.activation(-x, "gelu"), x, rtol=0, atol=1e-13)
+    assert og.activation(np.array([0.0]), "gelu")[0] == 0.0
+    assert abs(og.activation(np.array([12.0]), "gelu")[0] - 12.0) < 1e-12
+    assert abs(og.activation(np.array([-12.0]), "gelu")[0]) < 1e-12
+
+
+def test_gelu_lipschitz_constant_bounds_the_slope():
+    x = np.linspace(-8, 8, 200001)
+    y = og.activation(x, "gelu")
+    slope = np.abs(np.diff(y) / np.diff(x))
+    assert slope.max() <= og.LIPSCHITZ["gelu"] and slope.max() > 1.12
+
+
+def test_relu_and_none():
+    x = np.array([-2.0, -0.0, 0.0, 0.5, 3.0])
+    assert list(og.activation(x, "relu")) == [0.0, 0.0, 0.0, 0.5, 3.0]
+    assert list(og.activation(x, None)) == list(x)
+
+
+def test_gelu_without_sqrt2_is_caught(monkeypatch):
+    """Planted mistake: erf(x) instead of erf(x / sqrt 2) misses the table."""
+    monkeypatch.setattr(og, "activation", lambda x, act: x * 0.5 * (1.0 + og._erf(np.asarray(x))))
+    assert any(abs(og.activation(np.array([x]), "gelu")[0] - x * phi) > 1e-6 for x, phi in _PHI.items())
+
+
+def test_fused_epilogue_bias_rows_and_columns():
+    ij = np.array([[0, 0], [1, 2], [3, 1]])
+    pre = np.array([1.0, -2.0, 0.25])
+    bias = torch.tensor([10.0, 20.0, 30.0, 40.0], dtype=torch.float16)
+    d, mag = og.fused_epilogue(pre, np.zeros(3), ij, bias, 1, False, None)
+    assert list(d) == [11.0, 28.0, 20.25] and list(mag) == [10.0, 30.0, 20.0]
+    d, _ = og.fused_epilogue(pre, np.zeros(3), ij, bias, 1, True, "relu")
+    assert list(d) == [11.0, 18.0, 40.25]
+    strided = torch.tensor([10.0, 0.0, 20.0, 0.0, 30.0, 0.0, 40.0, 0.0], dtype=torch.float16)
+    d, _ = og.fused_epilogue(pre, np.zeros(3), ij, strided, 2, False, None)   # every other value
+    assert list(d) == [11.0, 28.0, 20.25]
