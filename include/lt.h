@@ -274,7 +274,10 @@ typedef struct lt_gemm_options {
     int32_t kernel;     /* lt_kernel */
     int32_t tile_m;     /* block tile (kernel-specific allowed values) */
     int32_t tile_n;
-    int32_t split_k;    /* SKINNY only: number of K slices (>= 1) */
+    int32_t split_k;    /* SKINNY: number of K slices (>= 1). TILED: K segments of each
+                           tile past the last whole round of 256 CUs (0: chosen by a
+                           cost model; 1: none, all tiles whole; > 1: forced, on all
+                           tiles when they fill no whole round) */
 } lt_gemm_options;
 
 /* What the planner chose, for banners and tests [P1 "Exercise": print the
@@ -292,6 +295,8 @@ typedef struct lt_gemm_plan_info {
     int64_t workspace_bytes; /* caller-provided scratch the run needs */
     int64_t mfma_per_wave_kstep; /* MFMA instructions per wave per K step (tile_k) */
     int32_t mfma_m, mfma_n, mfma_k; /* shape of the MFMA instruction the kernel issues */
+    int64_t sk_tiles;        /* TILED: tiles of the last round split into split_k K segments, 0 if none */
+    int32_t sk_workgroups;   /* TILED: workgroups of the split launch (sk_tiles * split_k) */
 } lt_gemm_plan_info;
 
 /* Validate and plan without launching. Checks: dtypes (A, B fp16 or bf16

@@ -106,7 +106,14 @@ struct Plan {
     Mat A, B, C, D;              // after the transposition, if any
     int64_t M = 0, N = 0, K = 0;
     bool a_k = false, b_k = false;
+    // tiled kernel: whole tiles, then a split-K remainder
+    int64_t dp_tiles = 0, sk_tiles = 0;
+    int sk_splits = 1;
+    int64_t sk_counter_bytes = 0;   // workspace: counters first, then partials
 };
+
+// Compute units of a gfx950 part (MI355X): the unit of wave quantisation.
+constexpr int64_t kCUs = 256;
 
 void transpose(Mat* m) {
     std::swap(m->e0, m->e1);
@@ -247,7 +254,51 @@ lt_status make_plan(const lt_tensor* tA, const lt_tensor* tB, const lt_tensor* t
             in.stages = ts.stages;
             in.lds_bytes = ts.lds_bytes;
             if (in.lds_bytes > 160 * 1024) return LT_ERR_LDS_OVERFLOW;
-            in.grid = tm_ * tn_;
+            {
+                // Wave quantisation ("CUTLASS, in depth", "Worked example:
+                // tile choice and wave quantisation"): ntiles whole tiles on
+                // kCUs compute units leave the last round part empty. The
+                // whole rounds stay data-parallel; the rem tiles of the last
+                // round can instead be split into S = kCUs / rem K segments
+                // (at most 8, at least 4 slices each), so that the last round
+                // fills the units too, at the price of the fp32 partials. In
+                // K-slice times: data-parallel takes ceil(ntiles/kCUs)*KT;
+                // split, the whole rounds, ceil(KT/S), and about 20 slices
+                // for a 256x256 partial written and read back. The split is
+                // taken when it saves a tenth. split_k = 1 turns it off;
+                // split_k > 1 forces S (on all tiles when they fill no whole
+                // round, else on the last round's).
+                const int64_t ntiles = tm_ * tn_;
+                const int64_t KTt = (p.K + ts.bk - 1) / ts.bk;
+                int64_t rem = ntiles % kCUs;
+                int64_t S = 1;
+                if (split == 0) {
+                    if (rem != 0) {
+                        S = std::min<int64_t>({kCUs / rem, 8, KTt / 4});
+                        if (S >= 2) {
+                            const int64_t t_dp = (ntiles + kCUs - 1) / kCUs * KTt;
+                            const int64_t t_split = ntiles / kCUs * KTt + (KTt + S - 1) / S + 20;
+                            if (!(10 * t_split < 9 * t_dp)) S = 1;
+                        }
+                    }
+                } else if (split > 1) {
+                    S = std::min<int64_t>(split, KTt);
+                    if (rem == 0) rem = std::min<int64_t>(ntiles, kCUs);
+                }
+                if (S < 2) {
+                    S = 1;
+                    rem = 0;
+                }
+                p.dp_tiles = ntiles - rem;
+                p.sk_tiles = rem;
+                p.sk_splits = static_cast<int>(S);
+                p.sk_counter_bytes = (rem * 4 + 255) / 256 * 256;
+                in.split_k = p.sk_splits;
+                in.grid = p.dp_tiles + rem * S;
+                in.sk_tiles = rem;
+                in.sk_workgroups = static_cast<int32_t>(rem * S);
+                in.workspace_bytes = rem > 0 ? p.sk_counter_bytes + rem * S * (int64_t)ts.bm * ts.bn * 4 : 0;
+            }
             // (wave_m/mf) * (wave_n/mf) * (bk/mfma_k): the analogue of counting mma
             // per warp per K slice ("CUTLASS and CuTe layouts", "The arch tag
             // is not one instruction")
@@ -416,7 +467,16 @@ lt_status lt_gemm_run_ex(const lt_tensor* A, const lt_tensor* B, const lt_tensor
             a.A0 = static_cast<const char*>(p.A.ptr) + kbase * (p.a_k ? 2 : 2 * a.lda);
             a.B0 = static_cast<const char*>(p.B.ptr) + kbase * (p.b_k ? 2 : 2 * a.ldb);
             a.group_m = std::min(a.tiles_m, 8);
-            a.xcd_remap = (a.tiles_m * a.tiles_n) % 8 == 0 ? 1 : 0;
+            a.dp_tiles = (int)p.dp_tiles;
+            a.sk_splits = p.sk_splits;
+            a.xcd_remap = p.dp_tiles % 8 == 0 ? 1 : 0;
+            a.counters = nullptr;
+            a.partials = nullptr;
+            if (p.sk_tiles > 0) {
+                a.counters = static_cast<int*>(workspace);
+                a.partials = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.sk_counter_bytes);
+                if ((err = lt::launch_zero_i32(a.counters, (int)p.sk_tiles, stream)) != 0) return LT_ERR_HIP;
+            }
             a.epi = ea;
             err = lt::launch_tiled(dt, p.a_k, p.b_k, a, stream);
             break;

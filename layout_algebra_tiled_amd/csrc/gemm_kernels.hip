@@ -262,6 +262,10 @@ __global__ __launch_bounds__(256) void skinny_reduce(SkinnyArgs p) {
 
 __global__ void zero_f32(float* p) { *p = 0.0f; }
 
+__global__ void zero_i32(int* p, int n) {
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0;
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -281,6 +285,12 @@ int launch_wave16(int dtype, const Wave16Args& a, void* stream) {
 
 int launch_zero_f32(float* p, void* stream) {
     hipLaunchKernelGGL(zero_f32, dim3(1), dim3(1), 0, static_cast<hipStream_t>(stream), p);
+    return static_cast<int>(hipGetLastError());
+}
+
+int launch_zero_i32(int* p, int n, void* stream) {
+    hipLaunchKernelGGL(zero_i32, dim3((n + 255) / 256 < 64 ? (n + 255) / 256 : 64), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), p, n);
     return static_cast<int>(hipGetLastError());
 }
 

@@ -54,6 +54,17 @@ struct TiledArgs {
     const void* A0;
     const void* B0;
     EpiArgs epi;
+    // Data-parallel tiles plus a split-K remainder: the first dp_tiles
+    // tiles (raster order) are computed whole, one workgroup each; each of
+    // the remaining tiles is split into sk_splits K segments, one workgroup
+    // each (a second launch), whose fp32 partials meet in `partials`
+    // ([tile][split][256*256]); the segment that finishes last (counted in
+    // `counters`, one int per split tile, zero on entry and left zero) adds
+    // the others and stores.
+    int dp_tiles;
+    int sk_splits;
+    float* partials;
+    int* counters;
 };
 
 // Skinny kernel: M <= 32, K-major A and B, N-major D; B streamed once.
@@ -96,5 +107,7 @@ int launch_tiled(int dtype, bool a_kmajor, bool b_kmajor, const TiledArgs& a, vo
 int launch_skinny(int dtype, const SkinnyArgs& a, void* stream);
 // *p = 0.0f on the stream (a one-thread kernel: no memset node in a captured graph)
 int launch_zero_f32(float* p, void* stream);
+// p[0..n) = 0 on the stream (a fill kernel, for the same reason)
+int launch_zero_i32(int* p, int n, void* stream);
 
 }  // namespace lt

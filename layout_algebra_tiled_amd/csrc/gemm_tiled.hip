@@ -49,15 +49,11 @@ struct TCfg {
     static_assert(IPW * (S - 1) < 64, "vmcnt counts at most 63 outstanding loads");
 };
 
-__device__ __forceinline__ void tile_of(int wg, const TiledArgs& p, int* tm, int* tn) {
-    // Consecutive workgroup ids go to different XCDs (round-robin dispatch);
-    // regroup them so each XCD walks a contiguous stretch of the raster, and
-    // raster down group_m tile rows before moving right, so tiles in flight
-    // together on one XCD share A rows and B columns in its L2 ("CUTLASS, in
-    // depth", "Kernel schedules": L2-friendly tile order).
-    const int ntiles = p.tiles_m * p.tiles_n;
-    int lin = wg;
-    if (p.xcd_remap) lin = (wg & 7) * (ntiles >> 3) + (wg >> 3);
+// Linear tile index -> tile coordinates: raster down group_m tile rows
+// before moving right, so tiles in flight together on one XCD share A rows
+// and B columns in its L2 ("CUTLASS, in depth", "Kernel schedules":
+// L2-friendly tile order).
+__device__ __forceinline__ void tile_coords(int lin, const TiledArgs& p, int* tm, int* tn) {
     const int gsz = p.group_m * p.tiles_n;
     const int grp = lin / gsz;
     const int first = grp * p.group_m;
@@ -65,6 +61,29 @@ __device__ __forceinline__ void tile_of(int wg, const TiledArgs& p, int* tm, int
     const int in = lin - grp * gsz;
     *tm = first + in % gm;
     *tn = in / gm;
+}
+
+// Workgroup -> (linear tile, K slices [kt0, kt1), split index or -1). In
+// the data-parallel launch consecutive workgroup ids go to different XCDs
+// (round-robin dispatch), so the ids are regrouped for each XCD to walk a
+// contiguous stretch of the raster. In the split launch workgroup r takes K
+// segment r % sk_splits of remainder tile r / sk_splits.
+template <bool SPLIT>
+__device__ __forceinline__ void work_of(int wg, const TiledArgs& p, int KT, int* lin, int* kt0, int* kt1,
+                                        int* seg) {
+    if constexpr (!SPLIT) {
+        *lin = p.xcd_remap ? (wg & 7) * (p.dp_tiles >> 3) + (wg >> 3) : wg;
+        *kt0 = 0;
+        *kt1 = KT;
+        *seg = -1;
+        return;
+    }
+    const int r = wg, S = p.sk_splits;
+    const int s = r % S;
+    *lin = p.dp_tiles + r / S;
+    *kt0 = s * KT / S;
+    *kt1 = (s + 1) * KT / S;
+    *seg = s;
 }
 
 // s_waitcnt with vmcnt = n (0 <= n <= 63, a constant), other counters
@@ -125,21 +144,24 @@ struct Operand {
     }
 };
 
-template <int DT, class Cf>
+template <int DT, class Cf, bool SPLIT>
 __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
     extern __shared__ __attribute__((aligned(1024))) char smem[];
     using V8 = typename Tr<DT>::V8;
     constexpr int BK = Cf::BK, S = Cf::S, KS = Cf::KS, FM = Cf::FM, FN = Cf::FN;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    int tm, tn;
-    tile_of(blockIdx.x, p, &tm, &tn);
-    const int m0 = tm * 256, n0 = tn * 256;
     // K slices: KT = ceil(K / BK). When BK does not divide K, the K range is
     // shifted to start at kbase = K - KT*BK < 0, so that only slice 0 is
     // partial: its first -kbase K positions are zero-filled in LDS, and every
     // later slice is a full, unpredicated copy.
     const int KT = (p.K + BK - 1) / BK;
     const int kbase = p.K - KT * BK;
+    int lin, kt0, kt1, seg;
+    work_of<SPLIT>(blockIdx.x, p, KT, &lin, &kt0, &kt1, &seg);
+    const int NS = kt1 - kt0;   // K slices this workgroup runs (>= 1)
+    int tm, tn;
+    tile_coords(lin, p, &tm, &tn);
+    const int m0 = tm * 256, n0 = tn * 256;
 
     // ---- copy: S-stage ring, stage s at s*STAGE (A slice, then B slice).
     // Up to four copy instructions of one operand write LDS through the same
@@ -163,8 +185,8 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
     auto issue = [&](int stage, int kt) {
         char* sa = smem + stage * Cf::STAGE + wave * Cf::OPI * 1024;
         char* sb = sa + Cf::OP_BYTES;
-        const char* ga = a_k0 + kt * a_ks;
-        const char* gb = b_k0 + kt * b_ks;
+        const char* ga = a_k0 + (kt0 + kt) * a_ks;
+        const char* gb = b_k0 + (kt0 + kt) * b_ks;
         // (groups of four: the instruction offset is at most 4095 bytes)
         static_for<0, Cf::OPI>([&](auto ic) {
             constexpr int i = decltype(ic)::value, g = i / 4, o = (i % 4) * 1024;
@@ -266,14 +288,14 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
             for (int v = 0; v < Mf::NACC; ++v) acc[i][j][v] = 0.0f;
 
     // ---- prologue: slices 0 .. S-1
-    if (kbase < 0)
+    if (kbase < 0 && kt0 == 0)
         issue_first_partial();
     else
         issue(0, 0);
 #pragma unroll
     for (int s = 1; s < S; ++s)
-        if (s < KT) issue(s, s);
-    if (KT >= S)
+        if (s < NS) issue(s, s);
+    if (NS >= S)
         LT_WAIT_VM(Cf::IPW * (S - 1));
     else
         LT_WAIT_VM(0);
@@ -336,9 +358,57 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
     const std::true_type yes{};
     const std::false_type no{};
     int t = 0;
-    for (; t + S < KT; ++t) slice(yes, yes, t);   // refill slice t+S
-    for (; t + 1 < KT; ++t) slice(yes, no, t);    // slices already in flight
+    for (; t + S < NS; ++t) slice(yes, yes, t);   // refill slice t+S
+    for (; t + 1 < NS; ++t) slice(yes, no, t);    // slices already in flight
     slice(no, no, t);                             // the last slice
+
+    // ---- split-K segment: publish the fp32 partial; the segment that
+    // arrives last adds the others' and goes on to the epilogue. No waiting:
+    // the others simply end. The partials and the arrival count cross XCDs,
+    // whose L2s are not coherent with each other: they are written and read
+    // with agent-scope relaxed atomics (the coherent path, past this XCD's
+    // L2), so no fence has to write back or invalidate a whole L2 while
+    // other tiles are running. Order: every store of the partial completes
+    // (vmcnt 0, then the barrier) before the count is incremented, and the
+    // last segment issues its reads only after the increment returned.
+    if constexpr (SPLIT) {
+        const int skt = lin - p.dp_tiles, NSPL = p.sk_splits;
+        // block (i, j) of split s2: register v of thread t at v*NT + t, so
+        // that one store (load) instruction covers 256 contiguous bytes
+        auto part = [&](int s2, int i, int j) {
+            return p.partials + (((int64_t)skt * NSPL + s2) * (FM * FN) + (i * FN + j)) * (Cf::NT * Mf::NACC) +
+                   threadIdx.x;
+        };
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                float* q = part(seg, i, j);
+#pragma unroll
+                for (int v = 0; v < Mf::NACC; ++v)
+                    __hip_atomic_store(q + v * Cf::NT, acc[i][j][v], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        LT_WAIT_VM(0);
+        __syncthreads();   // every store of the partial is complete; the LDS ring is free
+        int* flag = reinterpret_cast<int*>(smem);
+        if (threadIdx.x == 0)
+            *flag = __hip_atomic_fetch_add(&p.counters[skt], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        if (*flag != NSPL - 1) return;
+        for (int s2 = 0; s2 < NSPL; ++s2) {
+            if (s2 == seg) continue;
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j) {
+                    const float* q = part(s2, i, j);
+#pragma unroll
+                    for (int v = 0; v < Mf::NACC; ++v)
+                        acc[i][j][v] += __hip_atomic_load(q + v * Cf::NT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+        }
+        if (threadIdx.x == 0) __hip_atomic_store(&p.counters[skt], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
 
     // ---- epilogue: block (i, j), registers 4g..4g+3 hold row m = lane % MF
     // and four consecutive columns of the MF x MF block. A tile on a ragged
@@ -420,18 +490,31 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
 template <bool AK, bool BKM>
 using Chosen = TCfg<LT_TILED_NWM, LT_TILED_NWN, LT_TILED_BK, LT_TILED_S, LT_TILED_MF, AK, BKM>;
 
-template <int DT, bool AK, bool BKM>
-int launch_one(const TiledArgs& a, hipStream_t s) {
-    using Cf = Chosen<AK, BKM>;
+template <int DT, class Cf, bool SPLIT>
+int launch_mode(const TiledArgs& a, int grid, hipStream_t s) {
     static bool attr = false;
     if (!attr) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_tiled<DT, Cf>),
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_tiled<DT, Cf, SPLIT>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, Cf::LDS);
         if (e != hipSuccess) return static_cast<int>(e);
         attr = true;
     }
-    hipLaunchKernelGGL((gemm_tiled<DT, Cf>), dim3(a.tiles_m * a.tiles_n), dim3(Cf::NT), Cf::LDS, s, a);
+    hipLaunchKernelGGL((gemm_tiled<DT, Cf, SPLIT>), dim3(grid), dim3(Cf::NT), Cf::LDS, s, a);
     return static_cast<int>(hipGetLastError());
+}
+
+// The data-parallel tiles, then (same stream, so after them) the split
+// remainder.
+template <int DT, bool AK, bool BKM>
+int launch_one(const TiledArgs& a, hipStream_t s) {
+    using Cf = Chosen<AK, BKM>;
+    if (a.dp_tiles > 0) {
+        const int e = launch_mode<DT, Cf, false>(a, a.dp_tiles, s);
+        if (e != 0) return e;
+    }
+    const int split_wgs = (a.tiles_m * a.tiles_n - a.dp_tiles) * a.sk_splits;
+    if (split_wgs > 0) return launch_mode<DT, Cf, true>(a, split_wgs, s);
+    return 0;
 }
 
 template <int DT>

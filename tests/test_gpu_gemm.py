@@ -93,7 +93,8 @@ def test_tiled_ragged_all_outputs(M, N, K, dtype, a_major, b_major, alpha, beta,
     res, plan, _ = run_and_check(A, B, C, D, alpha, beta, kernel="tiled", expect_kernel="tiled",
                                  label="tiled-ragged")
     _ok(res)
-    assert plan["grid"] == ((M + 255) // 256) * ((N + 255) // 256)
+    tiles = ((M + 255) // 256) * ((N + 255) // 256)
+    assert plan["grid"] == tiles - plan["sk_tiles"] + plan["sk_workgroups"]
 
 
 def test_tiled_ragged_large_auto():
@@ -103,6 +104,47 @@ def test_tiled_ragged_large_auto():
     pts = sample_points(M, N, 3000, seed=5)
     res, plan, _ = run_and_check(A, B, C, D, 1.0, 0.25, points=pts, expect_kernel="tiled", label="ragged-auto")
     _ok(res)
+
+
+# ---------------------------------------------------------------------------
+# split remainder: when the tiles do not fill whole rounds of the 256 CUs,
+# the last round's tiles are split into K segments; the segments meet as
+# fp32 partials and the one that finishes last stores the tile
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("M,N,K,dtype,a_major,b_major,beta,split", [
+    (512, 768, 512, BF16, "row", "col", 0.0, 2),       # forced: 6 tiles in 2 segments
+    (512, 512, 640, F16, "row", "col", 0.5, 3),        # forced: segments of 3, 3 and 4 slices
+    (300, 520, 200, BF16, "row", "col", -1.0, 2),      # ragged tiles, partial first slice
+    (264, 392, 77, F16, "col", "row", 2.0, 2),         # M-/N-major operands
+    (1792, 1792, 7040, BF16, "row", "col", 0.0, 0),    # 49 tiles x 110 slices: 5 segments each
+    (512, 512, 512, BF16, "row", "col", 1.0, 1),       # forced off: data-parallel only
+])
+def test_tiled_split_remainder_all_outputs(M, N, K, dtype, a_major, b_major, beta, split):
+    A, B, C, D = _case(M, N, K, dtype, a_major, b_major, "row", 1.0, beta, seed=3 * M + K)
+    pts = None if M * N <= 600_000 else sample_points(M, N, 20000, seed=M)
+    res, plan, _ = run_and_check(A, B, C, D, 1.0, beta, kernel="tiled", split_k=split, points=pts,
+                                 expect_kernel="tiled", label=f"tiled-split{split}")
+    _ok(res)
+    assert (plan["sk_tiles"] > 0) == (split != 1)
+
+
+def test_tiled_split_remainder_repeated_runs_keep_counters_consistent():
+    """Three runs in a row on one workspace, the middle one with another
+    shape: the arrival counters start at zero every run."""
+    from layout_algebra_tiled_amd import gemm as g
+    ws = torch.full((64 << 20,), 255, dtype=torch.uint8, device="cuda")   # garbage on entry
+    for (M, N, K) in ((512, 768, 512), (768, 256, 1024), (512, 768, 512)):
+        A, B, C, D = _case(M, N, K, BF16, "row", "col", "row", 1.0, 0.0, seed=M + N)
+        dA, dB, dD = A.to("cuda"), B.to("cuda"), D.to("cuda")
+        dD.store.fill_(float("nan"))
+        g.gemm(dA.view(), dB.view(), dD.view(), None, 1.0, 0.0, workspace=ws)
+        torch.cuda.synchronize()
+        pts = all_points(M, N)
+        S, T = og.gemm_points(op(A), op(B), pts)
+        Dref, Cabs = og.epilogue(S, None, pts, 1.0, 0.0)
+        got = og.read_points(og.Operand(dD.store.cpu(), D.shape, D.stride), pts)
+        _ok(og.check(got, Dref, T, Cabs, 1.0, BF16))
 
 
 # ---------------------------------------------------------------------------

@@ -445,7 +445,52 @@ def test_plan_ragged_shapes_on_the_tiled_kernel():
         st, i = _plan(*_gemm_descs(M, N, K))
         assert st == "LT_OK" and i.kernel == expect, (M, N, K, st, i.kernel)
         if expect == L.LT_KERNEL_TILED:
-            assert i.grid == -(-M // 256) * -(-N // 256)
+            tiles = -(-M // 256) * -(-N // 256)
+            assert i.grid == tiles - i.sk_tiles + i.sk_workgroups
+
+
+def _split_plan(tiles, kt, split=0):
+    """The planner's rule, written out: whole rounds of 256 tiles stay
+    data-parallel; the last round's rem tiles are split into S K segments
+    when the modelled time (in K slices, 20 for the partials) drops by a
+    tenth, or when forced."""
+    rem = tiles % 256
+    if split == 1:
+        return tiles, 0, 1
+    if split == 0:
+        if rem == 0:
+            return tiles, 0, 1
+        S = min(256 // rem, 8, kt // 4)
+        t_dp = -(-tiles // 256) * kt
+        t_split = tiles // 256 * kt + -(-kt // max(S, 1)) + 20
+        if S < 2 or not 10 * t_split < 9 * t_dp:
+            return tiles, 0, 1
+        return tiles - rem, rem, S
+    S = min(split, kt)
+    rem = rem or min(tiles, 256)
+    return (tiles, 0, 1) if S < 2 else (tiles - rem, rem, S)
+
+
+def test_plan_split_remainder_fills_the_last_round():
+    for (M, N, K, split) in ((6144, 4096, 2048, 0), (4096, 4096, 4096, 0), (8192, 8192, 8192, 0),
+                             (512, 768, 512, 0), (512, 512, 640, 2), (2048, 2048, 64, 0), (4096, 4352, 1024, 0),
+                             (8192, 8192, 8192, 1), (512, 512, 512, 1), (512, 512, 128, 0), (1792, 1792, 7040, 0),
+                             (2048, 2048, 8192, 0), (8192, 8448, 8192, 0)):
+        st, i = _plan(*_gemm_descs(M, N, K), split=split)
+        assert st == "LT_OK" and i.kernel == L.LT_KERNEL_TILED, (M, N, K, st)
+        tiles, kt = (M // 256) * (N // 256), -(-K // 64)
+        dp, rem, S = _split_plan(tiles, kt, split)
+        assert (i.sk_tiles, i.split_k, i.grid) == (rem, S, dp + rem * S), (M, N, K, i.sk_tiles, i.split_k, i.grid)
+        assert i.sk_workgroups == rem * S
+        want_ws = ((rem * 4 + 255) // 256 * 256 + rem * S * 256 * 256 * 4) if rem else 0
+        assert i.workspace_bytes == want_ws
+    # the 6144x4096x2048 workload: 384 tiles = 1.5 rounds, but K is short
+    # (32 slices): the partials would cost more than the idle half round
+    st, i = _plan(*_gemm_descs(6144, 4096, 2048))
+    assert (i.sk_tiles, i.grid) == (0, 384)
+    # 49 tiles of 110 slices: whole tiles would leave 207 CUs idle
+    st, i = _plan(*_gemm_descs(1792, 1792, 7040))
+    assert (i.sk_tiles, i.split_k, i.grid) == (49, 5, 245)
 
 
 def test_plan_m_major_output_is_transposed():
