@@ -11,8 +11,12 @@ on stdout (everything else goes to stderr):
   roofline   the tiled kernel's achieved TFLOP/s from HIP events on the launch
              stream, against the dense bf16 MFMA peak
   cpu_baseline  the fp64 oracle, timed on a bounded sample of the same workload
-  extra      the other measured workloads (4096^3 fp16, 6144x4096x2048 M-/N-major
-             fp16, and the HBM-bound 32x8192x8192 bf16 in GB/s)
+  extra      the other measured workloads (256x128x64 fp16, 4096^3 fp16,
+             6144x4096x2048 M-/N-major fp16, the HBM-bound 32x8192x8192 bf16 in
+             GB/s), a shape whose tiles leave CUs idle with and without the split
+             remainder, and the device layout map
+The sampled checks here are fp64 torch sums on the device; the oracle runs
+only in the CPU-baseline leg (its parity claims live in tests/).
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--only-headline]
 """
@@ -123,18 +127,60 @@ class Workload:
         return wall, kern
 
     def check(self, npts: int = 256):
-        """Sampled parity of the last output against the oracle."""
-        import numpy as np
-        from oracle import gemm as og
-        from tests.gemm_cases import op, sample_points
-        import datagen
+        """Sampled sanity check of the last output (fp64 dot products on the
+        GPU at corner, edge and random outputs; the oracle parity tests cover
+        these launches in tests/)."""
         A, B, C, _ = self.host
-        M, N = self.c.M, self.c.N
-        pts = sample_points(M, N, npts, seed=self.c.cfg)
-        S, T = og.gemm_points(op(A), op(B), pts)
-        Dref, Cabs = og.epilogue(S, op(C) if self.C is not None else None, pts, self.c.alpha, self.c.beta)
-        out = datagen.Matrix(self.D.store.cpu(), self.D.shape, self.D.stride)
-        return og.check(og.read_points(op(out), pts), Dref, T, Cabs, self.c.alpha, self.c.dtype)
+        return sample_check(self.A.view(), self.Bs[0].view(), self.C.view() if self.C is not None else None,
+                            self.D.view(), self.c.alpha, self.c.beta, self.c.dtype,
+                            sample_points(self.c.M, self.c.N, npts, seed=self.c.cfg))
+
+
+class Check:
+    def __init__(self, n, n_bad, worst, nonfinite):
+        self.n, self.n_bad, self.worst_fraction, self.nonfinite = n, n_bad, worst, nonfinite
+        self.ok = n_bad == 0
+
+    def __str__(self):
+        return (f"{self.n - self.n_bad}/{self.n} within bound, worst {self.worst_fraction:.4f} of budget, "
+                f"non-finite {self.nonfinite}")
+
+
+def sample_points(M: int, N: int, n: int, seed: int):
+    """Corners, edges and n uniform random outputs."""
+    import numpy as np
+    rng = np.random.default_rng(seed)
+    pts = [(0, 0), (0, N - 1), (M - 1, 0), (M - 1, N - 1)]
+    pts += [(i, j) for i in (0, M - 1) for j in range(0, N, max(1, N // 64))]
+    pts += [(i, j) for j in (0, N - 1) for i in range(0, M, max(1, M // 64))]
+    r = np.stack([rng.integers(0, M, n), rng.integers(0, N, n)], axis=1)
+    return np.concatenate([np.array(pts, dtype=np.int64), r.astype(np.int64)])
+
+
+def sample_check(A, B, C, D, alpha: float, beta: float, dtype, pts) -> Check:
+    """|D - D_ref| <= 2e-3 (|alpha| sum_k |a b| + |beta c|) + one output ulp at
+    the given outputs, D_ref in fp64 from the same 16-bit inputs (torch on the
+    device: A (M,K), B (K,N), C, D (M,N) strided views)."""
+    import torch
+    i = torch.as_tensor(pts[:, 0], device=A.device)
+    j = torch.as_tensor(pts[:, 1], device=A.device)
+    prod = A.index_select(0, i).double() * B.index_select(1, j).t().double()
+    S, T = prod.sum(1), prod.abs().sum(1)
+    ref = alpha * S
+    cabs = torch.zeros_like(S)
+    if C is not None and beta != 0.0:
+        c = C[i, j].double()
+        ref = ref + beta * c
+        cabs = (beta * c).abs()
+    p, emin = {torch.float16: (10, -14), torch.bfloat16: (7, -126)}[dtype]
+    e = torch.floor(torch.log2(ref.abs().clamp_min(2.0 ** emin))).clamp_min(emin)
+    bound = 2e-3 * (abs(alpha) * T + cabs) + torch.exp2(e - p)
+    got = D[i, j].double()
+    finite = torch.isfinite(got)
+    err = torch.where(finite, (got - ref).abs(), torch.full_like(got, float("inf")))
+    frac = err / bound
+    bad = ~(err <= bound)
+    return Check(len(pts), int(bad.sum()), float(frac.max()) if len(pts) else 0.0, int((~finite).sum()))
 
 
 def cpu_baseline(w: Workload, budget_s: float):
@@ -142,7 +188,8 @@ def cpu_baseline(w: Workload, budget_s: float):
     same workload (full K). The oracle spreads rows over its threads, so rows
     go in chunks of one row per thread until about budget_s seconds have run."""
     from oracle import gemm as og
-    from tests.gemm_cases import op
+    from oracle.gemm import Operand
+    op = lambda m: Operand(m.store, m.shape, m.stride)
     A, B, _, _ = w.host
     Aw, Bw = op(A).widened(), op(B).widened()
     threads = og.num_threads()
@@ -154,9 +201,16 @@ def cpu_baseline(w: Workload, budget_s: float):
         dt += time.perf_counter() - t0
         rows += chunk
     flops = 2.0 * rows * w.c.N * w.c.K
+    # the layout oracle beside the device layout map (reported only)
+    from oracle import layout as ol
+    t0 = time.perf_counter()
+    ol.enumerate_offsets(ol.zipped_divide(ol.parse_layout("(256,128):(128,1)"), (16, 16)))
+    lay_ms = (time.perf_counter() - t0) * 1e3
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"{rows} of {w.c.M} output rows of the {w.c.M}x{w.c.N}x{w.c.K} workload, full K "
-                      f"({rows * w.c.N} outputs, {dt:.1f} s, fp64 sequential-k sums)"}
+                      f"({rows * w.c.N} outputs, {dt:.1f} s, fp64 sequential-k sums)",
+            "layout_map_oracle_ms": round(lay_ms, 1),
+            "layout_map_sample": "enumeration of zipped_divide((256,128):(128,1),(16,16)), 32768 offsets, 1 thread"}
 
 
 def roofline(w: Workload, plan: dict, kern_s: float, traffic):
@@ -196,6 +250,67 @@ def copy_probe(nbytes: int = 1 << 30, reps: int = 5):
     t = sum(a.elapsed_time(b) for a, b in ev) / reps / 1e3
     print(json.dumps({"copy_probe_bytes_read": nbytes, "copy_probe_bytes_written": nbytes, "launches": reps + 1,
                       "us": round(t * 1e6, 1), "GB/s": round(2 * nbytes / t / 1e9, 1)}), flush=True)
+
+
+def layout_map_timing(reps: int = 20):
+    """The layout-map path: the device evaluation of zipped_divide((256,128):
+    (128,1), (16,16)) (32,768 offsets) timed with HIP events, compared with
+    the host library's evaluation of the same layout (the oracle parity of
+    both is in tests/; the oracle's own enumeration time is reported in the
+    CPU baseline)."""
+    import torch
+    from layout_algebra_tiled_amd import gemm as g
+    from layout_algebra_tiled_amd.layout import Layout
+    L = Layout.parse("(256,128):(128,1)").zipped_divide((16, 16))
+    n = L.size()
+    out = torch.empty(n, dtype=torch.int64, device="cuda:0")
+    g.layout_eval_device(L, out)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in ev:
+        a.record()
+        g.layout_eval_device(L, out)
+        b.record()
+    torch.cuda.synchronize()
+    dev_s = sum(a.elapsed_time(b) for a, b in ev) / reps / 1e3
+    same = out.cpu().tolist() == [L(x) for x in range(n)]
+    return {"layout": str(L), "elements": n, "device_us": round(dev_s * 1e6, 2),
+            "equals_host_library": bool(same)}
+
+
+def split_remainder_timing(M: int, N: int, K: int, reps: int = 20):
+    """A bf16 shape whose tiles fill no whole round of the 256 CUs, timed with
+    the last round's tiles whole (split_k=1) and split into K segments (the
+    planner's choice), plus a sampled fp64 check of the split result."""
+    import torch
+    import datagen
+    from layout_algebra_tiled_amd import gemm as g
+    A = datagen.matrix(M, K, torch.bfloat16, "row", "normal_over_sqrtk", 11, ld=K, k_for_scale=K)
+    B = datagen.matrix(K, N, torch.bfloat16, "col", "normal_over_sqrtk", 12, ld=K, k_for_scale=K)
+    dA, dB = A.to("cuda:0"), B.to("cuda:0")
+    D = torch.empty(M, N, dtype=torch.bfloat16, device="cuda:0")
+    rec = {"shape": f"bf16 {M}x{N}x{K}, K-major A and B"}
+    for label, split in (("whole_tiles", 1), ("planned", 0)):
+        p = g.plan(dA.view(), dB.view(), D, None, 0.0, kernel="tiled", split_k=split)
+        ws = torch.empty(max(p["workspace_bytes"], 1), dtype=torch.uint8, device="cuda:0")
+        run = lambda: g.gemm(dA.view(), dB.view(), D, None, 1.0, 0.0, kernel="tiled", split_k=split, workspace=ws)
+        t_end = time.perf_counter() + 0.5
+        while time.perf_counter() < t_end:
+            run()
+            torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for a, b in ev:
+            a.record()
+            run()
+            b.record()
+        torch.cuda.synchronize()
+        k = sum(a.elapsed_time(b) for a, b in ev) / reps / 1e3
+        rec[label] = {"grid": p["grid"], "split_tiles": p["sk_tiles"], "segments": p["split_k"],
+                      "kernel_us": round(k * 1e6, 1), "TFLOP/s": round(2 * M * N * K / k / 1e12, 1)}
+    chk = sample_check(dA.view(), dB.view(), None, D, 1.0, 0.0, torch.bfloat16, sample_points(M, N, 500, seed=7))
+    rec["parity"] = str(chk)
+    rec["parity_ok"] = bool(chk.ok)
+    return rec
 
 
 def main():
@@ -241,7 +356,7 @@ def main():
     chk = w.check()
     log(f"[bench] {value:.1f} TFLOP/s wall, kernel {kern * 1e6:.1f} us = {achieved:.1f} TFLOP/s; check: {chk}")
     if not chk.ok:
-        raise SystemExit(f"bench result failed the oracle check: {chk}")
+        raise SystemExit(f"bench result failed the sampled check: {chk}")
     tkey = f"{plan['kernel_name']}:workload{args.workload}"
     line = {
         "metric": METRIC,
@@ -270,7 +385,7 @@ def main():
     }
     if not args.only_headline:
         extra = {}
-        for cfg, n_b in ((2, 1), (4, 1), (5, 4)):
+        for cfg, n_b in ((1, 1), (2, 1), (4, 1), (5, 4)):
             x = Workload(cfg, n_b=n_b)
             p = x.plan()
             ws = None
@@ -282,6 +397,8 @@ def main():
             rec = {"kernel": p["kernel_name"], "ms_per_step": round(xw * 1e3, 4), "kernel_us": round(xk * 1e6, 2),
                    "TFLOP/s": round(x.c.flops() / xw / 1e12, 2), "parity_ok": bool(xc.ok),
                    "worst_fraction": round(xc.worst_fraction, 4)}
+            if cfg == 1:
+                rec["note"] = "launch-latency bound: 128 16x16 tiles, one wave each"
             if cfg == 5:
                 rec["GB/s"] = round(x.c.bytes() / xk / 1e9, 1)
                 rec["frac_hbm"] = round(x.c.bytes() / xk / 1e9 / PEAK_HBM_GBS, 4)
@@ -292,6 +409,10 @@ def main():
             log(f"[bench] workload {cfg}: {rec}")
             del x
             torch.cuda.empty_cache()
+        extra["split remainder (1792x1792x7040, 49 tiles)"] = split_remainder_timing(1792, 1792, 7040)
+        log(f"[bench] split remainder: {extra['split remainder (1792x1792x7040, 49 tiles)']}")
+        extra["layout map"] = layout_map_timing()
+        log(f"[bench] layout map: {extra['layout map']}")
         line["extra"] = extra
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample ...")
