@@ -320,7 +320,9 @@ lt_status lt_gemm_workspace_size(const lt_tensor* A, const lt_tensor* B, const l
  * accumulation, fp32 epilogue, output rounded to nearest even. beta == 0
  * never reads C (C may be NULL). M == 0 or N == 0 does nothing; K == 0 gives
  * D = beta*C. `workspace` is caller-owned device memory of at least the
- * planned workspace_bytes (may be NULL when that is 0). Asynchronous on
+ * planned workspace_bytes, 256-byte aligned (may be NULL when that is 0;
+ * LT_ERR_WORKSPACE otherwise). Its contents need no initialisation, but two
+ * runs in flight at once must not share it. Asynchronous on
  * `stream`. */
 lt_status lt_gemm_run(const lt_tensor* A, const lt_tensor* B, const lt_tensor* C, const lt_tensor* D,
                       float alpha, float beta, const lt_gemm_options* opt, void* workspace,

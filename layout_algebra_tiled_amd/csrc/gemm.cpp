@@ -383,7 +383,8 @@ lt_status lt_gemm_run_ex(const lt_tensor* A, const lt_tensor* B, const lt_tensor
         return LT_ERR_INVALID_ARGUMENT;
     lt_status st = lt::make_plan(A, B, C, D, bnz, opt, &p);
     if (st != LT_OK) return st;
-    if ((size_t)p.info.workspace_bytes > workspace_bytes || (p.info.workspace_bytes > 0 && !workspace))
+    if ((size_t)p.info.workspace_bytes > workspace_bytes || (p.info.workspace_bytes > 0 && !workspace) ||
+        (p.info.workspace_bytes > 0 && reinterpret_cast<uintptr_t>(workspace) % 256 != 0))
         return LT_ERR_WORKSPACE;
     lt::EpiArgs ea;
     if (epi && (epi->bias || epi->activation != LT_ACT_NONE || epi->amax)) {

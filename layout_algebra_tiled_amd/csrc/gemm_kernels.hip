@@ -297,15 +297,11 @@ int launch_zero_i32(int* p, int n, void* stream) {
 int launch_skinny(int dtype, const SkinnyArgs& a, void* stream) {
     dim3 grid(a.N / kSkinnyBN, a.split_k), block(64 * kSkinnyWaves);
     hipStream_t s = static_cast<hipStream_t>(stream);
-    static bool attr[2] = {false, false};
+    static std::atomic<uint64_t> attr[2];
     const int which = dtype == LT_F16 ? 0 : 1;
-    if (!attr[which]) {
-        const void* k = which == 0 ? reinterpret_cast<const void*>(&gemm_skinny<LT_F16>)
-                                   : reinterpret_cast<const void*>(&gemm_skinny<LT_BF16>);
-        hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, kSkinnyLdsBytes);
-        if (e != hipSuccess) return static_cast<int>(e);
-        attr[which] = true;
-    }
+    const void* k = which == 0 ? reinterpret_cast<const void*>(&gemm_skinny<LT_F16>)
+                               : reinterpret_cast<const void*>(&gemm_skinny<LT_BF16>);
+    if (const int e = set_lds_limit_once(k, kSkinnyLdsBytes, attr[which])) return e;
     if (dtype == LT_F16)
         hipLaunchKernelGGL(gemm_skinny<LT_F16>, grid, block, kSkinnyLdsBytes, s, a);
     else

@@ -492,13 +492,9 @@ using Chosen = TCfg<LT_TILED_NWM, LT_TILED_NWN, LT_TILED_BK, LT_TILED_S, LT_TILE
 
 template <int DT, class Cf, bool SPLIT>
 int launch_mode(const TiledArgs& a, int grid, hipStream_t s) {
-    static bool attr = false;
-    if (!attr) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_tiled<DT, Cf, SPLIT>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, Cf::LDS);
-        if (e != hipSuccess) return static_cast<int>(e);
-        attr = true;
-    }
+    static std::atomic<uint64_t> attr{0};
+    if (const int e = set_lds_limit_once(reinterpret_cast<const void*>(&gemm_tiled<DT, Cf, SPLIT>), Cf::LDS, attr))
+        return e;
     hipLaunchKernelGGL((gemm_tiled<DT, Cf, SPLIT>), dim3(grid), dim3(Cf::NT), Cf::LDS, s, a);
     return static_cast<int>(hipGetLastError());
 }

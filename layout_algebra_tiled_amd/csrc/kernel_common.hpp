@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdint>
 
 #include "gemm_kernels.hpp"
@@ -142,6 +143,21 @@ __device__ __forceinline__ void store_n(uint16_t* D, const uint16_t* C, int64_t 
         if (beta != 0.0f) v += beta * Tr<DT>::to_f32(C[cof + e]);
         D[dof + e] = Tr<DT>::from_f32(v);
     }
+}
+
+// Raise a kernel's dynamic LDS limit to `bytes`, once per device (the
+// attribute belongs to the device the call is made on); `done` holds one bit
+// per device id. Returns 0 or the hipError_t.
+inline int set_lds_limit_once(const void* fn, int bytes, std::atomic<uint64_t>& done) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return static_cast<int>(e);
+    const uint64_t bit = 1ull << (dev & 63);
+    if (done.load(std::memory_order_acquire) & bit) return 0;
+    e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e != hipSuccess) return static_cast<int>(e);
+    done.fetch_or(bit, std::memory_order_release);
+    return 0;
 }
 
 }  // namespace lt

@@ -435,6 +435,12 @@ def test_plan_validation_statuses():
     A, B, C, D = _gemm_descs(32, 1024, 8192)
     st = L.lib().lt_gemm_run(ctypes.byref(A), ctypes.byref(B), None, ctypes.byref(D), 1.0, 0.0, None, None, 0, None)
     assert L.STATUS_NAMES[st] == "LT_ERR_WORKSPACE"
+    # a workspace that is big enough but not 256-byte aligned is refused too
+    ws = _plan(A, B, None, D)[1].workspace_bytes
+    assert ws > 0
+    st = L.lib().lt_gemm_run(ctypes.byref(A), ctypes.byref(B), None, ctypes.byref(D), 1.0, 0.0, None,
+                             ctypes.c_void_p(BASE + (5 << 30) + 64), ws, None)
+    assert L.STATUS_NAMES[st] == "LT_ERR_WORKSPACE"
 
 
 def test_plan_ragged_shapes_on_the_tiled_kernel():
