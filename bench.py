@@ -98,7 +98,7 @@ class Workload:
                self.C.store if self.C is not None else None, self.c.alpha, self.c.beta, layouts=self.lay,
                workspace=workspace)
 
-    def time(self, steps: int, warmup: int, warmup_s: float = 0.0, clock_probe: bool = False):
+    def time(self, steps: int, warmup: int, warmup_s: float = 0.0):
         """Wall time per step (barrier + synchronize around the timed steps)
         and the average kernel duration from HIP events on the launch stream.
         Warm-up runs at least `warmup` steps and at least `warmup_s` seconds:
@@ -107,17 +107,13 @@ class Workload:
         import torch
         t0 = time.perf_counter()
         t_end = t0 + warmup_s
-        probe = None
         i = 0
         while i < warmup or time.perf_counter() < t_end:
             self.run(i)
             i += 1
             if i % 16 == 0:
                 torch.cuda.synchronize()
-            if clock_probe and probe is None and time.perf_counter() - t0 > 0.6 * warmup_s:
-                probe = start_clock_probe()   # shader clocks, sampled under the sustained load
         torch.cuda.synchronize()
-        self.sclk_mhz = finish_clock_probe(probe)
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
@@ -139,38 +135,6 @@ class Workload:
         return sample_check(self.A.view(), self.Bs[0].view(), self.C.view() if self.C is not None else None,
                             self.D.view(), self.c.alpha, self.c.beta, self.c.dtype,
                             sample_points(self.c.M, self.c.N, npts, seed=self.c.cfg))
-
-
-def start_clock_probe():
-    """amd-smi's per-XCD graphics clocks, queried in the background while the
-    GPU is busy with the warm-up launches (None if the tool is missing)."""
-    import shutil
-    import subprocess
-    exe = shutil.which("amd-smi")
-    if not exe:
-        return None
-    return subprocess.Popen([exe, "metric", "-c", "--json"], stdout=subprocess.PIPE, stderr=subprocess.DEVNULL,
-                            text=True)
-
-
-def finish_clock_probe(probe):
-    """Mean graphics clock (MHz) over the XCDs of GPU 0 from the probe's JSON,
-    or None."""
-    if probe is None:
-        return None
-    try:
-        out, _ = probe.communicate(timeout=30)
-        data = json.loads(out)
-        if isinstance(data, dict) and "gpu_data" in data:
-            data = data["gpu_data"]
-        gpu = data[0] if isinstance(data, list) else data
-        clocks = gpu.get("clock", gpu)
-        vals = [v["clk"]["value"] for k, v in clocks.items() if k.startswith("gfx") and isinstance(v, dict)
-                and isinstance(v.get("clk"), dict) and isinstance(v["clk"].get("value"), (int, float))]
-        return round(sum(vals) / len(vals), 1) if vals else None
-    except Exception:   # a missing or changed tool output leaves the figure unreported
-        probe.kill()
-        return None
 
 
 class Check:
@@ -369,6 +333,11 @@ def main():
               "(the GEMM would shard by N or M with no exchange; see the design notes)", file=sys.stderr)
         sys.exit(2)
 
+    if not args.no_cpu_baseline:
+        # compile the C oracle (if stale) before the GPU is touched: a process
+        # that has initialised the GPU must not start other programs
+        from oracle import gemm as og
+        og.build()
     import torch
     from layout_algebra_tiled_amd import gemm as g
     arch = g.device_check()
@@ -386,7 +355,7 @@ def main():
         f"wave tile {plan['wave_m']}x{plan['wave_n']}, {plan['waves']} waves, {plan['stages']} LDS stages "
         f"({plan['lds_bytes']} B), grid {plan['grid']}, {plan['mfma_per_wave_kstep']} "
         f"MFMA {plan['mfma_m']}x{plan['mfma_n']}x{plan['mfma_k']} per wave per K step")
-    wall, kern = w.time(args.steps, args.warmup, args.warmup_seconds, clock_probe=True)
+    wall, kern = w.time(args.steps, args.warmup, args.warmup_seconds)
     flops = w.c.flops()
     value = flops / wall / 1e12
     achieved = flops / kern / 1e12
@@ -416,9 +385,6 @@ def main():
                                  "median": round(w.kernel_times[len(w.kernel_times) // 2] * 1e6, 1),
                                  "min": round(w.kernel_times[0] * 1e6, 1)},
                    "warmup_s": args.warmup_seconds,
-                   "sclk_mhz_under_load": w.sclk_mhz,
-                   "peak_at_sclk_TFLOPs": (round(256 * 4096 * w.sclk_mhz * 1e6 / 1e12, 1)
-                                           if w.sclk_mhz else None),
                    "parity": f"{chk.n - chk.n_bad}/{chk.n} sampled outputs in bound, worst "
                              f"{chk.worst_fraction:.3f} of budget"},
         "roofline": roofline(w, plan, kern, traffic_for(tkey)),

@@ -7,5 +7,10 @@ if ROOT not in sys.path:
 
 
 def pytest_configure(config):
+    # the C oracle is compiled (if stale) before any test touches the GPU: a
+    # process that has initialised the GPU must not start other programs
+    from oracle import gemm as og
+    og.build()
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU; run through the C-ABI library")
     config.addinivalue_line("markers", "slow: takes more than a few seconds on the CPU")
+

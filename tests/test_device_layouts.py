@@ -8,6 +8,8 @@ fragment. The unswizzled maps are also compared with the host layout algebra."""
 import os
 import subprocess
 
+from tests.proc import skip_if_gpu_initialised
+
 import pytest
 
 from layout_algebra_tiled_amd import Layout
@@ -18,6 +20,7 @@ CSRC = os.path.join(ROOT, "layout_algebra_tiled_amd", "csrc")
 
 @pytest.fixture(scope="module")
 def maps(tmp_path_factory):
+    skip_if_gpu_initialised()
     d = tmp_path_factory.mktemp("devlayout")
     exe = d / "dump"
     subprocess.check_call(["g++", "-std=c++17", "-O1", f"-I{CSRC}", "-o", str(exe),

@@ -5,6 +5,8 @@ import ctypes
 import os
 import subprocess
 
+from tests.proc import skip_if_gpu_initialised
+
 import numpy as np
 import pytest
 import torch
@@ -168,6 +170,7 @@ _C_MUTANTS = {
 
 @pytest.mark.parametrize("name", sorted(_C_MUTANTS))
 def test_c_mutant_is_caught(name, tmp_path):
+    skip_if_gpu_initialised()
     src = open(os.path.join(os.path.dirname(og.__file__), "gemm_oracle.c")).read()
     old, new = _C_MUTANTS[name]
     assert old in src
