@@ -412,37 +412,115 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
 
     // ---- epilogue: block (i, j), registers 4g..4g+3 hold row m = lane % MF
     // and four consecutive columns of the MF x MF block. A tile on a ragged
-    // edge stores only the outputs inside (M, N).
+    // edge stores only the outputs inside (M, N). With beta != 0 every C load
+    // of the wave is issued before the first is waited on (one memory round
+    // trip per tile, not one per block); the fragment registers are free by
+    // now and hold them.
+    constexpr int NG = Mf::NACC / 4;   // groups of four outputs per block
     auto epilogue = [&](auto edge) {
+        constexpr bool EDGE = decltype(edge)::value;
+        const bool use_c = p.beta != 0.0f;
+        u32x2 cv[FM][FN][NG];
+        auto load_c = [&](auto guarded) {
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                const int m = m0 + arow0 + i * Cf::MF + Mf::out_col(lane);
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+#pragma unroll
+                    for (int g = 0; g < NG; ++g) {
+                        const int n = n0 + brow0 + j * Cf::MF + Mf::out_row(lane, 4 * g);
+                        const u32x2* src = reinterpret_cast<const u32x2*>(p.C + (int64_t)m * p.ldc + n);
+                        if constexpr (decltype(guarded)::value)
+                            cv[i][j][g] = (m < p.M && n + 4 <= p.N) ? *src : u32x2{0u, 0u};
+                        else
+                            cv[i][j][g] = *src;
+                    }
+            }
+        };
+        if (!use_c) {
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+#pragma unroll
+                    for (int g = 0; g < NG; ++g) cv[i][j][g] = u32x2{0u, 0u};
+        } else {
+            load_c(std::integral_constant<bool, EDGE>{});   // a whole tile loads with no branch per block
+        }
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
             const int m = m0 + arow0 + i * Cf::MF + Mf::out_col(lane);
 #pragma unroll
             for (int j = 0; j < FN; ++j) {
 #pragma unroll
-                for (int g = 0; g < Mf::NACC / 4; ++g) {
+                for (int g = 0; g < NG; ++g) {
                     const int n = n0 + brow0 + j * Cf::MF + Mf::out_row(lane, 4 * g);
                     const float v[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
                                         acc[i][j][4 * g + 3]};
-                    if constexpr (decltype(edge)::value) {
+                    if constexpr (EDGE) {
                         if (m < p.M && n < p.N) {
                             if (n + 4 <= p.N)
-                                store4<DT>(p.D, p.C, (int64_t)m * p.ldd + n, (int64_t)m * p.ldc + n, v[0], v[1],
-                                           v[2], v[3], p.alpha, p.beta);
+                                store4_c<DT>(p.D, (int64_t)m * p.ldd + n, v, p.alpha, p.beta, cv[i][j][g]);
                             else
                                 store_n<DT>(p.D, p.C, (int64_t)m * p.ldd + n, (int64_t)m * p.ldc + n, v,
                                             p.N - n, p.alpha, p.beta);
                         }
                     } else {
-                        store4<DT>(p.D, p.C, (int64_t)m * p.ldd + n, (int64_t)m * p.ldc + n, v[0], v[1], v[2],
-                                   v[3], p.alpha, p.beta);
+                        store4_c<DT>(p.D, (int64_t)m * p.ldd + n, v, p.alpha, p.beta, cv[i][j][g]);
                     }
                 }
             }
         }
     };
-    // The fused epilogue (bias, activation, max |D|), for any tile.
+    // The fused epilogue (bias, activation, max |D|), for any tile. Its C
+    // values and bias entries are gathered before any is used, as above: a
+    // row bias is one value per block row i, a column bias four per (j, g),
+    // the same for every i.
     auto epilogue_fused = [&]() {
+        const EpiArgs& e = p.epi;
+        const bool use_c = p.beta != 0.0f;
+        float brow[FM];
+        uint16_t bcol[FN][NG][4];   // kept in the operand format until used: fewer registers
+#pragma unroll
+        for (int i = 0; i < FM; ++i) brow[i] = 0.0f;
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int g = 0; g < NG; ++g)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) bcol[j][g][q] = 0;
+        if (e.bias && e.bias_on_rows) {
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                const int m = m0 + arow0 + i * Cf::MF + Mf::out_col(lane);
+                brow[i] = m < p.M ? Tr<DT>::to_f32(e.bias[(int64_t)m * e.bias_stride]) : 0.0f;
+            }
+        } else if (e.bias) {
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int g = 0; g < NG; ++g)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int n = n0 + brow0 + j * Cf::MF + Mf::out_row(lane, 4 * g) + q;
+                        bcol[j][g][q] = n < p.N ? e.bias[(int64_t)n * e.bias_stride] : uint16_t{0};
+                    }
+        }
+        u32x2 cv[FM][FN][NG];
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const int m = m0 + arow0 + i * Cf::MF + Mf::out_col(lane);
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int g = 0; g < NG; ++g) {
+                    const int n = n0 + brow0 + j * Cf::MF + Mf::out_row(lane, 4 * g);
+                    cv[i][j][g] = use_c && m < p.M && n + 4 <= p.N
+                                      ? *reinterpret_cast<const u32x2*>(p.C + (int64_t)m * p.ldc + n)
+                                      : u32x2{0u, 0u};
+                }
+        }
         float amax = 0.0f;
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
@@ -450,17 +528,38 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
 #pragma unroll
             for (int j = 0; j < FN; ++j) {
 #pragma unroll
-                for (int g = 0; g < Mf::NACC / 4; ++g) {
+                for (int g = 0; g < NG; ++g) {
                     const int n = n0 + brow0 + j * Cf::MF + Mf::out_row(lane, 4 * g);
-                    const float v[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
-                                        acc[i][j][4 * g + 3]};
-                    if (m < p.M && n < p.N)
-                        store4_fused<DT>(p.D, p.C, (int64_t)m * p.ldd + n, (int64_t)m * p.ldc + n, v,
-                                         min(4, p.N - n), p.alpha, p.beta, p.epi, m, n, &amax);
+                    if (m >= p.M || n >= p.N) continue;
+                    const int cnt = min(4, p.N - n);
+                    const uint16_t c16[4] = {static_cast<uint16_t>(cv[i][j][g].x & 0xffff),
+                                             static_cast<uint16_t>(cv[i][j][g].x >> 16),
+                                             static_cast<uint16_t>(cv[i][j][g].y & 0xffff),
+                                             static_cast<uint16_t>(cv[i][j][g].y >> 16)};
+                    uint16_t o[4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        float v = p.alpha * acc[i][j][4 * g + q];
+                        if (use_c)   // a partial group (cnt < 4) reads its C elements here
+                            v += p.beta * Tr<DT>::to_f32(cnt == 4 ? c16[q]
+                                                                  : (q < cnt ? p.C[(int64_t)m * p.ldc + n + q]
+                                                                             : uint16_t{0}));
+                        v += e.bias_on_rows ? brow[i] : Tr<DT>::to_f32(bcol[j][g][q]);
+                        o[q] = Tr<DT>::from_f32(activate(v, e.act));
+                        if (q < cnt) amax = fmaxf(amax, fabsf(Tr<DT>::to_f32(o[q])));
+                    }
+                    if (cnt == 4) {
+                        u32x2 w;
+                        w.x = (uint32_t)o[0] | ((uint32_t)o[1] << 16);
+                        w.y = (uint32_t)o[2] | ((uint32_t)o[3] << 16);
+                        *reinterpret_cast<u32x2*>(p.D + (int64_t)m * p.ldd + n) = w;
+                    } else {
+                        for (int q = 0; q < cnt; ++q) p.D[(int64_t)m * p.ldd + n + q] = o[q];
+                    }
                 }
             }
         }
-        if (p.epi.amax) amax_commit(p.epi.amax, amax);
+        if (e.amax) amax_commit(e.amax, amax);
     };
     if (p.epi.fused)
         epilogue_fused();

@@ -84,6 +84,28 @@ __device__ __forceinline__ void store4(uint16_t* D, const uint16_t* C, int64_t d
     *reinterpret_cast<u32x2*>(D + dof) = o;
 }
 
+// store4 with the four C values already loaded (c = 0 when beta == 0), so a
+// caller can issue all its C loads before the first one is waited on.
+template <int DT>
+__device__ __forceinline__ void store4_c(uint16_t* D, int64_t dof, const float* a, float alpha, float beta,
+                                         u32x2 c) {
+    const float v0 = alpha * a[0] + beta * Tr<DT>::to_f32(static_cast<uint16_t>(c.x & 0xffff));
+    const float v1 = alpha * a[1] + beta * Tr<DT>::to_f32(static_cast<uint16_t>(c.x >> 16));
+    const float v2 = alpha * a[2] + beta * Tr<DT>::to_f32(static_cast<uint16_t>(c.y & 0xffff));
+    const float v3 = alpha * a[3] + beta * Tr<DT>::to_f32(static_cast<uint16_t>(c.y >> 16));
+    u32x2 o;
+    o.x = pack2<DT>(v0, v1);
+    o.y = pack2<DT>(v2, v3);
+    *reinterpret_cast<u32x2*>(D + dof) = o;
+}
+
+// The activation of the fused epilogue, in fp32.
+__device__ __forceinline__ float activate(float v, int act) {
+    if (act == LT_ACT_RELU) return v > 0.0f ? v : 0.0f;
+    if (act == LT_ACT_GELU) return 0.5f * v * (1.0f + erff(v * 0.70710678118654752f));
+    return v;
+}
+
 // One fused output: alpha*acc + beta*c + bias, then the activation (ReLU:
 // x > 0 ? x : 0; GELU: x * Phi(x) = 0.5 x (1 + erf(x / sqrt 2))), in fp32.
 template <int DT>
@@ -92,11 +114,7 @@ __device__ __forceinline__ float fused_value(float acc, float alpha, float beta,
     float v = alpha * acc;
     if (beta != 0.0f) v += beta * Tr<DT>::to_f32(C[cof]);
     if (e.bias) v += Tr<DT>::to_f32(e.bias[(int64_t)(e.bias_on_rows ? m : n) * e.bias_stride]);
-    if (e.act == LT_ACT_RELU)
-        v = v > 0.0f ? v : 0.0f;
-    else if (e.act == LT_ACT_GELU)
-        v = 0.5f * v * (1.0f + erff(v * 0.70710678118654752f));
-    return v;
+    return activate(v, e.act);
 }
 
 // Fused epilogue of the first cnt (1..4) of four consecutive N outputs of row
