@@ -65,6 +65,58 @@ def traffic_for(kernel_key: str):
     return rec.get("bytes_per_launch")
 
 
+class GpuSensors:
+    """Shader clock and board power of cuda:0 from the driver's sysfs files of
+    its PCI device (plain file reads: no other program is started). Each read
+    returns None where the files are absent or unreadable."""
+
+    def __init__(self):
+        import glob
+        import torch
+        self.sclk_path = self.power_path = None
+        try:
+            pr = torch.cuda.get_device_properties(0)
+            dev = f"/sys/bus/pci/devices/{pr.pci_domain_id:04x}:{pr.pci_bus_id:02x}:{pr.pci_device_id:02x}.0"
+        except Exception:
+            return
+        hw = sorted(glob.glob(dev + "/hwmon/hwmon*/"))
+        for name, attr in (("freq1_input", "sclk_path"), ("power1_input", "power_path")):
+            for d in hw:
+                if os.access(d + name, os.R_OK):
+                    setattr(self, attr, d + name)
+                    break
+        if self.sclk_path is None and os.access(dev + "/pp_dpm_sclk", os.R_OK):
+            self.sclk_path = dev + "/pp_dpm_sclk"
+
+    @staticmethod
+    def _read(path):
+        try:
+            return open(path).read() if path else None
+        except OSError:
+            return None
+
+    def sclk_mhz(self):
+        text = self._read(self.sclk_path)
+        if text is None:
+            return None
+        try:
+            if self.sclk_path.endswith("freq1_input"):
+                return int(text.split()[0]) / 1e6
+            for line in text.splitlines():   # the current level ends with '*': "S: 1803Mhz *"
+                if line.rstrip().endswith("*"):
+                    return float(line.split(":")[1].split()[0].lower().replace("mhz", ""))
+        except (ValueError, IndexError):
+            return None
+        return None
+
+    def power_w(self):
+        text = self._read(self.power_path)
+        try:
+            return int(text.split()[0]) / 1e6 if text else None
+        except (ValueError, IndexError):
+            return None
+
+
 class Workload:
     def __init__(self, cfg: int, n_b: int = 1):
         import torch
@@ -98,7 +150,7 @@ class Workload:
                self.C.store if self.C is not None else None, self.c.alpha, self.c.beta, layouts=self.lay,
                workspace=workspace)
 
-    def time(self, steps: int, warmup: int, warmup_s: float = 0.0):
+    def time(self, steps: int, warmup: int, warmup_s: float = 0.0, sample_clock: bool = False):
         """Wall time per step (barrier + synchronize around the timed steps)
         and the average kernel duration from HIP events on the launch stream.
         Warm-up runs at least `warmup` steps and at least `warmup_s` seconds:
@@ -108,12 +160,21 @@ class Workload:
         t0 = time.perf_counter()
         t_end = t0 + warmup_s
         i = 0
+        sensors = GpuSensors() if sample_clock else None
+        sclk, power = [], []
         while i < warmup or time.perf_counter() < t_end:
             self.run(i)
             i += 1
             if i % 16 == 0:
+                # sampled while the 16 launches just queued are running
+                if sensors is not None and time.perf_counter() - t0 > 0.5 * warmup_s:
+                    for lst, v in ((sclk, sensors.sclk_mhz()), (power, sensors.power_w())):
+                        if v is not None:
+                            lst.append(v)
                 torch.cuda.synchronize()
         torch.cuda.synchronize()
+        self.sclk_mhz = round(sum(sclk) / len(sclk), 1) if sclk else None
+        self.power_w = round(sum(power) / len(power), 1) if power else None
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
@@ -355,7 +416,7 @@ def main():
         f"wave tile {plan['wave_m']}x{plan['wave_n']}, {plan['waves']} waves, {plan['stages']} LDS stages "
         f"({plan['lds_bytes']} B), grid {plan['grid']}, {plan['mfma_per_wave_kstep']} "
         f"MFMA {plan['mfma_m']}x{plan['mfma_n']}x{plan['mfma_k']} per wave per K step")
-    wall, kern = w.time(args.steps, args.warmup, args.warmup_seconds)
+    wall, kern = w.time(args.steps, args.warmup, args.warmup_seconds, sample_clock=True)
     flops = w.c.flops()
     value = flops / wall / 1e12
     achieved = flops / kern / 1e12
@@ -385,6 +446,10 @@ def main():
                                  "median": round(w.kernel_times[len(w.kernel_times) // 2] * 1e6, 1),
                                  "min": round(w.kernel_times[0] * 1e6, 1)},
                    "warmup_s": args.warmup_seconds,
+                   "sclk_mhz_under_load": w.sclk_mhz,
+                   "board_power_w_under_load": w.power_w,
+                   "peak_at_sclk_TFLOPs": (round(256 * 4096 * w.sclk_mhz * 1e6 / 1e12, 1)
+                                           if w.sclk_mhz else None),
                    "parity": f"{chk.n - chk.n_bad}/{chk.n} sampled outputs in bound, worst "
                              f"{chk.worst_fraction:.3f} of budget"},
         "roofline": roofline(w, plan, kern, traffic_for(tkey)),
