@@ -180,7 +180,7 @@ lt_status make_plan(const lt_tensor* tA, const lt_tensor* tB, const lt_tensor* t
     const bool c_n = !beta_nonzero || p.C.e1 == 1 || p.C.s1 == 1;
 
     int kernel = opt ? opt->kernel : LT_KERNEL_AUTO;
-    const TiledShape ts = tiled_shape();
+    const TiledShape ts = tiled_shape(p.a_k, p.b_k);
     // M-major A and N-major B stream through the same kernel (transposed
     // fragment reads); any stride-1 mode of A and B works.
     // The tiled kernel addresses a K slice as a uniform base plus a per-lane
@@ -454,7 +454,7 @@ lt_status lt_gemm_run_ex(const lt_tensor* A, const lt_tensor* B, const lt_tensor
             // The tile grid: mode 1 of zipped_divide(D', (256,256)), where D'
             // is D's layout with M and N rounded up to whole tiles (the
             // outputs past (M, N) are predicated off in the epilogue).
-            const lt::TiledShape ts = lt::tiled_shape();
+            const lt::TiledShape ts = lt::tiled_shape(p.a_k, p.b_k);
             const int64_t mp = (p.M + ts.bm - 1) / ts.bm * ts.bm, np = (p.N + ts.bn - 1) / ts.bn * ts.bn;
             lt::Tree dl = lt::Tree::tuple({lt::Tree::leaf(mp, p.D.s0), lt::Tree::leaf(np, 1)});
             const int64_t tiler[2] = {ts.bm, ts.bn};

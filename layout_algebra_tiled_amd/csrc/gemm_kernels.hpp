@@ -99,7 +99,10 @@ struct TiledShape {
     int mfma_per_wave_slice; // MFMAs per wave per K slice
     int mfma_mn, mfma_k;     // MFMA instruction: mfma_mn x mfma_mn outputs, K depth
 };
-TiledShape tiled_shape();
+// The block shape the tiled kernel runs for the operands' major-ness (the
+// block tile, K slice, stages and LDS are the same for all; the wave layout
+// differs).
+TiledShape tiled_shape(bool a_kmajor, bool b_kmajor);
 
 // Each returns 0 on success or the hipError_t of the launch.
 int launch_wave16(int dtype, const Wave16Args& a, void* stream);

@@ -39,6 +39,10 @@ struct TCfg {
     static constexpr int FM = TWM / MF, FN = TWN / MF;        // MFMA blocks per wave
     static constexpr int KS = BK / MFMA::KSTEP;               // MFMA K steps per slice
     static constexpr bool AK = AK_, BKM = BK_MAJ_;            // K-major operands?
+    // One wave per SIMD (4 waves of 128x128): 256 accumulators per lane, held
+    // in AGPRs by MFMAs written as inline asm, in an issue order fixed here
+    // rather than by the compiler's scheduler.
+    static constexpr bool EXPLICIT = NW == 4 && MF_ == 16;
     static constexpr int OP_BYTES = 256 * BK * 2;             // one operand slice
     static constexpr int STAGE = 2 * OP_BYTES;
     static constexpr int LDS = S * STAGE;
@@ -98,6 +102,16 @@ __host__ __device__ __forceinline__ void static_for(F&& f) {
         f(std::integral_constant<int, B>{});
         static_for<B + 1, E>(f);
     }
+}
+
+// f(i, j) for every accumulator block, i < FM, j < FN, with i and j as
+// compile-time constants: unrolled whatever the block count, so the
+// accumulator array never needs a memory home.
+template <int FM, int FN, class F>
+__host__ __device__ __forceinline__ void for_blocks(F&& f) {
+    static_for<0, FM * FN>([&](auto ij) {
+        f(std::integral_constant<int, decltype(ij)::value / FN>{}, std::integral_constant<int, decltype(ij)::value % FN>{});
+    });
 }
 
 // One operand (A rows = M, or B rows = N) of the block tile.
@@ -200,6 +214,22 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
         });
     };
 
+    // Copy instruction c (< IPW) of slice kt into `stage`: A's OPI, then B's.
+    auto issue_one = [&](int stage, int kt, auto cc) {
+        constexpr int c = decltype(cc)::value;
+        char* sa = smem + stage * Cf::STAGE + wave * Cf::OPI * 1024;
+        if constexpr (c < Cf::OPI) {
+            constexpr int i = c, g = i / 4, o = (i % 4) * 1024;
+            const char* ga = a_k0 + (kt0 + kt) * a_ks;
+            __builtin_amdgcn_global_load_lds((ga - o) + aoffg[i], (LDS_AS void*)(sa + g * 4096), 16, o, 0);
+        } else {
+            constexpr int i = c - Cf::OPI, g = i / 4, o = (i % 4) * 1024;
+            const char* gb = b_k0 + (kt0 + kt) * b_ks;
+            __builtin_amdgcn_global_load_lds((gb - o) + boffg[i], (LDS_AS void*)(sa + Cf::OP_BYTES + g * 4096), 16,
+                                             o, 0);
+        }
+    };
+
     // Slice 0 when it is partial: a lane whose chunk lies below K = 0 writes
     // zeros where the copy would have put it (the copy's lane-linear LDS
     // position) instead of loading.
@@ -278,14 +308,22 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
         for (int b = 0; b < FN; ++b) bfr[buf][b] = read_frag(sb, boff, Cf::BKM, s, b);
     };
 
+    // fragment r of K step s: A block r (r < FM), else B block r - FM
+    auto read_one = [&](int stage, int s, int buf, auto rc) {
+        constexpr int r = decltype(rc)::value;
+        const char* sa = smem + stage * Cf::STAGE;
+        if constexpr (r < FM)
+            af[buf][r] = read_frag(sa, aoff, Cf::AK, s, r);
+        else
+            bfr[buf][r - FM] = read_frag(sa + Cf::OP_BYTES, boff, Cf::BKM, s, r - FM);
+    };
+
     using Acc = std::conditional_t<Cf::MF == 32, f32x16, f32x4>;
     Acc acc[FM][FN];
+    for_blocks<FM, FN>([&](auto i, auto j) {
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-            for (int v = 0; v < Mf::NACC; ++v) acc[i][j][v] = 0.0f;
+        for (int v = 0; v < Mf::NACC; ++v) acc[i][j][v] = 0.0f;
+    });
 
     // ---- prologue: slices 0 .. S-1
     if (kbase < 0 && kt0 == 0)
@@ -310,7 +348,7 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
     // a next slice but no refill, and the final slice.
     constexpr int NMF = FM * FN, NRD = (Cf::AK ? FM : 2 * FM) + (Cf::BKM ? FN : 2 * FN);
     int stage = 0;
-    auto slice = [&](auto has_next, auto refill, int t) {
+    auto slice_s = [&](auto has_next, auto refill, int t) {
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
             const int cur = s & 1, nxt = cur ^ 1;
@@ -355,12 +393,78 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
         }
         stage = stage + 1 == S ? 0 : stage + 1;
     };
+#if defined(__HIP_DEVICE_COMPILE__)
+    // The one-wave-per-SIMD schedule. Per K step: the MFMAs in block order,
+    // the next step's fragment reads spread over the first three quarters of
+    // them (one every few MFMAs, so the LDS sees a steady stream and the last
+    // read has a quarter of the step to land), and in the last step, after
+    // the barrier, the slice copies spread over all of them. The accumulators
+    // are asm operands bound to AGPRs ("a"), which keeps all 256 of them there.
+    auto mfma_one = [&](int cur, auto qc) {
+        constexpr int q = decltype(qc)::value, i = q / FN, j = q % FN;
+        auto& c = acc[i][j];
+        const V8 x = bfr[cur][j], y = af[cur][i];
+        if constexpr (DT == LT_BF16)
+            asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(x), "v"(y));
+        else
+            asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(c) : "v"(x), "v"(y));
+    };
+    auto slice_x = [&](auto has_next, auto refill, int t) {
+        static_for<0, KS>([&](auto sc) {
+            constexpr int s = decltype(sc)::value, cur = s & 1, nxt = cur ^ 1;
+            constexpr bool last = s + 1 == KS;
+            constexpr bool reads = !last || decltype(has_next)::value;
+            constexpr bool copies = last && decltype(refill)::value;
+            constexpr int NR = reads ? FM + FN : 0, NC = copies ? Cf::IPW : 0, NQ = FM * FN;
+            int rstage = stage, rs = s + 1;
+            if constexpr (last && decltype(has_next)::value) {
+                if constexpr (decltype(refill)::value)
+                    LT_WAIT_VM(Cf::IPW * (S - 2));   // slice t+1 landed (S-2 newer slices may fly)
+                else
+                    LT_WAIT_VM(0);
+                __syncthreads();   // slice t+1 visible to all; slice t's stage free
+                rstage = stage + 1 == S ? 0 : stage + 1;
+                rs = 0;
+            }
+            static_for<0, NQ>([&](auto qc) {
+                constexpr int q = decltype(qc)::value;
+                mfma_one(cur, qc);
+                static_for<0, (NC > 0 ? NC : 1)>([&](auto cc) {
+                    constexpr int c = decltype(cc)::value;
+                    if constexpr (NC > 0 && ((2 * c + 1) * NQ) / (2 * NC) == q) issue_one(stage, t + S, cc);
+                });
+                static_for<0, (NR > 0 ? NR : 1)>([&](auto rc) {
+                    constexpr int r = decltype(rc)::value;
+                    if constexpr (NR > 0 && (r * NQ * 3 / 4) / NR == q) read_one(rstage, rs, nxt, rc);
+                });
+            });
+        });
+        stage = stage + 1 == S ? 0 : stage + 1;
+    };
+#endif
+    auto slice = [&](auto has_next, auto refill, int t) {
+#if defined(__HIP_DEVICE_COMPILE__)
+        if constexpr (Cf::EXPLICIT)
+            slice_x(has_next, refill, t);
+        else
+#endif
+            slice_s(has_next, refill, t);
+    };
     const std::true_type yes{};
     const std::false_type no{};
+#if defined(__HIP_DEVICE_COMPILE__)
+    // the zeroed accumulators are written by VALU moves: wait states before
+    // the first inline-asm MFMA reads them (the compiler does not see it as one)
+    if constexpr (Cf::EXPLICIT) asm volatile("s_nop 7" ::: "memory");
+#endif
     int t = 0;
     for (; t + S < NS; ++t) slice(yes, yes, t);   // refill slice t+S
     for (; t + 1 < NS; ++t) slice(yes, no, t);    // slices already in flight
     slice(no, no, t);                             // the last slice
+#if defined(__HIP_DEVICE_COMPILE__)
+    // MFMA results before any VALU or memory instruction reads them
+    if constexpr (Cf::EXPLICIT) asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#endif
 
     // ---- split-K segment: publish the fp32 partial; the segment that
     // arrives last adds the others' and goes on to the epilogue. No waiting:
@@ -379,15 +483,12 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
             return p.partials + (((int64_t)skt * NSPL + s2) * (FM * FN) + (i * FN + j)) * (Cf::NT * Mf::NACC) +
                    threadIdx.x;
         };
+        for_blocks<FM, FN>([&](auto i, auto j) {
+            float* q = part(seg, i, j);
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-            for (int j = 0; j < FN; ++j) {
-                float* q = part(seg, i, j);
-#pragma unroll
-                for (int v = 0; v < Mf::NACC; ++v)
-                    __hip_atomic_store(q + v * Cf::NT, acc[i][j][v], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
+            for (int v = 0; v < Mf::NACC; ++v)
+                __hip_atomic_store(q + v * Cf::NT, acc[i][j][v], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        });
         LT_WAIT_VM(0);
         __syncthreads();   // every store of the partial is complete; the LDS ring is free
         int* flag = reinterpret_cast<int*>(smem);
@@ -397,15 +498,12 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
         if (*flag != NSPL - 1) return;
         for (int s2 = 0; s2 < NSPL; ++s2) {
             if (s2 == seg) continue;
+            for_blocks<FM, FN>([&](auto i, auto j) {
+                const float* q = part(s2, i, j);
 #pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int j = 0; j < FN; ++j) {
-                    const float* q = part(s2, i, j);
-#pragma unroll
-                    for (int v = 0; v < Mf::NACC; ++v)
-                        acc[i][j][v] += __hip_atomic_load(q + v * Cf::NT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                }
+                for (int v = 0; v < Mf::NACC; ++v)
+                    acc[i][j][v] += __hip_atomic_load(q + v * Cf::NT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            });
         }
         if (threadIdx.x == 0) __hip_atomic_store(&p.counters[skt], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
@@ -422,56 +520,47 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
         const bool use_c = p.beta != 0.0f;
         u32x2 cv[FM][FN][NG];
         auto load_c = [&](auto guarded) {
-#pragma unroll
-            for (int i = 0; i < FM; ++i) {
+            for_blocks<FM, FN>([&](auto i, auto j) {
                 const int m = m0 + arow0 + i * Cf::MF + Mf::out_col(lane);
-#pragma unroll
-                for (int j = 0; j < FN; ++j)
-#pragma unroll
-                    for (int g = 0; g < NG; ++g) {
-                        const int n = n0 + brow0 + j * Cf::MF + Mf::out_row(lane, 4 * g);
-                        const u32x2* src = reinterpret_cast<const u32x2*>(p.C + (int64_t)m * p.ldc + n);
-                        if constexpr (decltype(guarded)::value)
-                            cv[i][j][g] = (m < p.M && n + 4 <= p.N) ? *src : u32x2{0u, 0u};
-                        else
-                            cv[i][j][g] = *src;
-                    }
-            }
-        };
-        if (!use_c) {
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int j = 0; j < FN; ++j)
-#pragma unroll
-                    for (int g = 0; g < NG; ++g) cv[i][j][g] = u32x2{0u, 0u};
-        } else {
-            load_c(std::integral_constant<bool, EDGE>{});   // a whole tile loads with no branch per block
-        }
-#pragma unroll
-        for (int i = 0; i < FM; ++i) {
-            const int m = m0 + arow0 + i * Cf::MF + Mf::out_col(lane);
-#pragma unroll
-            for (int j = 0; j < FN; ++j) {
 #pragma unroll
                 for (int g = 0; g < NG; ++g) {
                     const int n = n0 + brow0 + j * Cf::MF + Mf::out_row(lane, 4 * g);
-                    const float v[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
-                                        acc[i][j][4 * g + 3]};
-                    if constexpr (EDGE) {
-                        if (m < p.M && n < p.N) {
-                            if (n + 4 <= p.N)
-                                store4_c<DT>(p.D, (int64_t)m * p.ldd + n, v, p.alpha, p.beta, cv[i][j][g]);
-                            else
-                                store_n<DT>(p.D, p.C, (int64_t)m * p.ldd + n, (int64_t)m * p.ldc + n, v,
-                                            p.N - n, p.alpha, p.beta);
-                        }
-                    } else {
-                        store4_c<DT>(p.D, (int64_t)m * p.ldd + n, v, p.alpha, p.beta, cv[i][j][g]);
+                    const u32x2* src = reinterpret_cast<const u32x2*>(p.C + (int64_t)m * p.ldc + n);
+                    if constexpr (decltype(guarded)::value)
+                        cv[i][j][g] = (m < p.M && n + 4 <= p.N) ? *src : u32x2{0u, 0u};
+                    else
+                        cv[i][j][g] = *src;
+                }
+            });
+        };
+        if (!use_c) {
+            for_blocks<FM, FN>([&](auto i, auto j) {
+#pragma unroll
+                for (int g = 0; g < NG; ++g) cv[i][j][g] = u32x2{0u, 0u};
+            });
+        } else {
+            load_c(std::integral_constant<bool, EDGE>{});   // a whole tile loads with no branch per block
+        }
+        for_blocks<FM, FN>([&](auto i, auto j) {
+            const int m = m0 + arow0 + i * Cf::MF + Mf::out_col(lane);
+#pragma unroll
+            for (int g = 0; g < NG; ++g) {
+                const int n = n0 + brow0 + j * Cf::MF + Mf::out_row(lane, 4 * g);
+                const float v[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                                    acc[i][j][4 * g + 3]};
+                if constexpr (EDGE) {
+                    if (m < p.M && n < p.N) {
+                        if (n + 4 <= p.N)
+                            store4_c<DT>(p.D, (int64_t)m * p.ldd + n, v, p.alpha, p.beta, cv[i][j][g]);
+                        else
+                            store_n<DT>(p.D, p.C, (int64_t)m * p.ldd + n, (int64_t)m * p.ldc + n, v, p.N - n,
+                                        p.alpha, p.beta);
                     }
+                } else {
+                    store4_c<DT>(p.D, (int64_t)m * p.ldd + n, v, p.alpha, p.beta, cv[i][j][g]);
                 }
             }
-        }
+        });
     };
     // The fused epilogue (bias, activation, max |D|), for any tile. Its C
     // values and bias entries are gathered before any is used, as above: a
@@ -508,25 +597,20 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
                     }
         }
         u32x2 cv[FM][FN][NG];
-#pragma unroll
-        for (int i = 0; i < FM; ++i) {
+        for_blocks<FM, FN>([&](auto i, auto j) {
             const int m = m0 + arow0 + i * Cf::MF + Mf::out_col(lane);
 #pragma unroll
-            for (int j = 0; j < FN; ++j)
-#pragma unroll
-                for (int g = 0; g < NG; ++g) {
-                    const int n = n0 + brow0 + j * Cf::MF + Mf::out_row(lane, 4 * g);
-                    cv[i][j][g] = use_c && m < p.M && n + 4 <= p.N
-                                      ? *reinterpret_cast<const u32x2*>(p.C + (int64_t)m * p.ldc + n)
-                                      : u32x2{0u, 0u};
-                }
-        }
+            for (int g = 0; g < NG; ++g) {
+                const int n = n0 + brow0 + j * Cf::MF + Mf::out_row(lane, 4 * g);
+                cv[i][j][g] = use_c && m < p.M && n + 4 <= p.N
+                                  ? *reinterpret_cast<const u32x2*>(p.C + (int64_t)m * p.ldc + n)
+                                  : u32x2{0u, 0u};
+            }
+        });
         float amax = 0.0f;
-#pragma unroll
-        for (int i = 0; i < FM; ++i) {
+        for_blocks<FM, FN>([&](auto i, auto j) {
             const int m = m0 + arow0 + i * Cf::MF + Mf::out_col(lane);
-#pragma unroll
-            for (int j = 0; j < FN; ++j) {
+            {
 #pragma unroll
                 for (int g = 0; g < NG; ++g) {
                     const int n = n0 + brow0 + j * Cf::MF + Mf::out_row(lane, 4 * g);
@@ -558,7 +642,7 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
                     }
                 }
             }
-        }
+        });
         if (e.amax) amax_commit(e.amax, amax);
     };
     if (p.epi.fused)
@@ -569,25 +653,17 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
         epilogue(std::false_type{});
 }
 
-// The instantiation the planner launches.
-#ifndef LT_TILED_NWM
-#define LT_TILED_NWM 4
-#endif
-#ifndef LT_TILED_NWN
-#define LT_TILED_NWN 2
-#endif
-#ifndef LT_TILED_BK
-#define LT_TILED_BK 64
-#endif
-#ifndef LT_TILED_S
-#define LT_TILED_S 2
-#endif
-#ifndef LT_TILED_MF
-#define LT_TILED_MF 16
-#endif
-
+// The instantiations the planner launches: K-major A and B run the
+// one-wave-per-SIMD kernel (4 waves of 128x128); when either operand needs
+// the transposing fragment reads, 8 waves of 64x128 (two per SIMD) with the
+// compiler's schedule, which measured faster there.
 template <bool AK, bool BKM>
-using Chosen = TCfg<LT_TILED_NWM, LT_TILED_NWN, LT_TILED_BK, LT_TILED_S, LT_TILED_MF, AK, BKM>;
+using Chosen = std::conditional_t<AK && BKM, TCfg<2, 2, 64, 2, 16, AK, BKM>, TCfg<4, 2, 64, 2, 16, AK, BKM>>;
+// The split-remainder launch always runs 8 waves: its fix-up adds the other
+// segments' fp32 partials in registers, and with 256 accumulators per lane
+// that step spills (measured 320 vs 91 us on 1792x1792x7040).
+template <bool AK, bool BKM>
+using ChosenSplit = TCfg<4, 2, 64, 2, 16, AK, BKM>;
 
 template <int DT, class Cf, bool SPLIT>
 int launch_mode(const TiledArgs& a, int grid, hipStream_t s) {
@@ -602,13 +678,12 @@ int launch_mode(const TiledArgs& a, int grid, hipStream_t s) {
 // remainder.
 template <int DT, bool AK, bool BKM>
 int launch_one(const TiledArgs& a, hipStream_t s) {
-    using Cf = Chosen<AK, BKM>;
     if (a.dp_tiles > 0) {
-        const int e = launch_mode<DT, Cf, false>(a, a.dp_tiles, s);
+        const int e = launch_mode<DT, Chosen<AK, BKM>, false>(a, a.dp_tiles, s);
         if (e != 0) return e;
     }
     const int split_wgs = (a.tiles_m * a.tiles_n - a.dp_tiles) * a.sk_splits;
-    if (split_wgs > 0) return launch_mode<DT, Cf, true>(a, split_wgs, s);
+    if (split_wgs > 0) return launch_mode<DT, ChosenSplit<AK, BKM>, true>(a, split_wgs, s);
     return 0;
 }
 
@@ -622,10 +697,17 @@ int launch_dt(bool ak, bool bk, const TiledArgs& a, hipStream_t s) {
 
 }  // namespace
 
-TiledShape tiled_shape() {
-    using Cf = Chosen<true, true>;
+template <class Cf>
+TiledShape shape_of() {
     return TiledShape{256, 256, Cf::BK, Cf::TWM, Cf::TWN, Cf::NW, Cf::S, Cf::LDS, Cf::FM * Cf::FN * Cf::KS,
                       Cf::MF, Cf::MFMA::KSTEP};
+}
+
+TiledShape tiled_shape(bool a_kmajor, bool b_kmajor) {
+    if (a_kmajor && b_kmajor) return shape_of<Chosen<true, true>>();
+    if (a_kmajor) return shape_of<Chosen<true, false>>();
+    if (b_kmajor) return shape_of<Chosen<false, true>>();
+    return shape_of<Chosen<false, false>>();
 }
 
 int launch_tiled(int dtype, bool a_kmajor, bool b_kmajor, const TiledArgs& a, void* stream) {
