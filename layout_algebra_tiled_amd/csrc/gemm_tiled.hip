@@ -292,13 +292,46 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
         // K rows KSTEP*s + 4q (+ the lane's own rows, folded into off[b]);
         // the row swizzle depends only on krow & 3, which KSTEP*s + 4q keeps
         const LDS_AS char* p0 = (const LDS_AS char*)(base + off[b] + (Mf::KSTEP * s) * 512);
-        i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(p0));
-        i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(p0 + 4 * 512));
+#if defined(__HIP_DEVICE_COMPILE__)
+        // Inline asm rather than the compiler's transposing-read builtin: for
+        // the builtin the compiler cannot tell that the LDS-DMA copies in
+        // flight write other bytes, and waits for all of them before each
+        // read, which exposed the whole copy latency once per slice. These
+        // reads are waited for explicitly (frag_wait).
+        const uint32_t a0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p0));
+        i16x4 lo, hi;
+        asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(lo) : "v"(a0));
+        asm volatile("ds_read_b64_tr_b16 %0, %1 offset:2048" : "=v"(hi) : "v"(a0));   // K rows + 4
+#else
+        (void)p0;
+        i16x4 lo{}, hi{};
+#endif
         i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         return __builtin_bit_cast(V8, v);
     };
 
     V8 af[2][FM], bfr[2][FN];
+    // With an M-/N-major operand (transposing reads in inline asm, which the
+    // compiler does not track): every LDS read in flight has landed, and the
+    // fragments of buffer `buf` pass through the wait as operands, so no use
+    // of them is scheduled above it. Called at the top of each K step; it
+    // also retires every read of a stage before the barrier that frees it.
+    auto frag_wait = [&](auto bufc) {
+#if defined(__HIP_DEVICE_COMPILE__)
+        if constexpr (!(Cf::AK && Cf::BKM)) {
+            constexpr int buf = decltype(bufc)::value;
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            static_for<0, FM>([&](auto i) {
+                V8& x = af[buf][decltype(i)::value];   // (named first: an asm operand alone is not a capture)
+                asm volatile("" : "+v"(x));
+            });
+            static_for<0, FN>([&](auto j) {
+                V8& x = bfr[buf][decltype(j)::value];
+                asm volatile("" : "+v"(x));
+            });
+        }
+#endif
+    };
     auto read_step = [&](int stage, int s, int buf) {
         const char* sa = smem + stage * Cf::STAGE;
         const char* sb = sa + Cf::OP_BYTES;
@@ -349,10 +382,10 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
     constexpr int NMF = FM * FN, NRD = (Cf::AK ? FM : 2 * FM) + (Cf::BKM ? FN : 2 * FN);
     int stage = 0;
     auto slice_s = [&](auto has_next, auto refill, int t) {
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            const int cur = s & 1, nxt = cur ^ 1;
-            if (s + 1 < KS) {
+        static_for<0, KS>([&](auto sc) {
+            constexpr int s = decltype(sc)::value, cur = s & 1, nxt = cur ^ 1;
+            frag_wait(std::integral_constant<int, cur>{});
+            if constexpr (s + 1 < KS) {
                 read_step(stage, s + 1, nxt);
             } else if constexpr (decltype(has_next)::value) {
                 if constexpr (decltype(refill)::value)
@@ -390,7 +423,7 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
                     __builtin_amdgcn_sched_group_barrier(0x020, Cf::IPW - VPG * GROUPS, 0);
                 if (NMF > MPG * GROUPS) __builtin_amdgcn_sched_group_barrier(0x008, NMF - MPG * GROUPS, 0);
             }
-        }
+        });
         stage = stage + 1 == S ? 0 : stage + 1;
     };
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -416,6 +449,7 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
             constexpr bool reads = !last || decltype(has_next)::value;
             constexpr bool copies = last && decltype(refill)::value;
             constexpr int NR = reads ? FM + FN : 0, NC = copies ? Cf::IPW : 0, NQ = FM * FN;
+            frag_wait(std::integral_constant<int, cur>{});
             int rstage = stage, rs = s + 1;
             if constexpr (last && decltype(has_next)::value) {
                 if constexpr (decltype(refill)::value)
@@ -653,12 +687,10 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
         epilogue(std::false_type{});
 }
 
-// The instantiations the planner launches: K-major A and B run the
-// one-wave-per-SIMD kernel (4 waves of 128x128); when either operand needs
-// the transposing fragment reads, 8 waves of 64x128 (two per SIMD) with the
-// compiler's schedule, which measured faster there.
+// The instantiation the planner launches for the data-parallel tiles: one
+// wave per SIMD (4 waves of 128x128), for every operand major-ness.
 template <bool AK, bool BKM>
-using Chosen = std::conditional_t<AK && BKM, TCfg<2, 2, 64, 2, 16, AK, BKM>, TCfg<4, 2, 64, 2, 16, AK, BKM>>;
+using Chosen = TCfg<2, 2, 64, 2, 16, AK, BKM>;
 // The split-remainder launch always runs 8 waves: its fix-up adds the other
 // segments' fp32 partials in registers, and with 256 accumulators per lane
 // that step spills (measured 320 vs 91 us on 1792x1792x7040).
