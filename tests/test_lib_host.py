@@ -542,3 +542,16 @@ def test_fused_epilogue_argument_checks_before_the_device():
     st = L.lib().lt_gemm_run_ex(ctypes.byref(A), ctypes.byref(B), None, ctypes.byref(D), 1.0, 0.0, None,
                                 ctypes.byref(neg), None, 0, None)
     assert L.STATUS_NAMES[st] == "LT_ERR_INVALID_ARGUMENT"
+
+
+def test_plan_reports_the_wave_layout_of_the_data_parallel_launch():
+    """The 256x256 kernel's data-parallel launch runs 4 waves of 128x128 (one
+    per SIMD) for every operand major-ness: 8 x 8 MFMA blocks x 2 K steps per
+    wave per 64-deep K slice."""
+    for a, b in (("k", "k"), ("m", "k"), ("k", "n"), ("m", "n")):
+        st, i = _plan(*_gemm_descs(2048, 2048, 1024, a=a, b=b), kernel=L.LT_KERNEL_TILED)
+        assert st == "LT_OK" and i.kernel == L.LT_KERNEL_TILED, (a, b, st)
+        assert (i.waves, i.wave_m, i.wave_n) == (4, 128, 128), (a, b)
+        assert (i.tile_m, i.tile_n, i.tile_k, i.stages) == (256, 256, 64, 2)
+        assert i.mfma_per_wave_kstep == 8 * 8 * 2 and (i.mfma_m, i.mfma_n, i.mfma_k) == (16, 16, 32)
+        assert i.lds_bytes == 2 * 2 * 256 * 64 * 2
