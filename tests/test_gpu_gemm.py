@@ -97,6 +97,21 @@ def test_tiled_ragged_all_outputs(M, N, K, dtype, a_major, b_major, alpha, beta,
     assert plan["grid"] == tiles - plan["sk_tiles"] + plan["sk_workgroups"]
 
 
+@pytest.mark.parametrize("K", [64, 128, 192, 320])
+@pytest.mark.parametrize("a_major,b_major", [("row", "col"), ("col", "row"), ("row", "row"), ("col", "col")])
+def test_tiled_slice_counts_every_major(K, a_major, b_major):
+    """The 256x256 kernel at 1, 2, 3 and 5 K slices (no refill, the refill
+    loop entered or not, several refills) for every operand major-ness, on 4
+    tiles, every output checked: the issue order of copies, fragment reads and
+    MFMAs, and its explicit waits, differ between those loop shapes."""
+    M, N = 512, 512
+    A, B, C, D = _case(M, N, K, BF16, a_major, b_major, "row", 1.0, 0.5, seed=K + 7)
+    res, plan, _ = run_and_check(A, B, C, D, 1.0, 0.5, kernel="tiled", split_k=1, expect_kernel="tiled",
+                                 label=f"slices {K // 64} {a_major}/{b_major}")
+    _ok(res)
+    assert plan["waves"] == 4 and plan["grid"] == 4
+
+
 def test_tiled_ragged_large_auto():
     """A ragged shape large enough for the automatic choice to take the 256x256 kernel."""
     M, N, K = 1000, 1304, 1000
