@@ -285,8 +285,9 @@ typedef struct lt_gemm_options {
 typedef struct lt_gemm_plan_info {
     int32_t kernel;          /* lt_kernel */
     int32_t tile_m, tile_n, tile_k;
-    int32_t wave_m, wave_n;  /* tile of one wave */
-    int32_t waves;           /* waves per workgroup */
+    int32_t wave_m, wave_n;  /* tile of one wave (TILED: of the data-parallel launch) */
+    int32_t waves;           /* waves per workgroup (TILED: 4, one per SIMD, in the data-parallel
+                                launch; the split launch runs 8 waves of 64x128) */
     int32_t stages;          /* LDS pipeline depth */
     int32_t split_k;
     int32_t a_kmajor, b_kmajor, d_nmajor;
