@@ -47,7 +47,7 @@ def log(*a):
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     for f in ("gemm_kernels.hip", "gemm_tiled.hip", "gemm_kernels.hpp", "kernel_common.hpp",
-              "device_layout.hpp", "gemm.cpp"):
+              "device_layout.hpp", "tiled_config.hpp", "gemm.cpp"):
         h.update(open(os.path.join(ROOT, "layout_algebra_tiled_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 
@@ -117,6 +117,50 @@ class GpuSensors:
             return None
 
 
+class StreamHold:
+    """Holds the current stream for a while with a bounded spin kernel
+    (torch.cuda._sleep), so that the launches queued behind it run back to
+    back: HIP events around each launch then time the kernel, not the host's
+    marshalling between launches (which exceeds a short kernel's duration)."""
+
+    def __init__(self):
+        import torch
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        n = 1 << 22
+        torch.cuda._sleep(n // 16)   # first launch outside the calibration
+        torch.cuda.synchronize()
+        e0.record()
+        torch.cuda._sleep(n)
+        e1.record()
+        torch.cuda.synchronize()
+        self.cycles_per_ms = n / max(e0.elapsed_time(e1), 1e-3)
+
+    def hold(self, ms: float):
+        import torch
+        torch.cuda._sleep(int(self.cycles_per_ms * ms))
+
+
+_HOLD = None
+
+
+def queued_kernel_times(run, n: int):
+    """Per-launch kernel durations (s) of n launches run(i) queued behind a
+    stream hold long enough for the host to enqueue all of them."""
+    import torch
+    global _HOLD
+    if _HOLD is None:
+        _HOLD = StreamHold()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    torch.cuda.synchronize()
+    _HOLD.hold(2.0 + 0.2 * n)
+    for i in range(n):
+        ev[i][0].record()
+        run(i)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    return sorted(a.elapsed_time(b) / 1e3 for a, b in ev)
+
+
 class Workload:
     def __init__(self, cfg: int, n_b: int = 1):
         import torch
@@ -144,15 +188,27 @@ class Workload:
         return g.plan(self.A.store, self.Bs[0].store, self.D.store, self.C.store if self.C is not None else None,
                       self.c.beta, layouts=self.lay)
 
-    def run(self, i: int = 0, workspace=None):
+    def run(self, i: int = 0):
         from layout_algebra_tiled_amd import gemm as g
+        if not hasattr(self, "ws"):
+            import torch
+            need = self.plan()["workspace_bytes"]
+            self.ws = torch.empty(need, dtype=torch.uint8, device="cuda:0") if need else None
         g.gemm(self.A.store, self.Bs[i % len(self.Bs)].store, self.D.store,
                self.C.store if self.C is not None else None, self.c.alpha, self.c.beta, layouts=self.lay,
-               workspace=workspace)
+               workspace=self.ws)
+
+    def queued_kernel_time(self, steps: int):
+        """Mean kernel duration (s) of `steps` launches queued back to back
+        behind a stream hold (HIP events around each launch)."""
+        t = queued_kernel_times(self.run, steps)
+        self.queued_times = t
+        return sum(t) / len(t)
 
     def time(self, steps: int, warmup: int, warmup_s: float = 0.0, sample_clock: bool = False):
         """Wall time per step (barrier + synchronize around the timed steps)
-        and the average kernel duration from HIP events on the launch stream.
+        and the average kernel duration from HIP events on the launch stream,
+        recorded around each launch inside the timed region.
         Warm-up runs at least `warmup` steps and at least `warmup_s` seconds:
         under sustained MFMA load the GPU's clocks settle only after some
         tens of milliseconds, and the timed steps should see steady state."""
@@ -328,13 +384,8 @@ def layout_map_timing(reps: int = 20):
     out = torch.empty(n, dtype=torch.int64, device="cuda:0")
     g.layout_eval_device(L, out)
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-    for a, b in ev:
-        a.record()
-        g.layout_eval_device(L, out)
-        b.record()
-    torch.cuda.synchronize()
-    dev_s = sum(a.elapsed_time(b) for a, b in ev) / reps / 1e3
+    ts = queued_kernel_times(lambda i: g.layout_eval_device(L, out), reps)
+    dev_s = sum(ts) / reps
     same = out.cpu().tolist() == [L(x) for x in range(n)]
     return {"layout": str(L), "elements": n, "device_us": round(dev_s * 1e6, 2),
             "equals_host_library": bool(same)}
@@ -360,14 +411,10 @@ def split_remainder_timing(M: int, N: int, K: int, reps: int = 20):
         while time.perf_counter() < t_end:
             run()
             torch.cuda.synchronize()
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-        for a, b in ev:
-            a.record()
-            run()
-            b.record()
-        torch.cuda.synchronize()
-        k = sum(a.elapsed_time(b) for a, b in ev) / reps / 1e3
-        rec[label] = {"grid": p["grid"], "split_tiles": p["sk_tiles"], "segments": p["split_k"],
+        ts = queued_kernel_times(lambda i: run(), reps)
+        k = sum(ts) / reps
+        rec[label] = {"tile": [p["tile_m"], p["tile_n"]], "grid": p["grid"], "split_tiles": p["sk_tiles"],
+                      "segments": p["split_k"],
                       "kernel_us": round(k * 1e6, 1), "TFLOP/s": round(2 * M * N * K / k / 1e12, 1)}
     chk = sample_check(dA.view(), dB.view(), None, D, 1.0, 0.0, torch.bfloat16, sample_points(M, N, 500, seed=7))
     rec["parity"] = str(chk)
@@ -459,14 +506,17 @@ def main():
         for cfg, n_b in ((1, 1), (2, 1), (4, 1), (5, 4)):
             x = Workload(cfg, n_b=n_b)
             p = x.plan()
-            ws = None
-            if p["workspace_bytes"]:
-                ws = torch.empty(p["workspace_bytes"], dtype=torch.uint8, device="cuda:0")
-            x.run(0, ws)
-            xw, xk = x.time(max(10, args.steps // 2), 5, args.warmup_seconds / 2)
+            x.run(0)
+            n = max(10, args.steps // 2)
+            xw, _ = x.time(n, 5, args.warmup_seconds / 2)
+            # launches queued back to back: the kernel's own duration (the
+            # small workloads are host-bound at one Python call per step)
+            xk = x.queued_kernel_time(n)
             xc = x.check(128)
-            rec = {"kernel": p["kernel_name"], "ms_per_step": round(xw * 1e3, 4), "kernel_us": round(xk * 1e6, 2),
-                   "TFLOP/s": round(x.c.flops() / xw / 1e12, 2), "parity_ok": bool(xc.ok),
+            rec = {"kernel": p["kernel_name"], "tile": [p["tile_m"], p["tile_n"], p["tile_k"]], "grid": p["grid"],
+                   "ms_per_step": round(xw * 1e3, 4), "kernel_us": round(xk * 1e6, 2),
+                   "kernel_us_median": round(x.queued_times[len(x.queued_times) // 2] * 1e6, 2),
+                   "TFLOP/s": round(x.c.flops() / xk / 1e12, 2), "parity_ok": bool(xc.ok),
                    "worst_fraction": round(xc.worst_fraction, 4)}
             if cfg == 1:
                 rec["note"] = "launch-latency bound: 128 16x16 tiles, one wave each"

@@ -23,7 +23,10 @@ BUILD = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["layout.cpp", "gemm.cpp", "device.hip", "gemm_kernels.hip", "gemm_tiled.hip"]
+SOURCES = ["layout.cpp", "gemm.cpp", "device.hip", "gemm_kernels.hip"]
+# The tiled kernel is compiled once per (dtype, A K-major?, B K-major?): each
+# object holds one variant's kernels, and the objects build in parallel.
+TILED_VARIANTS = [(dt, ak, bk) for dt in (1, 2) for ak in (1, 0) for bk in (1, 0)]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", f"-I{INCLUDE}", f"-I{CSRC}",
           "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
@@ -31,9 +34,10 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", f"-I{INCLUDE}"
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *COMMON, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(job) -> str:
+    src, defines, stem = job
+    obj = os.path.join(BUILD, stem + ".o")
+    cmd = [HIPCC, *COMMON, *defines, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     msgs = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if noise not in l)
@@ -46,9 +50,12 @@ def _compile(src: str) -> str:
 
 def build(verbose: bool = True) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    workers = min(len(SOURCES), max(1, (os.cpu_count() or 4)))
+    jobs = [("gemm_tiled.hip", [f"-DLT_TILED_DT={dt}", f"-DLT_TILED_AK={ak}", f"-DLT_TILED_BK={bk}"],
+             f"gemm_tiled_{dt}{ak}{bk}") for dt, ak, bk in TILED_VARIANTS]
+    jobs += [(src, [], os.path.splitext(src)[0]) for src in SOURCES]
+    workers = min(len(jobs), max(1, min(16, os.cpu_count() or 4)))
     with cf.ThreadPoolExecutor(max_workers=workers) as ex:
-        objs = list(ex.map(_compile, SOURCES))
+        objs = list(ex.map(_compile, jobs))
     tmp = OUT + f".tmp{os.getpid()}"
     cmd = [HIPCC, "-shared", f"--offload-arch={ARCH}", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)

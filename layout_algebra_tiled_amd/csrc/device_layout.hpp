@@ -86,13 +86,19 @@ struct KTile {
     LT_HD static constexpr int at(int row, int chunk) { return swz(chunks(chunk + C * row)); }
 };
 
-struct MNTile {
-    static constexpr int C = 32;                     // 256 elements per K row
-    static constexpr Flat<2> chunks{{32, 64}, {1, 32}};
+// W chunks (8*W elements of M or N) per K row: 32 for a 256-wide block tile,
+// 16 for a 128-wide one. The XOR term is at most 14, so it stays inside a
+// row of either width.
+template <int W>
+struct MNTileW {
+    static_assert(W == 16 || W == 32, "K rows of 128 or 256 elements");
+    static constexpr int C = W;
+    static constexpr Flat<2> chunks{{W, 64}, {1, W}};
     LT_HD static constexpr int at(int krow, int chunk) {
-        return chunks(chunk + 32 * krow) ^ (4 * (krow & 3) + 2 * ((krow >> 3) & 1));
+        return chunks(chunk + W * krow) ^ (4 * (krow & 3) + 2 * ((krow >> 3) & 1));
     }
 };
+using MNTile = MNTileW<32>;
 
 // Thread-value layouts of one mode, as logical products of compact 1-D
 // layouts ("Layouts as Algebra", "The threads are a layout too"): with T

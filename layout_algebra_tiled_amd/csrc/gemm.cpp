@@ -110,6 +110,7 @@ struct Plan {
     int64_t dp_tiles = 0, sk_tiles = 0;
     int sk_splits = 1;
     int64_t sk_counter_bytes = 0;   // workspace: counters first, then partials
+    int tile_n = 256;               // tiled kernel: block tile 256 x tile_n
 };
 
 // Compute units of a gfx950 part (MI355X): the unit of wave quantisation.
@@ -180,7 +181,7 @@ lt_status make_plan(const lt_tensor* tA, const lt_tensor* tB, const lt_tensor* t
     const bool c_n = !beta_nonzero || p.C.e1 == 1 || p.C.s1 == 1;
 
     int kernel = opt ? opt->kernel : LT_KERNEL_AUTO;
-    const TiledShape ts = tiled_shape(p.a_k, p.b_k);
+    const TiledShape ts = tiled_shape(p.a_k, p.b_k, 256);
     // M-major A and N-major B stream through the same kernel (transposed
     // fragment reads); any stride-1 mode of A and B works.
     // The tiled kernel addresses a K slice as a uniform base plus a per-lane
@@ -243,68 +244,86 @@ lt_status make_plan(const lt_tensor* tA, const lt_tensor* tB, const lt_tensor* t
         }
         case LT_KERNEL_TILED: {
             if (!tiled_ok) return d_n && c_n ? LT_ERR_NOT_DIVISIBLE : LT_ERR_UNSUPPORTED;
-            if (opt && ((opt->tile_m && opt->tile_m != ts.bm) || (opt->tile_n && opt->tile_n != ts.bn)))
-                return LT_ERR_UNSUPPORTED;
-            in.tile_m = ts.bm;
-            in.tile_n = ts.bn;
-            in.tile_k = ts.bk;
-            in.wave_m = ts.wave_m;
-            in.wave_n = ts.wave_n;
-            in.waves = ts.waves;
-            in.stages = ts.stages;
-            in.lds_bytes = ts.lds_bytes;
-            if (in.lds_bytes > 160 * 1024) return LT_ERR_LDS_OVERFLOW;
-            {
-                // Wave quantisation ("CUTLASS, in depth", "Worked example:
-                // tile choice and wave quantisation"): ntiles whole tiles on
-                // kCUs compute units leave the last round part empty. The
-                // whole rounds stay data-parallel; the rem tiles of the last
-                // round can instead be split into S = kCUs / rem K segments
-                // (at most 8, at least 4 slices each), so that the last round
-                // fills the units too, at the price of the fp32 partials. In
-                // K-slice times: data-parallel takes ceil(ntiles/kCUs)*KT;
-                // split, the whole rounds, ceil(KT/S), and about 20 slices
-                // for a 256x256 partial written and read back. The split is
-                // taken when it saves a tenth. split_k = 1 turns it off;
-                // split_k > 1 forces S (on all tiles when they fill no whole
-                // round, else on the last round's).
-                const int64_t ntiles = tm_ * tn_;
-                const int64_t KTt = (p.K + ts.bk - 1) / ts.bk;
-                int64_t rem = ntiles % kCUs;
-                int64_t S = 1;
-                if (split == 0) {
-                    if (rem != 0) {
-                        S = std::min<int64_t>({kCUs / rem, 8, KTt / 4});
-                        if (S >= 2) {
-                            const int64_t t_dp = (ntiles + kCUs - 1) / kCUs * KTt;
-                            const int64_t t_split = ntiles / kCUs * KTt + (KTt + S - 1) / S + 20;
-                            if (!(10 * t_split < 9 * t_dp)) S = 1;
-                        }
+            const int want_n = opt ? opt->tile_n : 0;
+            if (opt && opt->tile_m && opt->tile_m != 256) return LT_ERR_UNSUPPORTED;
+            if (want_n != 0 && want_n != 256 && want_n != 128) return LT_ERR_UNSUPPORTED;
+            if (want_n == 128 && split > 1) return LT_ERR_UNSUPPORTED;   // 256x128 tiles are never split
+            // Block tile and wave quantisation ("CUTLASS, in depth", "Worked
+            // example: tile choice and wave quantisation"): ntiles whole
+            // tiles on kCUs compute units leave the last round part empty.
+            // Costs in K-slice times of a 256x128 tile (a 256x256 slice
+            // counts two):
+            //   256x256, data-parallel: ceil(n256/kCUs) * KT * 2;
+            //   256x256 with the last round's rem tiles split into S K
+            //     segments (S = kCUs/rem, at most 8, at least 4 slices
+            //     each): whole rounds, ceil(KT/S), and about 20 slices for a
+            //     256x256 fp32 partial written and read back, all times 2;
+            //     taken when it saves a tenth;
+            //   256x128: ceil(n128/kCUs) * KT * 23/20 (a 256x128 tile reads
+            //     a sixth more LDS bytes per flop and has half the work to
+            //     hide its prologue and epilogue behind).
+            // split_k = 1 turns the split off; split_k > 1 forces S (on all
+            // 256x256 tiles when they fill no whole round, else on the last
+            // round's).
+            const int64_t KTt = (p.K + ts.bk - 1) / ts.bk;
+            const int64_t n256 = tm_ * tn_;
+            int64_t rem = n256 % kCUs;
+            int64_t S = 1;
+            int64_t c256 = (n256 + kCUs - 1) / kCUs * KTt * 2;
+            if (split == 0) {
+                if (rem != 0) {
+                    S = std::min<int64_t>({kCUs / rem, 8, KTt / 4});
+                    if (S >= 2) {
+                        const int64_t t_split = (n256 / kCUs * KTt + (KTt + S - 1) / S + 20) * 2;
+                        if (10 * t_split < 9 * c256)
+                            c256 = t_split;
+                        else
+                            S = 1;
                     }
-                } else if (split > 1) {
-                    S = std::min<int64_t>(split, KTt);
-                    if (rem == 0) rem = std::min<int64_t>(ntiles, kCUs);
                 }
-                if (S < 2) {
-                    S = 1;
-                    rem = 0;
-                }
-                p.dp_tiles = ntiles - rem;
-                p.sk_tiles = rem;
-                p.sk_splits = static_cast<int>(S);
-                p.sk_counter_bytes = (rem * 4 + 255) / 256 * 256;
-                in.split_k = p.sk_splits;
-                in.grid = p.dp_tiles + rem * S;
-                in.sk_tiles = rem;
-                in.sk_workgroups = static_cast<int32_t>(rem * S);
-                in.workspace_bytes = rem > 0 ? p.sk_counter_bytes + rem * S * (int64_t)ts.bm * ts.bn * 4 : 0;
+            } else if (split > 1) {
+                S = std::min<int64_t>(split, KTt);
+                if (rem == 0) rem = std::min<int64_t>(n256, kCUs);
             }
+            if (S < 2) {
+                S = 1;
+                rem = 0;
+            }
+            const int64_t n128 = tm_ * ((p.N + 127) / 128);
+            const int64_t c128x20 = (n128 + kCUs - 1) / kCUs * KTt * 23;
+            int tile_n = 256;
+            if (want_n == 128 || (want_n == 0 && split <= 1 && c128x20 < c256 * 20)) tile_n = 128;
+            if (tile_n == 128) {
+                S = 1;
+                rem = 0;
+            }
+            const TiledShape tsc = tiled_shape(p.a_k, p.b_k, tile_n);
+            in.tile_m = tsc.bm;
+            in.tile_n = tsc.bn;
+            in.tile_k = tsc.bk;
+            in.wave_m = tsc.wave_m;
+            in.wave_n = tsc.wave_n;
+            in.waves = tsc.waves;
+            in.stages = tsc.stages;
+            in.lds_bytes = tsc.lds_bytes;
+            if (in.lds_bytes > 160 * 1024) return LT_ERR_LDS_OVERFLOW;
+            const int64_t ntiles = tile_n == 128 ? n128 : n256;
+            p.tile_n = tile_n;
+            p.dp_tiles = ntiles - rem;
+            p.sk_tiles = rem;
+            p.sk_splits = static_cast<int>(S);
+            p.sk_counter_bytes = (rem * 4 + 255) / 256 * 256;
+            in.split_k = p.sk_splits;
+            in.grid = p.dp_tiles + rem * S;
+            in.sk_tiles = rem;
+            in.sk_workgroups = static_cast<int32_t>(rem * S);
+            in.workspace_bytes = rem > 0 ? p.sk_counter_bytes + rem * S * (int64_t)ts.bm * ts.bn * 4 : 0;
             // (wave_m/mf) * (wave_n/mf) * (bk/mfma_k): the analogue of counting mma
             // per warp per K slice ("CUTLASS and CuTe layouts", "The arch tag
             // is not one instruction")
-            in.mfma_per_wave_kstep = ts.mfma_per_wave_slice;
-            in.mfma_m = in.mfma_n = ts.mfma_mn;
-            in.mfma_k = ts.mfma_k;
+            in.mfma_per_wave_kstep = tsc.mfma_per_wave_slice;
+            in.mfma_m = in.mfma_n = tsc.mfma_mn;
+            in.mfma_k = tsc.mfma_k;
             break;
         }
         case LT_KERNEL_SKINNY: {
@@ -338,6 +357,44 @@ lt_status make_plan(const lt_tensor* tA, const lt_tensor* tB, const lt_tensor* t
     return LT_OK;
 }
 
+// The last plan made on this thread, keyed by the bytes of its arguments: a
+// workspace query followed by the run of the same problem (or a loop of runs)
+// plans once. The plan depends on nothing but these arguments.
+struct PlanKey {
+    lt_tensor t[4];
+    lt_gemm_options opt;
+    int32_t has_c, has_opt, bnz;
+};
+
+lt_status plan_cached(const lt_tensor* tA, const lt_tensor* tB, const lt_tensor* tC, const lt_tensor* tD,
+                      int beta_nonzero, const lt_gemm_options* opt, Plan* plan) {
+    thread_local PlanKey last_key;
+    thread_local Plan last_plan;
+    thread_local bool have_last = false;
+    if (!tA || !tB || !tD) return LT_ERR_INVALID_ARGUMENT;
+    PlanKey k;
+    std::memset(&k, 0, sizeof(k));
+    std::memcpy(&k.t[0], tA, sizeof(lt_tensor));
+    std::memcpy(&k.t[1], tB, sizeof(lt_tensor));
+    if (tC && beta_nonzero) std::memcpy(&k.t[2], tC, sizeof(lt_tensor));
+    std::memcpy(&k.t[3], tD, sizeof(lt_tensor));
+    if (opt) std::memcpy(&k.opt, opt, sizeof(lt_gemm_options));
+    k.has_c = tC && beta_nonzero ? 1 : 0;
+    k.has_opt = opt ? 1 : 0;
+    k.bnz = beta_nonzero ? 1 : 0;
+    if (have_last && std::memcmp(&k, &last_key, sizeof(k)) == 0) {
+        *plan = last_plan;
+        return LT_OK;
+    }
+    const lt_status st = make_plan(tA, tB, tC, tD, beta_nonzero, opt, plan);
+    if (st == LT_OK) {
+        last_key = k;
+        last_plan = *plan;
+        have_last = true;
+    }
+    return st;
+}
+
 }  // namespace
 }  // namespace lt
 
@@ -362,7 +419,7 @@ lt_status lt_gemm_workspace_size(const lt_tensor* A, const lt_tensor* B, const l
                                  int32_t beta_nonzero, const lt_gemm_options* opt, size_t* bytes) {
     if (!bytes) return LT_ERR_INVALID_ARGUMENT;
     lt::Plan p;
-    lt_status st = lt::make_plan(A, B, C, D, beta_nonzero, opt, &p);
+    lt_status st = lt::plan_cached(A, B, C, D, beta_nonzero, opt, &p);
     if (st != LT_OK) return st;
     *bytes = static_cast<size_t>(p.info.workspace_bytes);
     return LT_OK;
@@ -381,7 +438,7 @@ lt_status lt_gemm_run_ex(const lt_tensor* A, const lt_tensor* B, const lt_tensor
     const int bnz = beta != 0.0f;
     if (epi && (epi->activation < LT_ACT_NONE || epi->activation > LT_ACT_GELU || epi->bias_stride < 0))
         return LT_ERR_INVALID_ARGUMENT;
-    lt_status st = lt::make_plan(A, B, C, D, bnz, opt, &p);
+    lt_status st = lt::plan_cached(A, B, C, D, bnz, opt, &p);
     if (st != LT_OK) return st;
     if ((size_t)p.info.workspace_bytes > workspace_bytes || (p.info.workspace_bytes > 0 && !workspace) ||
         (p.info.workspace_bytes > 0 && reinterpret_cast<uintptr_t>(workspace) % 256 != 0))
@@ -454,7 +511,7 @@ lt_status lt_gemm_run_ex(const lt_tensor* A, const lt_tensor* B, const lt_tensor
             // The tile grid: mode 1 of zipped_divide(D', (256,256)), where D'
             // is D's layout with M and N rounded up to whole tiles (the
             // outputs past (M, N) are predicated off in the epilogue).
-            const lt::TiledShape ts = lt::tiled_shape(p.a_k, p.b_k);
+            const lt::TiledShape ts = lt::tiled_shape(p.a_k, p.b_k, p.tile_n);
             const int64_t mp = (p.M + ts.bm - 1) / ts.bm * ts.bm, np = (p.N + ts.bn - 1) / ts.bn * ts.bn;
             lt::Tree dl = lt::Tree::tuple({lt::Tree::leaf(mp, p.D.s0), lt::Tree::leaf(np, 1)});
             const int64_t tiler[2] = {ts.bm, ts.bn};
@@ -479,7 +536,7 @@ lt_status lt_gemm_run_ex(const lt_tensor* A, const lt_tensor* B, const lt_tensor
                 if ((err = lt::launch_zero_i32(a.counters, (int)p.sk_tiles, stream)) != 0) return LT_ERR_HIP;
             }
             a.epi = ea;
-            err = lt::launch_tiled(dt, p.a_k, p.b_k, a, stream);
+            err = lt::launch_tiled(dt, p.a_k, p.b_k, p.tile_n, a, stream);
             break;
         }
         case LT_KERNEL_SKINNY: {

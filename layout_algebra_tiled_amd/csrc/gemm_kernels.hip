@@ -9,6 +9,7 @@
 #include "device_layout.hpp"
 #include "gemm_kernels.hpp"
 #include "kernel_common.hpp"
+#include "tiled_config.hpp"
 
 namespace lt {
 namespace {
@@ -292,6 +293,34 @@ int launch_zero_i32(int* p, int n, void* stream) {
     hipLaunchKernelGGL(zero_i32, dim3((n + 255) / 256 < 64 ? (n + 255) / 256 : 64), dim3(256), 0,
                        static_cast<hipStream_t>(stream), p, n);
     return static_cast<int>(hipGetLastError());
+}
+
+template <class Cf>
+TiledShape shape_of() {
+    return TiledShape{Cf::BM, Cf::BN, Cf::BK, Cf::TWM, Cf::TWN, Cf::NW, Cf::S, Cf::LDS, Cf::FM * Cf::FN * Cf::KS,
+                      Cf::MF, Cf::MFMA::KSTEP};
+}
+
+template <bool AK, bool BKM>
+TiledShape shape_for(int tile_n) {
+    return tile_n == 128 ? shape_of<Dp128<AK, BKM>>() : shape_of<Dp256<AK, BKM>>();
+}
+
+TiledShape tiled_shape(bool a_kmajor, bool b_kmajor, int tile_n) {
+    if (a_kmajor && b_kmajor) return shape_for<true, true>(tile_n);
+    if (a_kmajor) return shape_for<true, false>(tile_n);
+    if (b_kmajor) return shape_for<false, true>(tile_n);
+    return shape_for<false, false>(tile_n);
+}
+
+int launch_tiled(int dtype, bool a_kmajor, bool b_kmajor, int tile_n, const TiledArgs& a, void* stream) {
+    static_assert(LT_F16 == 1 && LT_BF16 == 2, "variant names carry the dtype code");
+    if (dtype == LT_F16) {
+        if (a_kmajor) return b_kmajor ? launch_tiled_11_1(a, tile_n, stream) : launch_tiled_11_0(a, tile_n, stream);
+        return b_kmajor ? launch_tiled_10_1(a, tile_n, stream) : launch_tiled_10_0(a, tile_n, stream);
+    }
+    if (a_kmajor) return b_kmajor ? launch_tiled_21_1(a, tile_n, stream) : launch_tiled_21_0(a, tile_n, stream);
+    return b_kmajor ? launch_tiled_20_1(a, tile_n, stream) : launch_tiled_20_0(a, tile_n, stream);
 }
 
 int launch_skinny(int dtype, const SkinnyArgs& a, void* stream) {

@@ -1,17 +1,17 @@
-// Block-tiled GEMM for gfx950: D = alpha * A*B + beta * C with a 256x256 block
-// tile, fp16/bf16 operands, fp32 accumulation in MFMAs (16x16x32 by default).
-// M, N and K need not be multiples of the tile: edge tiles clamp their copy
-// rows and store only the outputs inside (M, N); a partial K slice is zero-
-// filled in LDS.
+// Block-tiled GEMM for gfx950: D = alpha * A*B + beta * C with a 256x256 or
+// 256x128 block tile, fp16/bf16 operands, fp32 accumulation in 16x16x32
+// MFMAs. M, N and K need not be multiples of the tile: edge tiles clamp their
+// copy rows and store only the outputs inside (M, N); a partial K slice is
+// zero-filled in LDS.
 //
 // Structure (the tiled GEMM of "Layouts as Algebra: CUTLASS & CuTe", "The
 // kernel, in three lines", redesigned for CDNA4):
-//   - local_tile: workgroup -> one 256x256 tile of D (XCD-aware raster order);
+//   - local_tile: workgroup -> one block tile of D (XCD-aware raster order);
 //   - the K loop streams BK-deep slices of the A and B tiles through an
 //     S-stage LDS ring filled by direct global-to-LDS 16-byte loads
 //     (global_load_lds_dwordx4; the copy's thread-value layout puts lane l's
 //     16 bytes at stored chunk l, and the lane fetches the logical chunk the
-//     swizzle stores there);
+//     swizzle stores there; the maps are in tiled_config.hpp);
 //   - local_partition: each wave owns a TWM x TWN sub-tile and reads its MFMA
 //     fragments from LDS one K step ahead of the MFMAs that use them
 //     (ds_read_b128 for K-major operands, the transposing ds_read_b64_tr_b16
@@ -19,39 +19,19 @@
 //   - epilogue alpha*acc + beta*C, rounded once, 8-byte stores.
 // One workgroup barrier per K slice: it publishes slice t+1 and frees slice
 // t's stage, into which slice t+S is loaded at once.
+//
+// This file is compiled once per (dtype, A major-ness, B major-ness), chosen
+// by LT_TILED_DT / LT_TILED_AK / LT_TILED_BK, each object holding that
+// variant's kernels; the dispatch is in gemm_kernels.hip.
 
 #include <type_traits>
 
-#include "device_layout.hpp"
 #include "gemm_kernels.hpp"
 #include "kernel_common.hpp"
+#include "tiled_config.hpp"
 
 namespace lt {
 namespace {
-
-template <int NWM_, int NWN_, int BK_, int S_, int MF_, bool AK_, bool BK_MAJ_>
-struct TCfg {
-    static constexpr int BM = 256, BN = 256, BK = BK_, S = S_;
-    static constexpr int NWM = NWM_, NWN = NWN_, NW = NWM * NWN, NT = 64 * NW;
-    static constexpr int TWM = BM / NWM, TWN = BN / NWN;      // wave tile
-    using MFMA = dev::Mfma<MF_>;                              // MF x MF outputs per instruction
-    static constexpr int MF = MF_;
-    static constexpr int FM = TWM / MF, FN = TWN / MF;        // MFMA blocks per wave
-    static constexpr int KS = BK / MFMA::KSTEP;               // MFMA K steps per slice
-    static constexpr bool AK = AK_, BKM = BK_MAJ_;            // K-major operands?
-    // One wave per SIMD (4 waves of 128x128): 256 accumulators per lane, held
-    // in AGPRs by MFMAs written as inline asm, in an issue order fixed here
-    // rather than by the compiler's scheduler.
-    static constexpr bool EXPLICIT = NW == 4 && MF_ == 16;
-    static constexpr int OP_BYTES = 256 * BK * 2;             // one operand slice
-    static constexpr int STAGE = 2 * OP_BYTES;
-    static constexpr int LDS = S * STAGE;
-    static constexpr int OPI = OP_BYTES / 1024 / NW;          // copy instructions per wave per operand
-    static constexpr int IPW = 2 * OPI;                       // ... per slice
-    static_assert(OP_BYTES % (1024 * NW) == 0, "copy must split evenly over waves");
-    static_assert(KS % 2 == 0, "fragment double buffer assumes an even K-step count");
-    static_assert(IPW * (S - 1) < 64, "vmcnt counts at most 63 outstanding loads");
-};
 
 // Linear tile index -> tile coordinates: raster down group_m tile rows
 // before moving right, so tiles in flight together on one XCD share A rows
@@ -95,11 +75,14 @@ __device__ __forceinline__ void work_of(int wg, const TiledArgs& p, int KT, int*
 // would not be instantiable in the host compilation pass.)
 #define LT_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (0x7 << 4) | (0xf << 8) | (((n) >> 4) << 14))
 
-// Compile-time loop: f(integral_constant<int, I>) for I in [B, E).
+template <int I>
+using ic = std::integral_constant<int, I>;
+
+// Compile-time loop: f(ic<I>) for I in [B, E).
 template <int B, int E, class F>
 __host__ __device__ __forceinline__ void static_for(F&& f) {
     if constexpr (B < E) {
-        f(std::integral_constant<int, B>{});
+        f(ic<B>{});
         static_for<B + 1, E>(f);
     }
 }
@@ -109,60 +92,93 @@ __host__ __device__ __forceinline__ void static_for(F&& f) {
 // accumulator array never needs a memory home.
 template <int FM, int FN, class F>
 __host__ __device__ __forceinline__ void for_blocks(F&& f) {
-    static_for<0, FM * FN>([&](auto ij) {
-        f(std::integral_constant<int, decltype(ij)::value / FN>{}, std::integral_constant<int, decltype(ij)::value % FN>{});
-    });
+    static_for<0, FM * FN>([&](auto ij) { f(ic<decltype(ij)::value / FN>{}, ic<decltype(ij)::value % FN>{}); });
 }
 
-// One operand (A rows = M, or B rows = N) of the block tile.
-template <class Cf, bool KMAJ>
-struct Operand {
-    // Byte offset of the source of copy instruction i (of this wave) for
-    // the K slice that starts at k = 0, relative to the operand's base; a K
-    // slice adds kslice_bytes. K-major: element (row, k) at row*ld + k;
-    // M/N-major: at k*ld + row. Rows past the operand's extent `rows` (a
-    // ragged edge tile) are clamped to its last row (last 8-element chunk):
-    // valid memory whose products land only in outputs that are not stored.
-    // (__host__ __device__: it is called from lambdas inside the kernel, which
-    // the compiler treats as host-device.)
-    static __host__ __device__ __forceinline__ uint32_t offset(int64_t ld, int row0, int rows, int wave, int lane,
-                                                               int i) {
-        const int q = dev::kCopyTV(lane + 64 * (wave * Cf::OPI + i));   // stored chunk
-        if constexpr (KMAJ) {
-            using T = dev::KTile<Cf::BK>;
-            const int row = q / T::C;
-            const int lchunk = dev::KTile<Cf::BK>::at(row, q % T::C) - T::C * row;   // involution
-            const int r = min(row0 + row, rows - 1);
-            return (uint32_t)(((int64_t)r * ld + 8 * lchunk) * 2);
-        } else {
-            const int krow = q / 32;
-            const int lchunk = dev::MNTile::at(krow, q % 32) - 32 * krow;
-            const int c = min(row0 + 8 * lchunk, rows - 8);
-            return (uint32_t)(((int64_t)krow * ld + c) * 2);
-        }
+// Issue slots of the one-wave-per-SIMD schedule, over the NQ MFMAs of a K
+// step: copy c of NC follows MFMA (2c+1)*NQ/(2*NC) (spread over the whole
+// step), fragment read r of NR follows MFMA r*(3/4)*NQ/NR (spread over the
+// first three quarters, so the last read has a quarter of the step to land).
+// -1: nothing after MFMA q.
+constexpr int copy_after(int q, int nc, int nq) {
+    for (int c = 0; c < nc; ++c)
+        if ((2 * c + 1) * nq / (2 * nc) == q) return c;
+    return -1;
+}
+constexpr int read_after(int q, int nr, int nq) {
+    for (int r = 0; r < nr; ++r)
+        if (r * nq * 3 / 4 / nr == q) return r;
+    return -1;
+}
+
+// One MFMA operand fragment (8 16-bit values per lane). From a K-major LDS
+// tile it is one 16-byte read. From an M/N-major tile it is two transposing
+// 8-byte reads written as inline asm, which the compiler does not track: the
+// two halves stay separate registers until the explicit wait has retired the
+// reads (pin() passes each through an empty asm after that wait), and are
+// joined into the MFMA operand only when the MFMA is issued, so no copy of a
+// destination register can be placed before its data has landed.
+template <class V8, bool KMAJ>
+struct Frag;
+template <class V8>
+struct Frag<V8, true> {
+    V8 v;
+    __device__ __forceinline__ V8 get() const { return v; }
+    __device__ __forceinline__ void pin() {}
+};
+template <class V8>
+struct Frag<V8, false> {
+    i16x4 lo, hi;
+    __device__ __forceinline__ V8 get() const {
+        return __builtin_bit_cast(V8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     }
-    // K offset, within its slice, of the chunk copy instruction i of this
-    // lane fetches (K-major: the chunk's first K; M/N-major: its K row).
-    static __host__ __device__ __forceinline__ int kpos(int wave, int lane, int i) {
-        const int q = dev::kCopyTV(lane + 64 * (wave * Cf::OPI + i));
-        if constexpr (KMAJ) {
-            using T = dev::KTile<Cf::BK>;
-            const int row = q / T::C;
-            return 8 * (dev::KTile<Cf::BK>::at(row, q % T::C) - T::C * row);
-        } else {
-            return q / 32;
-        }
-    }
-    static __host__ __device__ __forceinline__ int64_t kslice_bytes(int64_t ld) {
-        return KMAJ ? (int64_t)Cf::BK * 2 : (int64_t)Cf::BK * ld * 2;
+    __device__ __forceinline__ void pin() {
+#if defined(__HIP_DEVICE_COMPILE__)
+        asm volatile("" : "+v"(lo));
+        asm volatile("" : "+v"(hi));
+#endif
     }
 };
 
+// The two transposing reads of an M/N-major fragment: K rows 4q..4q+3 of
+// the lane's group come from `p0` (q = 0) and four K rows further (q = 1).
+template <class V8, int KROW_BYTES>
+__device__ __forceinline__ Frag<V8, false> read_tr(const LDS_AS char* p0) {
+    Frag<V8, false> f;
+#if defined(__HIP_DEVICE_COMPILE__)
+    // Inline asm rather than the compiler's transposing-read builtin: for
+    // the builtin the compiler cannot tell that the LDS-DMA copies in flight
+    // write other bytes, and waits for all of them before each read, which
+    // exposed the whole copy latency once per slice.
+    const uint32_t a0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p0));
+    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(f.lo) : "v"(a0));
+    if constexpr (KROW_BYTES == 512)
+        asm volatile("ds_read_b64_tr_b16 %0, %1 offset:2048" : "=v"(f.hi) : "v"(a0));
+    else
+        asm volatile("ds_read_b64_tr_b16 %0, %1 offset:1024" : "=v"(f.hi) : "v"(a0));
+#else
+    (void)p0;
+    f.lo = i16x4{};
+    f.hi = i16x4{};
+#endif
+    return f;
+}
+
+}  // namespace
+
+// The kernel's body is compiled in the device pass only: the host pass needs
+// just the launch stub (and with the body in view it silently emits no stub
+// for a kernel whose generic lambdas call the direct-to-LDS builtin).
 template <int DT, class Cf, bool SPLIT>
 __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
+#if defined(__HIP_DEVICE_COMPILE__)
     extern __shared__ __attribute__((aligned(1024))) char smem[];
     using V8 = typename Tr<DT>::V8;
     constexpr int BK = Cf::BK, S = Cf::S, KS = Cf::KS, FM = Cf::FM, FN = Cf::FN;
+    using OA = Operand<Cf, Cf::AK, Cf::BM>;
+    using OB = Operand<Cf, Cf::BKM, Cf::BN>;
+    using FA = Frag<V8, Cf::AK>;
+    using FB = Frag<V8, Cf::BKM>;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     // K slices: KT = ceil(K / BK). When BK does not divide K, the K range is
     // shifted to start at kbase = K - KT*BK < 0, so that only slice 0 is
@@ -175,7 +191,7 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
     const int NS = kt1 - kt0;   // K slices this workgroup runs (>= 1)
     int tm, tn;
     tile_coords(lin, p, &tm, &tn);
-    const int m0 = tm * 256, n0 = tn * 256;
+    const int m0 = tm * Cf::BM, n0 = tn * Cf::BN;
 
     // ---- copy: S-stage ring, stage s at s*STAGE (A slice, then B slice).
     // Up to four copy instructions of one operand write LDS through the same
@@ -183,76 +199,56 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
     // which the hardware adds to both the global and the LDS address; the
     // global source is a uniform slice base plus a per-lane 32-bit offset,
     // minus that same instruction offset.
-    uint32_t aoffg[Cf::OPI], boffg[Cf::OPI];
+    uint32_t aoffg[OA::OPI], boffg[OB::OPI];
 #pragma unroll
-    for (int i = 0; i < Cf::OPI; ++i) {
-        aoffg[i] = Operand<Cf, Cf::AK>::offset(p.lda, m0, p.M, wave, lane, i);
-        boffg[i] = Operand<Cf, Cf::BKM>::offset(p.ldb, n0, p.N, wave, lane, i);
-    }
-    const int64_t a_ks = Operand<Cf, Cf::AK>::kslice_bytes(p.lda);
-    const int64_t b_ks = Operand<Cf, Cf::BKM>::kslice_bytes(p.ldb);
+    for (int i = 0; i < OA::OPI; ++i) aoffg[i] = OA::offset(p.lda, m0, p.M, wave, lane, i);
+#pragma unroll
+    for (int i = 0; i < OB::OPI; ++i) boffg[i] = OB::offset(p.ldb, n0, p.N, wave, lane, i);
+    const int64_t a_ks = OA::kslice_bytes(p.lda);
+    const int64_t b_ks = OB::kslice_bytes(p.ldb);
     // slice 0 sources: the operands' bases moved by kbase (the host does
     // that, so the slice address stays a kernel argument plus a multiple of
     // the slice stride); lanes whose chunk lies below K = 0 never load
     const char* a_k0 = reinterpret_cast<const char*>(p.A0);
     const char* b_k0 = reinterpret_cast<const char*>(p.B0);
-    auto issue = [&](int stage, int kt) {
-        char* sa = smem + stage * Cf::STAGE + wave * Cf::OPI * 1024;
-        char* sb = sa + Cf::OP_BYTES;
-        const char* ga = a_k0 + (kt0 + kt) * a_ks;
-        const char* gb = b_k0 + (kt0 + kt) * b_ks;
-        // (groups of four: the instruction offset is at most 4095 bytes)
-        static_for<0, Cf::OPI>([&](auto ic) {
-            constexpr int i = decltype(ic)::value, g = i / 4, o = (i % 4) * 1024;
-            const void* src = (ga - o) + aoffg[i];
-            __builtin_amdgcn_global_load_lds(src, (LDS_AS void*)(sa + g * 4096), 16, o, 0);
-        });
-        static_for<0, Cf::OPI>([&](auto ic) {
-            constexpr int i = decltype(ic)::value, g = i / 4, o = (i % 4) * 1024;
-            const void* src = (gb - o) + boffg[i];
-            __builtin_amdgcn_global_load_lds(src, (LDS_AS void*)(sb + g * 4096), 16, o, 0);
-        });
-    };
+    auto a_lds = [&](int stage) { return smem + stage * Cf::STAGE + wave * OA::OPI * 1024; };
+    auto b_lds = [&](int stage) { return smem + stage * Cf::STAGE + Cf::A_BYTES + wave * OB::OPI * 1024; };
 
     // Copy instruction c (< IPW) of slice kt into `stage`: A's OPI, then B's.
+    // (groups of four: the instruction offset is at most 4095 bytes)
     auto issue_one = [&](int stage, int kt, auto cc) {
         constexpr int c = decltype(cc)::value;
-        char* sa = smem + stage * Cf::STAGE + wave * Cf::OPI * 1024;
-        if constexpr (c < Cf::OPI) {
+        if constexpr (c < OA::OPI) {
             constexpr int i = c, g = i / 4, o = (i % 4) * 1024;
             const char* ga = a_k0 + (kt0 + kt) * a_ks;
-            __builtin_amdgcn_global_load_lds((ga - o) + aoffg[i], (LDS_AS void*)(sa + g * 4096), 16, o, 0);
+            __builtin_amdgcn_global_load_lds((ga - o) + aoffg[i], (LDS_AS void*)(a_lds(stage) + g * 4096), 16, o, 0);
         } else {
-            constexpr int i = c - Cf::OPI, g = i / 4, o = (i % 4) * 1024;
+            constexpr int i = c - OA::OPI, g = i / 4, o = (i % 4) * 1024;
             const char* gb = b_k0 + (kt0 + kt) * b_ks;
-            __builtin_amdgcn_global_load_lds((gb - o) + boffg[i], (LDS_AS void*)(sa + Cf::OP_BYTES + g * 4096), 16,
-                                             o, 0);
+            __builtin_amdgcn_global_load_lds((gb - o) + boffg[i], (LDS_AS void*)(b_lds(stage) + g * 4096), 16, o, 0);
         }
     };
+    auto issue = [&](int stage, int kt) { static_for<0, Cf::IPW>([&](auto cc) { issue_one(stage, kt, cc); }); };
 
     // Slice 0 when it is partial: a lane whose chunk lies below K = 0 writes
     // zeros where the copy would have put it (the copy's lane-linear LDS
     // position) instead of loading.
     auto issue_first_partial = [&]() {
-        char* sa = smem + wave * Cf::OPI * 1024;
-        char* sb = sa + Cf::OP_BYTES;
-        static_for<0, Cf::OPI>([&](auto ic) {
-            constexpr int i = decltype(ic)::value, g = i / 4, o = (i % 4) * 1024;
-            if (kbase + Operand<Cf, Cf::AK>::kpos(wave, lane, i) >= 0) {
-                const void* src = (a_k0 - o) + aoffg[i];
-                __builtin_amdgcn_global_load_lds(src, (LDS_AS void*)(sa + g * 4096), 16, o, 0);
-            } else {
-                *(LDS_AS u32x4*)(sa + g * 4096 + o + 16 * lane) = u32x4{0u, 0u, 0u, 0u};
-            }
+        static_for<0, OA::OPI>([&](auto ic_) {
+            constexpr int i = decltype(ic_)::value, g = i / 4, o = (i % 4) * 1024;
+            char* d = a_lds(0) + g * 4096;
+            if (kbase + OA::kpos(wave, lane, i) >= 0)
+                __builtin_amdgcn_global_load_lds((a_k0 - o) + aoffg[i], (LDS_AS void*)d, 16, o, 0);
+            else
+                *(LDS_AS u32x4*)(d + o + 16 * lane) = u32x4{0u, 0u, 0u, 0u};
         });
-        static_for<0, Cf::OPI>([&](auto ic) {
-            constexpr int i = decltype(ic)::value, g = i / 4, o = (i % 4) * 1024;
-            if (kbase + Operand<Cf, Cf::BKM>::kpos(wave, lane, i) >= 0) {
-                const void* src = (b_k0 - o) + boffg[i];
-                __builtin_amdgcn_global_load_lds(src, (LDS_AS void*)(sb + g * 4096), 16, o, 0);
-            } else {
-                *(LDS_AS u32x4*)(sb + g * 4096 + o + 16 * lane) = u32x4{0u, 0u, 0u, 0u};
-            }
+        static_for<0, OB::OPI>([&](auto ic_) {
+            constexpr int i = decltype(ic_)::value, g = i / 4, o = (i % 4) * 1024;
+            char* d = b_lds(0) + g * 4096;
+            if (kbase + OB::kpos(wave, lane, i) >= 0)
+                __builtin_amdgcn_global_load_lds((b_k0 - o) + boffg[i], (LDS_AS void*)d, 16, o, 0);
+            else
+                *(LDS_AS u32x4*)(d + o + 16 * lane) = u32x4{0u, 0u, 0u, 0u};
         });
     };
 
@@ -269,7 +265,7 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
     } else {
 #pragma unroll
         for (int b = 0; b < FM; ++b)
-            aoff[b] = 16 * dev::MNTile::at(Mf::tr_krow(lane, 0), (arow0 + Cf::MF * b + Mf::tr_col(lane)) >> 3) +
+            aoff[b] = 16 * OA::MT::at(Mf::tr_krow(lane, 0), (arow0 + Cf::MF * b + Mf::tr_col(lane)) >> 3) +
                       2 * (Mf::tr_col(lane) & 7);
     }
     if constexpr (Cf::BKM) {
@@ -279,79 +275,64 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
     } else {
 #pragma unroll
         for (int b = 0; b < FN; ++b)
-            boff[b] = 16 * dev::MNTile::at(Mf::tr_krow(lane, 0), (brow0 + Cf::MF * b + Mf::tr_col(lane)) >> 3) +
+            boff[b] = 16 * OB::MT::at(Mf::tr_krow(lane, 0), (brow0 + Cf::MF * b + Mf::tr_col(lane)) >> 3) +
                       2 * (Mf::tr_col(lane) & 7);
     }
 
-    // Read the fragments of K step s of the slice in `stage`.
-    auto read_frag = [&](const char* base, const int* off, bool kmaj, int s, int b) -> V8 {
-        if (kmaj) {
-            // row block b: +MF rows of BK*2 bytes
-            return *(const LDS_AS V8*)(base + off[s] + b * Cf::MF * BK * 2);
-        }
-        // K rows KSTEP*s + 4q (+ the lane's own rows, folded into off[b]);
-        // the row swizzle depends only on krow & 3, which KSTEP*s + 4q keeps
-        const LDS_AS char* p0 = (const LDS_AS char*)(base + off[b] + (Mf::KSTEP * s) * 512);
-#if defined(__HIP_DEVICE_COMPILE__)
-        // Inline asm rather than the compiler's transposing-read builtin: for
-        // the builtin the compiler cannot tell that the LDS-DMA copies in
-        // flight write other bytes, and waits for all of them before each
-        // read, which exposed the whole copy latency once per slice. These
-        // reads are waited for explicitly (frag_wait).
-        const uint32_t a0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p0));
-        i16x4 lo, hi;
-        asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(lo) : "v"(a0));
-        asm volatile("ds_read_b64_tr_b16 %0, %1 offset:2048" : "=v"(hi) : "v"(a0));   // K rows + 4
-#else
-        (void)p0;
-        i16x4 lo{}, hi{};
-#endif
-        i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        return __builtin_bit_cast(V8, v);
+    // Fragment b of K step s of the slice in `stage`. K-major: row block b
+    // is MF rows of BK*2 bytes further. M/N-major: K rows KSTEP*s + 4q (+
+    // the lane's own rows, folded into off[b]); the row swizzle depends only
+    // on krow & 3 and bit 3 of krow, which KSTEP*s + 4q keeps.
+    auto read_a = [&](int stage, int s, int b) -> FA {
+        const char* base = smem + stage * Cf::STAGE;
+        if constexpr (Cf::AK)
+            return FA{*(const LDS_AS V8*)(base + aoff[s] + b * Cf::MF * BK * 2)};
+        else
+            return read_tr<V8, OA::KROW_BYTES>(
+                (const LDS_AS char*)(base + aoff[b] + Mf::KSTEP * s * OA::KROW_BYTES));
+    };
+    auto read_b = [&](int stage, int s, int b) -> FB {
+        const char* base = smem + stage * Cf::STAGE + Cf::A_BYTES;
+        if constexpr (Cf::BKM)
+            return FB{*(const LDS_AS V8*)(base + boff[s] + b * Cf::MF * BK * 2)};
+        else
+            return read_tr<V8, OB::KROW_BYTES>(
+                (const LDS_AS char*)(base + boff[b] + Mf::KSTEP * s * OB::KROW_BYTES));
     };
 
-    V8 af[2][FM], bfr[2][FN];
+    FA af[2][FM];
+    FB bfr[2][FN];
     // With an M-/N-major operand (transposing reads in inline asm, which the
-    // compiler does not track): every LDS read in flight has landed, and the
-    // fragments of buffer `buf` pass through the wait as operands, so no use
-    // of them is scheduled above it. Called at the top of each K step; it
-    // also retires every read of a stage before the barrier that frees it.
+    // compiler does not track): every LDS read in flight has landed, then
+    // the fragments of buffer `buf` pass through empty asm statements, so no
+    // use (or copy) of them is scheduled above the wait. Called at the top
+    // of each K step; it also retires every read of a stage before the
+    // barrier that frees it.
     auto frag_wait = [&](auto bufc) {
-#if defined(__HIP_DEVICE_COMPILE__)
         if constexpr (!(Cf::AK && Cf::BKM)) {
             constexpr int buf = decltype(bufc)::value;
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            static_for<0, FM>([&](auto i) {
-                V8& x = af[buf][decltype(i)::value];   // (named first: an asm operand alone is not a capture)
-                asm volatile("" : "+v"(x));
-            });
-            static_for<0, FN>([&](auto j) {
-                V8& x = bfr[buf][decltype(j)::value];
-                asm volatile("" : "+v"(x));
-            });
+            static_for<0, FM>([&](auto i) { af[buf][decltype(i)::value].pin(); });
+            static_for<0, FN>([&](auto j) { bfr[buf][decltype(j)::value].pin(); });
         }
-#endif
     };
     auto read_step = [&](int stage, int s, int buf) {
-        const char* sa = smem + stage * Cf::STAGE;
-        const char* sb = sa + Cf::OP_BYTES;
 #pragma unroll
-        for (int b = 0; b < FM; ++b) af[buf][b] = read_frag(sa, aoff, Cf::AK, s, b);
+        for (int b = 0; b < FM; ++b) af[buf][b] = read_a(stage, s, b);
 #pragma unroll
-        for (int b = 0; b < FN; ++b) bfr[buf][b] = read_frag(sb, boff, Cf::BKM, s, b);
+        for (int b = 0; b < FN; ++b) bfr[buf][b] = read_b(stage, s, b);
     };
-
     // fragment r of K step s: A block r (r < FM), else B block r - FM
     auto read_one = [&](int stage, int s, int buf, auto rc) {
         constexpr int r = decltype(rc)::value;
-        const char* sa = smem + stage * Cf::STAGE;
         if constexpr (r < FM)
-            af[buf][r] = read_frag(sa, aoff, Cf::AK, s, r);
+            af[buf][r] = read_a(stage, s, r);
         else
-            bfr[buf][r - FM] = read_frag(sa + Cf::OP_BYTES, boff, Cf::BKM, s, r - FM);
+            bfr[buf][r - FM] = read_b(stage, s, r - FM);
     };
 
-    using Acc = std::conditional_t<Cf::MF == 32, f32x16, f32x4>;
+    using Acc = f32x4;
+    static_assert(Cf::MF == 16, "the tiled kernel issues 16x16x32 MFMAs");
     Acc acc[FM][FN];
     for_blocks<FM, FN>([&](auto i, auto j) {
 #pragma unroll
@@ -384,7 +365,7 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
     auto slice_s = [&](auto has_next, auto refill, int t) {
         static_for<0, KS>([&](auto sc) {
             constexpr int s = decltype(sc)::value, cur = s & 1, nxt = cur ^ 1;
-            frag_wait(std::integral_constant<int, cur>{});
+            frag_wait(ic<cur>{});
             if constexpr (s + 1 < KS) {
                 read_step(stage, s + 1, nxt);
             } else if constexpr (decltype(has_next)::value) {
@@ -399,12 +380,7 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
-                for (int j = 0; j < FN; ++j) {
-                    if constexpr (Cf::MF == 32)
-                        acc[i][j] = Tr<DT>::mfma32(bfr[cur][j], af[cur][i], acc[i][j]);
-                    else
-                        acc[i][j] = Tr<DT>::mfma16(bfr[cur][j], af[cur][i], acc[i][j]);
-                }
+                for (int j = 0; j < FN; ++j) acc[i][j] = Tr<DT>::mfma16(bfr[cur][j].get(), af[cur][i].get(), acc[i][j]);
             // Issue order for this step: groups of two MFMAs, then two of the
             // slice copies (last step only), then two fragment reads for the
             // next step, until the reads are out; the remaining MFMAs cover
@@ -426,17 +402,16 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
         });
         stage = stage + 1 == S ? 0 : stage + 1;
     };
-#if defined(__HIP_DEVICE_COMPILE__)
     // The one-wave-per-SIMD schedule. Per K step: the MFMAs in block order,
     // the next step's fragment reads spread over the first three quarters of
     // them (one every few MFMAs, so the LDS sees a steady stream and the last
     // read has a quarter of the step to land), and in the last step, after
     // the barrier, the slice copies spread over all of them. The accumulators
-    // are asm operands bound to AGPRs ("a"), which keeps all 256 of them there.
+    // are asm operands bound to AGPRs ("a"), which keeps all of them there.
     auto mfma_one = [&](int cur, auto qc) {
         constexpr int q = decltype(qc)::value, i = q / FN, j = q % FN;
         auto& c = acc[i][j];
-        const V8 x = bfr[cur][j], y = af[cur][i];
+        const V8 x = bfr[cur][j].get(), y = af[cur][i].get();
         if constexpr (DT == LT_BF16)
             asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(x), "v"(y));
         else
@@ -449,7 +424,8 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
             constexpr bool reads = !last || decltype(has_next)::value;
             constexpr bool copies = last && decltype(refill)::value;
             constexpr int NR = reads ? FM + FN : 0, NC = copies ? Cf::IPW : 0, NQ = FM * FN;
-            frag_wait(std::integral_constant<int, cur>{});
+            static_assert(Cf::IPW <= NQ && 4 * (FM + FN) <= 3 * NQ, "one copy and one read per MFMA at most");
+            frag_wait(ic<cur>{});
             int rstage = stage, rs = s + 1;
             if constexpr (last && decltype(has_next)::value) {
                 if constexpr (decltype(refill)::value)
@@ -463,42 +439,31 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
             static_for<0, NQ>([&](auto qc) {
                 constexpr int q = decltype(qc)::value;
                 mfma_one(cur, qc);
-                static_for<0, (NC > 0 ? NC : 1)>([&](auto cc) {
-                    constexpr int c = decltype(cc)::value;
-                    if constexpr (NC > 0 && ((2 * c + 1) * NQ) / (2 * NC) == q) issue_one(stage, t + S, cc);
-                });
-                static_for<0, (NR > 0 ? NR : 1)>([&](auto rc) {
-                    constexpr int r = decltype(rc)::value;
-                    if constexpr (NR > 0 && (r * NQ * 3 / 4) / NR == q) read_one(rstage, rs, nxt, rc);
-                });
+                constexpr int c = copy_after(q, NC, NQ);
+                if constexpr (c >= 0) issue_one(stage, t + S, ic<c>{});
+                constexpr int r = read_after(q, NR, NQ);
+                if constexpr (r >= 0) read_one(rstage, rs, nxt, ic<r>{});
             });
         });
         stage = stage + 1 == S ? 0 : stage + 1;
     };
-#endif
     auto slice = [&](auto has_next, auto refill, int t) {
-#if defined(__HIP_DEVICE_COMPILE__)
         if constexpr (Cf::EXPLICIT)
             slice_x(has_next, refill, t);
         else
-#endif
             slice_s(has_next, refill, t);
     };
     const std::true_type yes{};
     const std::false_type no{};
-#if defined(__HIP_DEVICE_COMPILE__)
     // the zeroed accumulators are written by VALU moves: wait states before
     // the first inline-asm MFMA reads them (the compiler does not see it as one)
     if constexpr (Cf::EXPLICIT) asm volatile("s_nop 7" ::: "memory");
-#endif
     int t = 0;
     for (; t + S < NS; ++t) slice(yes, yes, t);   // refill slice t+S
     for (; t + 1 < NS; ++t) slice(yes, no, t);    // slices already in flight
     slice(no, no, t);                             // the last slice
-#if defined(__HIP_DEVICE_COMPILE__)
     // MFMA results before any VALU or memory instruction reads them
     if constexpr (Cf::EXPLICIT) asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
-#endif
 
     // ---- split-K segment: publish the fp32 partial; the segment that
     // arrives last adds the others' and goes on to the epilogue. No waiting:
@@ -644,36 +609,34 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
         float amax = 0.0f;
         for_blocks<FM, FN>([&](auto i, auto j) {
             const int m = m0 + arow0 + i * Cf::MF + Mf::out_col(lane);
-            {
 #pragma unroll
-                for (int g = 0; g < NG; ++g) {
-                    const int n = n0 + brow0 + j * Cf::MF + Mf::out_row(lane, 4 * g);
-                    if (m >= p.M || n >= p.N) continue;
-                    const int cnt = min(4, p.N - n);
-                    const uint16_t c16[4] = {static_cast<uint16_t>(cv[i][j][g].x & 0xffff),
-                                             static_cast<uint16_t>(cv[i][j][g].x >> 16),
-                                             static_cast<uint16_t>(cv[i][j][g].y & 0xffff),
-                                             static_cast<uint16_t>(cv[i][j][g].y >> 16)};
-                    uint16_t o[4];
+            for (int g = 0; g < NG; ++g) {
+                const int n = n0 + brow0 + j * Cf::MF + Mf::out_row(lane, 4 * g);
+                if (m >= p.M || n >= p.N) continue;
+                const int cnt = min(4, p.N - n);
+                const uint16_t c16[4] = {static_cast<uint16_t>(cv[i][j][g].x & 0xffff),
+                                         static_cast<uint16_t>(cv[i][j][g].x >> 16),
+                                         static_cast<uint16_t>(cv[i][j][g].y & 0xffff),
+                                         static_cast<uint16_t>(cv[i][j][g].y >> 16)};
+                uint16_t o[4];
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        float v = p.alpha * acc[i][j][4 * g + q];
-                        if (use_c)   // a partial group (cnt < 4) reads its C elements here
-                            v += p.beta * Tr<DT>::to_f32(cnt == 4 ? c16[q]
-                                                                  : (q < cnt ? p.C[(int64_t)m * p.ldc + n + q]
-                                                                             : uint16_t{0}));
-                        v += e.bias_on_rows ? brow[i] : Tr<DT>::to_f32(bcol[j][g][q]);
-                        o[q] = Tr<DT>::from_f32(activate(v, e.act));
-                        if (q < cnt) amax = fmaxf(amax, fabsf(Tr<DT>::to_f32(o[q])));
-                    }
-                    if (cnt == 4) {
-                        u32x2 w;
-                        w.x = (uint32_t)o[0] | ((uint32_t)o[1] << 16);
-                        w.y = (uint32_t)o[2] | ((uint32_t)o[3] << 16);
-                        *reinterpret_cast<u32x2*>(p.D + (int64_t)m * p.ldd + n) = w;
-                    } else {
-                        for (int q = 0; q < cnt; ++q) p.D[(int64_t)m * p.ldd + n + q] = o[q];
-                    }
+                for (int q = 0; q < 4; ++q) {
+                    float v = p.alpha * acc[i][j][4 * g + q];
+                    if (use_c)   // a partial group (cnt < 4) reads its C elements here
+                        v += p.beta * Tr<DT>::to_f32(cnt == 4 ? c16[q]
+                                                              : (q < cnt ? p.C[(int64_t)m * p.ldc + n + q]
+                                                                         : uint16_t{0}));
+                    v += e.bias_on_rows ? brow[i] : Tr<DT>::to_f32(bcol[j][g][q]);
+                    o[q] = Tr<DT>::from_f32(activate(v, e.act));
+                    if (q < cnt) amax = fmaxf(amax, fabsf(Tr<DT>::to_f32(o[q])));
+                }
+                if (cnt == 4) {
+                    u32x2 w;
+                    w.x = (uint32_t)o[0] | ((uint32_t)o[1] << 16);
+                    w.y = (uint32_t)o[2] | ((uint32_t)o[3] << 16);
+                    *reinterpret_cast<u32x2*>(p.D + (int64_t)m * p.ldd + n) = w;
+                } else {
+                    for (int q = 0; q < cnt; ++q) p.D[(int64_t)m * p.ldd + n + q] = o[q];
                 }
             }
         });
@@ -681,21 +644,16 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
     };
     if (p.epi.fused)
         epilogue_fused();
-    else if (m0 + 256 > p.M || n0 + 256 > p.N)
+    else if (m0 + Cf::BM > p.M || n0 + Cf::BN > p.N)
         epilogue(std::true_type{});
     else
         epilogue(std::false_type{});
+#else
+    (void)p;
+#endif
 }
 
-// The instantiation the planner launches for the data-parallel tiles: one
-// wave per SIMD (4 waves of 128x128), for every operand major-ness.
-template <bool AK, bool BKM>
-using Chosen = TCfg<2, 2, 64, 2, 16, AK, BKM>;
-// The split-remainder launch always runs 8 waves: its fix-up adds the other
-// segments' fp32 partials in registers, and with 256 accumulators per lane
-// that step spills (measured 320 vs 91 us on 1792x1792x7040).
-template <bool AK, bool BKM>
-using ChosenSplit = TCfg<4, 2, 64, 2, 16, AK, BKM>;
+namespace {
 
 template <int DT, class Cf, bool SPLIT>
 int launch_mode(const TiledArgs& a, int grid, hipStream_t s) {
@@ -706,46 +664,32 @@ int launch_mode(const TiledArgs& a, int grid, hipStream_t s) {
     return static_cast<int>(hipGetLastError());
 }
 
-// The data-parallel tiles, then (same stream, so after them) the split
-// remainder.
+}  // namespace
+
+// 256x128 tiles: the data-parallel launch only (the planner never splits
+// them). 256x256 tiles: the data-parallel tiles, then (same stream, so after
+// them) the split remainder.
 template <int DT, bool AK, bool BKM>
-int launch_one(const TiledArgs& a, hipStream_t s) {
+int launch_variant(const TiledArgs& a, int tile_n, void* stream) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (tile_n == 128) return a.dp_tiles > 0 ? launch_mode<DT, Dp128<AK, BKM>, false>(a, a.dp_tiles, s) : 0;
     if (a.dp_tiles > 0) {
-        const int e = launch_mode<DT, Chosen<AK, BKM>, false>(a, a.dp_tiles, s);
+        const int e = launch_mode<DT, Dp256<AK, BKM>, false>(a, a.dp_tiles, s);
         if (e != 0) return e;
     }
     const int split_wgs = (a.tiles_m * a.tiles_n - a.dp_tiles) * a.sk_splits;
-    if (split_wgs > 0) return launch_mode<DT, ChosenSplit<AK, BKM>, true>(a, split_wgs, s);
+    if (split_wgs > 0) return launch_mode<DT, Split256<AK, BKM>, true>(a, split_wgs, s);
     return 0;
 }
 
-template <int DT>
-int launch_dt(bool ak, bool bk, const TiledArgs& a, hipStream_t s) {
-    if (ak && bk) return launch_one<DT, true, true>(a, s);
-    if (ak && !bk) return launch_one<DT, true, false>(a, s);
-    if (!ak && bk) return launch_one<DT, false, true>(a, s);
-    return launch_one<DT, false, false>(a, s);
+// This translation unit's variant as a plain function named by the variant
+// (declared in gemm_kernels.hpp): launch_tiled_<dtype><A K-major>_<B K-major>.
+#if defined(LT_TILED_DT) && defined(LT_TILED_AK) && defined(LT_TILED_BK)
+#define LT_CAT(dt, ak, bk) launch_tiled_##dt##ak##_##bk
+#define LT_NAME(dt, ak, bk) LT_CAT(dt, ak, bk)
+int LT_NAME(LT_TILED_DT, LT_TILED_AK, LT_TILED_BK)(const TiledArgs& a, int tile_n, void* stream) {
+    return launch_variant<LT_TILED_DT, LT_TILED_AK != 0, LT_TILED_BK != 0>(a, tile_n, stream);
 }
-
-}  // namespace
-
-template <class Cf>
-TiledShape shape_of() {
-    return TiledShape{256, 256, Cf::BK, Cf::TWM, Cf::TWN, Cf::NW, Cf::S, Cf::LDS, Cf::FM * Cf::FN * Cf::KS,
-                      Cf::MF, Cf::MFMA::KSTEP};
-}
-
-TiledShape tiled_shape(bool a_kmajor, bool b_kmajor) {
-    if (a_kmajor && b_kmajor) return shape_of<Chosen<true, true>>();
-    if (a_kmajor) return shape_of<Chosen<true, false>>();
-    if (b_kmajor) return shape_of<Chosen<false, true>>();
-    return shape_of<Chosen<false, false>>();
-}
-
-int launch_tiled(int dtype, bool a_kmajor, bool b_kmajor, const TiledArgs& a, void* stream) {
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    return dtype == LT_F16 ? launch_dt<LT_F16>(a_kmajor, b_kmajor, a, s)
-                           : launch_dt<LT_BF16>(a_kmajor, b_kmajor, a, s);
-}
+#endif
 
 }  // namespace lt

@@ -24,11 +24,18 @@ KERNEL_NAMES = {v: k for k, v in KERNELS.items()}
 def tensor_desc(t: torch.Tensor, layout: Optional[Layout] = None) -> L.lt_tensor:
     """(pointer, dtype, layout) of a tensor; the layout defaults to the view's
     own shape and strides. With an explicit layout, ``t`` is the storage and
-    the layout addresses it from ``t.data_ptr()``."""
+    the layout addresses it from ``t.data_ptr()``: its cosize (the elements it
+    reaches) must fit in what the storage holds from there, else ValueError
+    (the C ABI sees only a pointer and cannot check this)."""
     if t.dtype not in _DT:
         raise TypeError(f"unsupported dtype {t.dtype}")
     if layout is None:
         layout = Layout.make(list(t.shape), list(t.stride()))
+    else:
+        room = t.untyped_storage().nbytes() // t.element_size() - t.storage_offset()
+        if layout.size() > 0 and layout.cosize() > room:
+            raise ValueError(f"layout {layout} reaches {layout.cosize()} elements; the storage holds {room} "
+                             f"from the tensor's first element")
     d = L.lt_tensor()
     d.ptr = t.data_ptr()
     d.dtype = _DT[t.dtype]
@@ -83,13 +90,22 @@ def gemm(A: torch.Tensor, B: torch.Tensor, D: torch.Tensor, C: Optional[torch.Te
     dC = tensor_desc(C, la.get("C")) if C is not None else None
     o = _opts(kernel, tile, split_k)
     ws_ptr, ws_bytes = None, 0
-    need = ctypes.c_size_t(0)
-    L.check(L.lib().lt_gemm_workspace_size(ctypes.byref(dA), ctypes.byref(dB), ctypes.byref(dC) if dC else None,
-                                           ctypes.byref(dD), int(beta != 0.0), ctypes.byref(o),
-                                           ctypes.byref(need)), "gemm_workspace_size")
-    if need.value:
-        if workspace is None:
+    sid = _stream(stream)
+    if workspace is None:
+        # Size it (the library refuses a run whose workspace is too small,
+        # so a caller-provided one needs no query). The tensor is freed when
+        # this call returns while the kernels may still be using it on the
+        # launch stream: record that stream so the caching allocator does
+        # not hand the memory out before they finish.
+        need = ctypes.c_size_t(0)
+        L.check(L.lib().lt_gemm_workspace_size(ctypes.byref(dA), ctypes.byref(dB),
+                                               ctypes.byref(dC) if dC else None, ctypes.byref(dD),
+                                               int(beta != 0.0), ctypes.byref(o), ctypes.byref(need)),
+                "gemm_workspace_size")
+        if need.value:
             workspace = torch.empty(need.value, dtype=torch.uint8, device=D.device)
+            workspace.record_stream(torch.cuda.ExternalStream(sid, device=D.device))
+    if workspace is not None:
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     epi = None
     if bias is not None or activation not in (None, "none") or amax is not None:
@@ -102,7 +118,7 @@ def gemm(A: torch.Tensor, B: torch.Tensor, D: torch.Tensor, C: Optional[torch.Te
     L.check(L.lib().lt_gemm_run_ex(ctypes.byref(dA), ctypes.byref(dB), ctypes.byref(dC) if dC else None,
                                    ctypes.byref(dD), float(alpha), float(beta), ctypes.byref(o),
                                    ctypes.byref(epi) if epi is not None else None, ws_ptr, ws_bytes,
-                                   _stream(stream)), "gemm_run")
+                                   sid), "gemm_run")
 
 
 def layout_eval_device(layout: Layout, out: torch.Tensor, n: Optional[int] = None, stream=None) -> None:

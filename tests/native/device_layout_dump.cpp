@@ -36,6 +36,9 @@ int main() {
     std::printf("mntile 64 32\n");
     for (int k = 0; k < 64; ++k)
         for (int c = 0; c < 32; ++c) std::printf("%d ", MNTile::at(k, c));
+    std::printf("\nmntile 64 16\n");
+    for (int k = 0; k < 64; ++k)
+        for (int c = 0; c < 16; ++c) std::printf("%d ", MNTileW<16>::at(k, c));
     std::printf("\ntr\n");
     for (int l = 0; l < 64; ++l) std::printf("%d %d %d ", tr_krow(l, 0), tr_krow(l, 1), tr_col(l));
     std::printf("\ncopy\n");

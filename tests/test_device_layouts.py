@@ -85,27 +85,30 @@ def test_copy_fetches_what_swizzle_stores(maps, bk):
         assert inv[q] == (row, lchunk)
 
 
-def _mntile(maps):
-    v = maps[("mntile", "64", "32")]
-    return v, (lambda k, c: v[k * 32 + c])
+def _mntile(maps, w=32):
+    v = maps[("mntile", "64", str(w))]
+    return v, (lambda k, c: v[k * w + c])
 
 
-def test_mntile_bijection(maps):
-    v, at = _mntile(maps)
-    assert sorted(v) == list(range(64 * 32))
-    for k in range(64):   # each K row keeps its own 32 chunks
-        assert sorted(at(k, c) for c in range(32)) == list(range(32 * k, 32 * (k + 1)))
-        for c in range(32):   # an involution inside the row
-            assert at(k, at(k, c) - 32 * k) - 32 * k == c
+@pytest.mark.parametrize("w", [32, 16])
+def test_mntile_bijection(maps, w):
+    v, at = _mntile(maps, w)
+    assert sorted(v) == list(range(64 * w))
+    for k in range(64):   # each K row keeps its own w chunks
+        assert sorted(at(k, c) for c in range(w)) == list(range(w * k, w * (k + 1)))
+        for c in range(w):   # an involution inside the row
+            assert at(k, at(k, c) - w * k) - w * k == c
 
 
-@pytest.mark.parametrize("mf", [32, 16])
-def test_transposed_reads_hand_each_lane_its_fragment(maps, mf):
-    """The M/N-major operand path: lanes address the LDS tile as the kernel
-    does, the read semantics measured on gfx950 are applied, and every lane
-    must receive the MFMA fragment of its row and K values; each 32-lane half
-    must touch 32 distinct 8-byte bank pairs (no LDS bank conflict)."""
-    _, at = _mntile(maps)
+@pytest.mark.parametrize("mf,w", [(32, 32), (16, 32), (16, 16)])
+def test_transposed_reads_hand_each_lane_its_fragment(maps, mf, w):
+    """The M/N-major operand path: lanes address the LDS tile (K rows of 8*w
+    elements: 256 for a 256-wide block tile, 128 for a 128-wide one) as the
+    kernel does, the read semantics measured on gfx950 are applied, and every
+    lane must receive the MFMA fragment of its row and K values; each 32-lane
+    half must touch 32 distinct 8-byte bank pairs (no LDS bank conflict)."""
+    _, at = _mntile(maps, w)
+    width = 8 * w
     kstep = 512 // mf
     tr = maps[("mtr", str(mf))]
     krow0 = [tr[3 * l] for l in range(64)]
@@ -113,10 +116,11 @@ def test_transposed_reads_hand_each_lane_its_fragment(maps, mf):
     col = [tr[3 * l + 2] for l in range(64)]
     lds = {}
     for k in range(64):
-        for mn in range(256):
+        for mn in range(width):
             lds[at(k, mn // 8) * 16 + (mn % 8) * 2] = (k, mn)
+    bases = [b for b in ((0, 32, 96, 224) if mf == 32 else (0, 16, 48, 112, 240)) if b + mf <= width]
     for s in range(64 // kstep):          # K step
-        for base in (0, 32, 96, 224) if mf == 32 else (0, 16, 112, 240):
+        for base in bases:
             for q, krow in ((0, krow0), (1, krow1)):
                 addr = []
                 for l in range(64):

@@ -34,13 +34,17 @@ def _bias(n, dtype, seed, stride=1):
 
 
 CASES = [
-    # (label, M, N, K, dtype, a, b, d, beta, kernel, split_k, expect)
-    ("wave16", 250, 130, 72, F16, "row", "col", "row", 0.5, "auto", 0, "wave16"),
-    ("tiled", 512, 512, 256, BF16, "row", "col", "row", 0.0, "auto", 0, "tiled"),
-    ("tiled-ragged", 300, 520, 200, F16, "row", "col", "row", -1.0, "tiled", 0, "tiled"),
-    ("tiled-mn", 264, 392, 96, BF16, "col", "row", "row", 1.0, "tiled", 0, "tiled"),
-    ("skinny", 32, 1024, 4096, BF16, "row", "col", "row", 0.0, "auto", 0, "skinny"),
-    ("skinny-split", 17, 512, 4096, F16, "row", "col", "row", 0.5, "auto", 2, "skinny"),
+    # (label, M, N, K, dtype, a, b, d, beta, kernel, split_k, expect, block tile)
+    ("wave16", 250, 130, 72, F16, "row", "col", "row", 0.5, "auto", 0, "wave16", None),
+    ("tiled", 512, 512, 256, BF16, "row", "col", "row", 0.0, "auto", 0, "tiled", None),
+    ("tiled-256", 512, 512, 256, F16, "row", "col", "row", 0.5, "tiled", 1, "tiled", (256, 256)),
+    ("tiled-ragged", 300, 520, 200, F16, "row", "col", "row", -1.0, "tiled", 0, "tiled", None),
+    ("tiled-ragged-256", 300, 520, 200, BF16, "row", "col", "row", 1.0, "tiled", 0, "tiled", (256, 256)),
+    ("tiled-mn", 264, 392, 96, BF16, "col", "row", "row", 1.0, "tiled", 0, "tiled", None),
+    ("tiled-mn-256", 264, 392, 96, F16, "col", "row", "row", 0.0, "tiled", 0, "tiled", (256, 256)),
+    ("tiled-split", 512, 768, 512, BF16, "row", "col", "row", 0.5, "tiled", 2, "tiled", None),
+    ("skinny", 32, 1024, 4096, BF16, "row", "col", "row", 0.0, "auto", 0, "skinny", None),
+    ("skinny-split", 17, 512, 4096, F16, "row", "col", "row", 0.5, "auto", 2, "skinny", None),
 ]
 
 
@@ -48,11 +52,13 @@ CASES = [
 @pytest.mark.parametrize("per_row", [False, True])
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
 def test_fused_epilogue_all_kernels(case, per_row, act):
-    label, M, N, K, dtype, a, b, d, beta, kernel, split, expect = case
+    label, M, N, K, dtype, a, b, d, beta, kernel, split, expect, tile = case
     A, B, C, D = _case(M, N, K, dtype, a, b, d, beta, seed=M + N + K)
     bias = _bias(M if per_row else N, dtype, seed=K)
     res, plan, amax, wmax = run_and_check_fused(A, B, C, D, 1.5, beta, bias, per_row, act, kernel=kernel,
-                                                split_k=split, expect_kernel=expect, label=label)
+                                                split_k=split, expect_kernel=expect, label=label, tile=tile)
+    if tile:
+        assert plan["tile_n"] == tile[1]
     assert res.ok, str(res)
     assert amax == wmax
 

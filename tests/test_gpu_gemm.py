@@ -9,7 +9,7 @@ import pytest
 import torch
 
 import datagen
-from tests.gemm_cases import all_points, op, run_and_check, sample_points, say
+from tests.gemm_cases import all_points, check_all_rows, op, run_and_check, run_gemm, sample_points, say
 from oracle import gemm as og
 
 pytestmark = pytest.mark.gpu
@@ -88,28 +88,31 @@ def test_tiled_padded_leading_dimensions():
     (1, 300, 64, F16, "row", "col", 1.0, 0.0, None),               # one row
     (700, 9, 328, BF16, "row", "col", 1.0, 1.0, (328, 328, 16)),   # nine columns, padded D and C
 ])
-def test_tiled_ragged_all_outputs(M, N, K, dtype, a_major, b_major, alpha, beta, lds):
+@pytest.mark.parametrize("tile_n", [256, 128])
+def test_tiled_ragged_all_outputs(M, N, K, dtype, a_major, b_major, alpha, beta, lds, tile_n):
     A, B, C, D = _case(M, N, K, dtype, a_major, b_major, "row", alpha, beta, seed=M + N + K, lds=lds)
-    res, plan, _ = run_and_check(A, B, C, D, alpha, beta, kernel="tiled", expect_kernel="tiled",
-                                 label="tiled-ragged")
+    res, plan, _ = run_and_check(A, B, C, D, alpha, beta, kernel="tiled", tile=(256, tile_n),
+                                 expect_kernel="tiled", label="tiled-ragged")
     _ok(res)
-    tiles = ((M + 255) // 256) * ((N + 255) // 256)
-    assert plan["grid"] == tiles - plan["sk_tiles"] + plan["sk_workgroups"]
+    tiles = ((M + 255) // 256) * ((N + tile_n - 1) // tile_n)
+    assert plan["tile_n"] == tile_n and plan["grid"] == tiles - plan["sk_tiles"] + plan["sk_workgroups"]
 
 
-@pytest.mark.parametrize("K", [64, 128, 192, 320])
+@pytest.mark.parametrize("K", [64, 128, 192, 256, 320])
 @pytest.mark.parametrize("a_major,b_major", [("row", "col"), ("col", "row"), ("row", "row"), ("col", "col")])
-def test_tiled_slice_counts_every_major(K, a_major, b_major):
-    """The 256x256 kernel at 1, 2, 3 and 5 K slices (no refill, the refill
-    loop entered or not, several refills) for every operand major-ness, on 4
-    tiles, every output checked: the issue order of copies, fragment reads and
-    MFMAs, and its explicit waits, differ between those loop shapes."""
+@pytest.mark.parametrize("tile_n", [256, 128])
+def test_tiled_slice_counts_every_major(K, a_major, b_major, tile_n):
+    """The 256x256 (2 LDS stages) and 256x128 (3 stages) kernels at 1 to 5 K
+    slices (no refill, the refill loop entered or not, several refills) for
+    every operand major-ness, on 4 (8) tiles, every output checked: the issue
+    order of copies, fragment reads and MFMAs, and its explicit waits, differ
+    between those loop shapes."""
     M, N = 512, 512
     A, B, C, D = _case(M, N, K, BF16, a_major, b_major, "row", 1.0, 0.5, seed=K + 7)
-    res, plan, _ = run_and_check(A, B, C, D, 1.0, 0.5, kernel="tiled", split_k=1, expect_kernel="tiled",
-                                 label=f"slices {K // 64} {a_major}/{b_major}")
+    res, plan, _ = run_and_check(A, B, C, D, 1.0, 0.5, kernel="tiled", split_k=1, tile=(256, tile_n),
+                                 expect_kernel="tiled", label=f"slices {K // 64} {a_major}/{b_major} 256x{tile_n}")
     _ok(res)
-    assert plan["waves"] == 4 and plan["grid"] == 4
+    assert plan["waves"] == 4 and plan["grid"] == 2 * 512 // tile_n * 2 and plan["tile_n"] == tile_n
 
 
 def test_tiled_ragged_large_auto():
@@ -264,14 +267,21 @@ def test_skinny_with_beta():
 # the full-size workloads, sampled outputs, benchmark launch configuration
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("cfg,kernel", [(2, "tiled"), (3, "tiled"), (4, None), (5, "skinny")])
-def test_full_size_workloads_sampled(cfg, kernel):
+@pytest.mark.parametrize("cfg,kernel,tile_n", [(2, "tiled", 256), (3, "tiled", 256), (4, "tiled", 128),
+                                                (5, "skinny", None)])
+def test_full_size_workloads_every_output(cfg, kernel, tile_n):
+    """The benchmark's workloads at full size, in the launch configuration
+    the benchmark times (the automatic plan), every output checked against
+    the oracle: at these sizes the XCD regrouping of workgroups and the
+    raster groups past the first are in play."""
     c = datagen.config(cfg)
     say(f"[gemm] generating inputs of workload {cfg}: {c.name}")
     A, B, C, D = c.make()
-    pts = sample_points(c.M, c.N, 4000, seed=cfg)
-    res, plan, out = run_and_check(A, B, C if c.beta != 0 else None, D, c.alpha, c.beta, points=pts,
-                                   expect_kernel=kernel, label=f"cfg{cfg}")
+    C = C if c.beta != 0 else None
+    plan, out = run_gemm(A, B, C, D, c.alpha, c.beta, expect_kernel=kernel, label=f"cfg{cfg}")
+    if tile_n:
+        assert plan["tile_n"] == tile_n, plan
+    res = check_all_rows(A, B, C, out, c.alpha, c.beta)
+    say(f"[gemm] cfg{cfg}: {res}")
     _ok(res)
-    # every output finite (cheap full scan)
-    assert torch.isfinite(out.view().float()).all()
+    assert res.n == c.M * c.N

@@ -1,0 +1,181 @@
+"""Checks on the gfx950 machine code of the built library (CPU only: the code
+objects are extracted from liblt.so and disassembled with the ROCm LLVM
+tools).
+
+1. Every tiled-kernel variant is present as device code with a host-side
+   launch stub, so no configuration the planner can pick is missing.
+2. The transposing LDS reads of M/N-major operands are inline asm that the
+   compiler does not track. For each such read, every control-flow path from
+   it must reach an `s_waitcnt lgkmcnt(0)` before any instruction names one of
+   its destination registers (a read of them would see stale data, a write
+   would be overwritten when the load lands)."""
+
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+from tests.proc import skip_if_gpu_initialised
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "layout_algebra_tiled_amd", "liblt.so")
+LLVM = "/opt/rocm/llvm/bin"
+
+_FUNC = re.compile(r"^([0-9a-f]+) <([^>]+)>:$")
+_INST = re.compile(r"^\s+(\S+)\s*(.*?)\s*//\s*([0-9A-Fa-f]+):")
+_TARGET = re.compile(r"<([^>+]+)\+0x([0-9a-f]+)>")
+_VREG = re.compile(r"\bv\[(\d+):(\d+)\]|\bv(\d+)\b")
+
+
+def _regs(operands: str):
+    out = set()
+    for a, b, one in _VREG.findall(operands):
+        if one:
+            out.add(int(one))
+        else:
+            out.update(range(int(a), int(b) + 1))
+    return out
+
+
+def _functions(text: str):
+    """{name: [(addr, mnemonic, operands, comment)]} of a disassembly."""
+    funcs, cur = {}, None
+    for line in text.splitlines():
+        m = _FUNC.match(line)
+        if m:
+            cur = funcs.setdefault(m.group(2), [])
+            continue
+        if cur is None:
+            continue
+        m = _INST.match(line)
+        if m:
+            comment = line.split("//", 1)[1]
+            cur.append((int(m.group(3), 16), m.group(1), m.group(2), comment))
+    return funcs
+
+
+@pytest.fixture(scope="module")
+def disasm(tmp_path_factory):
+    skip_if_gpu_initialised()
+    if not os.path.exists(LIB):
+        pytest.skip("library not built")
+    if not os.path.exists(os.path.join(LLVM, "llvm-objdump")):
+        pytest.skip("ROCm llvm-objdump not available")
+    d = tmp_path_factory.mktemp("isa")
+    lib = d / "liblt.so"
+    shutil.copy(LIB, lib)
+    subprocess.run([os.path.join(LLVM, "llvm-objdump"), "--offloading", str(lib)], cwd=d, check=True,
+                   capture_output=True)
+    funcs, addrs = {}, {}
+    for co in sorted(d.glob("liblt.so.*gfx950")):
+        text = subprocess.run([os.path.join(LLVM, "llvm-objdump"), "-d", "--mcpu=gfx950", str(co)],
+                              capture_output=True, text=True, check=True).stdout
+        for line in text.splitlines():
+            m = _FUNC.match(line)
+            if m:
+                addrs[(co.name, m.group(2))] = int(m.group(1), 16)
+        for name, insts in _functions(text).items():
+            funcs[(co.name, name)] = insts
+    nm = subprocess.run(["nm", "-C", str(LIB)], capture_output=True, text=True, check=True).stdout
+    return funcs, addrs, nm
+
+
+def test_every_tiled_variant_has_device_code_and_a_stub(disasm):
+    funcs, _, nm = disasm
+    names = {n for (_, n) in funcs}
+    want = set()
+    for dt in (1, 2):
+        for ak in ("0", "1"):
+            for bk in ("0", "1"):
+                a, b = ("b1" if ak == "1" else "b0"), ("b1" if bk == "1" else "b0")
+                # Dp256, Dp128 and the split launch of each variant
+                want.add(f"_ZN2lt10gemm_tiledILi{dt}ENS_4TCfgILi256ELi256ELi2ELi2ELi64ELi2ELi16EL{a}EL{b}EEELb0EEEvNS_9TiledArgsE")
+                want.add(f"_ZN2lt10gemm_tiledILi{dt}ENS_4TCfgILi256ELi128ELi2ELi2ELi64ELi3ELi16EL{a}EL{b}EEELb0EEEvNS_9TiledArgsE")
+                want.add(f"_ZN2lt10gemm_tiledILi{dt}ENS_4TCfgILi256ELi256ELi4ELi2ELi64ELi2ELi16EL{a}EL{b}EEELb1EEEvNS_9TiledArgsE")
+    assert want <= names, sorted(want - names)
+    undefined_stubs = [l for l in nm.splitlines() if " U " in l and "__device_stub__" in l]
+    assert not undefined_stubs, undefined_stubs
+
+
+def _successors(insts, i, index_of, func_addr):
+    addr, mn, ops, comment = insts[i]
+    if mn == "s_endpgm":
+        return []
+    nxt = [i + 1] if i + 1 < len(insts) else []
+    if mn.startswith("s_branch") or mn.startswith("s_cbranch"):
+        m = _TARGET.search(comment)
+        assert m, (mn, comment)
+        tgt = index_of[func_addr + int(m.group(2), 16)]
+        return [tgt] if mn.startswith("s_branch") else nxt + [tgt]
+    return nxt
+
+
+def unwaited_uses(insts, base):
+    """(read, instruction) pairs where an instruction names a destination
+    register of a transposing read on some path from it before an
+    lgkmcnt(0) wait (or the kernel ends first). Returns (violations,
+    number of reads checked)."""
+    index_of = {a: i for i, (a, _, _, _) in enumerate(insts)}
+    bad, n = [], 0
+    for r, (_, mn, ops, _) in enumerate(insts):
+        if mn != "ds_read_b64_tr_b16":
+            continue
+        n += 1
+        dest = _regs(ops.split(",")[0])
+        seen, todo = set(), _successors(insts, r, index_of, base)
+        while todo:
+            j = todo.pop()
+            if j in seen:
+                continue
+            seen.add(j)
+            _, mnj, opsj, _ = insts[j]
+            if mnj == "s_waitcnt" and "lgkmcnt(0)" in opsj:
+                continue
+            if _regs(opsj) & dest or mnj == "s_endpgm":
+                bad.append((insts[r][:3], insts[j][:3]))
+                continue
+            todo.extend(_successors(insts, j, index_of, base))
+    return bad, n
+
+
+_GOOD = """0000000000001000 <k>:
+	ds_read_b64_tr_b16 v[4:5], v0                              // 000000001000: D9C60000 04000000
+	ds_read_b64_tr_b16 v[6:7], v0 offset:2048                  // 000000001008: D9C60800 06000000
+	v_mfma_f32_16x16x32_bf16 a[0:3], v[8:11], v[12:15], a[0:3]  // 000000001010: 00000000 00000000
+	s_cbranch_scc1 2                                           // 000000001018: BF850002 <k+0x24>
+	s_waitcnt lgkmcnt(0)                                       // 00000000101C: BF8CC07F
+	s_branch 1                                                 // 000000001020: BF820001 <k+0x28>
+	s_waitcnt vmcnt(0) lgkmcnt(0)                              // 000000001024: BF8C0070
+	v_mov_b32_e32 v8, v4                                       // 000000001028: 7E100304
+	s_endpgm                                                   // 00000000102C: BF810000
+"""
+
+
+def test_checker_accepts_waited_reads_and_catches_early_use():
+    """The path walk itself, on a hand-written fragment: both paths from the
+    reads wait before v4 is copied; moving the copy above the wait, or
+    taking the wait off one branch path, must be reported."""
+    insts = _functions(_GOOD)["k"]
+    assert unwaited_uses(insts, 0x1000) == ([], 2)
+    early = _GOOD.replace("v_mfma_f32_16x16x32_bf16 a[0:3], v[8:11]", "v_mfma_f32_16x16x32_bf16 a[0:3], v[4:7]")
+    bad, _ = unwaited_uses(_functions(early)["k"], 0x1000)
+    assert len(bad) == 2 and all(b[1][1].startswith("v_mfma") for b in bad)
+    one_path = _GOOD.replace("s_waitcnt vmcnt(0) lgkmcnt(0)", "s_waitcnt vmcnt(0)")
+    bad, _ = unwaited_uses(_functions(one_path)["k"], 0x1000)
+    assert {b[1][1] for b in bad} == {"v_mov_b32_e32", "s_endpgm"}   # v4 copied; v6:7 never waited
+
+
+def test_transposing_reads_are_waited_before_use(disasm):
+    funcs, addrs, _ = disasm
+    kernels, reads = 0, 0
+    for key, insts in funcs.items():
+        bad, n = unwaited_uses(insts, addrs[key])
+        assert not bad, f"{key[1]}: {bad[:3]}"
+        if n:
+            kernels += 1
+            reads += n
+    # every kernel of a variant with an M/N-major operand issues transposing
+    # reads: 3 such variants per dtype, 3 launch configurations each
+    assert kernels >= 18 and reads > 1000, (kernels, reads)

@@ -279,9 +279,9 @@ def _desc(ptr, dtype, shape, stride):
     return d
 
 
-def _plan(A, B, C, D, bnz=0, kernel=0, split=0):
+def _plan(A, B, C, D, bnz=0, kernel=0, split=0, tile_n=0):
     o = L.lt_gemm_options()
-    o.kernel, o.split_k = kernel, split
+    o.kernel, o.split_k, o.tile_n = kernel, split, tile_n
     info = L.lt_gemm_plan_info()
     st = L.lib().lt_gemm_plan(ctypes.byref(A), ctypes.byref(B), ctypes.byref(C) if C else None, ctypes.byref(D),
                               bnz, ctypes.byref(o), ctypes.byref(info))
@@ -412,8 +412,14 @@ def test_plan_validation_statuses():
     # predicated); the automatic choice keeps a problem smaller than one tile
     # on the 16x16 kernel
     A, B, C, D = _gemm_descs(250, 256, 64)
-    st, i = _plan(A, B, C, D, kernel=L.LT_KERNEL_TILED)
-    assert st == "LT_OK" and i.kernel == L.LT_KERNEL_TILED and i.grid == 1
+    st, i = _plan(A, B, C, D, kernel=L.LT_KERNEL_TILED)   # one 256x256 tile = two 256x128 ones
+    assert st == "LT_OK" and i.kernel == L.LT_KERNEL_TILED and (i.tile_n, i.grid) == (128, 2)
+    st, i = _plan(A, B, C, D, kernel=L.LT_KERNEL_TILED, tile_n=256)
+    assert st == "LT_OK" and (i.tile_n, i.grid) == (256, 1)
+    # block tiles other than 256x256 and 256x128 are refused, and so is a
+    # split of 256x128 tiles
+    assert _plan(A, B, C, D, kernel=L.LT_KERNEL_TILED, tile_n=64)[0] == "LT_ERR_UNSUPPORTED"
+    assert _plan(A, B, C, D, kernel=L.LT_KERNEL_TILED, tile_n=128, split=2)[0] == "LT_ERR_UNSUPPORTED"
     assert _plan(A, B, C, D)[1].kernel == L.LT_KERNEL_WAVE16
     # K-major operands copy whole 16-byte chunks of K: K % 8 != 0 is refused
     A = _desc(BASE, L.LT_BF16, [256, 60], [64, 1])
@@ -451,52 +457,65 @@ def test_plan_ragged_shapes_on_the_tiled_kernel():
         st, i = _plan(*_gemm_descs(M, N, K))
         assert st == "LT_OK" and i.kernel == expect, (M, N, K, st, i.kernel)
         if expect == L.LT_KERNEL_TILED:
-            tiles = -(-M // 256) * -(-N // 256)
+            tiles = -(-M // 256) * -(-N // i.tile_n)
             assert i.grid == tiles - i.sk_tiles + i.sk_workgroups
 
 
-def _split_plan(tiles, kt, split=0):
-    """The planner's rule, written out: whole rounds of 256 tiles stay
-    data-parallel; the last round's rem tiles are split into S K segments
-    when the modelled time (in K slices, 20 for the partials) drops by a
-    tenth, or when forced."""
-    rem = tiles % 256
-    if split == 1:
-        return tiles, 0, 1
+def _tile_plan(M, N, K, split=0, want_n=0):
+    """The planner's rule, written out, in K-slice times of a 256x128 tile:
+    256x256 tiles cost 2 per slice; their whole rounds of 256 tiles stay
+    data-parallel and the last round's rem tiles are split into S K segments
+    when that saves a tenth (20 slices for the partials) or when forced;
+    256x128 tiles cost 23/20 per slice and are never split. Returns
+    (tile_n, data-parallel tiles, split tiles, S)."""
+    kt = -(-K // 64)
+    n256 = -(-M // 256) * -(-N // 256)
+    rem, S = n256 % 256, 1
+    c256 = -(-n256 // 256) * kt * 2
     if split == 0:
-        if rem == 0:
-            return tiles, 0, 1
-        S = min(256 // rem, 8, kt // 4)
-        t_dp = -(-tiles // 256) * kt
-        t_split = tiles // 256 * kt + -(-kt // max(S, 1)) + 20
-        if S < 2 or not 10 * t_split < 9 * t_dp:
-            return tiles, 0, 1
-        return tiles - rem, rem, S
-    S = min(split, kt)
-    rem = rem or min(tiles, 256)
-    return (tiles, 0, 1) if S < 2 else (tiles - rem, rem, S)
+        if rem:
+            S = min(256 // rem, 8, kt // 4)
+            if S >= 2:
+                t_split = (n256 // 256 * kt + -(-kt // S) + 20) * 2
+                if 10 * t_split < 9 * c256:
+                    c256 = t_split
+                else:
+                    S = 1
+    elif split > 1:
+        S = min(split, kt)
+        rem = rem or min(n256, 256)
+    if S < 2:
+        S, rem = 1, 0
+    n128 = -(-M // 256) * -(-N // 128)
+    if want_n == 128 or (want_n == 0 and split <= 1 and -(-n128 // 256) * kt * 23 < c256 * 20):
+        return 128, n128, 0, 1
+    return 256, n256 - rem, rem, S
 
 
-def test_plan_split_remainder_fills_the_last_round():
+def test_plan_tile_choice_and_split_remainder():
     for (M, N, K, split) in ((6144, 4096, 2048, 0), (4096, 4096, 4096, 0), (8192, 8192, 8192, 0),
                              (512, 768, 512, 0), (512, 512, 640, 2), (2048, 2048, 64, 0), (4096, 4352, 1024, 0),
                              (8192, 8192, 8192, 1), (512, 512, 512, 1), (512, 512, 128, 0), (1792, 1792, 7040, 0),
-                             (2048, 2048, 8192, 0), (8192, 8448, 8192, 0)):
-        st, i = _plan(*_gemm_descs(M, N, K), split=split)
+                             (2048, 2048, 8192, 0), (8192, 8448, 8192, 0), (300, 520, 200, 0), (6144, 4096, 2048, 1)):
+        st, i = _plan(*_gemm_descs(M, N, K), kernel=L.LT_KERNEL_TILED, split=split)
         assert st == "LT_OK" and i.kernel == L.LT_KERNEL_TILED, (M, N, K, st)
-        tiles, kt = (M // 256) * (N // 256), -(-K // 64)
-        dp, rem, S = _split_plan(tiles, kt, split)
-        assert (i.sk_tiles, i.split_k, i.grid) == (rem, S, dp + rem * S), (M, N, K, i.sk_tiles, i.split_k, i.grid)
+        tn, dp, rem, S = _tile_plan(M, N, K, split)
+        assert (i.tile_n, i.sk_tiles, i.split_k, i.grid) == (tn, rem, S, dp + rem * S), \
+            (M, N, K, i.tile_n, i.sk_tiles, i.split_k, i.grid)
         assert i.sk_workgroups == rem * S
         want_ws = ((rem * 4 + 255) // 256 * 256 + rem * S * 256 * 256 * 4) if rem else 0
         assert i.workspace_bytes == want_ws
-    # the 6144x4096x2048 workload: 384 tiles = 1.5 rounds, but K is short
-    # (32 slices): the partials would cost more than the idle half round
-    st, i = _plan(*_gemm_descs(6144, 4096, 2048))
-    assert (i.sk_tiles, i.grid) == (0, 384)
+    # the 6144x4096x2048 workload: 384 256x256 tiles = 1.5 rounds, and K is
+    # too short (32 slices) for the split to pay; 768 256x128 tiles fill
+    # three whole rounds
+    st, i = _plan(*_gemm_descs(6144, 4096, 2048, a="m", b="n"))
+    assert (i.tile_n, i.sk_tiles, i.grid) == (128, 0, 768)
+    # 8192^3: 1,024 256x256 tiles are four whole rounds
+    st, i = _plan(*_gemm_descs(8192, 8192, 8192))
+    assert (i.tile_n, i.sk_tiles, i.grid) == (256, 0, 1024)
     # 49 tiles of 110 slices: whole tiles would leave 207 CUs idle
     st, i = _plan(*_gemm_descs(1792, 1792, 7040))
-    assert (i.sk_tiles, i.split_k, i.grid) == (49, 5, 245)
+    assert (i.tile_n, i.sk_tiles, i.split_k, i.grid) == (256, 49, 5, 245)
 
 
 def test_plan_m_major_output_is_transposed():
@@ -545,13 +564,19 @@ def test_fused_epilogue_argument_checks_before_the_device():
 
 
 def test_plan_reports_the_wave_layout_of_the_data_parallel_launch():
-    """The 256x256 kernel's data-parallel launch runs 4 waves of 128x128 (one
-    per SIMD) for every operand major-ness: 8 x 8 MFMA blocks x 2 K steps per
-    wave per 64-deep K slice."""
+    """The data-parallel launch runs 4 waves (one per SIMD) for every operand
+    major-ness: 256x256 tiles as 128x128 wave tiles (8 x 8 MFMA blocks x 2 K
+    steps per wave per 64-deep K slice, 2 stages of 64 KiB), 256x128 tiles as
+    128x64 wave tiles (8 x 4 blocks, 3 stages of 48 KiB)."""
     for a, b in (("k", "k"), ("m", "k"), ("k", "n"), ("m", "n")):
-        st, i = _plan(*_gemm_descs(2048, 2048, 1024, a=a, b=b), kernel=L.LT_KERNEL_TILED)
+        st, i = _plan(*_gemm_descs(2048, 2048, 1024, a=a, b=b), kernel=L.LT_KERNEL_TILED, tile_n=256)
         assert st == "LT_OK" and i.kernel == L.LT_KERNEL_TILED, (a, b, st)
         assert (i.waves, i.wave_m, i.wave_n) == (4, 128, 128), (a, b)
         assert (i.tile_m, i.tile_n, i.tile_k, i.stages) == (256, 256, 64, 2)
         assert i.mfma_per_wave_kstep == 8 * 8 * 2 and (i.mfma_m, i.mfma_n, i.mfma_k) == (16, 16, 32)
         assert i.lds_bytes == 2 * 2 * 256 * 64 * 2
+        st, i = _plan(*_gemm_descs(2048, 2048, 1024, a=a, b=b), kernel=L.LT_KERNEL_TILED, tile_n=128)
+        assert st == "LT_OK" and (i.waves, i.wave_m, i.wave_n) == (4, 128, 64), (a, b)
+        assert (i.tile_m, i.tile_n, i.tile_k, i.stages, i.grid) == (256, 128, 64, 3, 128)
+        assert i.mfma_per_wave_kstep == 8 * 4 * 2
+        assert i.lds_bytes == 3 * (256 + 128) * 64 * 2
