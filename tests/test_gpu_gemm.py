@@ -112,7 +112,7 @@ def test_tiled_slice_counts_every_major(K, a_major, b_major, tile_n):
     res, plan, _ = run_and_check(A, B, C, D, 1.0, 0.5, kernel="tiled", split_k=1, tile=(256, tile_n),
                                  expect_kernel="tiled", label=f"slices {K // 64} {a_major}/{b_major} 256x{tile_n}")
     _ok(res)
-    assert plan["waves"] == 4 and plan["grid"] == 2 * 512 // tile_n * 2 and plan["tile_n"] == tile_n
+    assert plan["waves"] == 4 and plan["grid"] == (512 // 256) * (512 // tile_n) and plan["tile_n"] == tile_n
 
 
 def test_tiled_ragged_large_auto():
