@@ -298,3 +298,107 @@ def test_fused_epilogue_bias_rows_and_columns():
     strided = torch.tensor([10.0, 0.0, 20.0, 0.0, 30.0, 0.0, 40.0, 0.0], dtype=torch.float16)
     d, _ = og.fused_epilogue(pre, np.zeros(3), ij, strided, 2, False, None)   # every other value
     assert list(d) == [11.0, 28.0, 20.25]
+
+
+# ---------------------------------------------------------------------------
+# The tolerance itself: bound() and check_fused() against budgets worked out
+# by hand from the stated bound
+#   |D - D_ref| <= 2e-3 * (|alpha| * sum_k |a b| + |beta c|) + one output ulp
+# (and, through an activation, that budget times its Lipschitz constant),
+# never through the functions under test. Planted mutants of the oracle's
+# source must each fail one of these pins.
+# ---------------------------------------------------------------------------
+
+# (dtype, alpha, T, |beta c|, D_ref, budget)
+_BOUND_CASES = [
+    # fp16, alpha 2, T 10, |beta c| 0.5 at D_ref 1: 2e-3 * 20.5 + 2^-10
+    (torch.float16, 2.0, 10.0, 0.5, 1.0, 0.041 + 2.0 ** -10),
+    # a negative alpha counts by its magnitude; ulp of 5 in fp16 is 2^(2-10)
+    (torch.float16, -3.0, 4.0, 0.0, -5.0, 0.024 + 2.0 ** -8),
+    # fp16 below the smallest normal (2^-14): the subnormal spacing 2^-24
+    (torch.float16, 1.0, 0.0, 0.0, 6.0e-5, 2.0 ** -24),
+    # bf16 at D_ref = 0 with nothing summed: the 2^-133 floor
+    (torch.bfloat16, 1.0, 0.0, 0.0, 0.0, 2.0 ** -133),
+    # bf16 at 3: 2e-3 * (0.5 * 8 + 1) + 2^(1-7)
+    (torch.bfloat16, 0.5, 8.0, 1.0, 3.0, 0.01 + 2.0 ** -6),
+    # beta c alone (alpha 0): 2e-3 * 0.75 + ulp(0.25) = 2^(-2-10)
+    (torch.float16, 0.0, 100.0, 0.75, 0.25, 0.0015 + 2.0 ** -12),
+]
+
+# (activation, Lipschitz constant): fp16, alpha 1, T 10, |beta c| + |bias| 0.5, D_ref 1
+_FUSED_CASES = [(None, 1.0), ("relu", 1.0), ("gelu", 1.13)]
+
+
+def _pin_bound(m):
+    for dt, alpha, T, cabs, dref, want in _BOUND_CASES:
+        got = m.bound(np.array([T]), np.array([cabs]), np.array([dref]), alpha, dt)[0]
+        assert abs(got - want) <= 1e-15 * max(want, 1e-300) or got == want, (dt, alpha, T, cabs, dref, got, want)
+        # check() accepts just inside the hand budget and refuses just outside
+        for side, ok in ((0.999, True), (1.001, False)):
+            r = m.check(np.array([dref + side * want]), np.array([dref]), np.array([T]), np.array([cabs]),
+                        alpha, dt)
+            assert r.ok == ok, (dt, alpha, T, cabs, dref, side)
+
+
+def _pin_check_fused(m):
+    for act, lip in _FUSED_CASES:
+        want = lip * 2e-3 * (10.0 + 0.5) + 2.0 ** -10
+        for side, ok in ((0.999, True), (1.001, False)):
+            r = m.check_fused(np.array([1.0 + side * want]), np.array([1.0]), np.array([10.0]), np.array([0.5]),
+                              1.0, torch.float16, act)
+            assert r.ok == ok, (act, side, want)
+    # alpha enters by magnitude here too
+    want = 2e-3 * (2.0 * 10.0 + 0.5) + 2.0 ** -10
+    r = m.check_fused(np.array([1.0 + 1.001 * want]), np.array([1.0]), np.array([10.0]), np.array([0.5]),
+                      -2.0, torch.float16, "relu")
+    assert not r.ok
+    r = m.check_fused(np.array([1.0 + 0.999 * want]), np.array([1.0]), np.array([10.0]), np.array([0.5]),
+                      -2.0, torch.float16, "relu")
+    assert r.ok
+
+
+def test_bound_equals_hand_computed_budgets():
+    _pin_bound(og)
+
+
+def test_check_fused_equals_hand_computed_budgets():
+    _pin_check_fused(og)
+
+
+_BOUND_MUTANTS = {
+    "coefficient_2e-2": ("return 2e-3 * (abs(alpha) * T + Cabs)", "return 2e-2 * (abs(alpha) * T + Cabs)"),
+    "alpha_not_abs": ("return 2e-3 * (abs(alpha) * T + Cabs)", "return 2e-3 * (alpha * T + Cabs)"),
+    "beta_c_dropped": ("return 2e-3 * (abs(alpha) * T + Cabs)", "return 2e-3 * (abs(alpha) * T)"),
+    "ulp_dropped": ("+ Cabs) + ulp_out(Dref, dtype)", "+ Cabs)"),
+    "fused_lipschitz_dropped": ("b = LIPSCHITZ[act] * 2e-3", "b = 2e-3"),
+    "fused_coefficient": ("b = LIPSCHITZ[act] * 2e-3", "b = LIPSCHITZ[act] * 2e-2"),
+    "fused_alpha_not_abs": ("(abs(alpha) * T.reshape(-1) + mag)", "(alpha * T.reshape(-1) + mag)"),
+    "fused_mag_dropped": ("(abs(alpha) * T.reshape(-1) + mag)", "(abs(alpha) * T.reshape(-1))"),
+    "fused_ulp_dropped": ("+ mag) + ulp_out(Dref, dtype)", "+ mag)"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(_BOUND_MUTANTS))
+def test_bound_mutant_is_caught(name, tmp_path):
+    import importlib.util
+    src = open(og.__file__).read()
+    old, new = _BOUND_MUTANTS[name]
+    assert src.count(old) == 1, name
+    path = tmp_path / "gemm_mutant.py"
+    path.write_text(src.replace(old, new))
+    import sys
+    modname = f"oracle_gemm_mutant_{name}"
+    spec = importlib.util.spec_from_file_location(modname, path)
+    mutant = importlib.util.module_from_spec(spec)
+    sys.modules[modname] = mutant   # (its dataclasses look their module up there)
+    try:
+        spec.loader.exec_module(mutant)
+    finally:
+        sys.modules.pop(modname, None)
+    caught = 0
+    for pin in (_pin_bound, _pin_check_fused):
+        try:
+            pin(mutant)
+        except AssertionError:
+            caught += 1
+    assert caught > 0, name
