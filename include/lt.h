@@ -359,6 +359,29 @@ lt_status lt_gemm_run_ex(const lt_tensor* A, const lt_tensor* B, const lt_tensor
                          float alpha, float beta, const lt_gemm_options* opt, const lt_epilogue* epi,
                          void* workspace, size_t workspace_bytes, void* stream);
 
+/* Size of the device scratch array of lt_gemm_run_noalloc, per GPU: 64 MiB
+ * for split-K partials plus 4 KiB for arrival counters. Every plan the
+ * automatic choice makes fits (a split remainder has at most 256 segments of
+ * 256x256 fp32 partials; the skinny split needs under 2 MiB); forced splits
+ * may not. */
+#define LT_NOALLOC_SCRATCH_BYTES ((size_t)64 * 1024 * 1024 + 4096)
+
+/* lt_gemm_run_ex for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same plan and kernels, with the scratch they need (split-K partials
+ * and arrival counters) taken from a static device array of
+ * LT_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs on
+ * until the process ends; no workspace argument, and no device memory is
+ * allocated or freed by the call. LT_ERR_WORKSPACE if the plan needs more
+ * scratch than that (nothing is launched). What must start at zero is
+ * cleared on the stream by the call itself; the array keeps the last call's
+ * contents. Every call on one GPU shares that GPU's array: calls that
+ * overlap on one GPU (on different streams, or from different threads
+ * without ordering) race and give wrong results. Asynchronous on `stream`. */
+lt_status lt_gemm_run_noalloc(const lt_tensor* A, const lt_tensor* B, const lt_tensor* C, const lt_tensor* D,
+                              float alpha, float beta, const lt_gemm_options* opt, const lt_epilogue* epi,
+                              void* stream);
+
 /* Library version string. */
 const char* lt_version(void);
 

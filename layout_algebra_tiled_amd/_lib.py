@@ -11,6 +11,7 @@ import os
 
 LT_MAX_LEAVES = 32
 LT_MAX_NODES = 64
+LT_NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024 + 4096
 
 LT_OK = 0
 STATUS_NAMES = {
@@ -106,6 +107,8 @@ SIGNATURES = {
                     ctypes.c_int),
     "lt_gemm_run_ex": ([_T, _T, _T, _T, ctypes.c_float, ctypes.c_float, _P(lt_gemm_options), _P(lt_epilogue),
                         _vp, _sz, _vp], ctypes.c_int),
+    "lt_gemm_run_noalloc": ([_T, _T, _T, _T, ctypes.c_float, ctypes.c_float, _P(lt_gemm_options), _P(lt_epilogue),
+                             _vp], ctypes.c_int),
     "lt_version": ([], ctypes.c_char_p),
 }
 

@@ -14,9 +14,18 @@
 #include <algorithm>
 #include <cstring>
 
+#include <mutex>
+
 #include "gemm_kernels.hpp"
 #include "layout_host.hpp"
 #include "lt.h"
+
+// Scratch of the allocation-free entry point (lt_gemm_run_noalloc): the
+// split-K partials and arrival counters live here instead of in a caller's
+// workspace. Each GPU the library runs on holds its own copy until the
+// process ends. In host code this name is only a stand-in for the symbol:
+// kernels get the device address looked up below, never the name itself.
+static __device__ __align__(256) unsigned char scratch[LT_NOALLOC_SCRATCH_BYTES];
 
 namespace lt {
 
@@ -395,6 +404,25 @@ lt_status plan_cached(const lt_tensor* tA, const lt_tensor* tB, const lt_tensor*
     return st;
 }
 
+// The device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64] = {};
+
+lt_status scratch_address(void** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return LT_ERR_HIP;
+    if (dev < 0 || dev >= 64) return LT_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return LT_ERR_HIP;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return LT_OK;
+}
+
 }  // namespace
 }  // namespace lt
 
@@ -565,6 +593,23 @@ lt_status lt_gemm_run_ex(const lt_tensor* A, const lt_tensor* B, const lt_tensor
             return LT_ERR_INVALID_ARGUMENT;
     }
     return err == 0 ? LT_OK : LT_ERR_HIP;
+}
+
+lt_status lt_gemm_run_noalloc(const lt_tensor* A, const lt_tensor* B, const lt_tensor* C, const lt_tensor* D,
+                              float alpha, float beta, const lt_gemm_options* opt, const lt_epilogue* epi,
+                              void* stream) {
+    lt::Plan p;
+    lt_status st = lt::plan_cached(A, B, C, D, beta != 0.0f, opt, &p);
+    if (st != LT_OK) return st;
+    if (p.info.workspace_bytes > (int64_t)LT_NOALLOC_SCRATCH_BYTES) return LT_ERR_WORKSPACE;
+    if (p.info.workspace_bytes == 0 || p.empty)
+        return lt_gemm_run_ex(A, B, C, D, alpha, beta, opt, epi, nullptr, 0, stream);
+    st = lt::ensure_device();   // the architecture gate comes before the device is touched
+    if (st != LT_OK) return st;
+    void* ws = nullptr;
+    st = lt::scratch_address(&ws);
+    if (st != LT_OK) return st;
+    return lt_gemm_run_ex(A, B, C, D, alpha, beta, opt, epi, ws, LT_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 }  // extern "C"

@@ -76,6 +76,18 @@ def plan(A, B, D, C=None, beta: float = 0.0, kernel="auto", tile=None, split_k=0
 ACTIVATIONS = {None: L.LT_ACT_NONE, "none": L.LT_ACT_NONE, "relu": L.LT_ACT_RELU, "gelu": L.LT_ACT_GELU}
 
 
+def _epilogue(bias, bias_stride, bias_per_row, activation, amax) -> Optional[L.lt_epilogue]:
+    """The fused-epilogue descriptor, or None for the plain alpha/beta one."""
+    if bias is None and activation in (None, "none") and amax is None:
+        return None
+    if activation not in ACTIVATIONS:
+        raise ValueError(f"unknown activation {activation!r}")
+    if amax is not None and amax.dtype != torch.float32:
+        raise ValueError("amax must be a float32 device tensor")
+    return L.lt_epilogue(bias.data_ptr() if bias is not None else None, int(bias_stride), int(bool(bias_per_row)),
+                         ACTIVATIONS[activation], amax.data_ptr() if amax is not None else None)
+
+
 def gemm(A: torch.Tensor, B: torch.Tensor, D: torch.Tensor, C: Optional[torch.Tensor] = None,
          alpha: float = 1.0, beta: float = 0.0, *, kernel="auto", tile=None, split_k: int = 0,
          layouts: Optional[dict] = None, workspace: Optional[torch.Tensor] = None, stream=None,
@@ -107,18 +119,30 @@ def gemm(A: torch.Tensor, B: torch.Tensor, D: torch.Tensor, C: Optional[torch.Te
             workspace.record_stream(torch.cuda.ExternalStream(sid, device=D.device))
     if workspace is not None:
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
-    epi = None
-    if bias is not None or activation not in (None, "none") or amax is not None:
-        if activation not in ACTIVATIONS:
-            raise ValueError(f"unknown activation {activation!r}")
-        if amax is not None and amax.dtype != torch.float32:
-            raise ValueError("amax must be a float32 device tensor")
-        epi = L.lt_epilogue(bias.data_ptr() if bias is not None else None, int(bias_stride), int(bool(bias_per_row)),
-                            ACTIVATIONS[activation], amax.data_ptr() if amax is not None else None)
+    epi = _epilogue(bias, bias_stride, bias_per_row, activation, amax)
     L.check(L.lib().lt_gemm_run_ex(ctypes.byref(dA), ctypes.byref(dB), ctypes.byref(dC) if dC else None,
                                    ctypes.byref(dD), float(alpha), float(beta), ctypes.byref(o),
                                    ctypes.byref(epi) if epi is not None else None, ws_ptr, ws_bytes,
                                    sid), "gemm_run")
+
+
+def gemm_noalloc(A: torch.Tensor, B: torch.Tensor, D: torch.Tensor, C: Optional[torch.Tensor] = None,
+                 alpha: float = 1.0, beta: float = 0.0, *, kernel="auto", tile=None, split_k: int = 0,
+                 layouts: Optional[dict] = None, stream=None, bias: Optional[torch.Tensor] = None,
+                 bias_stride: int = 1, bias_per_row: bool = False, activation: Optional[str] = None,
+                 amax: Optional[torch.Tensor] = None) -> None:
+    """gemm() through lt_gemm_run_noalloc: no workspace, no device memory
+    allocated; the scratch comes from the library's static per-GPU array
+    (calls that overlap on one GPU race on it)."""
+    la = layouts or {}
+    dA, dB, dD = tensor_desc(A, la.get("A")), tensor_desc(B, la.get("B")), tensor_desc(D, la.get("D"))
+    dC = tensor_desc(C, la.get("C")) if C is not None else None
+    o = _opts(kernel, tile, split_k)
+    epi = _epilogue(bias, bias_stride, bias_per_row, activation, amax)
+    L.check(L.lib().lt_gemm_run_noalloc(ctypes.byref(dA), ctypes.byref(dB), ctypes.byref(dC) if dC else None,
+                                        ctypes.byref(dD), float(alpha), float(beta), ctypes.byref(o),
+                                        ctypes.byref(epi) if epi is not None else None, _stream(stream)),
+            "gemm_run_noalloc")
 
 
 def layout_eval_device(layout: Layout, out: torch.Tensor, n: Optional[int] = None, stream=None) -> None:

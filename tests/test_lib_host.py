@@ -580,3 +580,21 @@ def test_plan_reports_the_wave_layout_of_the_data_parallel_launch():
         assert (i.tile_m, i.tile_n, i.tile_k, i.stages, i.grid) == (256, 128, 64, 3, 128)
         assert i.mfma_per_wave_kstep == 8 * 4 * 2
         assert i.lds_bytes == 3 * (256 + 128) * 64 * 2
+
+
+def test_noalloc_refuses_oversized_plans_before_the_device():
+    """lt_gemm_run_noalloc refuses a plan whose scratch exceeds its static
+    array (a forced 8-way split of 256 tiles: 512 MiB of partials) with
+    LT_ERR_WORKSPACE before touching the device, and every automatic plan of
+    the tiled and skinny kernels fits it."""
+    A, B, C, D = _gemm_descs(8192, 8192, 8192)
+    o = L.lt_gemm_options()
+    o.split_k = 8
+    st = L.lib().lt_gemm_run_noalloc(ctypes.byref(A), ctypes.byref(B), None, ctypes.byref(D), 1.0, 0.0,
+                                     ctypes.byref(o), None, None)
+    assert L.STATUS_NAMES[st] == "LT_ERR_WORKSPACE"
+    for M, N, K in ((256, 256, 65536), (1792, 1792, 7040), (2304, 2304, 4096), (32, 64, 65536), (32, 8192, 8192),
+                    (7936, 8192, 8192)):
+        st, i = _plan(*_gemm_descs(M, N, K))
+        assert st == "LT_OK" and i.workspace_bytes <= L.LT_NOALLOC_SCRATCH_BYTES, (M, N, K, i.workspace_bytes)
+
