@@ -598,3 +598,14 @@ def test_noalloc_refuses_oversized_plans_before_the_device():
         st, i = _plan(*_gemm_descs(M, N, K))
         assert st == "LT_OK" and i.workspace_bytes <= L.LT_NOALLOC_SCRATCH_BYTES, (M, N, K, i.workspace_bytes)
 
+def test_oversized_explicit_layout_is_refused_before_the_library():
+    """An explicit layout that reaches past the tensor's storage is refused by
+    the binding (the C ABI sees only a pointer)."""
+    import torch
+    from layout_algebra_tiled_amd import gemm as g
+    t = torch.empty(100, dtype=torch.float16)
+    with pytest.raises(ValueError):
+        g.tensor_desc(t, Layout.make([10, 20], [20, 1]))
+    g.tensor_desc(t, Layout.make([10, 10], [10, 1]))          # exactly fits
+    with pytest.raises(ValueError):
+        g.tensor_desc(t[50:], Layout.make([10, 10], [10, 1]))  # the view starts 50 elements in
