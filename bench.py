@@ -162,11 +162,15 @@ def queued_kernel_times(run, n: int):
 
 
 class Workload:
-    def __init__(self, cfg: int, n_b: int = 1):
+    def __init__(self, cfg: int, n_b: int = 1, mnk=None):
+        import dataclasses
         import torch
         import datagen
         from layout_algebra_tiled_amd.layout import Layout
         self.c = datagen.config(cfg)
+        if mnk:
+            self.c = dataclasses.replace(self.c, M=mnk[0], N=mnk[1], K=mnk[2],
+                                         name=f"{self.c.name} at {mnk[0]}x{mnk[1]}x{mnk[2]}")
         c = self.c
         log(f"[bench] preparing workload {cfg}: {c.name}")
         A, B, C, D = c.make()
@@ -344,6 +348,24 @@ def roofline(w: Workload, plan: dict, kern_s: float, traffic):
             "frac": round(tf / PEAK_TFLOPS, 4), "traffic": traffic}
 
 
+def torch_matmul_timing(w: Workload, steps: int):
+    """torch.matmul (the vendor GEMM library) on the same operands, for scale:
+    queued launches after a warm-up, HIP events around each."""
+    import torch
+    A, B = w.A.view(), w.Bs[0].view()
+    out = torch.empty(w.c.M, w.c.N, dtype=w.c.dtype, device="cuda:0")
+    run = lambda i: torch.matmul(A, B, out=out)
+    t_end = time.perf_counter() + 1.0
+    while time.perf_counter() < t_end:
+        for _ in range(8):
+            run(0)
+        torch.cuda.synchronize()
+    ts = queued_kernel_times(run, steps)
+    mean = sum(ts) / len(ts)
+    return {"us_mean": round(mean * 1e6, 1), "us_min": round(ts[0] * 1e6, 1),
+            "TFLOP/s": round(w.c.flops() / mean / 1e12, 1)}
+
+
 def copy_probe(nbytes: int = 1 << 30, reps: int = 5):
     """A plain device copy of known size through the library's layout gather
     with the identity layout (n):(1): it reads and writes exactly nbytes per
@@ -435,6 +457,11 @@ def main():
                     help="warm up for at least this long as well as --warmup steps (clocks settle)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a 1 GiB identity-layout copy (HBM byte-counter calibration)")
+    ap.add_argument("--mnk", type=str, default=None,
+                    help="M,N,K: the headline workload's layouts and distributions at another size (profiling "
+                         "runs; the reported metric is defined at 8192^3 only)")
+    ap.add_argument("--also-torch-matmul", action="store_true",
+                    help="also time torch.matmul (the vendor GEMM library) on the same operands, for scale")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -457,7 +484,8 @@ def main():
 
     # the skinny workload's B (128 MiB) would sit in the 256 MB last-level
     # cache between steps: rotate four copies so every step streams B from HBM
-    w = Workload(args.workload, n_b=4 if args.workload == 5 else 1)
+    mnk = tuple(int(x) for x in args.mnk.split(",")) if args.mnk else None
+    w = Workload(args.workload, n_b=4 if args.workload == 5 else 1, mnk=mnk)
     plan = w.plan()
     log(f"[bench] plan: {plan['kernel_name']} tile {plan['tile_m']}x{plan['tile_n']}x{plan['tile_k']}, "
         f"wave tile {plan['wave_m']}x{plan['wave_n']}, {plan['waves']} waves, {plan['stages']} LDS stages "
@@ -501,6 +529,9 @@ def main():
                              f"{chk.worst_fraction:.3f} of budget"},
         "roofline": roofline(w, plan, kern, traffic_for(tkey)),
     }
+    if args.also_torch_matmul:
+        line["torch_matmul"] = torch_matmul_timing(w, args.steps)
+        log(f"[bench] torch.matmul on the same operands: {line['torch_matmul']}")
     if not args.only_headline:
         extra = {}
         for cfg, n_b in ((1, 1), (2, 1), (4, 1), (5, 4)):

@@ -112,31 +112,22 @@ constexpr int read_after(int q, int nr, int nq) {
 }
 
 // One MFMA operand fragment (8 16-bit values per lane). From a K-major LDS
-// tile it is one 16-byte read. From an M/N-major tile it is two transposing
-// 8-byte reads written as inline asm, which the compiler does not track: the
-// two halves stay separate registers until the explicit wait has retired the
-// reads (pin() passes each through an empty asm after that wait), and are
-// joined into the MFMA operand only when the MFMA is issued, so no copy of a
-// destination register can be placed before its data has landed.
+// tile it is one 16-byte read; from an M/N-major tile, two transposing
+// 8-byte reads (ds_read_b64_tr_b16 through the compiler's builtin, so the
+// compiler tracks them: it waits for each before its first use, and any copy
+// of the registers it makes comes after that wait).
 template <class V8, bool KMAJ>
 struct Frag;
 template <class V8>
 struct Frag<V8, true> {
     V8 v;
     __device__ __forceinline__ V8 get() const { return v; }
-    __device__ __forceinline__ void pin() {}
 };
 template <class V8>
 struct Frag<V8, false> {
     i16x4 lo, hi;
     __device__ __forceinline__ V8 get() const {
         return __builtin_bit_cast(V8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-    }
-    __device__ __forceinline__ void pin() {
-#if defined(__HIP_DEVICE_COMPILE__)
-        asm volatile("" : "+v"(lo));
-        asm volatile("" : "+v"(hi));
-#endif
     }
 };
 
@@ -145,24 +136,30 @@ struct Frag<V8, false> {
 template <class V8, int KROW_BYTES>
 __device__ __forceinline__ Frag<V8, false> read_tr(const LDS_AS char* p0) {
     Frag<V8, false> f;
-#if defined(__HIP_DEVICE_COMPILE__)
-    // Inline asm rather than the compiler's transposing-read builtin: for
-    // the builtin the compiler cannot tell that the LDS-DMA copies in flight
-    // write other bytes, and waits for all of them before each read, which
-    // exposed the whole copy latency once per slice.
-    const uint32_t a0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p0));
-    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(f.lo) : "v"(a0));
-    if constexpr (KROW_BYTES == 512)
-        asm volatile("ds_read_b64_tr_b16 %0, %1 offset:2048" : "=v"(f.hi) : "v"(a0));
-    else
-        asm volatile("ds_read_b64_tr_b16 %0, %1 offset:1024" : "=v"(f.hi) : "v"(a0));
-#else
-    (void)p0;
-    f.lo = i16x4{};
-    f.hi = i16x4{};
-#endif
+    LDS_AS char* p = const_cast<LDS_AS char*>(p0);   // (the builtin takes a non-const pointer; it only reads)
+    f.lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)p);
+    f.hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(p + 4 * KROW_BYTES));
     return f;
 }
+
+// Direct global-to-LDS copy of 16 bytes per lane (global_load_lds_dwordx4):
+// lane l reads gbase + voff + IMM and writes LDS at lds + IMM + 16*l. gbase
+// and lds are wave-uniform (SGPRs), voff a per-lane 32-bit byte offset, so
+// no address arithmetic runs per copy. Inline asm: the compiler does not
+// see these as writes to LDS, so it never waits for copies in flight before
+// an LDS read of other bytes; the kernel orders copies and reads itself
+// (vmcnt waits, then the workgroup barrier). M0 carries the LDS base and is
+// written here before every copy; nothing else in these kernels uses M0.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"   // M0 is a reserved register; see above
+template <int IMM>
+__device__ __forceinline__ void copy16(uint32_t lds, const char* gbase, uint32_t voff) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2 offset:%3"
+                 :
+                 : "s"(lds), "v"(voff), "s"(gbase), "i"(IMM)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
 
 }  // namespace
 
@@ -179,7 +176,9 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
     using OB = Operand<Cf, Cf::BKM, Cf::BN>;
     using FA = Frag<V8, Cf::AK>;
     using FB = Frag<V8, Cf::BKM>;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    // (the wave index is uniform: read it into an SGPR so that LDS bases
+    // derived from it are scalars)
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     // K slices: KT = ceil(K / BK). When BK does not divide K, the K range is
     // shifted to start at kbase = K - KT*BK < 0, so that only slice 0 is
     // partial: its first -kbase K positions are zero-filled in LDS, and every
@@ -213,6 +212,9 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
     const char* b_k0 = reinterpret_cast<const char*>(p.B0);
     auto a_lds = [&](int stage) { return smem + stage * Cf::STAGE + wave * OA::OPI * 1024; };
     auto b_lds = [&](int stage) { return smem + stage * Cf::STAGE + Cf::A_BYTES + wave * OB::OPI * 1024; };
+    auto lds_u32 = [](const char* p) {
+        return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const LDS_AS char*)p));
+    };
 
     // Copy instruction c (< IPW) of slice kt into `stage`: A's OPI, then B's.
     // (groups of four: the instruction offset is at most 4095 bytes)
@@ -221,11 +223,11 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
         if constexpr (c < OA::OPI) {
             constexpr int i = c, g = i / 4, o = (i % 4) * 1024;
             const char* ga = a_k0 + (kt0 + kt) * a_ks;
-            __builtin_amdgcn_global_load_lds((ga - o) + aoffg[i], (LDS_AS void*)(a_lds(stage) + g * 4096), 16, o, 0);
+            copy16<o>(lds_u32(a_lds(stage) + g * 4096), ga - o, aoffg[i]);
         } else {
             constexpr int i = c - OA::OPI, g = i / 4, o = (i % 4) * 1024;
             const char* gb = b_k0 + (kt0 + kt) * b_ks;
-            __builtin_amdgcn_global_load_lds((gb - o) + boffg[i], (LDS_AS void*)(b_lds(stage) + g * 4096), 16, o, 0);
+            copy16<o>(lds_u32(b_lds(stage) + g * 4096), gb - o, boffg[i]);
         }
     };
     auto issue = [&](int stage, int kt) { static_for<0, Cf::IPW>([&](auto cc) { issue_one(stage, kt, cc); }); };
@@ -238,7 +240,7 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
             constexpr int i = decltype(ic_)::value, g = i / 4, o = (i % 4) * 1024;
             char* d = a_lds(0) + g * 4096;
             if (kbase + OA::kpos(wave, lane, i) >= 0)
-                __builtin_amdgcn_global_load_lds((a_k0 - o) + aoffg[i], (LDS_AS void*)d, 16, o, 0);
+                copy16<o>(lds_u32(d), a_k0 - o, aoffg[i]);
             else
                 *(LDS_AS u32x4*)(d + o + 16 * lane) = u32x4{0u, 0u, 0u, 0u};
         });
@@ -246,7 +248,7 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
             constexpr int i = decltype(ic_)::value, g = i / 4, o = (i % 4) * 1024;
             char* d = b_lds(0) + g * 4096;
             if (kbase + OB::kpos(wave, lane, i) >= 0)
-                __builtin_amdgcn_global_load_lds((b_k0 - o) + boffg[i], (LDS_AS void*)d, 16, o, 0);
+                copy16<o>(lds_u32(d), b_k0 - o, boffg[i]);
             else
                 *(LDS_AS u32x4*)(d + o + 16 * lane) = u32x4{0u, 0u, 0u, 0u};
         });
@@ -302,20 +304,6 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
 
     FA af[2][FM];
     FB bfr[2][FN];
-    // With an M-/N-major operand (transposing reads in inline asm, which the
-    // compiler does not track): every LDS read in flight has landed, then
-    // the fragments of buffer `buf` pass through empty asm statements, so no
-    // use (or copy) of them is scheduled above the wait. Called at the top
-    // of each K step; it also retires every read of a stage before the
-    // barrier that frees it.
-    auto frag_wait = [&](auto bufc) {
-        if constexpr (!(Cf::AK && Cf::BKM)) {
-            constexpr int buf = decltype(bufc)::value;
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            static_for<0, FM>([&](auto i) { af[buf][decltype(i)::value].pin(); });
-            static_for<0, FN>([&](auto j) { bfr[buf][decltype(j)::value].pin(); });
-        }
-    };
     auto read_step = [&](int stage, int s, int buf) {
 #pragma unroll
         for (int b = 0; b < FM; ++b) af[buf][b] = read_a(stage, s, b);
@@ -362,10 +350,9 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
     // a next slice but no refill, and the final slice.
     constexpr int NMF = FM * FN, NRD = (Cf::AK ? FM : 2 * FM) + (Cf::BKM ? FN : 2 * FN);
     int stage = 0;
-    auto slice_s = [&](auto has_next, auto refill, int t) {
+    auto slice_s = [&](auto has_next, auto refill, int t, auto par) {
         static_for<0, KS>([&](auto sc) {
-            constexpr int s = decltype(sc)::value, cur = s & 1, nxt = cur ^ 1;
-            frag_wait(ic<cur>{});
+            constexpr int s = decltype(sc)::value, cur = (decltype(par)::value + s) & 1, nxt = cur ^ 1;
             if constexpr (s + 1 < KS) {
                 read_step(stage, s + 1, nxt);
             } else if constexpr (decltype(has_next)::value) {
@@ -417,15 +404,14 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
         else
             asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(c) : "v"(x), "v"(y));
     };
-    auto slice_x = [&](auto has_next, auto refill, int t) {
+    auto slice_x = [&](auto has_next, auto refill, int t, auto par) {
         static_for<0, KS>([&](auto sc) {
-            constexpr int s = decltype(sc)::value, cur = s & 1, nxt = cur ^ 1;
+            constexpr int s = decltype(sc)::value, cur = (decltype(par)::value + s) & 1, nxt = cur ^ 1;
             constexpr bool last = s + 1 == KS;
             constexpr bool reads = !last || decltype(has_next)::value;
             constexpr bool copies = last && decltype(refill)::value;
             constexpr int NR = reads ? FM + FN : 0, NC = copies ? Cf::IPW : 0, NQ = FM * FN;
             static_assert(Cf::IPW <= NQ && 4 * (FM + FN) <= 3 * NQ, "one copy and one read per MFMA at most");
-            frag_wait(ic<cur>{});
             int rstage = stage, rs = s + 1;
             if constexpr (last && decltype(has_next)::value) {
                 if constexpr (decltype(refill)::value)
@@ -447,11 +433,23 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
         });
         stage = stage + 1 == S ? 0 : stage + 1;
     };
+    // slice t (local index); with one K step per slice its fragment buffer
+    // is t's parity, a compile-time index in each of two copies of the body
     auto slice = [&](auto has_next, auto refill, int t) {
-        if constexpr (Cf::EXPLICIT)
-            slice_x(has_next, refill, t);
-        else
-            slice_s(has_next, refill, t);
+        auto go = [&](auto par) {
+            if constexpr (Cf::EXPLICIT)
+                slice_x(has_next, refill, t, par);
+            else
+                slice_s(has_next, refill, t, par);
+        };
+        if constexpr (KS % 2 == 0) {
+            go(ic<0>{});
+        } else {
+            if (t & 1)
+                go(ic<1>{});
+            else
+                go(ic<0>{});
+        }
     };
     const std::true_type yes{};
     const std::false_type no{};

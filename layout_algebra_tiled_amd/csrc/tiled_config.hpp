@@ -35,7 +35,10 @@ struct TCfg {
     static constexpr int OPB = B_BYTES / 1024 / NW;           // ... for B
     static constexpr int IPW = OPA + OPB;                     // ... per slice
     static_assert(A_BYTES % (1024 * NW) == 0 && B_BYTES % (1024 * NW) == 0, "copy must split evenly over waves");
-    static_assert(KS % 2 == 0, "fragment double buffer assumes an even K-step count");
+    // Fragments are double-buffered over K steps: with an even step count per
+    // slice every slice starts on buffer 0; with one step per slice the
+    // buffer alternates with the slice's parity.
+    static_assert(KS == 1 || KS % 2 == 0, "one K step per slice, or an even count");
     static_assert(IPW * (S - 1) < 64, "vmcnt counts at most 63 outstanding loads");
     static_assert(BM <= 256 && BN <= 256 && (BM == 256 || BM == 128) && (BN == 256 || BN == 128), "tile");
 };

@@ -4,11 +4,17 @@ tools).
 
 1. Every tiled-kernel variant is present as device code with a host-side
    launch stub, so no configuration the planner can pick is missing.
-2. The transposing LDS reads of M/N-major operands are inline asm that the
-   compiler does not track. For each such read, every control-flow path from
-   it must reach an `s_waitcnt lgkmcnt(0)` before any instruction names one of
-   its destination registers (a read of them would see stale data, a write
-   would be overwritten when the load lands)."""
+2. The transposing LDS reads of M/N-major operands land in registers some
+   time after they issue. For each such read, every control-flow path from it
+   must retire it with an `s_waitcnt lgkmcnt(N)` before any instruction names
+   one of its destination registers (a read of them would see stale data, a
+   write would be overwritten when the load lands). LDS operations retire in
+   order, so lgkmcnt(N) retires the read once N or more LDS operations were
+   issued after it on that path (with a scalar load in between, which may
+   retire out of order, only lgkmcnt(0) counts).
+3. The tiled kernels' direct-to-LDS copies are inline asm that set M0
+   themselves: there, M0 is written only by the `s_mov_b32 m0, sN` right
+   before each copy, and read by nothing else."""
 
 import os
 import re
@@ -112,11 +118,14 @@ def _successors(insts, i, index_of, func_addr):
     return nxt
 
 
+_LGKM = re.compile(r"lgkmcnt\((\d+)\)")
+
+
 def unwaited_uses(insts, base):
     """(read, instruction) pairs where an instruction names a destination
-    register of a transposing read on some path from it before an
-    lgkmcnt(0) wait (or the kernel ends first). Returns (violations,
-    number of reads checked)."""
+    register of a transposing read on some path from it before the read is
+    retired (or the kernel ends first). Returns (violations, number of reads
+    checked)."""
     index_of = {a: i for i, (a, _, _, _) in enumerate(insts)}
     bad, n = [], 0
     for r, (_, mn, ops, _) in enumerate(insts):
@@ -124,20 +133,39 @@ def unwaited_uses(insts, base):
             continue
         n += 1
         dest = _regs(ops.split(",")[0])
-        seen, todo = set(), _successors(insts, r, index_of, base)
+        # state: (instruction, LDS ops issued since the read (capped), scalar load since)
+        seen, todo = set(), [(j, 0, False) for j in _successors(insts, r, index_of, base)]
         while todo:
-            j = todo.pop()
-            if j in seen:
+            j, after, smem = todo.pop()
+            if (j, after, smem) in seen:
                 continue
-            seen.add(j)
+            seen.add((j, after, smem))
             _, mnj, opsj, _ = insts[j]
-            if mnj == "s_waitcnt" and "lgkmcnt(0)" in opsj:
-                continue
+            if mnj == "s_waitcnt":
+                m = _LGKM.search(opsj)
+                if m and (int(m.group(1)) == 0 or (not smem and after >= int(m.group(1)))):
+                    continue
             if _regs(opsj) & dest or mnj == "s_endpgm":
                 bad.append((insts[r][:3], insts[j][:3]))
                 continue
-            todo.extend(_successors(insts, j, index_of, base))
+            after = min(after + (1 if mnj.startswith("ds_") else 0), 64)
+            smem = smem or mnj.startswith("s_load") or mnj.startswith("s_buffer_load")
+            todo.extend((k, after, smem) for k in _successors(insts, j, index_of, base))
     return bad, n
+
+
+def m0_misuse(insts):
+    """Instructions that name M0 other than the copies' own `s_mov_b32 m0,
+    sN` immediately followed by a direct-to-LDS copy."""
+    bad = []
+    for i, (_, mn, ops, _) in enumerate(insts):
+        if not re.search(r"\bm0\b", ops):
+            continue
+        ok = (mn == "s_mov_b32" and ops.startswith("m0, s") and i + 1 < len(insts)
+              and insts[i + 1][1] == "global_load_lds_dwordx4")
+        if not ok:
+            bad.append(insts[i][:3])
+    return bad
 
 
 _GOOD = """0000000000001000 <k>:
@@ -155,10 +183,16 @@ _GOOD = """0000000000001000 <k>:
 
 def test_checker_accepts_waited_reads_and_catches_early_use():
     """The path walk itself, on a hand-written fragment: both paths from the
-    reads wait before v4 is copied; moving the copy above the wait, or
-    taking the wait off one branch path, must be reported."""
+    reads wait before v4 is copied; moving the copy above the wait, taking
+    the wait off one branch path, or waiting with a count that leaves the
+    read in flight, must be reported."""
     insts = _functions(_GOOD)["k"]
     assert unwaited_uses(insts, 0x1000) == ([], 2)
+    # lgkmcnt(1) after the second read retires the first one only
+    partial = _GOOD.replace("s_waitcnt lgkmcnt(0)                                       // 00000000101C",
+                            "s_waitcnt lgkmcnt(1)                                       // 00000000101C")
+    bad, _ = unwaited_uses(_functions(partial)["k"], 0x1000)
+    assert bad and all(b[0][2].startswith("v[6:7]") for b in bad)
     early = _GOOD.replace("v_mfma_f32_16x16x32_bf16 a[0:3], v[8:11]", "v_mfma_f32_16x16x32_bf16 a[0:3], v[4:7]")
     bad, _ = unwaited_uses(_functions(early)["k"], 0x1000)
     assert len(bad) == 2 and all(b[1][1].startswith("v_mfma") for b in bad)
@@ -173,6 +207,8 @@ def test_transposing_reads_are_waited_before_use(disasm):
     for key, insts in funcs.items():
         bad, n = unwaited_uses(insts, addrs[key])
         assert not bad, f"{key[1]}: {bad[:3]}"
+        if "gemm_tiled" in key[1]:   # the kernels whose copies are inline asm
+            assert not m0_misuse(insts), f"{key[1]}: {m0_misuse(insts)[:3]}"
         if n:
             kernels += 1
             reads += n
