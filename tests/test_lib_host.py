@@ -325,7 +325,7 @@ def test_plan_kernel_choice_for_the_workloads():
     st, i = _plan(*_gemm_descs(4096, 4096, 4096, L.LT_F16), bnz=1)
     assert st == "LT_OK" and i.kernel == L.LT_KERNEL_TILED and i.grid == 256
     st, i = _plan(*_gemm_descs(8192, 8192, 8192))
-    assert st == "LT_OK" and i.kernel == L.LT_KERNEL_TILED and i.grid == 1024
+    assert st == "LT_OK" and i.kernel == L.LT_KERNEL_TILED and (i.tiles, i.grid) == (1024, 1024)
     assert (i.tile_m, i.tile_n) == (256, 256) and i.tile_k in (32, 64) and i.waves in (4, 8)
     assert i.waves * i.wave_m * i.wave_n == 256 * 256 and i.stages >= 2
     st, i = _plan(*_gemm_descs(32, 8192, 8192))
@@ -385,7 +385,7 @@ def test_plan_closed_forms_reproduce_page_arithmetic():
     assert i.lds_bytes == i.stages * stage_bytes(i.tile_m, i.tile_n, i.tile_k, 2)
     assert (i.mfma_m, i.mfma_n, i.mfma_k) in ((32, 32, 16), (16, 16, 32))
     assert i.mfma_per_wave_kstep == instr_per_wave(i.wave_m, i.wave_n, i.tile_k, i.mfma_m, i.mfma_n, i.mfma_k)
-    assert i.grid / 256 == 4.0   # 1,024 tiles on 256 CUs: whole waves
+    assert i.tiles / 256 == 4.0   # 1,024 tiles on 256 CUs: whole waves
 
 
 def test_plan_validation_statuses():
@@ -458,7 +458,7 @@ def test_plan_ragged_shapes_on_the_tiled_kernel():
         assert st == "LT_OK" and i.kernel == expect, (M, N, K, st, i.kernel)
         if expect == L.LT_KERNEL_TILED:
             tiles = -(-M // 256) * -(-N // i.tile_n)
-            assert i.grid == tiles - i.sk_tiles + i.sk_workgroups
+            assert i.tiles == tiles and i.grid == tiles - i.sk_tiles + i.sk_workgroups
 
 
 def _tile_plan(M, N, K, split=0, want_n=0):
@@ -502,6 +502,7 @@ def test_plan_tile_choice_and_split_remainder():
         tn, dp, rem, S = _tile_plan(M, N, K, split)
         assert (i.tile_n, i.sk_tiles, i.split_k, i.grid) == (tn, rem, S, dp + rem * S), \
             (M, N, K, i.tile_n, i.sk_tiles, i.split_k, i.grid)
+        assert i.tiles == dp + rem
         assert i.sk_workgroups == rem * S
         want_ws = ((rem * 4 + 255) // 256 * 256 + rem * S * 256 * 256 * 4) if rem else 0
         assert i.workspace_bytes == want_ws
@@ -509,10 +510,10 @@ def test_plan_tile_choice_and_split_remainder():
     # too short (32 slices) for the split to pay; 768 256x128 tiles fill
     # three whole rounds
     st, i = _plan(*_gemm_descs(6144, 4096, 2048, a="m", b="n"))
-    assert (i.tile_n, i.sk_tiles, i.grid) == (128, 0, 768)
-    # 8192^3: 1,024 256x256 tiles are four whole rounds
+    assert (i.tile_n, i.sk_tiles, i.tiles, i.grid) == (128, 0, 768, 768)
+    # 8192^3: 1,024 256x256 tiles are four whole rounds, one per workgroup
     st, i = _plan(*_gemm_descs(8192, 8192, 8192))
-    assert (i.tile_n, i.sk_tiles, i.grid) == (256, 0, 1024)
+    assert (i.tile_n, i.sk_tiles, i.tiles, i.grid) == (256, 0, 1024, 1024)
     # 49 tiles of 110 slices: whole tiles would leave 207 CUs idle
     st, i = _plan(*_gemm_descs(1792, 1792, 7040))
     assert (i.tile_n, i.sk_tiles, i.split_k, i.grid) == (256, 49, 5, 245)
