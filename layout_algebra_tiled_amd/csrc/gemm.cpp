@@ -214,8 +214,13 @@ lt_status make_plan(const lt_tensor* tA, const lt_tensor* tB, const lt_tensor* t
     const bool tiled_pays = p.M * p.N >= (int64_t)ts.bm * ts.bn &&
                             2 * tm_ * ts.bm * tn_ * ts.bn <= 3 * p.M * p.N;
     int split = (opt && opt->split_k > 0) ? opt->split_k : 0;
+    // The skinny kernel addresses 32 rows of A and 32 columns of B as a
+    // uniform base plus a 32-bit per-lane byte offset.
+    const bool skinny_offsets_fit = (31 * (p.A.e0 == 1 ? 0 : p.A.s0) + 256) * 2 < (int64_t(1) << 32) &&
+                                    (31 * p.B.s1 + 256) * 2 < (int64_t(1) << 32);
     auto skinny_ok_for = [&](int s) {
-        if (!(p.M <= 32 && p.a_k && p.b_k && d_n && c_n && p.N % kSkinnyBN == 0 && s >= 1)) return false;
+        if (!(p.M <= 32 && p.a_k && p.b_k && d_n && c_n && p.N % kSkinnyBN == 0 && s >= 1 && skinny_offsets_fit))
+            return false;
         const int64_t per = (int64_t)s * kSkinnyKQuantum;
         return p.K > 0 && p.K % per == 0;
     };
@@ -349,17 +354,17 @@ lt_status make_plan(const lt_tensor* tA, const lt_tensor* tB, const lt_tensor* t
             in.tile_n = kSkinnyBN;
             in.tile_k = static_cast<int32_t>(p.K / split);
             in.wave_m = 32;
-            in.wave_n = kSkinnyBN;
+            in.wave_n = kSkinnyBN / kSkinnyWaves;   // the two waves split the columns
             in.waves = kSkinnyWaves;
             in.split_k = split;
             in.grid = (p.N / kSkinnyBN) * split;
             in.tiles = p.N / kSkinnyBN;
-            in.lds_bytes = kSkinnyLdsBytes;
-            in.stages = kSkinnyStages;
+            in.lds_bytes = lt::SkinnyCfg::LDS;
+            in.stages = lt::SkinnyCfg::R;
             in.workspace_bytes = split > 1 ? (int64_t)split * 32 * p.N * 4 : 0;
-            in.mfma_per_wave_kstep = 4;   // one 32x32x16 per 16 of a 64-deep K block
-            in.mfma_m = in.mfma_n = 32;
-            in.mfma_k = 16;
+            in.mfma_per_wave_kstep = 4;   // two 16x16x32 (the two 16-row halves of A) per 32 of a 64-deep K block
+            in.mfma_m = in.mfma_n = 16;
+            in.mfma_k = 32;
             break;
         }
         default:
@@ -587,7 +592,7 @@ lt_status lt_gemm_run_ex(const lt_tensor* A, const lt_tensor* B, const lt_tensor
             a.alpha = alpha;
             a.beta = beta;
             a.split_k = p.info.split_k;
-            a.k_per_wave = (int)(p.K / ((int64_t)a.split_k * lt::kSkinnyWaves));
+            a.k_per_wg = (int)(p.K / a.split_k);
             a.epi = ea;
             err = lt::launch_skinny(dt, a, stream);
             break;

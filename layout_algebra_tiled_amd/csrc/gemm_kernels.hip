@@ -97,119 +97,158 @@ __global__ __launch_bounds__(256) void gemm_wave16(Wave16Args p) {
 // exactly once at full bandwidth ("CUTLASS, in depth", "Worked example: tile
 // choice and wave quantisation": narrow N tile plus split-K for decode-like
 // shapes, or treat the product as memory-bound). Each workgroup owns 32
-// columns of N; its four waves split the workgroup's K range. Every wave owns
-// a private ring of kSkinnyStages LDS slots; a slot holds a 64-deep K slice of
-// the 32 A rows and of the 32 B columns (4 KiB each), filled by direct
-// global-to-LDS loads in which 8 lanes cover one row's 128 contiguous bytes,
-// so every load instruction reads 8 whole cache lines. One explicit vmcnt
-// wait per slot and no barriers; the four waves' partial sums meet in LDS at
-// the end. With split_k > 1 the K range is split over workgroups too and fp32
-// partials go to a workspace that skinny_reduce sums.
+// columns of N and its two waves 16 of them each, with all 32 rows of A (two
+// 16x16x32 MFMAs per 32 of K share the wave's B fragment), so A, read by
+// every workgroup and served by L2, crosses to a CU once per 32 columns. The
+// pair streams its K range through a ring of SkinnyCfg::R slots in LDS, each
+// 128 deep of the 32 A rows and 32 B columns, filled by direct global-to-LDS
+// copies in which 16 lanes cover the 256 contiguous bytes of one row or
+// column (the longer the run per column, the closer the stream gets to the
+// HBM peak: 32 columns 16 KiB apart are open at once per workgroup). Each
+// wave copies its own 16 columns and 16 of the A rows; per slot it waits for
+// its own copies, then a workgroup barrier makes the partner's visible and
+// frees the slot read before. With split_k > 1 the K range is split over
+// workgroups and fp32 partials go to a workspace that skinny_reduce sums.
 // ---------------------------------------------------------------------------
 
 template <int DT>
 __global__ __launch_bounds__(64 * kSkinnyWaves, 1) void gemm_skinny(SkinnyArgs p) {
+#if defined(__HIP_DEVICE_COMPILE__)   // generic lambdas around the LDS-copy builtin: device pass only
     extern __shared__ __attribute__((aligned(1024))) char smem[];
     using V8 = typename Tr<DT>::V8;
-    constexpr int R = kSkinnyStages;
-    constexpr int HALF = 32 * 64 * 2;                 // 32 rows x 64 K x 16 bit
-    constexpr int SLOT = 2 * HALF;                    // A rows, then B columns
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    using SC = SkinnyCfg;
+    constexpr int R = SC::R, SK = SC::SK, CB = SC::CB, HALF = SC::HALF, SLOT = SC::SLOT, NW = SC::NW;
+    constexpr int LPC = CB / 16;                      // lanes per row in a copy (16)
+    constexpr int CPI = 64 / LPC;                     // rows per copy instruction (4)
+    constexpr int NH = NW / 2;                        // copies per wave per half slot (4)
+    static_assert(LPC == 16 && NH * CPI == 16 && kSkinnyWaves == 2, "a wave copies 16 rows of each half");
+    const int lane = threadIdx.x & 63;
+    const int ch = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // column half
     const int n0 = blockIdx.x * kSkinnyBN, sk = blockIdx.y;
-    const int kbeg = (sk * kSkinnyWaves + wave) * p.k_per_wave;
-    const int nst = p.k_per_wave / 64;                // slots to stream
-    char* ring = smem + wave * R * SLOT;
+    const int kbeg = sk * p.k_per_wg;
+    const int nst = p.k_per_wg / SK;                  // slots to stream
+    char* ring = smem;
 
-    // Copy: instruction j fills rows 8j .. 8j+7 of each half-slot, 8 lanes
-    // per row; both halves use the K-major tile layout (128-byte rows of 8
-    // chunks, chunk ^ ((row >> 1) & 7)), so each lane fetches the logical
-    // chunk stored at its position. Rows of A past M repeat row M-1 (their
-    // outputs are never stored).
-    const uint16_t* ga[4];
-    const uint16_t* gb[4];
+    // Both halves of a slot (A rows, then B columns) hold 32 256-byte rows of
+    // 16-byte chunks; chunk q of row c is stored at position q ^ (c & 15), so
+    // the 16 lanes of a fragment read that share q and take consecutive c
+    // land on 16 distinct 16-byte bank groups.
+    // Copy j of a half, lane L fills byte (4 ch + j)*1024 + 16L: row c =
+    // 16 ch + 4 j + L/16, stored position L%16, i.e. logical chunk
+    // (L%16) ^ (c & 15). Every address is a workgroup-uniform base plus a
+    // 32-bit per-lane byte offset (32 rows of A or columns of B span far less
+    // than 4 GiB). Rows of A past M repeat row M-1 (their outputs are never
+    // stored).
+    const int cl = lane / LPC, cs = lane % LPC;
+    uint32_t aoff[NH], boff[NH];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int row = 8 * j + (lane >> 3);
-        const int lchunk = dev::KTile<64>::at(row, lane & 7) - 8 * row;
-        ga[j] = p.A + (int64_t)min(row, p.M - 1) * p.lda + kbeg + 8 * lchunk;
-        gb[j] = p.B + (int64_t)(n0 + row) * p.ldb + kbeg + 8 * lchunk;
+    for (int j = 0; j < NH; ++j) {
+        const int c = 16 * ch + j * CPI + cl;
+        aoff[j] = 2u * (uint32_t)(min(c, p.M - 1) * p.lda + 8 * (cs ^ (c & 15)));
+        boff[j] = 2u * (uint32_t)(c * p.ldb + 8 * (cs ^ (c & 15)));
     }
-    // Fragment offsets inside a half-slot: row lane%32, K chunk 2s + lane/32
-    const int frow = lane & 31, fh = lane >> 5;
-    int foff[4];
+    // 16x16x32 MFMA step s of a slot covers K 32s .. 32s+31: lane (r, g)
+    // holds 8 of them, K 32s + 8g .. +7, of B column 16 ch + r (the row
+    // operand) and of A row 16 mb + r for the two 16-row blocks mb of A.
+    const int fr = lane & 15, fg = lane >> 4;
+    int afo[SC::KSTEPS], bfo[SC::KSTEPS];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) foff[s] = 16 * dev::KTile<64>::at(frow, 2 * s + fh);
+    for (int s = 0; s < SC::KSTEPS; ++s) {
+        const int q = 4 * s + fg;
+        afo[s] = fr * CB + 16 * (q ^ fr);                                      // row fr (+16 for mb = 1)
+        bfo[s] = HALF + (16 * ch + fr) * CB + 16 * (q ^ ((16 * ch + fr) & 15));
+    }
 
-    // Each wave starts its walk over its K range at a slot picked by a small
-    // hash of (workgroup, wave) and wraps around. B's columns are 2^k bytes
-    // apart for power-of-two K, so without the rotation every wave of the GPU
-    // streams addresses with the same low bits at the same time and piles
-    // onto a few DRAM channels (measured: 36.6 us unrotated vs 31.0 us on the
-    // 32x8192x8192 workload). The K sum is order-free.
-    const int rot = (blockIdx.x * 13 + wave * 7 + (blockIdx.x >> 3)) % nst;
-    auto issue = [&](int slot, int st) {
-        char* dst = ring + slot * SLOT;
+    // Each workgroup starts its walk over its K range at a slot picked by a
+    // small hash of its index and wraps around. B's columns are 2^k bytes
+    // apart for power-of-two K, so without the rotation every workgroup of
+    // the GPU streams addresses with the same low bits at the same time and
+    // piles onto a few DRAM channels (measured: 36.6 us unrotated vs 31.0 us
+    // on the 32x8192x8192 workload with an earlier ring layout). The K sum is
+    // order-free.
+    const int rot = (blockIdx.x * 13 + (blockIdx.x >> 3)) % nst;
+    auto issue = [&](auto slot_c, int st) {
+        constexpr int slot = decltype(slot_c)::value;
+        char* dst = ring + slot * SLOT + ch * NH * 1024;
         int sr = st + rot;
         sr = sr >= nst ? sr - nst : sr;
+        const int64_t k = kbeg + sr * SK;
+        const char* ab = reinterpret_cast<const char*>(p.A + k);
+        const char* bb = reinterpret_cast<const char*>(p.B + (int64_t)n0 * p.ldb + k);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const void* a = ga[j] + sr * 64;
-            const void* b = gb[j] + sr * 64;
-            __builtin_amdgcn_global_load_lds(a, (LDS_AS void*)(dst + j * 1024), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds(b, (LDS_AS void*)(dst + HALF + j * 1024), 16, 0, 0);
+        for (int j = 0; j < NH; ++j)
+            __builtin_amdgcn_global_load_lds(ab + aoff[j], (LDS_AS void*)(dst + j * 1024), 16, 0, 0);
+#pragma unroll
+        for (int j = 0; j < NH; ++j)
+            __builtin_amdgcn_global_load_lds(bb + boff[j], (LDS_AS void*)(dst + HALF + j * 1024), 16, 0, 0);
+    };
+    f32x4 acc[2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto compute = [&](auto slot_c) {
+        constexpr int slot = decltype(slot_c)::value;
+        const char* sl = ring + slot * SLOT;
+        V8 a0[SC::KSTEPS], a1[SC::KSTEPS], b[SC::KSTEPS];
+#pragma unroll
+        for (int s = 0; s < SC::KSTEPS; ++s) {
+            b[s] = *(const LDS_AS V8*)(sl + bfo[s]);
+            a0[s] = *(const LDS_AS V8*)(sl + afo[s]);
+            a1[s] = *(const LDS_AS V8*)(sl + afo[s] + 16 * CB);
+        }
+        // B as the row operand: each lane ends with four consecutive N
+#pragma unroll
+        for (int s = 0; s < SC::KSTEPS; ++s) {
+            acc[0] = Tr<DT>::mfma16(b[s], a0[s], acc[0]);
+            acc[1] = Tr<DT>::mfma16(b[s], a1[s], acc[1]);
         }
     };
 
-    f32x16 acc;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
-
-    for (int r = 0; r < R - 1 && r < nst; ++r) issue(r, r);
-    int slot = 0;
-    for (int t = 0; t < nst; ++t) {
-        if (t + R - 1 < nst) {
-            issue(slot == 0 ? R - 1 : slot - 1, t + R - 1);
-            // slot t landed: 8 loads per slot, R-1 newer slots may fly
-            __builtin_amdgcn_s_waitcnt(((8 * (R - 1)) & 15) | (0x7 << 4) | (0xf << 8) | (((8 * (R - 1)) >> 4) << 14));
-        } else {
-            __builtin_amdgcn_s_waitcnt(0 | (0x7 << 4) | (0xf << 8));
+    // Iteration t: wait for this wave's copies of slot t, barrier (the
+    // partner's copies of slot t are in; both waves are done with slot t-1),
+    // refill slot t-1's ring slot with slot t+R-1, compute slot t. R - 1
+    // slots are in flight while slot t computes.
+    // Steady state: every slot of a trip issues unconditionally.
+    int t0 = 0;
+    if (nst >= 2 * R - 1) {
+        static_for<0, R - 1>([&](auto r) { issue(r, r.value); });
+        for (; t0 + 2 * R - 1 <= nst; t0 += R) {
+            static_for<0, R>([&](auto r) {
+                LT_WAIT_VM(NW * (R - 2));
+                __builtin_amdgcn_s_barrier();
+                issue(ic<(r.value + R - 1) % R>{}, t0 + r.value + R - 1);
+                compute(r);
+            });
         }
-        const char* sl = ring + slot * SLOT;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            V8 a = *(const LDS_AS V8*)(sl + foff[s]);
-            V8 b = *(const LDS_AS V8*)(sl + HALF + foff[s]);
-            // B as the row operand: each lane ends with four consecutive N
-            acc = Tr<DT>::mfma32(b, a, acc);
+    } else {
+        static_for<0, R - 1>([&](auto r) {
+            if (r.value < nst) issue(r, r.value);
+        });
+    }
+    // The last slots (fewer than 2R - 1): the same steps, then drain. nst
+    // and t0 are the same for both waves, so both meet every barrier.
+    static_for<0, 2 * R - 2>([&](auto i) {
+        const int t = t0 + i.value;
+        if (t < nst) {
+            if (t + R - 2 < nst) {
+                LT_WAIT_VM(NW * (R - 2));
+            } else {
+                LT_WAIT_VM(0);
+            }
+            __builtin_amdgcn_s_barrier();
+            if (t + R - 1 < nst) issue(ic<(i.value + R - 1) % R>{}, t + R - 1);
+            compute(ic<i.value % R>{});
         }
-        slot = slot + 1 == R ? 0 : slot + 1;
-    }
+    });
 
-    // Partial sums of the four waves meet in LDS (each wave's own ring).
-    __builtin_amdgcn_s_waitcnt(0 | (0x7 << 4) | (0xf << 8));
-    float* red = reinterpret_cast<float*>(ring);
-    if (wave > 0) {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) red[v * 64 + lane] = acc[v];
-    }
-    __syncthreads();
-    if (wave != 0) return;
-#pragma unroll
-    for (int w = 1; w < kSkinnyWaves; ++w) {
-        const float* o = reinterpret_cast<const float*>(smem + w * R * SLOT);
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc[v] += o[v * 64 + lane];
-    }
-
-    // lane holds m = lane % 32 and n = n0 + 8g + 4*(lane/32) + 0..3
-    const int m = frow;
+    // lane holds m = 16 mb + lane % 16 and n = n0 + 16 ch + 4 (lane / 16) + 0..3
+    const int n = n0 + 16 * ch + 4 * fg;
     if (p.split_k == 1 && p.epi.fused) {
         float amax = 0.0f;
-        if (m < p.M) {
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int n = n0 + 8 * g + 4 * fh;
-                const float v[4] = {acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]};
+        for (int mb = 0; mb < 2; ++mb) {
+            const int m = 16 * mb + fr;
+            if (m < p.M) {
+                const float v[4] = {acc[mb][0], acc[mb][1], acc[mb][2], acc[mb][3]};
                 store4_fused<DT>(p.D, p.C, (int64_t)m * p.ldd + n, (int64_t)m * p.ldc + n, v, 4, p.alpha, p.beta,
                                  p.epi, m, n, &amax);
             }
@@ -217,22 +256,19 @@ __global__ __launch_bounds__(64 * kSkinnyWaves, 1) void gemm_skinny(SkinnyArgs p
         if (p.epi.amax) amax_commit(p.epi.amax, amax);
         return;
     }
-    if (m >= p.M) return;
-    if (p.split_k == 1) {
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const int n = n0 + 8 * g + 4 * fh;
-            store4<DT>(p.D, p.C, (int64_t)m * p.ldd + n, (int64_t)m * p.ldc + n, acc[4 * g], acc[4 * g + 1],
-                       acc[4 * g + 2], acc[4 * g + 3], p.alpha, p.beta);
-        }
-    } else {
-        float* w = p.ws + ((int64_t)sk * 32 + m) * p.N;
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const int n = n0 + 8 * g + 4 * fh;
-            *reinterpret_cast<f32x4*>(w + n) = f32x4{acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]};
+    for (int mb = 0; mb < 2; ++mb) {
+        const int m = 16 * mb + fr;
+        if (m >= p.M) continue;
+        if (p.split_k == 1) {
+            store4<DT>(p.D, p.C, (int64_t)m * p.ldd + n, (int64_t)m * p.ldc + n, acc[mb][0], acc[mb][1],
+                       acc[mb][2], acc[mb][3], p.alpha, p.beta);
+        } else {
+            float* w = p.ws + ((int64_t)sk * 32 + m) * p.N;
+            *reinterpret_cast<f32x4*>(w + n) = acc[mb];
         }
     }
+#endif
 }
 
 // Sum of the split_k fp32 partials, then the epilogue: one thread per four
@@ -323,18 +359,20 @@ int launch_tiled(int dtype, bool a_kmajor, bool b_kmajor, int tile_n, const Tile
     return b_kmajor ? launch_tiled_20_1(a, tile_n, stream) : launch_tiled_20_0(a, tile_n, stream);
 }
 
-int launch_skinny(int dtype, const SkinnyArgs& a, void* stream) {
+template <int DT>
+int launch_skinny_dt(const SkinnyArgs& a, hipStream_t s) {
+    static std::atomic<uint64_t> attr;
     dim3 grid(a.N / kSkinnyBN, a.split_k), block(64 * kSkinnyWaves);
+    constexpr int lds = SkinnyCfg::LDS;
+    if (const int e = set_lds_limit_once(reinterpret_cast<const void*>(&gemm_skinny<DT>), lds, attr)) return e;
+    hipLaunchKernelGGL(gemm_skinny<DT>, grid, block, lds, s, a);
+    return 0;
+}
+
+int launch_skinny(int dtype, const SkinnyArgs& a, void* stream) {
     hipStream_t s = static_cast<hipStream_t>(stream);
-    static std::atomic<uint64_t> attr[2];
-    const int which = dtype == LT_F16 ? 0 : 1;
-    const void* k = which == 0 ? reinterpret_cast<const void*>(&gemm_skinny<LT_F16>)
-                               : reinterpret_cast<const void*>(&gemm_skinny<LT_BF16>);
-    if (const int e = set_lds_limit_once(k, kSkinnyLdsBytes, attr[which])) return e;
-    if (dtype == LT_F16)
-        hipLaunchKernelGGL(gemm_skinny<LT_F16>, grid, block, kSkinnyLdsBytes, s, a);
-    else
-        hipLaunchKernelGGL(gemm_skinny<LT_BF16>, grid, block, kSkinnyLdsBytes, s, a);
+    const int le = dtype == LT_F16 ? launch_skinny_dt<LT_F16>(a, s) : launch_skinny_dt<LT_BF16>(a, s);
+    if (le) return le;
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.split_k == 1) return static_cast<int>(e);
     const int64_t quads = (int64_t)a.M * (a.N / 4);

@@ -78,16 +78,33 @@ struct SkinnyArgs {
     int M, N, K;
     float alpha, beta;
     int split_k;
-    int k_per_wave;               // K elements per wave (a multiple of 64)
+    int k_per_wg;                 // K elements per workgroup (a multiple of 128)
     EpiArgs epi;
 };
 
-constexpr int kSkinnyWaves = 4;     // waves per workgroup (split the K range)
+constexpr int kSkinnyWaves = 2;     // waves per workgroup (16 of its columns each)
 constexpr int kSkinnyBN = 32;       // columns of N per workgroup
-constexpr int kSkinnyStages = 5;    // LDS ring slots per wave (64 K of A and B each)
-constexpr int kSkinnyLdsBytes = kSkinnyWaves * kSkinnyStages * 2 * 32 * 64 * 2;   // 160 KiB
-// K per wave must be a whole number of 64-deep slots
-constexpr int kSkinnyKQuantum = kSkinnyWaves * 64;
+// The two waves of a skinny workgroup take 16 of its 32 columns each and
+// share one LDS ring. A slot of the ring holds 128 deep of the 32 A rows and
+// the 32 B columns (256 contiguous bytes of each row or column); each wave
+// copies its 16 B columns and 16 of the A rows. The ring depth keeps the
+// slots in flight within the 6-bit vmcnt and the ring within 160 KiB of LDS.
+struct SkinnyCfg {
+    static constexpr int SK = 128;                 // K per slot
+    static constexpr int CB = 2 * SK;              // bytes of one row or column per slot
+    static constexpr int HALF = 32 * CB;           // bytes of the A (or B) half of a slot
+    static constexpr int SLOT = 2 * HALF;          // bytes of one slot
+    static constexpr int NW = SLOT / 2048;         // 16-byte-per-lane copies per wave per slot
+    static constexpr int KSTEPS = SK / 32;         // 16x16x32 MFMA steps per slot
+    static constexpr int R_VM = 1 + 63 / NW;
+    static constexpr int R_LDS = 160 * 1024 / SLOT;
+    static constexpr int R = R_VM < R_LDS ? R_VM : R_LDS;   // ring slots: R - 1 slots in flight
+    static constexpr int LDS = R * SLOT;           // bytes per workgroup
+    static_assert(R >= 3, "the ring issues a slot after the barrier that frees it");
+};
+// The K range of a workgroup must be a whole number of 128-deep slots (kept
+// at 256, a multiple of that, for the eligibility rule)
+constexpr int kSkinnyKQuantum = 256;
 
 // Compile-time shape of the tiled kernel the planner launches.
 struct TiledShape {

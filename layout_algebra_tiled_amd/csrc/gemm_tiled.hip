@@ -70,23 +70,6 @@ __device__ __forceinline__ void work_of(int wg, const TiledArgs& p, int KT, int*
     *seg = s;
 }
 
-// s_waitcnt with vmcnt = n (0 <= n <= 63, a constant), other counters
-// untouched. (A macro: a __device__ helper template around the target builtin
-// would not be instantiable in the host compilation pass.)
-#define LT_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (0x7 << 4) | (0xf << 8) | (((n) >> 4) << 14))
-
-template <int I>
-using ic = std::integral_constant<int, I>;
-
-// Compile-time loop: f(ic<I>) for I in [B, E).
-template <int B, int E, class F>
-__host__ __device__ __forceinline__ void static_for(F&& f) {
-    if constexpr (B < E) {
-        f(ic<B>{});
-        static_for<B + 1, E>(f);
-    }
-}
-
 // f(i, j) for every accumulator block, i < FM, j < FN, with i and j as
 // compile-time constants: unrolled whatever the block count, so the
 // accumulator array never needs a memory home.

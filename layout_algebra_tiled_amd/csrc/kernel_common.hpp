@@ -6,11 +6,29 @@
 
 #include <atomic>
 #include <cstdint>
+#include <type_traits>
 
 #include "gemm_kernels.hpp"
 #include "lt.h"
 
 namespace lt {
+
+// s_waitcnt with vmcnt = n (0 <= n <= 63, a constant), other counters
+// untouched. (A macro: a __device__ helper template around the target builtin
+// would not be instantiable in the host compilation pass.)
+#define LT_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (0x7 << 4) | (0xf << 8) | (((n) >> 4) << 14))
+
+template <int I>
+using ic = std::integral_constant<int, I>;
+
+// Compile-time loop: f(ic<I>) for I in [B, E).
+template <int B, int E, class F>
+__host__ __device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (B < E) {
+        f(ic<B>{});
+        static_for<B + 1, E>(f);
+    }
+}
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;

@@ -252,11 +252,16 @@ def test_loop_scratch_checker_finds_a_reload_in_a_loop():
 def test_tiled_kernels_keep_scratch_out_of_the_k_loop(disasm):
     """The tiled kernels keep every value of the K loop in registers: a
     spill there costs a memory round trip per slice. Outside it (index
-    set-up, the epilogue) a few dwords may spill."""
+    set-up, the epilogue) a few dwords may spill. The skinny kernels (A's
+    fragments of the slots in flight held in registers) do not spill at all."""
     funcs, addrs, _ = disasm
     meta = disasm_meta()
     tiled = [k for k in funcs if "gemm_tiled" in k[1]]
     assert len(tiled) == 24
+    skinny = [k for k in funcs if "gemm_skinny" in k[1]]
+    assert len(skinny) == 2
+    for key in skinny:
+        assert meta[key[1]]["priv"] == 0, (key[1], meta[key[1]])
     for key in tiled:
         assert meta[key[1]]["priv"] <= 16, (key[1], meta[key[1]])
         if meta[key[1]]["priv"]:
