@@ -163,10 +163,12 @@ __global__ __launch_bounds__(64 * kSkinnyWaves, 1) void gemm_skinny(SkinnyArgs p
     // small hash of its index and wraps around. B's columns are 2^k bytes
     // apart for power-of-two K, so without the rotation every workgroup of
     // the GPU streams addresses with the same low bits at the same time and
-    // piles onto a few DRAM channels (measured: 36.6 us unrotated vs 31.0 us
-    // on the 32x8192x8192 workload with an earlier ring layout). The K sum is
-    // order-free.
-    const int rot = (blockIdx.x * 13 + (blockIdx.x >> 3)) % nst;
+    // piles onto a few DRAM channels. The hash matters: streaming this
+    // kernel's B pattern alone (32 columns of 16 KiB per workgroup, 256
+    // workgroups) takes 32.3 us with no rotation, 30.3 us with start slot
+    // g % 64, 24.4 us with (13 g + g/8) % 64 and 23.0 us with the
+    // (41 g + 7 (g/32)) % 64 used here. The K sum is order-free.
+    const int rot = (blockIdx.x * 41 + (blockIdx.x >> 5) * 7) % nst;
     auto issue = [&](auto slot_c, int st) {
         constexpr int slot = decltype(slot_c)::value;
         char* dst = ring + slot * SLOT + ch * NH * 1024;
@@ -224,16 +226,18 @@ __global__ __launch_bounds__(64 * kSkinnyWaves, 1) void gemm_skinny(SkinnyArgs p
             if (r.value < nst) issue(r, r.value);
         });
     }
-    // The last slots (fewer than 2R - 1): the same steps, then drain. nst
-    // and t0 are the same for both waves, so both meet every barrier.
+    // The last slots (fewer than 2R - 1): the same steps; once nothing is
+    // left to issue, each slot waits only for itself (min(R - 2, nst-1-t)
+    // newer slots may still fly), so the last slots' MFMAs overlap the
+    // arrival of the ones after them. nst and t0 are the same for both
+    // waves, so both meet every barrier.
     static_for<0, 2 * R - 2>([&](auto i) {
         const int t = t0 + i.value;
         if (t < nst) {
-            if (t + R - 2 < nst) {
-                LT_WAIT_VM(NW * (R - 2));
-            } else {
-                LT_WAIT_VM(0);
-            }
+            const int newer = min(R - 2, nst - 1 - t);
+            static_for<0, R - 1>([&](auto c) {
+                if (newer == c.value) LT_WAIT_VM(NW * c.value);
+            });
             __builtin_amdgcn_s_barrier();
             if (t + R - 1 < nst) issue(ic<(i.value + R - 1) % R>{}, t + R - 1);
             compute(ic<i.value % R>{});
