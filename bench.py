@@ -182,7 +182,7 @@ def queued_block_time(run, n: int):
 
 
 class Workload:
-    def __init__(self, cfg: int, n_b: int = 1, mnk=None):
+    def __init__(self, cfg: int, n_b: int = 1, mnk=None, beta=None):
         import dataclasses
         import torch
         import datagen
@@ -191,6 +191,8 @@ class Workload:
         if mnk:
             self.c = dataclasses.replace(self.c, M=mnk[0], N=mnk[1], K=mnk[2],
                                          name=f"{self.c.name} at {mnk[0]}x{mnk[1]}x{mnk[2]}")
+        if beta is not None:
+            self.c = dataclasses.replace(self.c, beta=beta, name=f"{self.c.name} with beta={beta}")
         c = self.c
         log(f"[bench] preparing workload {cfg}: {c.name}")
         A, B, C, D = c.make()
@@ -480,6 +482,8 @@ def main():
     ap.add_argument("--mnk", type=str, default=None,
                     help="M,N,K: the headline workload's layouts and distributions at another size (profiling "
                          "runs; the reported metric is defined at 8192^3 only)")
+    ap.add_argument("--beta", type=float, default=None,
+                    help="the headline workload with another beta (profiling runs)")
     ap.add_argument("--also-torch-matmul", action="store_true",
                     help="also time torch.matmul (the vendor GEMM library) on the same operands, for scale")
     args = ap.parse_args()
@@ -505,7 +509,7 @@ def main():
     # the skinny workload's B (128 MiB) would sit in the 256 MB last-level
     # cache between steps: rotate four copies so every step streams B from HBM
     mnk = tuple(int(x) for x in args.mnk.split(",")) if args.mnk else None
-    w = Workload(args.workload, n_b=4 if args.workload == 5 else 1, mnk=mnk)
+    w = Workload(args.workload, n_b=4 if args.workload == 5 else 1, mnk=mnk, beta=args.beta)
     plan = w.plan()
     log(f"[bench] plan: {plan['kernel_name']} tile {plan['tile_m']}x{plan['tile_n']}x{plan['tile_k']}, "
         f"wave tile {plan['wave_m']}x{plan['wave_n']}, {plan['waves']} waves, {plan['stages']} LDS stages "
@@ -515,8 +519,12 @@ def main():
     flops = w.c.flops()
     value = flops / wall / 1e12
     achieved = flops / kern / 1e12
+    # after the timed region: the same launches queued back to back between
+    # one pair of events (no event between launches)
+    b2b = queued_block_time(w.run, args.steps)
     chk = w.check()
-    log(f"[bench] {value:.1f} TFLOP/s wall, kernel {kern * 1e6:.1f} us = {achieved:.1f} TFLOP/s; check: {chk}")
+    log(f"[bench] {value:.1f} TFLOP/s wall, kernel {kern * 1e6:.1f} us = {achieved:.1f} TFLOP/s "
+        f"(back to back {b2b * 1e6:.1f} us); check: {chk}")
     if not chk.ok:
         raise SystemExit(f"bench result failed the sampled check: {chk}")
     tkey = f"{plan['kernel_name']}:workload{args.workload}"
@@ -539,7 +547,8 @@ def main():
                    "grid": plan["grid"], "pct_of_peak": round(100 * value / PEAK_TFLOPS, 2),
                    "kernel_us": {"mean": round(kern * 1e6, 1),
                                  "median": round(w.kernel_times[len(w.kernel_times) // 2] * 1e6, 1),
-                                 "min": round(w.kernel_times[0] * 1e6, 1)},
+                                 "min": round(w.kernel_times[0] * 1e6, 1),
+                                 "back_to_back": round(b2b * 1e6, 1)},
                    "warmup_s": args.warmup_seconds,
                    "sclk_mhz_under_load": w.sclk_mhz,
                    "board_power_w_under_load": w.power_w,
