@@ -60,7 +60,9 @@ typedef enum lt_status {
     LT_ERR_CAPACITY = 12           /* result needs more leaves/nodes than lt_layout holds, or text buffer too small */
 } lt_status;
 
-/* Static description of a status code (never NULL). */
+/* Static description of a status code (never NULL). Every call reports a
+ * status and the caller checks it, as the pages ask of can_implement
+ * [P3 "Failure modes": always check the return status; P1 "Pitfalls"]. */
 const char* lt_status_string(lt_status s);
 
 /* ------------------------------------------------------------------------ */
@@ -92,7 +94,9 @@ typedef struct lt_layout {
     int8_t tree[LT_MAX_NODES];
 } lt_layout;
 
-/* Check that L is well formed (tree consistent, extents >= 1, strides >= 0). */
+/* Check that L is well formed: the tree is consistent and shape and stride
+ * are congruent [P4 "A shape is a tree"; P2 3.5.4], extents >= 1, strides
+ * >= 0. Returns LT_OK or LT_ERR_INVALID_LAYOUT; writes nothing. */
 lt_status lt_layout_validate(const lt_layout* L);
 
 /* Parse the printed form, e.g. "((16,16),(16,8)):((128,1),(2048,16))".
@@ -105,7 +109,11 @@ lt_status lt_layout_parse(const char* text, lt_layout* out);
 lt_status lt_layout_format(const lt_layout* L, char* buf, size_t cap, size_t* needed);
 
 /* A flat layout with `rank` leaves as its top-level modes (rank 1 gives a
- * bare "s:d" root). */
+ * bare "s:d" root): the make_layout(make_shape(...), make_stride(...)) of the
+ * pages [P2 3.5.3; P1 "Two programs: the algebra, then the GEMM"]. shape and
+ * stride are host arrays of `rank` entries; 1 <= rank <= LT_MAX_LEAVES, else
+ * LT_ERR_INVALID_ARGUMENT; a negative extent or stride gives
+ * LT_ERR_INVALID_LAYOUT. */
 lt_status lt_make_layout(int32_t rank, const int64_t* shape, const int64_t* stride, lt_layout* out);
 
 /* Compact strides: first mode fastest (the natural, colexicographic default
@@ -113,10 +121,16 @@ lt_status lt_make_layout(int32_t rank, const int64_t* shape, const int64_t* stri
 lt_status lt_make_colmajor(int32_t rank, const int64_t* shape, lt_layout* out);
 lt_status lt_make_rowmajor(int32_t rank, const int64_t* shape, lt_layout* out);
 
-/* Concatenate n layouts as the top-level modes of a new layout. */
+/* Concatenate n layouts as the top-level modes of a new layout: shapes and
+ * strides nest, so a mode may itself be a tuple [P4 "A shape is a tree"; P3
+ * "CuTe: layouts as functions"]. LT_ERR_CAPACITY if the result needs more
+ * than LT_MAX_LEAVES leaves or LT_MAX_NODES nodes. */
 lt_status lt_make_tuple(int32_t n, const lt_layout* modes, lt_layout* out);
 
-/* Top-level mode i of L (a leaf root has one mode, itself). */
+/* Top-level mode i of L (a leaf root has one mode, itself): CuTe's
+ * layout<i>, e.g. the tile and tile-grid modes of a zipped divide [P1 "A
+ * layout is a shape and a stride"]. LT_ERR_INVALID_ARGUMENT if i < 0 or
+ * i >= rank. */
 lt_status lt_mode(const lt_layout* L, int32_t i, lt_layout* out);
 
 /* size = product of extents; cosize = largest offset reached + 1, the memory
@@ -302,7 +316,9 @@ typedef struct lt_gemm_plan_info {
                                 plus split_k - 1 more per split tile) */
 } lt_gemm_plan_info;
 
-/* Validate and plan without launching. Checks: dtypes (A, B fp16 or bf16
+/* Validate and plan without launching: the can_implement half of the
+ * pages' check [P3 "A complete Hopper GEMM with the builder API"; P1
+ * "Pitfalls"]. Checks: dtypes (A, B fp16 or bf16
  * alike; C and D of one 16-bit type), shapes (A (M,K), B (K,N), C/D (M,N)),
  * each mode a single stride, a stride-1 mode per operand, 16-byte aligned
  * bases and other strides a multiple of 8 elements (LT_ERR_MISALIGNED_OPERAND),
@@ -384,7 +400,9 @@ lt_status lt_gemm_run_noalloc(const lt_tensor* A, const lt_tensor* B, const lt_t
                               float alpha, float beta, const lt_gemm_options* opt, const lt_epilogue* epi,
                               void* stream);
 
-/* Library version string. */
+/* Library version string (static storage, never NULL). The pages' kernels
+ * carry their architecture in the build [P1 "Results"]; this library is built
+ * for gfx950 only, and the string names that target. */
 const char* lt_version(void);
 
 #ifdef __cplusplus
