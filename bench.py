@@ -437,8 +437,10 @@ def layout_map_timing(reps: int = 20):
 
 def split_remainder_timing(M: int, N: int, K: int, reps: int = 20):
     """A bf16 shape whose tiles fill no whole round of the 256 CUs, timed with
-    the last round's tiles whole (split_k=1) and split into K segments (the
-    planner's choice), plus a sampled fp64 check of the split result."""
+    the split turned off (split_k=1: the planner then takes whole tiles of
+    its choice) and with the planner's choice (the last round's 256x256
+    tiles split into K segments), plus a sampled fp64 check of the split
+    result."""
     import torch
     import datagen
     from layout_algebra_tiled_amd import gemm as g
@@ -595,8 +597,8 @@ def main():
             log(f"[bench] workload {cfg}: {rec}")
             del x
             torch.cuda.empty_cache()
-        extra["split remainder (1792x1792x7040, 49 tiles)"] = split_remainder_timing(1792, 1792, 7040)
-        log(f"[bench] split remainder: {extra['split remainder (1792x1792x7040, 49 tiles)']}")
+        extra["split remainder (2048x2048x8192, 64 tiles)"] = split_remainder_timing(2048, 2048, 8192)
+        log(f"[bench] split remainder: {extra['split remainder (2048x2048x8192, 64 tiles)']}")
         extra["layout map"] = layout_map_timing()
         log(f"[bench] layout map: {extra['layout map']}")
         line["extra"] = extra

@@ -271,9 +271,10 @@ lt_status make_plan(const lt_tensor* tA, const lt_tensor* tB, const lt_tensor* t
             //   256x256, data-parallel: ceil(n256/kCUs) * KT * 2;
             //   256x256 with the last round's rem tiles split into S K
             //     segments (S = kCUs/rem, at most 8, at least 4 slices
-            //     each): whole rounds, ceil(KT/S), and about 20 slices for a
-            //     256x256 fp32 partial written and read back, all times 2;
-            //     taken when it saves a tenth;
+            //     each): whole rounds, ceil(KT/S), and 12 slices for each of
+            //     the S-1 fp32 partials the last segment reads back through
+            //     the coherent path (measured: 58 us for 4 partials, 125 us
+            //     for 7), all times 2; taken when it saves 3 %;
             //   256x128: ceil(n128/kCUs) * KT * 23/20 (a 256x128 tile reads
             //     a sixth more LDS bytes per flop and has half the work to
             //     hide its prologue and epilogue behind).
@@ -289,8 +290,8 @@ lt_status make_plan(const lt_tensor* tA, const lt_tensor* tB, const lt_tensor* t
                 if (rem != 0) {
                     S = std::min<int64_t>({kCUs / rem, 8, KTt / 4});
                     if (S >= 2) {
-                        const int64_t t_split = (n256 / kCUs * KTt + (KTt + S - 1) / S + 20) * 2;
-                        if (10 * t_split < 9 * c256)
+                        const int64_t t_split = (n256 / kCUs * KTt + (KTt + S - 1) / S + 12 * (S - 1)) * 2;
+                        if (100 * t_split < 97 * c256)
                             c256 = t_split;
                         else
                             S = 1;

@@ -465,7 +465,8 @@ def _tile_plan(M, N, K, split=0, want_n=0):
     """The planner's rule, written out, in K-slice times of a 256x128 tile:
     256x256 tiles cost 2 per slice; their whole rounds of 256 tiles stay
     data-parallel and the last round's rem tiles are split into S K segments
-    when that saves a tenth (20 slices for the partials) or when forced;
+    when that saves 3 % (12 slices per partial the last segment reads back)
+    or when forced;
     256x128 tiles cost 23/20 per slice and are never split. Returns
     (tile_n, data-parallel tiles, split tiles, S)."""
     kt = -(-K // 64)
@@ -476,8 +477,8 @@ def _tile_plan(M, N, K, split=0, want_n=0):
         if rem:
             S = min(256 // rem, 8, kt // 4)
             if S >= 2:
-                t_split = (n256 // 256 * kt + -(-kt // S) + 20) * 2
-                if 10 * t_split < 9 * c256:
+                t_split = (n256 // 256 * kt + -(-kt // S) + 12 * (S - 1)) * 2
+                if 100 * t_split < 97 * c256:
                     c256 = t_split
                 else:
                     S = 1
@@ -514,9 +515,16 @@ def test_plan_tile_choice_and_split_remainder():
     # 8192^3: 1,024 256x256 tiles are four whole rounds, one per workgroup
     st, i = _plan(*_gemm_descs(8192, 8192, 8192))
     assert (i.tile_n, i.sk_tiles, i.tiles, i.grid) == (256, 0, 1024, 1024)
-    # 49 tiles of 110 slices: whole tiles would leave 207 CUs idle
+    # 49 256x256 tiles of 110 slices: a 5-way split would pay 4 partials'
+    # read-back (measured 90.3 us); 98 whole 256x128 tiles win (80.2 us)
     st, i = _plan(*_gemm_descs(1792, 1792, 7040))
-    assert (i.tile_n, i.sk_tiles, i.split_k, i.grid) == (256, 49, 5, 245)
+    assert (i.tile_n, i.sk_tiles, i.split_k, i.grid) == (128, 0, 1, 98)
+    # 64 256x256 tiles of 128 slices: 4 segments each (256 workgroups)
+    st, i = _plan(*_gemm_descs(2048, 2048, 8192))
+    assert (i.tile_n, i.sk_tiles, i.split_k, i.grid) == (256, 64, 4, 256)
+    # 1,056 tiles: four whole rounds and 32 tiles split 8 ways (a 4 % saving)
+    st, i = _plan(*_gemm_descs(8192, 8448, 8192))
+    assert (i.tile_n, i.sk_tiles, i.split_k, i.grid) == (256, 32, 8, 1024 + 256)
 
 
 def test_plan_m_major_output_is_transposed():
