@@ -310,6 +310,31 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
         for (int v = 0; v < Mf::NACC; ++v) acc[i][j][v] = 0.0f;
     });
 
+    // ---- C prefetch (256x128 tiles, 3 stages, beta != 0, plain epilogue,
+    // a whole tile, at least 3 slices): the 64 KiB C tile is copied into LDS
+    // while the last slices run, into the two stages that no longer receive
+    // slices: rows 0..191 (48 KiB) into slice NS-3's stage after that
+    // slice's barrier, rows 192..255 into slice NS-2's stage after its
+    // barrier. Chunk q (8 elements) of C row r sits at position q ^ (r mod
+    // 16) of its 256-byte row, so the epilogue's 16 lanes that read one
+    // column group of 16 consecutive rows hit 16 distinct bank groups. Copy k
+    // (0..15) of wave w fills 1 KiB: rows 16k + 4w .. 16k + 4w + 3, lane l
+    // row 16k + 4w + l/16, stored position l%16.
+    constexpr bool CPF_CFG = !SPLIT && Cf::EXPLICIT && S == 3 && Cf::BN == 128 && Cf::BM == 256;
+    constexpr int CROW = Cf::BN * 2;                  // bytes of one C row
+    constexpr int CX_ROWS = Cf::STAGE / CROW;         // rows that fit one stage (192)
+    static_assert(!CPF_CFG || (CX_ROWS == 192 && Cf::NW == 4), "C prefetch layout");
+    const bool cpf = CPF_CFG && p.beta != 0.0f && !p.epi.fused && m0 + Cf::BM <= p.M && n0 + Cf::BN <= p.N &&
+                     NS >= S && (int64_t)p.ldc * 2 * Cf::BM < (int64_t(1) << 32);
+    auto issue_c = [&](int st, auto kc) {   // copy k of the C tile into stage st (k >= 12: rows 192..255)
+        constexpr int k = decltype(kc)::value;
+        constexpr int slot = k < 12 ? k : k - 12;
+        const uint32_t cvoff =
+            2u * (uint32_t)((wave * 4 + lane / 16) * p.ldc + 8 * ((lane % 16) ^ ((wave * 4 + lane / 16) & 15)));
+        const char* c_tile = reinterpret_cast<const char*>(p.C + (int64_t)(m0 + 16 * k) * p.ldc + n0);
+        copy16<0>(lds_u32(smem + st * Cf::STAGE + (slot * 4 + wave) * 1024), c_tile, cvoff);
+    };
+
     // ---- prologue: slices 0 .. S-1
     if (kbase < 0 && kt0 == 0)
         issue_first_partial();
@@ -387,18 +412,25 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
         else
             asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(c) : "v"(x), "v"(y));
     };
-    auto slice_x = [&](auto has_next, auto refill, int t, auto par) {
+    // cpc: 0, or 1 / 2 for the slice that also copies the first 12 / last 4
+    // copies of the C tile (into its own stage, after its barrier)
+    auto slice_x = [&](auto has_next, auto refill, int t, auto par, auto cpc) {
+        constexpr int CP = decltype(cpc)::value;
         static_for<0, KS>([&](auto sc) {
             constexpr int s = decltype(sc)::value, cur = (decltype(par)::value + s) & 1, nxt = cur ^ 1;
             constexpr bool last = s + 1 == KS;
             constexpr bool reads = !last || decltype(has_next)::value;
             constexpr bool copies = last && decltype(refill)::value;
-            constexpr int NR = reads ? FM + FN : 0, NC = copies ? Cf::IPW : 0, NQ = FM * FN;
+            constexpr int NCP = !last ? 0 : CP == 1 ? 12 : CP == 2 ? 4 : 0;
+            constexpr int NR = reads ? FM + FN : 0, NC = copies ? Cf::IPW : NCP, NQ = FM * FN;
             static_assert(Cf::IPW <= NQ && 4 * (FM + FN) <= 3 * NQ, "one copy and one read per MFMA at most");
+            static_assert(CP == 0 || (!decltype(refill)::value && decltype(has_next)::value), "C copies");
             int rstage = stage, rs = s + 1;
             if constexpr (last && decltype(has_next)::value) {
                 if constexpr (decltype(refill)::value)
                     LT_WAIT_VM(Cf::IPW * (S - 2));   // slice t+1 landed (S-2 newer slices may fly)
+                else if constexpr (CP == 2)
+                    LT_WAIT_VM(12);                  // slice t+1 landed; the first 12 C copies may fly
                 else
                     LT_WAIT_VM(0);
                 __syncthreads();   // slice t+1 visible to all; slice t's stage free
@@ -409,7 +441,12 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
                 constexpr int q = decltype(qc)::value;
                 mfma_one(cur, qc);
                 constexpr int c = copy_after(q, NC, NQ);
-                if constexpr (c >= 0) issue_one(stage, t + S, ic<c>{});
+                if constexpr (c >= 0) {
+                    if constexpr (copies)
+                        issue_one(stage, t + S, ic<c>{});
+                    else
+                        issue_c(stage, ic<CP == 1 ? c : 12 + c>{});
+                }
                 constexpr int r = read_after(q, NR, NQ);
                 if constexpr (r >= 0) read_one(rstage, rs, nxt, ic<r>{});
             });
@@ -418,10 +455,10 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
     };
     // slice t (local index); with one K step per slice its fragment buffer
     // is t's parity, a compile-time index in each of two copies of the body
-    auto slice = [&](auto has_next, auto refill, int t) {
+    auto slice = [&](auto has_next, auto refill, int t, auto cpc) {
         auto go = [&](auto par) {
             if constexpr (Cf::EXPLICIT)
-                slice_x(has_next, refill, t, par);
+                slice_x(has_next, refill, t, par, cpc);
             else
                 slice_s(has_next, refill, t, par);
         };
@@ -439,55 +476,6 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
     // the zeroed accumulators are written by VALU moves: wait states before
     // the first inline-asm MFMA reads them (the compiler does not see it as one)
     if constexpr (Cf::EXPLICIT) asm volatile("s_nop 7" ::: "memory");
-    int t = 0;
-    for (; t + S < NS; ++t) slice(yes, yes, t);   // refill slice t+S
-    for (; t + 1 < NS; ++t) slice(yes, no, t);    // slices already in flight
-    slice(no, no, t);                             // the last slice
-    // MFMA results before any VALU or memory instruction reads them
-    if constexpr (Cf::EXPLICIT) asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
-
-    // ---- split-K segment: publish the fp32 partial; the segment that
-    // arrives last adds the others' and goes on to the epilogue. No waiting:
-    // the others simply end. The partials and the arrival count cross XCDs,
-    // whose L2s are not coherent with each other: they are written and read
-    // with agent-scope relaxed atomics (the coherent path, past this XCD's
-    // L2), so no fence has to write back or invalidate a whole L2 while
-    // other tiles are running. Order: every store of the partial completes
-    // (vmcnt 0, then the barrier) before the count is incremented, and the
-    // last segment issues its reads only after the increment returned.
-    if constexpr (SPLIT) {
-        const int skt = lin - p.dp_tiles, NSPL = p.sk_splits;
-        // block (i, j) of split s2: register v of thread t at v*NT + t, so
-        // that one store (load) instruction covers 256 contiguous bytes
-        auto part = [&](int s2, int i, int j) {
-            return p.partials + (((int64_t)skt * NSPL + s2) * (FM * FN) + (i * FN + j)) * (Cf::NT * Mf::NACC) +
-                   threadIdx.x;
-        };
-        for_blocks<FM, FN>([&](auto i, auto j) {
-            float* q = part(seg, i, j);
-#pragma unroll
-            for (int v = 0; v < Mf::NACC; ++v)
-                __hip_atomic_store(q + v * Cf::NT, acc[i][j][v], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        });
-        LT_WAIT_VM(0);
-        __syncthreads();   // every store of the partial is complete; the LDS ring is free
-        int* flag = reinterpret_cast<int*>(smem);
-        if (threadIdx.x == 0)
-            *flag = __hip_atomic_fetch_add(&p.counters[skt], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __syncthreads();
-        if (*flag != NSPL - 1) return;
-        for (int s2 = 0; s2 < NSPL; ++s2) {
-            if (s2 == seg) continue;
-            for_blocks<FM, FN>([&](auto i, auto j) {
-                const float* q = part(s2, i, j);
-#pragma unroll
-                for (int v = 0; v < Mf::NACC; ++v)
-                    acc[i][j][v] += __hip_atomic_load(q + v * Cf::NT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            });
-        }
-        if (threadIdx.x == 0) __hip_atomic_store(&p.counters[skt], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-
     // ---- epilogue: block (i, j), registers 4g..4g+3 hold row m = lane % MF
     // and four consecutive columns of the MF x MF block. A tile on a ragged
     // edge stores only the outputs inside (M, N). With beta != 0 every C load
@@ -517,6 +505,21 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
             for_blocks<FM, FN>([&](auto i, auto j) {
 #pragma unroll
                 for (int g = 0; g < NG; ++g) cv[i][j][g] = u32x2{0u, 0u};
+            });
+        } else if (CPF_CFG && !EDGE && cpf) {
+            // the C tile is in LDS: rows < 192 in slice NS-3's stage, the
+            // rest in slice NS-2's
+            LT_WAIT_VM(0);
+            __syncthreads();   // every wave's C copies landed
+            const int sx = (NS - 3) % S, sy = (NS - 2) % S;
+            for_blocks<FM, FN>([&](auto i, auto j) {
+                const int r = arow0 + i * Cf::MF + Mf::out_col(lane);
+                const char* row = smem + (r < CX_ROWS ? sx * Cf::STAGE + r * CROW : sy * Cf::STAGE + (r - CX_ROWS) * CROW);
+#pragma unroll
+                for (int g = 0; g < NG; ++g) {
+                    const int c = brow0 + j * Cf::MF + Mf::out_row(lane, 4 * g);
+                    cv[i][j][g] = *(const LDS_AS u32x2*)(row + 16 * ((c >> 3) ^ (r & 15)) + 2 * (c & 7));
+                }
             });
         } else {
             load_c(std::integral_constant<bool, EDGE>{});   // a whole tile loads with no branch per block
@@ -623,6 +626,71 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
         });
         if (e.amax) amax_commit(e.amax, amax);
     };
+    int t = 0;
+    for (; t + S < NS; ++t) slice(yes, yes, t, ic<0>{});   // refill slice t+S
+    // The C-prefetch path runs its last slices and its epilogue on its own:
+    // no control flow joins the two paths while MFMA results are in flight
+    // (at a join the compiler may copy accumulators, and it cannot see the
+    // inline-asm MFMAs' wait states).
+    if constexpr (CPF_CFG) {
+        if (cpf) {   // S == 3 and NS >= 3: slices NS-3 and NS-2 copy the C tile
+            slice(yes, no, t, ic<1>{});
+            ++t;
+            slice(yes, no, t, ic<2>{});
+            ++t;
+            slice(no, no, t, ic<0>{});
+            asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+            epilogue(std::false_type{});   // a whole tile, beta != 0, plain epilogue
+            return;
+        }
+    }
+    for (; t + 1 < NS; ++t) slice(yes, no, t, ic<0>{});   // slices already in flight
+    slice(no, no, t, ic<0>{});                            // the last slice
+    // MFMA results before any VALU or memory instruction reads them
+    if constexpr (Cf::EXPLICIT) asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+
+    // ---- split-K segment: publish the fp32 partial; the segment that
+    // arrives last adds the others' and goes on to the epilogue. No waiting:
+    // the others simply end. The partials and the arrival count cross XCDs,
+    // whose L2s are not coherent with each other: they are written and read
+    // with agent-scope relaxed atomics (the coherent path, past this XCD's
+    // L2), so no fence has to write back or invalidate a whole L2 while
+    // other tiles are running. Order: every store of the partial completes
+    // (vmcnt 0, then the barrier) before the count is incremented, and the
+    // last segment issues its reads only after the increment returned.
+    if constexpr (SPLIT) {
+        const int skt = lin - p.dp_tiles, NSPL = p.sk_splits;
+        // block (i, j) of split s2: register v of thread t at v*NT + t, so
+        // that one store (load) instruction covers 256 contiguous bytes
+        auto part = [&](int s2, int i, int j) {
+            return p.partials + (((int64_t)skt * NSPL + s2) * (FM * FN) + (i * FN + j)) * (Cf::NT * Mf::NACC) +
+                   threadIdx.x;
+        };
+        for_blocks<FM, FN>([&](auto i, auto j) {
+            float* q = part(seg, i, j);
+#pragma unroll
+            for (int v = 0; v < Mf::NACC; ++v)
+                __hip_atomic_store(q + v * Cf::NT, acc[i][j][v], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        });
+        LT_WAIT_VM(0);
+        __syncthreads();   // every store of the partial is complete; the LDS ring is free
+        int* flag = reinterpret_cast<int*>(smem);
+        if (threadIdx.x == 0)
+            *flag = __hip_atomic_fetch_add(&p.counters[skt], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        if (*flag != NSPL - 1) return;
+        for (int s2 = 0; s2 < NSPL; ++s2) {
+            if (s2 == seg) continue;
+            for_blocks<FM, FN>([&](auto i, auto j) {
+                const float* q = part(s2, i, j);
+#pragma unroll
+                for (int v = 0; v < Mf::NACC; ++v)
+                    acc[i][j][v] += __hip_atomic_load(q + v * Cf::NT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            });
+        }
+        if (threadIdx.x == 0) __hip_atomic_store(&p.counters[skt], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+
     if (p.epi.fused)
         epilogue_fused();
     else if (m0 + Cf::BM > p.M || n0 + Cf::BN > p.N)

@@ -282,6 +282,12 @@ def test_skinny_with_beta():
     (6144, 4096, 256, F16, "col", "row", 2.0, -1.0, 128),    # M-/N-major, 768 tiles, C read
     (4100, 4104, 192, BF16, "row", "row", 1.0, 0.5, 128),    # 561 ragged tiles, no XCD regrouping
     (4104, 4112, 192, F16, "col", "col", 1.0, 0.0, 256),     # 289 ragged tiles of 256x256
+    # 256x128 tiles with beta != 0: the C tile staged through LDS during the
+    # last slices (interior tiles), exactly three slices, a partial first
+    # slice, ragged edge tiles that read C from global memory
+    (4608, 3584, 192, F16, "row", "col", 1.0, 0.5, 128),     # 504 tiles, 3 slices
+    (4608, 3584, 200, BF16, "col", "row", -1.5, 2.0, 128),   # 4 slices, the first partial
+    (4100, 4104, 320, F16, "row", "row", 1.0, -1.0, 128),    # ragged: edge tiles read C directly
 ])
 def test_many_rounds_tiled_all_outputs(M, N, K, dtype, a_major, b_major, alpha, beta, tile_n):
     A, B, C, D = _case(M, N, K, dtype, a_major, b_major, "row", alpha, beta, seed=M + K + tile_n)

@@ -285,11 +285,72 @@ def _successors(insts, i, index_of, func_addr):
 _LGKM = re.compile(r"lgkmcnt\((\d+)\)")
 
 
+_SPAIR = re.compile(r"^s\[(\d+):(\d+)\]$")
+_SREG = re.compile(r"\bs\[(\d+):(\d+)\]|\bs(\d+)\b")
+
+
+def _sregs(operands: str):
+    out = set()
+    for a, b, one in _SREG.findall(operands):
+        out.update([int(one)] if one else range(int(a), int(b) + 1))
+    return out
+
+
+def _uniform_flags(mn, ops, flags):
+    """Track what the structurizer's uniform branch flags make certain:
+    SGPR pairs set to -1 or 0 by `s_mov_b64`, and `vcc` certainly zero after
+    `s_andn2_b64 vcc, exec, s[a:b]` of a -1 pair or `s_and_b64 vcc, exec,
+    s[a:b]` of a 0 pair (zero whatever exec holds), certainly non-zero after
+    the opposite pairings (vcc = exec, taken as non-zero: the structurizer
+    tests these flags in uniform control flow, where exec is the whole wave). Any other instruction that names a tracked pair's
+    registers (or vcc) in any operand forgets that fact, so the tracking only
+    ever prunes paths that cannot run. Returns the new frozenset of facts."""
+    parts = [x.strip() for x in ops.split(",")] if ops else []
+    first = parts[0] if parts else ""
+    named = _sregs(ops)
+    facts = set()
+    for f in flags:   # forget pairs this instruction names
+        if f in ("vcc0", "vccN"):
+            facts.add(f)
+            continue
+        lo, hi = (int(x) for x in _SPAIR.match(f[1]).groups())
+        if not (named & set(range(lo, hi + 1))) or (mn in ("s_and_b64", "s_andn2_b64") and first == "vcc"):
+            facts.add(f)
+    if "vcc" in ops and not mn.startswith("s_cbranch_vcc"):
+        facts.discard("vcc0")
+        facts.discard("vccN")
+    if first == "vcc" and len(parts) == 3 and parts[1] == "exec":
+        # exec AND NOT -1, exec AND 0: zero whatever exec holds
+        if (mn == "s_andn2_b64" and ("m1", parts[2]) in facts) or (mn == "s_and_b64" and ("z", parts[2]) in facts):
+            facts.add("vcc0")
+        # exec AND -1, exec AND NOT 0: exec itself, non-zero in the uniform
+        # control flow where the structurizer tests its flags
+        if (mn == "s_and_b64" and ("m1", parts[2]) in facts) or (mn == "s_andn2_b64" and ("z", parts[2]) in facts):
+            facts.add("vccN")
+    if mn == "s_mov_b64" and _SPAIR.match(first) and len(parts) == 2 and parts[1] in ("-1", "0"):
+        facts.add(("m1" if parts[1] == "-1" else "z", first))
+    return frozenset(facts)
+
+
+def _pruned_successors(insts, j, index_of, base, flags):
+    """Successors of instruction j, without the branch side that a certainly
+    zero vcc rules out."""
+    mn = insts[j][1]
+    succ = _successors(insts, j, index_of, base)
+    if mn in ("s_cbranch_vccz", "s_cbranch_vccnz") and len(succ) == 2:
+        if "vcc0" in flags:
+            return [succ[1]] if mn == "s_cbranch_vccz" else [succ[0]]
+        if "vccN" in flags:
+            return [succ[0]] if mn == "s_cbranch_vccz" else [succ[1]]
+    return succ
+
+
 def unwaited_uses(insts, base):
     """(read, instruction) pairs where an instruction names a destination
     register of a transposing read on some path from it before the read is
-    retired (or the kernel ends first). Returns (violations, number of reads
-    checked)."""
+    retired (or the kernel ends first). Paths that a uniform branch flag
+    rules out (`_uniform_flags`) are not followed. Returns (violations,
+    number of reads checked)."""
     index_of = {a: i for i, (a, _, _, _) in enumerate(insts)}
     bad, n = [], 0
     for r, (_, mn, ops, _) in enumerate(insts):
@@ -297,13 +358,16 @@ def unwaited_uses(insts, base):
             continue
         n += 1
         dest = _regs(ops.split(",")[0])
-        # state: (instruction, LDS ops issued since the read (capped), scalar load since)
-        seen, todo = set(), [(j, 0, False) for j in _successors(insts, r, index_of, base)]
+        # state: (instruction, LDS ops issued since the read (capped), scalar
+        # load since, uniform-flag facts)
+        seen = set()
+        todo = [(j, 0, False, frozenset()) for j in _successors(insts, r, index_of, base)]
         while todo:
-            j, after, smem = todo.pop()
-            if (j, after, smem) in seen:
+            state = todo.pop()
+            if state in seen:
                 continue
-            seen.add((j, after, smem))
+            seen.add(state)
+            j, after, smem, flags = state
             _, mnj, opsj, _ = insts[j]
             if mnj == "s_waitcnt":
                 m = _LGKM.search(opsj)
@@ -314,7 +378,8 @@ def unwaited_uses(insts, base):
                 continue
             after = min(after + (1 if mnj.startswith("ds_") else 0), 64)
             smem = smem or mnj.startswith("s_load") or mnj.startswith("s_buffer_load")
-            todo.extend((k, after, smem) for k in _successors(insts, j, index_of, base))
+            nflags = _uniform_flags(mnj, opsj, flags)
+            todo.extend((k, after, smem, nflags) for k in _pruned_successors(insts, j, index_of, base, nflags))
     return bad, n
 
 
@@ -363,6 +428,35 @@ def test_checker_accepts_waited_reads_and_catches_early_use():
     one_path = _GOOD.replace("s_waitcnt vmcnt(0) lgkmcnt(0)", "s_waitcnt vmcnt(0)")
     bad, _ = unwaited_uses(_functions(one_path)["k"], 0x1000)
     assert {b[1][1] for b in bad} == {"v_mov_b32_e32", "s_endpgm"}   # v4 copied; v6:7 never waited
+
+
+_FLAGGED = """0000000000001000 <k>:
+	ds_read_b64_tr_b16 v[4:5], v0                              // 000000001000: D9C60000 04000000
+	s_mov_b64 s[0:1], -1                                       // 000000001008: BE8001C1
+	s_andn2_b64 vcc, exec, s[0:1]                              // 00000000100C: 89EA007E
+	s_cbranch_vccz 1                                           // 000000001010: BF860001 <k+0x18>
+	s_endpgm                                                   // 000000001014: BF810000
+	s_waitcnt lgkmcnt(0)                                       // 000000001018: BF8CC07F
+	v_mov_b32_e32 v8, v4                                       // 00000000101C: 7E100304
+	s_endpgm                                                   // 000000001020: BF810000
+"""
+
+
+def test_checker_follows_only_the_branch_a_uniform_flag_allows():
+    """exec AND NOT -1 is zero, so the vccz branch is always taken and the
+    early s_endpgm is unreachable; with the flag set to 0, or overwritten
+    before the test, or tested as exec AND -1 (vcc = exec, so vccz never
+    taken), that s_endpgm is reachable and reported."""
+    ok = _functions(_FLAGGED)["k"]
+    assert unwaited_uses(ok, 0x1000) == ([], 1)
+    zero = _FLAGGED.replace("s_mov_b64 s[0:1], -1 ", "s_mov_b64 s[0:1], 0  ")
+    bad, _ = unwaited_uses(_functions(zero)["k"], 0x1000)
+    assert [b[1][1] for b in bad] == ["s_endpgm"]
+    # a compare that writes the pair forgets what it held
+    assert _uniform_flags("v_cmp_gt_u32_e64", "s[0:1], v1, v2", frozenset({("m1", "s[0:1]")})) == frozenset()
+    anded = _FLAGGED.replace("s_andn2_b64 vcc, exec, s[0:1]", "s_and_b64 vcc, exec, s[0:1]  ")
+    bad, _ = unwaited_uses(_functions(anded)["k"], 0x1000)
+    assert [b[1][1] for b in bad] == ["s_endpgm"]
 
 
 def test_transposing_reads_are_waited_before_use(disasm):
