@@ -101,10 +101,12 @@ __global__ __launch_bounds__(256) void gemm_wave16(Wave16Args p) {
 // 16x16x32 MFMAs per 32 of K share the wave's B fragment), so A, read by
 // every workgroup and served by L2, crosses to a CU once per 32 columns. The
 // pair streams its K range through a ring of SkinnyCfg::R slots in LDS, each
-// 128 deep of the 32 A rows and 32 B columns, filled by direct global-to-LDS
-// copies in which 16 lanes cover the 256 contiguous bytes of one row or
-// column (the longer the run per column, the closer the stream gets to the
-// HBM peak: 32 columns 16 KiB apart are open at once per workgroup). Each
+// SkinnyCfg::SK (256) deep of the 32 A rows and 32 B columns, filled by
+// direct global-to-LDS copies in which 32 lanes cover the 512 contiguous
+// bytes of one row or column (the longer the run per column, the closer the
+// stream gets to the HBM peak: 32 columns 16 KiB apart are open at once per
+// workgroup; 256-byte runs measured 25.4 us, 512-byte runs 23.9 us on the
+// 32x8192x8192 workload). Each
 // wave copies its own 16 columns and 16 of the A rows; per slot it waits for
 // its own copies, then a workgroup barrier makes the partner's visible and
 // frees the slot read before. With split_k > 1 the K range is split over
@@ -118,10 +120,10 @@ __global__ __launch_bounds__(64 * kSkinnyWaves, 1) void gemm_skinny(SkinnyArgs p
     using V8 = typename Tr<DT>::V8;
     using SC = SkinnyCfg;
     constexpr int R = SC::R, SK = SC::SK, CB = SC::CB, HALF = SC::HALF, SLOT = SC::SLOT, NW = SC::NW;
-    constexpr int LPC = CB / 16;                      // lanes per row in a copy (16)
-    constexpr int CPI = 64 / LPC;                     // rows per copy instruction (4)
-    constexpr int NH = NW / 2;                        // copies per wave per half slot (4)
-    static_assert(LPC == 16 && NH * CPI == 16 && kSkinnyWaves == 2, "a wave copies 16 rows of each half");
+    constexpr int LPC = CB / 16;                      // lanes per row in a copy (32)
+    constexpr int CPI = 64 / LPC;                     // rows per copy instruction (2)
+    constexpr int NH = NW / 2;                        // copies per wave per half slot (8)
+    static_assert(LPC >= 16 && NH * CPI == 16 && kSkinnyWaves == 2, "a wave copies 16 rows of each half");
     const int lane = threadIdx.x & 63;
     const int ch = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // column half
     const int n0 = blockIdx.x * kSkinnyBN, sk = blockIdx.y;
@@ -129,13 +131,13 @@ __global__ __launch_bounds__(64 * kSkinnyWaves, 1) void gemm_skinny(SkinnyArgs p
     const int nst = p.k_per_wg / SK;                  // slots to stream
     char* ring = smem;
 
-    // Both halves of a slot (A rows, then B columns) hold 32 256-byte rows of
-    // 16-byte chunks; chunk q of row c is stored at position q ^ (c & 15), so
-    // the 16 lanes of a fragment read that share q and take consecutive c
+    // Both halves of a slot (A rows, then B columns) hold 32 rows of CB bytes
+    // in 16-byte chunks; chunk q of row c is stored at position q ^ (c & 15),
+    // so the 16 lanes of a fragment read that share q and take consecutive c
     // land on 16 distinct 16-byte bank groups.
-    // Copy j of a half, lane L fills byte (4 ch + j)*1024 + 16L: row c =
-    // 16 ch + 4 j + L/16, stored position L%16, i.e. logical chunk
-    // (L%16) ^ (c & 15). Every address is a workgroup-uniform base plus a
+    // Copy j of a half, lane L fills byte (NH ch + j)*1024 + 16L: row c =
+    // 16 ch + CPI j + L/LPC, stored position L%LPC, i.e. logical chunk
+    // (L%LPC) ^ (c & 15). Every address is a workgroup-uniform base plus a
     // 32-bit per-lane byte offset (32 rows of A or columns of B span far less
     // than 4 GiB). Rows of A past M repeat row M-1 (their outputs are never
     // stored).

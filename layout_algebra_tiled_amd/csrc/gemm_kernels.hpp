@@ -85,12 +85,12 @@ struct SkinnyArgs {
 constexpr int kSkinnyWaves = 2;     // waves per workgroup (16 of its columns each)
 constexpr int kSkinnyBN = 32;       // columns of N per workgroup
 // The two waves of a skinny workgroup take 16 of its 32 columns each and
-// share one LDS ring. A slot of the ring holds 128 deep of the 32 A rows and
-// the 32 B columns (256 contiguous bytes of each row or column); each wave
+// share one LDS ring. A slot of the ring holds 256 deep of the 32 A rows and
+// the 32 B columns (512 contiguous bytes of each row or column); each wave
 // copies its 16 B columns and 16 of the A rows. The ring depth keeps the
 // slots in flight within the 6-bit vmcnt and the ring within 160 KiB of LDS.
 struct SkinnyCfg {
-    static constexpr int SK = 128;                 // K per slot
+    static constexpr int SK = 256;                 // K per slot
     static constexpr int CB = 2 * SK;              // bytes of one row or column per slot
     static constexpr int HALF = 32 * CB;           // bytes of the A (or B) half of a slot
     static constexpr int SLOT = 2 * HALF;          // bytes of one slot
@@ -102,8 +102,7 @@ struct SkinnyCfg {
     static constexpr int LDS = R * SLOT;           // bytes per workgroup
     static_assert(R >= 3, "the ring issues a slot after the barrier that frees it");
 };
-// The K range of a workgroup must be a whole number of 128-deep slots (kept
-// at 256, a multiple of that, for the eligibility rule)
+// The K range of a workgroup must be a whole number of 256-deep slots
 constexpr int kSkinnyKQuantum = 256;
 
 // Compile-time shape of the tiled kernel the planner launches.

@@ -249,11 +249,11 @@ def test_two_calls_in_a_row_different_sizes():
 @pytest.mark.parametrize("M,N,K,split", [(32, 1024, 4096, 0), (17, 512, 4096, 1), (17, 512, 4096, 2),
                                          (32, 256, 2048, 4), (1, 64, 512, 1), (32, 64, 256, 1),
                                          (8, 128, 3072, 3),
-                                         # 128-deep slots: 9 per wave (one steady trip of the ring, 5 drained)
+                                         # 18 256-deep slots (3 steady trips of the 4-slot ring, 6 drained)
                                          (32, 256, 4608, 1),
-                                         # 64-deep slots: 19 per wave (one steady trip, 11 drained)
+                                         # 19 slots: 4 steady trips, 3 drained
                                          (20, 512, 4864, 1),
-                                         # 128-deep slots: 32 per wave, 7 steady trips
+                                         # 64 slots, 15 steady trips
                                          (31, 96, 16384, 1)])
 def test_skinny_all_outputs(M, N, K, split):
     A, B, C, D = _case(M, N, K, BF16, "row", "col", "row", 1.0, 0.0, dist="normal", seed=71)
