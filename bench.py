@@ -182,7 +182,7 @@ def queued_block_time(run, n: int):
 
 
 class Workload:
-    def __init__(self, cfg: int, n_b: int = 1, mnk=None, beta=None):
+    def __init__(self, cfg: int, n_b: int = 1, mnk=None, beta=None, persistent=None):
         import dataclasses
         import torch
         import datagen
@@ -194,6 +194,7 @@ class Workload:
         if beta is not None:
             self.c = dataclasses.replace(self.c, beta=beta, name=f"{self.c.name} with beta={beta}")
         c = self.c
+        self.persistent = persistent   # None: the planner's choice
         log(f"[bench] preparing workload {cfg}: {c.name}")
         A, B, C, D = c.make()
         self.host = (A, B, C, D)
@@ -212,7 +213,7 @@ class Workload:
     def plan(self):
         from layout_algebra_tiled_amd import gemm as g
         return g.plan(self.A.store, self.Bs[0].store, self.D.store, self.C.store if self.C is not None else None,
-                      self.c.beta, layouts=self.lay)
+                      self.c.beta, layouts=self.lay, persistent=self.persistent)
 
     def run(self, i: int = 0):
         from layout_algebra_tiled_amd import gemm as g
@@ -222,7 +223,7 @@ class Workload:
             self.ws = torch.empty(need, dtype=torch.uint8, device="cuda:0") if need else None
         g.gemm(self.A.store, self.Bs[i % len(self.Bs)].store, self.D.store,
                self.C.store if self.C is not None else None, self.c.alpha, self.c.beta, layouts=self.lay,
-               workspace=self.ws)
+               workspace=self.ws, persistent=self.persistent)
 
     def queued_kernel_time(self, steps: int):
         """Mean kernel duration (s) of `steps` launches queued back to back
@@ -486,6 +487,9 @@ def main():
                          "runs; the reported metric is defined at 8192^3 only)")
     ap.add_argument("--beta", type=float, default=None,
                     help="the headline workload with another beta (profiling runs)")
+    ap.add_argument("--persistent", choices=("auto", "on", "off"), default="auto",
+                    help="the persistent launch of 256x128 tiles: the planner's choice, forced on or off "
+                         "(profiling runs)")
     ap.add_argument("--also-torch-matmul", action="store_true",
                     help="also time torch.matmul (the vendor GEMM library) on the same operands, for scale")
     args = ap.parse_args()
@@ -511,7 +515,8 @@ def main():
     # the skinny workload's B (128 MiB) would sit in the 256 MB last-level
     # cache between steps: rotate four copies so every step streams B from HBM
     mnk = tuple(int(x) for x in args.mnk.split(",")) if args.mnk else None
-    w = Workload(args.workload, n_b=4 if args.workload == 5 else 1, mnk=mnk, beta=args.beta)
+    pers = {"auto": None, "on": True, "off": False}[args.persistent]
+    w = Workload(args.workload, n_b=4 if args.workload == 5 else 1, mnk=mnk, beta=args.beta, persistent=pers)
     plan = w.plan()
     log(f"[bench] plan: {plan['kernel_name']} tile {plan['tile_m']}x{plan['tile_n']}x{plan['tile_k']}, "
         f"wave tile {plan['wave_m']}x{plan['wave_n']}, {plan['waves']} waves, {plan['stages']} LDS stages "
@@ -546,7 +551,8 @@ def main():
         "config": {"workload": f"{w.c.name}: D = alpha*A*B + beta*C, alpha={w.c.alpha}, beta={w.c.beta}, "
                                f"fp32 accumulate", "M": w.c.M, "N": w.c.N, "K": w.c.K,
                    "kernel": plan["kernel_name"], "tile": [plan["tile_m"], plan["tile_n"], plan["tile_k"]],
-                   "grid": plan["grid"], "pct_of_peak": round(100 * value / PEAK_TFLOPS, 2),
+                   "grid": plan["grid"], "persistent": bool(plan["persistent"]),
+                   "pct_of_peak": round(100 * value / PEAK_TFLOPS, 2),
                    "kernel_us": {"mean": round(kern * 1e6, 1),
                                  "median": round(w.kernel_times[len(w.kernel_times) // 2] * 1e6, 1),
                                  "min": round(w.kernel_times[0] * 1e6, 1),
@@ -577,6 +583,7 @@ def main():
             xb = queued_block_time(x.run, n)
             xc = x.check(128)
             rec = {"kernel": p["kernel_name"], "tile": [p["tile_m"], p["tile_n"], p["tile_k"]], "grid": p["grid"],
+                   "persistent": bool(p["persistent"]),
                    "ms_per_step": round(xw * 1e3, 4), "kernel_us": round(xk * 1e6, 2),
                    "kernel_us_median": round(x.queued_times[len(x.queued_times) // 2] * 1e6, 2),
                    "kernel_us_back_to_back": round(xb * 1e6, 2),

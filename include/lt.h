@@ -292,6 +292,11 @@ typedef struct lt_gemm_options {
                            tile past the last whole round of 256 CUs (0: chosen by a
                            cost model; 1: none, all tiles whole; > 1: forced, on all
                            tiles when they fill no whole round) */
+    int32_t persistent; /* TILED, 256x128 tiles: 0 = chosen (persistent when the tiles
+                           are whole, K is a multiple of 64 with at least 4 slices,
+                           there are more tiles than compute units and beta is 0);
+                           1 = one workgroup per tile; 2 = persistent
+                           (LT_ERR_UNSUPPORTED where the tile or K conditions fail) */
 } lt_gemm_options;
 
 /* What the planner chose, for banners and tests [P1 "Exercise": print the
@@ -313,7 +318,11 @@ typedef struct lt_gemm_plan_info {
     int64_t sk_tiles;        /* TILED: tiles of the last round split into split_k K segments, 0 if none */
     int32_t sk_workgroups;   /* TILED: workgroups of the split launch (sk_tiles * split_k) */
     int64_t tiles;           /* output tiles of the block tiling (TILED: one workgroup per tile,
-                                plus split_k - 1 more per split tile) */
+                                plus split_k - 1 more per split tile, unless persistent) */
+    int32_t persistent;      /* TILED: 1 if one workgroup per compute unit walks a list of
+                                tiles ["CUTLASS, in depth", "Kernel schedules"]; grid is
+                                then the workgroup count. A fused epilogue (lt_gemm_run_ex)
+                                runs one workgroup per tile instead. */
 } lt_gemm_plan_info;
 
 /* Validate and plan without launching: the can_implement half of the

@@ -120,6 +120,7 @@ struct Plan {
     int sk_splits = 1;
     int64_t sk_counter_bytes = 0;   // workspace: counters first, then partials
     int tile_n = 256;               // tiled kernel: block tile 256 x tile_n
+    int persist_grid = 0;           // > 0: persistent launch of this many workgroups
 };
 
 // Compute units of a gfx950 part (MI355X): the unit of wave quantisation.
@@ -324,13 +325,33 @@ lt_status make_plan(const lt_tensor* tA, const lt_tensor* tB, const lt_tensor* t
             in.lds_bytes = tsc.lds_bytes;
             if (in.lds_bytes > 160 * 1024) return LT_ERR_LDS_OVERFLOW;
             const int64_t ntiles = tile_n == 128 ? n128 : n256;
+            // Persistent launch of 256x128 tiles ("CUTLASS, in depth",
+            // "Kernel schedules"): one workgroup per compute unit walks its
+            // tiles and copies the next tile's first slices while the
+            // current one finishes. Whole tiles only, K a multiple of the
+            // slice depth, at least 4 slices per tile; chosen when the
+            // tiles take more than one round of the compute units and beta
+            // is 0. (With beta != 0 the one-workgroup-per-tile launch stages
+            // C through the LDS stages its last slices free, which the
+            // persistent launch fills with the next tile's slices; its C
+            // loads into registers measured slower: 6144x4096x2048 fp16
+            // 105-113 us per tile against 107-118 persistent, 95-104 us
+            // persistent with beta = 0.)
+            const int want_p = opt ? opt->persistent : 0;
+            if (want_p < 0 || want_p > 2) return LT_ERR_INVALID_ARGUMENT;
+            const bool persist_ok =
+                tile_n == 128 && p.M % tsc.bm == 0 && p.N % tsc.bn == 0 && p.K % tsc.bk == 0 && KTt >= 4;
+            if (want_p == 2 && !persist_ok) return LT_ERR_UNSUPPORTED;
+            const bool persist = persist_ok && (want_p == 2 || (want_p == 0 && ntiles > kCUs && !beta_nonzero));
+            p.persist_grid = persist ? (int)std::min<int64_t>(ntiles, kCUs) : 0;
+            in.persistent = persist ? 1 : 0;
             p.tile_n = tile_n;
             p.dp_tiles = ntiles - rem;
             p.sk_tiles = rem;
             p.sk_splits = static_cast<int>(S);
             p.sk_counter_bytes = (rem * 4 + 255) / 256 * 256;
             in.split_k = p.sk_splits;
-            in.grid = p.dp_tiles + rem * S;
+            in.grid = persist ? p.persist_grid : p.dp_tiles + rem * S;
             in.tiles = ntiles;
             in.sk_tiles = rem;
             in.sk_workgroups = static_cast<int32_t>(rem * S);
@@ -564,6 +585,8 @@ lt_status lt_gemm_run_ex(const lt_tensor* A, const lt_tensor* B, const lt_tensor
             a.group_m = std::min(a.tiles_m, 8);
             a.dp_tiles = (int)p.dp_tiles;
             a.sk_splits = p.sk_splits;
+            // (a persistent grid is the tile count or 256: a multiple of 8
+            // whenever the tile count is)
             a.xcd_remap = p.dp_tiles % 8 == 0 ? 1 : 0;
             a.counters = nullptr;
             a.partials = nullptr;
@@ -573,7 +596,8 @@ lt_status lt_gemm_run_ex(const lt_tensor* A, const lt_tensor* B, const lt_tensor
                 if ((err = lt::launch_zero_i32(a.counters, (int)p.sk_tiles, stream)) != 0) return LT_ERR_HIP;
             }
             a.epi = ea;
-            err = lt::launch_tiled(dt, p.a_k, p.b_k, p.tile_n, a, stream);
+            // the fused epilogue runs in the one-workgroup-per-tile launch
+            err = lt::launch_tiled(dt, p.a_k, p.b_k, p.tile_n, ea.fused ? 0 : p.persist_grid, a, stream);
             break;
         }
         case LT_KERNEL_SKINNY: {

@@ -355,14 +355,16 @@ TiledShape tiled_shape(bool a_kmajor, bool b_kmajor, int tile_n) {
     return shape_for<false, false>(tile_n);
 }
 
-int launch_tiled(int dtype, bool a_kmajor, bool b_kmajor, int tile_n, const TiledArgs& a, void* stream) {
+int launch_tiled(int dtype, bool a_kmajor, bool b_kmajor, int tile_n, int persist_grid, const TiledArgs& a,
+                 void* stream) {
     static_assert(LT_F16 == 1 && LT_BF16 == 2, "variant names carry the dtype code");
+    const int pg = persist_grid;
     if (dtype == LT_F16) {
-        if (a_kmajor) return b_kmajor ? launch_tiled_11_1(a, tile_n, stream) : launch_tiled_11_0(a, tile_n, stream);
-        return b_kmajor ? launch_tiled_10_1(a, tile_n, stream) : launch_tiled_10_0(a, tile_n, stream);
+        if (a_kmajor) return b_kmajor ? launch_tiled_11_1(a, tile_n, pg, stream) : launch_tiled_11_0(a, tile_n, pg, stream);
+        return b_kmajor ? launch_tiled_10_1(a, tile_n, pg, stream) : launch_tiled_10_0(a, tile_n, pg, stream);
     }
-    if (a_kmajor) return b_kmajor ? launch_tiled_21_1(a, tile_n, stream) : launch_tiled_21_0(a, tile_n, stream);
-    return b_kmajor ? launch_tiled_20_1(a, tile_n, stream) : launch_tiled_20_0(a, tile_n, stream);
+    if (a_kmajor) return b_kmajor ? launch_tiled_21_1(a, tile_n, pg, stream) : launch_tiled_21_0(a, tile_n, pg, stream);
+    return b_kmajor ? launch_tiled_20_1(a, tile_n, pg, stream) : launch_tiled_20_0(a, tile_n, pg, stream);
 }
 
 template <int DT>

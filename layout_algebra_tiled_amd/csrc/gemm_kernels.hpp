@@ -121,18 +121,19 @@ TiledShape tiled_shape(bool a_kmajor, bool b_kmajor, int tile_n);
 
 // Each returns 0 on success or the hipError_t of the launch.
 int launch_wave16(int dtype, const Wave16Args& a, void* stream);
-int launch_tiled(int dtype, bool a_kmajor, bool b_kmajor, int tile_n, const TiledArgs& a, void* stream);
+int launch_tiled(int dtype, bool a_kmajor, bool b_kmajor, int tile_n, int persist_grid, const TiledArgs& a,
+                 void* stream);
 // The variants of the tiled kernel, launch_tiled_<dtype><A K-major>_<B
 // K-major>; each is compiled in a translation unit of its own
 // (gemm_tiled.hip built with LT_TILED_DT / LT_TILED_AK / LT_TILED_BK).
-int launch_tiled_11_1(const TiledArgs& a, int tile_n, void* stream);
-int launch_tiled_11_0(const TiledArgs& a, int tile_n, void* stream);
-int launch_tiled_10_1(const TiledArgs& a, int tile_n, void* stream);
-int launch_tiled_10_0(const TiledArgs& a, int tile_n, void* stream);
-int launch_tiled_21_1(const TiledArgs& a, int tile_n, void* stream);
-int launch_tiled_21_0(const TiledArgs& a, int tile_n, void* stream);
-int launch_tiled_20_1(const TiledArgs& a, int tile_n, void* stream);
-int launch_tiled_20_0(const TiledArgs& a, int tile_n, void* stream);
+int launch_tiled_11_1(const TiledArgs& a, int tile_n, int persist_grid, void* stream);
+int launch_tiled_11_0(const TiledArgs& a, int tile_n, int persist_grid, void* stream);
+int launch_tiled_10_1(const TiledArgs& a, int tile_n, int persist_grid, void* stream);
+int launch_tiled_10_0(const TiledArgs& a, int tile_n, int persist_grid, void* stream);
+int launch_tiled_21_1(const TiledArgs& a, int tile_n, int persist_grid, void* stream);
+int launch_tiled_21_0(const TiledArgs& a, int tile_n, int persist_grid, void* stream);
+int launch_tiled_20_1(const TiledArgs& a, int tile_n, int persist_grid, void* stream);
+int launch_tiled_20_0(const TiledArgs& a, int tile_n, int persist_grid, void* stream);
 int launch_skinny(int dtype, const SkinnyArgs& a, void* stream);
 // *p = 0.0f on the stream (a one-thread kernel: no memset node in a captured graph)
 int launch_zero_f32(float* p, void* stream);

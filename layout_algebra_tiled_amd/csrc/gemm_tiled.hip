@@ -47,6 +47,12 @@ __device__ __forceinline__ void tile_coords(int lin, const TiledArgs& p, int* tm
     *tn = in / gm;
 }
 
+// Launches of the tiled kernel: one workgroup per tile (the data-parallel
+// launch), one per K segment of the split remainder's tiles, or one per
+// compute unit walking a list of whole tiles (persistent; with C loaded for
+// beta != 0, or without).
+enum TiledMode : int { kDataParallel = 0, kSplit = 1, kPersistent = 2, kPersistentC = 3 };
+
 // Workgroup -> (linear tile, K slices [kt0, kt1), split index or -1). In
 // the data-parallel launch consecutive workgroup ids go to different XCDs
 // (round-robin dispatch), so the ids are regrouped for each XCD to walk a
@@ -149,9 +155,11 @@ __device__ __forceinline__ void copy16(uint32_t lds, const char* gbase, uint32_t
 // The kernel's body is compiled in the device pass only: the host pass needs
 // just the launch stub (and with the body in view it silently emits no stub
 // for a kernel whose generic lambdas call the direct-to-LDS builtin).
-template <int DT, class Cf, bool SPLIT>
+template <int DT, class Cf, int MODE>
 __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
 #if defined(__HIP_DEVICE_COMPILE__)
+    constexpr bool SPLIT = MODE == kSplit;
+    constexpr bool PERS = MODE == kPersistent || MODE == kPersistentC;
     extern __shared__ __attribute__((aligned(1024))) char smem[];
     using V8 = typename Tr<DT>::V8;
     constexpr int BK = Cf::BK, S = Cf::S, KS = Cf::KS, FM = Cf::FM, FN = Cf::FN;
@@ -169,11 +177,34 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
     const int KT = (p.K + BK - 1) / BK;
     const int kbase = p.K - KT * BK;
     int lin, kt0, kt1, seg;
-    work_of<SPLIT>(blockIdx.x, p, KT, &lin, &kt0, &kt1, &seg);
+    // Persistent launch: this workgroup's tiles are first + j*step, j <
+    // ntl. With the XCD regrouping, XCD x owns the stretch of dp_tiles/8
+    // tiles from x*dp_tiles/8 and its workgroups take them in turn, so the
+    // tiles in flight on one XCD are consecutive in the raster, as in the
+    // data-parallel launch.
+    int first = 0, step = 0, ntl = 1;
+    if constexpr (PERS) {
+        if (p.xcd_remap) {
+            const int x = blockIdx.x & 7, l = blockIdx.x >> 3, wpx = gridDim.x >> 3, tpx = p.dp_tiles >> 3;
+            first = x * tpx + l;
+            step = wpx;
+            ntl = (tpx - l + wpx - 1) / wpx;
+        } else {
+            first = blockIdx.x;
+            step = gridDim.x;
+            ntl = (p.dp_tiles - (int)blockIdx.x + step - 1) / step;
+        }
+        lin = first;
+        kt0 = 0;
+        kt1 = KT;
+        seg = -1;
+    } else {
+        work_of<SPLIT>(blockIdx.x, p, KT, &lin, &kt0, &kt1, &seg);
+    }
     const int NS = kt1 - kt0;   // K slices this workgroup runs (>= 1)
     int tm, tn;
     tile_coords(lin, p, &tm, &tn);
-    const int m0 = tm * Cf::BM, n0 = tn * Cf::BN;
+    int m0 = tm * Cf::BM, n0 = tn * Cf::BN;   // (the persistent launch moves them tile by tile)
 
     // ---- copy: S-stage ring, stage s at s*STAGE (A slice, then B slice).
     // Up to four copy instructions of one operand write LDS through the same
@@ -181,39 +212,49 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
     // which the hardware adds to both the global and the LDS address; the
     // global source is a uniform slice base plus a per-lane 32-bit offset,
     // minus that same instruction offset.
+    // (the persistent launch runs whole tiles only: its offsets are taken
+    // from the tile's first row, which a scalar tile base adds)
     uint32_t aoffg[OA::OPI], boffg[OB::OPI];
 #pragma unroll
-    for (int i = 0; i < OA::OPI; ++i) aoffg[i] = OA::offset(p.lda, m0, p.M, wave, lane, i);
+    for (int i = 0; i < OA::OPI; ++i)
+        aoffg[i] = PERS ? OA::offset(p.lda, 0, Cf::BM, wave, lane, i) : OA::offset(p.lda, m0, p.M, wave, lane, i);
 #pragma unroll
-    for (int i = 0; i < OB::OPI; ++i) boffg[i] = OB::offset(p.ldb, n0, p.N, wave, lane, i);
+    for (int i = 0; i < OB::OPI; ++i)
+        boffg[i] = PERS ? OB::offset(p.ldb, 0, Cf::BN, wave, lane, i) : OB::offset(p.ldb, n0, p.N, wave, lane, i);
     const int64_t a_ks = OA::kslice_bytes(p.lda);
     const int64_t b_ks = OB::kslice_bytes(p.ldb);
     // slice 0 sources: the operands' bases moved by kbase (the host does
     // that, so the slice address stays a kernel argument plus a multiple of
     // the slice stride); lanes whose chunk lies below K = 0 never load
-    const char* a_k0 = reinterpret_cast<const char*>(p.A0);
-    const char* b_k0 = reinterpret_cast<const char*>(p.B0);
+    // (the persistent launch: the current tile's first rows)
+    const char* a_k0 = reinterpret_cast<const char*>(p.A0) + (PERS ? OA::tile_bytes(p.lda, m0) : 0);
+    const char* b_k0 = reinterpret_cast<const char*>(p.B0) + (PERS ? OB::tile_bytes(p.ldb, n0) : 0);
     auto a_lds = [&](int stage) { return smem + stage * Cf::STAGE + wave * OA::OPI * 1024; };
     auto b_lds = [&](int stage) { return smem + stage * Cf::STAGE + Cf::A_BYTES + wave * OB::OPI * 1024; };
     auto lds_u32 = [](const char* p) {
         return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const LDS_AS char*)p));
     };
 
-    // Copy instruction c (< IPW) of slice kt into `stage`: A's OPI, then B's.
-    // (groups of four: the instruction offset is at most 4095 bytes)
-    auto issue_one = [&](int stage, int kt, auto cc) {
+    // Copy instruction c (< IPW) of the slice whose A and B sources start
+    // at ga and gb into `stage`: A's OPI, then B's. (groups of four: the
+    // instruction offset is at most 4095 bytes)
+    auto issue_one = [&](int stage, const char* ga, const char* gb, auto cc) {
         constexpr int c = decltype(cc)::value;
         if constexpr (c < OA::OPI) {
             constexpr int i = c, g = i / 4, o = (i % 4) * 1024;
-            const char* ga = a_k0 + (kt0 + kt) * a_ks;
             copy16<o>(lds_u32(a_lds(stage) + g * 4096), ga - o, aoffg[i]);
         } else {
             constexpr int i = c - OA::OPI, g = i / 4, o = (i % 4) * 1024;
-            const char* gb = b_k0 + (kt0 + kt) * b_ks;
             copy16<o>(lds_u32(b_lds(stage) + g * 4096), gb - o, boffg[i]);
         }
     };
-    auto issue = [&](int stage, int kt) { static_for<0, Cf::IPW>([&](auto cc) { issue_one(stage, kt, cc); }); };
+    auto issue_at = [&](int stage, const char* ga, const char* gb) {
+        static_for<0, Cf::IPW>([&](auto cc) { issue_one(stage, ga, gb, cc); });
+    };
+    // slice kt of this workgroup's K range
+    auto src_a = [&](int kt) { return a_k0 + (kt0 + kt) * a_ks; };
+    auto src_b = [&](int kt) { return b_k0 + (kt0 + kt) * b_ks; };
+    auto issue = [&](int stage, int kt) { issue_at(stage, src_a(kt), src_b(kt)); };
 
     // Slice 0 when it is partial: a lane whose chunk lies below K = 0 writes
     // zeros where the copy would have put it (the copy's lane-linear LDS
@@ -412,10 +453,27 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
         else
             asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(c) : "v"(x), "v"(y));
     };
+    // the same with a zero accumulator input: the first K step of a tile
+    // in the persistent launch starts each block at zero this way
+    auto mfma_first = [&](int cur, auto qc) {
+        constexpr int q = decltype(qc)::value, i = q / FN, j = q % FN;
+        auto& c = acc[i][j];
+        const V8 x = bfr[cur][j].get(), y = af[cur][i].get();
+        if constexpr (DT == LT_BF16)
+            asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=a"(c) : "v"(x), "v"(y));
+        else
+            asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, 0" : "=a"(c) : "v"(x), "v"(y));
+    };
     // cpc: 0, or 1 / 2 for the slice that also copies the first 12 / last 4
-    // copies of the C tile (into its own stage, after its barrier)
-    auto slice_x = [&](auto has_next, auto refill, int t, auto par, auto cpc) {
+    // copies of the C tile (into its own stage, after its barrier). ga, gb:
+    // the sources of the slice a refill copies. first: the slice starts a
+    // tile of the persistent launch (its first K step zeroes the
+    // accumulators). waitc: the vmcnt the barrier waits for, or -1 for the
+    // count the variant implies.
+    auto slice_x = [&](auto has_next, auto refill, const char* ga, const char* gb, auto par, auto cpc, auto first,
+                       auto waitc) {
         constexpr int CP = decltype(cpc)::value;
+        constexpr int WAITC = decltype(waitc)::value;
         static_for<0, KS>([&](auto sc) {
             constexpr int s = decltype(sc)::value, cur = (decltype(par)::value + s) & 1, nxt = cur ^ 1;
             constexpr bool last = s + 1 == KS;
@@ -427,7 +485,9 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
             static_assert(CP == 0 || (!decltype(refill)::value && decltype(has_next)::value), "C copies");
             int rstage = stage, rs = s + 1;
             if constexpr (last && decltype(has_next)::value) {
-                if constexpr (decltype(refill)::value)
+                if constexpr (WAITC >= 0)
+                    LT_WAIT_VM(WAITC);
+                else if constexpr (decltype(refill)::value)
                     LT_WAIT_VM(Cf::IPW * (S - 2));   // slice t+1 landed (S-2 newer slices may fly)
                 else if constexpr (CP == 2)
                     LT_WAIT_VM(12);                  // slice t+1 landed; the first 12 C copies may fly
@@ -439,11 +499,14 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
             }
             static_for<0, NQ>([&](auto qc) {
                 constexpr int q = decltype(qc)::value;
-                mfma_one(cur, qc);
+                if constexpr (decltype(first)::value && s == 0)
+                    mfma_first(cur, qc);
+                else
+                    mfma_one(cur, qc);
                 constexpr int c = copy_after(q, NC, NQ);
                 if constexpr (c >= 0) {
                     if constexpr (copies)
-                        issue_one(stage, t + S, ic<c>{});
+                        issue_one(stage, ga, gb, ic<c>{});
                     else
                         issue_c(stage, ic<CP == 1 ? c : 12 + c>{});
                 }
@@ -453,12 +516,14 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
         });
         stage = stage + 1 == S ? 0 : stage + 1;
     };
+    const std::true_type yes{};
+    const std::false_type no{};
     // slice t (local index); with one K step per slice its fragment buffer
     // is t's parity, a compile-time index in each of two copies of the body
     auto slice = [&](auto has_next, auto refill, int t, auto cpc) {
         auto go = [&](auto par) {
             if constexpr (Cf::EXPLICIT)
-                slice_x(has_next, refill, t, par, cpc);
+                slice_x(has_next, refill, src_a(t + S), src_b(t + S), par, cpc, no, ic<-1>{});
             else
                 slice_s(has_next, refill, t, par);
         };
@@ -471,8 +536,6 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
                 go(ic<0>{});
         }
     };
-    const std::true_type yes{};
-    const std::false_type no{};
     // the zeroed accumulators are written by VALU moves: wait states before
     // the first inline-asm MFMA reads them (the compiler does not see it as one)
     if constexpr (Cf::EXPLICIT) asm volatile("s_nop 7" ::: "memory");
@@ -626,6 +689,95 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
         });
         if (e.amax) amax_commit(e.amax, amax);
     };
+    // ---- persistent launch (whole tiles, K a multiple of BK, NS >= 4): the
+    // K loop runs over the concatenation of this workgroup's tiles' slices,
+    // so the next tile's first two slices are copied while the current
+    // tile's last slices run, and its third right after the current tile's
+    // epilogue. (The compiler places the epilogue's waits for the C values
+    // counting only the loads it sees, not the copies, so those waits also
+    // cover every copy issued before the epilogue: the third slice's copies
+    // come after it so that the epilogue never waits for them.) ("CUTLASS,
+    // in depth", "Kernel schedules": a persistent kernel walks tiles from a
+    // tile scheduler and overlaps one tile's epilogue with the next tile's
+    // main loop.)
+    if constexpr (PERS) {
+        static_assert(Cf::EXPLICIT && S == 3 && KS % 2 == 0, "the persistent launch runs the 3-stage explicit schedule");
+        constexpr bool WITH_C = MODE == kPersistentC;
+        constexpr int NCL = FM * FN * NG;   // C loads per lane, one group of four outputs each
+        static_assert(Cf::IPW + NCL < 64, "vmcnt range");
+        u32x2 cvp[FM][FN][NG];
+        auto load_c_regs = [&]() {
+            for_blocks<FM, FN>([&](auto i, auto j) {
+                const int m = m0 + arow0 + i * Cf::MF + Mf::out_col(lane);
+#pragma unroll
+                for (int g = 0; g < NG; ++g) {
+                    const int n = n0 + brow0 + j * Cf::MF + Mf::out_row(lane, 4 * g);
+                    cvp[i][j][g] = *reinterpret_cast<const u32x2*>(p.C + (int64_t)m * p.ldc + n);
+                }
+            });
+        };
+        auto store_tile = [&]() {
+            for_blocks<FM, FN>([&](auto i, auto j) {
+                const int m = m0 + arow0 + i * Cf::MF + Mf::out_col(lane);
+#pragma unroll
+                for (int g = 0; g < NG; ++g) {
+                    const int n = n0 + brow0 + j * Cf::MF + Mf::out_row(lane, 4 * g);
+                    const float v[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                                        acc[i][j][4 * g + 3]};
+                    store4_c<DT>(p.D, (int64_t)m * p.ldd + n, v, p.alpha, p.beta,
+                                 WITH_C ? cvp[i][j][g] : u32x2{0u, 0u});
+                }
+            });
+        };
+        // Every tile runs the same slice sequence, so no control flow
+        // joins while MFMA results are in flight (at a join the compiler
+        // may copy accumulators): the last tile takes itself as its "next"
+        // tile, whose first two slices are then copied again into stages
+        // nobody reads, and waited for before the workgroup ends.
+        int m0n = m0, n0n = n0;
+        const char* na = a_k0;
+        const char* nb = b_k0;
+        for (int j = 0;; ++j) {
+            const bool more = j + 1 < ntl;
+            if (more) {
+                int tmj, tnj;
+                tile_coords(first + (j + 1) * step, p, &tmj, &tnj);
+                m0n = tmj * Cf::BM;
+                n0n = tnj * Cf::BN;
+                na = reinterpret_cast<const char*>(p.A0) + OA::tile_bytes(p.lda, m0n);
+                nb = reinterpret_cast<const char*>(p.B0) + OB::tile_bytes(p.ldb, n0n);
+            }
+            // slice t refills slice t+S of the sequence: this tile's, else
+            // the next tile's slice t+S-NS
+            auto ref_a = [&](int t) { return t + S < NS ? a_k0 + (t + S) * a_ks : na + (t + S - NS) * a_ks; };
+            auto ref_b = [&](int t) { return t + S < NS ? b_k0 + (t + S) * b_ks : nb + (t + S - NS) * b_ks; };
+            // C for this tile's epilogue is loaded first and flies for the
+            // whole tile: slices 0 and 1 wait for slices 1 and 2, which the C
+            // loads and one more slice follow; from slice 2 on the slice
+            // waited for is newer than the C loads
+            constexpr int W01 = WITH_C ? Cf::IPW + NCL : -1;
+            if constexpr (WITH_C) load_c_regs();
+            slice_x(yes, yes, ref_a(0), ref_b(0), ic<0>{}, ic<0>{}, yes, ic<W01>{});
+            slice_x(yes, yes, ref_a(1), ref_b(1), ic<0>{}, ic<0>{}, no, ic<W01>{});
+            for (int t = 2; t + 1 < NS; ++t) slice_x(yes, yes, ref_a(t), ref_b(t), ic<0>{}, ic<0>{}, no, ic<-1>{});
+            // the tile's last slice: the barrier waits for the next tile's
+            // slice 0 while its slice 1 may fly
+            const int st_last = stage;
+            slice_x(yes, no, a_k0, b_k0, ic<0>{}, ic<0>{}, no, ic<Cf::IPW>{});
+            asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");   // MFMA results before VALU reads
+            store_tile();
+            if (!more) break;
+            issue_at(st_last, na + 2 * a_ks, nb + 2 * b_ks);   // the next tile's slice 2
+            m0 = m0n;
+            n0 = n0n;
+            a_k0 = na;
+            b_k0 = nb;
+        }
+        // no copy into LDS, nor a read of the unused fragments, outlives
+        // the workgroup
+        __builtin_amdgcn_s_waitcnt(0);
+        return;
+    }
     int t = 0;
     for (; t + S < NS; ++t) slice(yes, yes, t, ic<0>{});   // refill slice t+S
     // The C-prefetch path runs its last slices and its epilogue on its own:
@@ -704,30 +856,36 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
 
 namespace {
 
-template <int DT, class Cf, bool SPLIT>
+template <int DT, class Cf, int MODE>
 int launch_mode(const TiledArgs& a, int grid, hipStream_t s) {
     static std::atomic<uint64_t> attr{0};
-    if (const int e = set_lds_limit_once(reinterpret_cast<const void*>(&gemm_tiled<DT, Cf, SPLIT>), Cf::LDS, attr))
+    if (const int e = set_lds_limit_once(reinterpret_cast<const void*>(&gemm_tiled<DT, Cf, MODE>), Cf::LDS, attr))
         return e;
-    hipLaunchKernelGGL((gemm_tiled<DT, Cf, SPLIT>), dim3(grid), dim3(Cf::NT), Cf::LDS, s, a);
+    hipLaunchKernelGGL((gemm_tiled<DT, Cf, MODE>), dim3(grid), dim3(Cf::NT), Cf::LDS, s, a);
     return static_cast<int>(hipGetLastError());
 }
 
 }  // namespace
 
-// 256x128 tiles: the data-parallel launch only (the planner never splits
-// them). 256x256 tiles: the data-parallel tiles, then (same stream, so after
-// them) the split remainder.
+// 256x128 tiles: one workgroup per tile, or (persist_grid > 0) a
+// persistent launch of persist_grid workgroups walking the tiles; the
+// planner never splits them. 256x256 tiles: the data-parallel tiles, then
+// (same stream, so after them) the split remainder.
 template <int DT, bool AK, bool BKM>
-int launch_variant(const TiledArgs& a, int tile_n, void* stream) {
+int launch_variant(const TiledArgs& a, int tile_n, int persist_grid, void* stream) {
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (tile_n == 128) return a.dp_tiles > 0 ? launch_mode<DT, Dp128<AK, BKM>, false>(a, a.dp_tiles, s) : 0;
+    if (tile_n == 128) {
+        if (persist_grid > 0)
+            return a.beta != 0.0f ? launch_mode<DT, Dp128<AK, BKM>, kPersistentC>(a, persist_grid, s)
+                                  : launch_mode<DT, Dp128<AK, BKM>, kPersistent>(a, persist_grid, s);
+        return a.dp_tiles > 0 ? launch_mode<DT, Dp128<AK, BKM>, kDataParallel>(a, a.dp_tiles, s) : 0;
+    }
     if (a.dp_tiles > 0) {
-        const int e = launch_mode<DT, Dp256<AK, BKM>, false>(a, a.dp_tiles, s);
+        const int e = launch_mode<DT, Dp256<AK, BKM>, kDataParallel>(a, a.dp_tiles, s);
         if (e != 0) return e;
     }
     const int split_wgs = (a.tiles_m * a.tiles_n - a.dp_tiles) * a.sk_splits;
-    if (split_wgs > 0) return launch_mode<DT, Split256<AK, BKM>, true>(a, split_wgs, s);
+    if (split_wgs > 0) return launch_mode<DT, Split256<AK, BKM>, kSplit>(a, split_wgs, s);
     return 0;
 }
 
@@ -736,8 +894,8 @@ int launch_variant(const TiledArgs& a, int tile_n, void* stream) {
 #if defined(LT_TILED_DT) && defined(LT_TILED_AK) && defined(LT_TILED_BK)
 #define LT_CAT(dt, ak, bk) launch_tiled_##dt##ak##_##bk
 #define LT_NAME(dt, ak, bk) LT_CAT(dt, ak, bk)
-int LT_NAME(LT_TILED_DT, LT_TILED_AK, LT_TILED_BK)(const TiledArgs& a, int tile_n, void* stream) {
-    return launch_variant<LT_TILED_DT, LT_TILED_AK != 0, LT_TILED_BK != 0>(a, tile_n, stream);
+int LT_NAME(LT_TILED_DT, LT_TILED_AK, LT_TILED_BK)(const TiledArgs& a, int tile_n, int persist_grid, void* stream) {
+    return launch_variant<LT_TILED_DT, LT_TILED_AK != 0, LT_TILED_BK != 0>(a, tile_n, persist_grid, stream);
 }
 #endif
 

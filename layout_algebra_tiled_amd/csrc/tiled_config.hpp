@@ -87,6 +87,12 @@ struct Operand {
         if (KMAJ) return (uint32_t)(((int64_t)imin(row0 + r, rows - 1) * ld + 8 * c) * 2);
         return (uint32_t)(((int64_t)r * ld + imin(row0 + 8 * c, rows - 8)) * 2);
     }
+    // Bytes from the operand's base to the first row of a block tile that
+    // starts at row0: for an interior tile, offset(ld, row0, rows, ...) =
+    // tile_bytes(ld, row0) + offset(ld, 0, ROWS, ...).
+    LT_HD static constexpr int64_t tile_bytes(int64_t ld, int row0) {
+        return KMAJ ? (int64_t)row0 * ld * 2 : (int64_t)row0 * 2;
+    }
     // K offset, within its slice, of what that copy fetches.
     LT_HD static constexpr int kpos(int wave, int lane, int i) {
         return KMAJ ? 8 * src_chunk(wave, lane, i) : src_row(wave, lane, i);

@@ -43,11 +43,12 @@ def tensor_desc(t: torch.Tensor, layout: Optional[Layout] = None) -> L.lt_tensor
     return d
 
 
-def _opts(kernel: Union[str, int], tile=None, split_k: int = 0) -> L.lt_gemm_options:
+def _opts(kernel: Union[str, int], tile=None, split_k: int = 0, persistent=None) -> L.lt_gemm_options:
     o = L.lt_gemm_options()
     o.kernel = KERNELS[kernel] if isinstance(kernel, str) else int(kernel)
     o.tile_m, o.tile_n = tile if tile else (0, 0)
     o.split_k = split_k
+    o.persistent = 0 if persistent is None else (2 if persistent else 1)
     return o
 
 
@@ -59,12 +60,13 @@ def _stream(stream) -> int:
     return int(stream)
 
 
-def plan(A, B, D, C=None, beta: float = 0.0, kernel="auto", tile=None, split_k=0, layouts=None) -> dict:
+def plan(A, B, D, C=None, beta: float = 0.0, kernel="auto", tile=None, split_k=0, layouts=None,
+         persistent=None) -> dict:
     la = layouts or {}
     dA, dB, dD = tensor_desc(A, la.get("A")), tensor_desc(B, la.get("B")), tensor_desc(D, la.get("D"))
     dC = tensor_desc(C, la.get("C")) if C is not None else None
     info = L.lt_gemm_plan_info()
-    o = _opts(kernel, tile, split_k)
+    o = _opts(kernel, tile, split_k, persistent)
     L.check(L.lib().lt_gemm_plan(ctypes.byref(dA), ctypes.byref(dB), ctypes.byref(dC) if dC else None,
                                  ctypes.byref(dD), int(beta != 0.0), ctypes.byref(o), ctypes.byref(info)),
             "gemm_plan")
@@ -90,17 +92,20 @@ def _epilogue(bias, bias_stride, bias_per_row, activation, amax) -> Optional[L.l
 
 def gemm(A: torch.Tensor, B: torch.Tensor, D: torch.Tensor, C: Optional[torch.Tensor] = None,
          alpha: float = 1.0, beta: float = 0.0, *, kernel="auto", tile=None, split_k: int = 0,
-         layouts: Optional[dict] = None, workspace: Optional[torch.Tensor] = None, stream=None,
+         persistent: Optional[bool] = None, layouts: Optional[dict] = None,
+         workspace: Optional[torch.Tensor] = None, stream=None,
          bias: Optional[torch.Tensor] = None, bias_stride: int = 1, bias_per_row: bool = False,
          activation: Optional[str] = None, amax: Optional[torch.Tensor] = None) -> None:
     """D = act(alpha * A @ B + beta * C + bias) (asynchronous on ``stream``).
     ``bias`` (D's dtype, one value per column, or per row with
     ``bias_per_row``), ``activation`` ("relu", "gelu") and ``amax`` (a float32
-    device scalar receiving max |D|) select the fused epilogue."""
+    device scalar receiving max |D|) select the fused epilogue. ``persistent``
+    (None: the planner's choice) forces the persistent launch of 256x128
+    tiles on or off."""
     la = layouts or {}
     dA, dB, dD = tensor_desc(A, la.get("A")), tensor_desc(B, la.get("B")), tensor_desc(D, la.get("D"))
     dC = tensor_desc(C, la.get("C")) if C is not None else None
-    o = _opts(kernel, tile, split_k)
+    o = _opts(kernel, tile, split_k, persistent)
     ws_ptr, ws_bytes = None, 0
     sid = _stream(stream)
     if workspace is None:
@@ -128,7 +133,8 @@ def gemm(A: torch.Tensor, B: torch.Tensor, D: torch.Tensor, C: Optional[torch.Te
 
 def gemm_noalloc(A: torch.Tensor, B: torch.Tensor, D: torch.Tensor, C: Optional[torch.Tensor] = None,
                  alpha: float = 1.0, beta: float = 0.0, *, kernel="auto", tile=None, split_k: int = 0,
-                 layouts: Optional[dict] = None, stream=None, bias: Optional[torch.Tensor] = None,
+                 persistent: Optional[bool] = None, layouts: Optional[dict] = None, stream=None,
+                 bias: Optional[torch.Tensor] = None,
                  bias_stride: int = 1, bias_per_row: bool = False, activation: Optional[str] = None,
                  amax: Optional[torch.Tensor] = None) -> None:
     """gemm() through lt_gemm_run_noalloc: no workspace, no device memory
@@ -137,7 +143,7 @@ def gemm_noalloc(A: torch.Tensor, B: torch.Tensor, D: torch.Tensor, C: Optional[
     la = layouts or {}
     dA, dB, dD = tensor_desc(A, la.get("A")), tensor_desc(B, la.get("B")), tensor_desc(D, la.get("D"))
     dC = tensor_desc(C, la.get("C")) if C is not None else None
-    o = _opts(kernel, tile, split_k)
+    o = _opts(kernel, tile, split_k, persistent)
     epi = _epilogue(bias, bias_stride, bias_per_row, activation, amax)
     L.check(L.lib().lt_gemm_run_noalloc(ctypes.byref(dA), ctypes.byref(dB), ctypes.byref(dC) if dC else None,
                                         ctypes.byref(dD), float(alpha), float(beta), ctypes.byref(o),

@@ -39,7 +39,7 @@ def all_points(M: int, N: int) -> np.ndarray:
 
 def run_gemm(A: datagen.Matrix, B: datagen.Matrix, C: Optional[datagen.Matrix], D: datagen.Matrix,
              alpha: float, beta: float, kernel="auto", split_k: int = 0, tile=None,
-             expect_kernel: Optional[str] = None, label: str = ""):
+             expect_kernel: Optional[str] = None, label: str = "", persistent=None):
     """Run D = alpha*A*B + beta*C on cuda:0 through the library, D pre-filled
     with NaN (an output the kernel never writes fails any check). Returns
     (plan dict, output matrix on the CPU)."""
@@ -48,7 +48,7 @@ def run_gemm(A: datagen.Matrix, B: datagen.Matrix, C: Optional[datagen.Matrix], 
 
     M, N = D.shape
     say(f"[gemm] {label} M={M} N={N} K={A.shape[1]} {A.dtype} A{A.stride} B{B.stride} D{D.stride} "
-        f"alpha={alpha} beta={beta} kernel={kernel} tile={tile} split_k={split_k}")
+        f"alpha={alpha} beta={beta} kernel={kernel} tile={tile} split_k={split_k} persistent={persistent}")
     dev = torch.device("cuda:0")
     dA, dB, dD = A.to(dev), B.to(dev), D.to(dev)
     dC = C.to(dev) if C is not None else None
@@ -58,11 +58,11 @@ def run_gemm(A: datagen.Matrix, B: datagen.Matrix, C: Optional[datagen.Matrix], 
     if C is not None:
         lay["C"] = Layout.make(list(C.shape), list(C.stride))
     plan = g.plan(dA.store, dB.store, dD.store, dC.store if dC is not None else None, beta, kernel=kernel,
-                  tile=tile, split_k=split_k, layouts=lay)
+                  tile=tile, split_k=split_k, layouts=lay, persistent=persistent)
     if expect_kernel:
         assert plan["kernel_name"] == expect_kernel, plan
     g.gemm(dA.store, dB.store, dD.store, dC.store if dC is not None else None, alpha, beta, kernel=kernel,
-           tile=tile, split_k=split_k, layouts=lay)
+           tile=tile, split_k=split_k, layouts=lay, persistent=persistent)
     torch.cuda.synchronize()
     out = datagen.Matrix(dD.store.cpu(), D.shape, D.stride)
     say(f"[gemm] {label} ran {plan['kernel_name']} tile {plan['tile_m']}x{plan['tile_n']} grid={plan['grid']} "
@@ -113,13 +113,14 @@ def check_all_rows(A, B, C, out, alpha, beta, chunk: int = 512) -> og.CheckResul
 
 def run_and_check(A: datagen.Matrix, B: datagen.Matrix, C: Optional[datagen.Matrix], D: datagen.Matrix,
                   alpha: float, beta: float, points: Optional[np.ndarray] = None, kernel="auto",
-                  split_k: int = 0, tile=None, expect_kernel: Optional[str] = None, label: str = ""):
+                  split_k: int = 0, tile=None, expect_kernel: Optional[str] = None, label: str = "",
+                  persistent=None):
     """Run D = alpha*A*B + beta*C on cuda:0 through the library and check the
     result against the oracle (every output, or the given points). Returns
     (CheckResult, plan dict, output)."""
     M, N = D.shape
     plan, out = run_gemm(A, B, C, D, alpha, beta, kernel=kernel, split_k=split_k, tile=tile,
-                         expect_kernel=expect_kernel, label=label)
+                         expect_kernel=expect_kernel, label=label, persistent=persistent)
     res = check_points(A, B, C, out, alpha, beta, all_points(M, N) if points is None else points)
     say(f"[gemm] {label} {plan['kernel_name']} grid={plan['grid']} split_k={plan['split_k']}: {res}")
     return res, plan, out

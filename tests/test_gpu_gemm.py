@@ -115,6 +115,51 @@ def test_tiled_slice_counts_every_major(K, a_major, b_major, tile_n):
     assert plan["waves"] == 4 and plan["grid"] == (512 // 256) * (512 // tile_n) and plan["tile_n"] == tile_n
 
 
+# ---------------------------------------------------------------------------
+# the persistent launch of 256x128 tiles: one workgroup per compute unit
+# walks its tiles, copying the next tile's first slices while the current
+# one finishes (every output checked)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("M,N,K,dtype,a_major,b_major,alpha,beta", [
+    # 320 tiles, a multiple of 8 (XCD regrouping): 8 workgroups take 2 tiles,
+    # 4 K slices (the fewest the launch takes)
+    (4096, 2560, 256, BF16, "row", "col", 1.0, 0.0),
+    # 128 tiles: one each, 5 slices, M-/N-major operands, C loaded
+    (2048, 2048, 320, F16, "col", "row", 2.0, -1.0),
+    # 135 tiles, not a multiple of 8 (no regrouping)
+    (2304, 1920, 256, F16, "row", "row", 1.0, 0.5),
+    # 323 tiles on 256 workgroups without regrouping: 67 take two
+    (4864, 2176, 512, BF16, "col", "col", 1.0, 1.0),
+    # 528 tiles: 2 or 3 per workgroup; 7 slices
+    (6144, 2816, 448, BF16, "row", "col", 1.0, -0.5),
+    # 256 tiles, 16 slices, bf16 M-major A
+    (2048, 4096, 1024, BF16, "col", "col", 0.5, 0.0),
+])
+def test_tiled_persistent_all_outputs(M, N, K, dtype, a_major, b_major, alpha, beta):
+    A, B, C, D = _case(M, N, K, dtype, a_major, b_major, "row", alpha, beta, seed=M + K)
+    res, plan, _ = run_and_check(A, B, C, D, alpha, beta, kernel="tiled", tile=(256, 128), persistent=True,
+                                 expect_kernel="tiled", label="tiled-persistent")
+    _ok(res)
+    tiles = (M // 256) * (N // 128)
+    assert plan["persistent"] == 1 and plan["grid"] == min(tiles, 256) and plan["tiles"] == tiles
+
+
+def test_tiled_persistent_matches_one_workgroup_per_tile():
+    """The same problem through both launches of the 256x128 kernel: the
+    same products summed in the same order, so the outputs agree bit for
+    bit."""
+    from tests.gemm_cases import run_gemm
+    M, N, K = 4096, 2304, 512
+    A, B, C, D = _case(M, N, K, BF16, "row", "col", "row", 1.0, 0.75, seed=3)
+    p1, o1 = run_gemm(A, B, C, D, 1.0, 0.75, kernel="tiled", tile=(256, 128), persistent=True,
+                      label="persistent")
+    p0, o0 = run_gemm(A, B, C, D, 1.0, 0.75, kernel="tiled", tile=(256, 128), persistent=False,
+                      label="per-tile")
+    assert p1["persistent"] == 1 and p0["persistent"] == 0
+    assert torch.equal(o1.store.view(torch.int16), o0.store.view(torch.int16))
+
+
 def test_tiled_ragged_large_auto():
     """A ragged shape large enough for the automatic choice to take the 256x256 kernel."""
     M, N, K = 1000, 1304, 1000
@@ -270,7 +315,8 @@ def test_skinny_with_beta():
 
 
 # ---------------------------------------------------------------------------
-# more tiles than CUs (several rounds), every output: K-major and M/N-major,
+# more tiles than CUs (several rounds of one workgroup per tile; the
+# persistent launch has tests of its own), every output: K-major and M/N-major,
 # partial first slices, fewer slices than stages, ragged edges, beta != 0,
 # tile counts with and without the per-XCD regrouping of workgroups
 # ---------------------------------------------------------------------------
@@ -292,7 +338,7 @@ def test_skinny_with_beta():
 def test_many_rounds_tiled_all_outputs(M, N, K, dtype, a_major, b_major, alpha, beta, tile_n):
     A, B, C, D = _case(M, N, K, dtype, a_major, b_major, "row", alpha, beta, seed=M + K + tile_n)
     plan, out = run_gemm(A, B, C, D, alpha, beta, kernel="tiled", split_k=1, tile=(256, tile_n),
-                         expect_kernel="tiled", label=f"rounds 256x{tile_n}")
+                         expect_kernel="tiled", label=f"rounds 256x{tile_n}", persistent=False)
     tiles = ((M + 255) // 256) * ((N + tile_n - 1) // tile_n)
     assert plan["tiles"] == plan["grid"] == tiles > 256, plan
     res = check_all_rows(A, B, C, out, alpha, beta)

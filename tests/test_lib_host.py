@@ -279,9 +279,11 @@ def _desc(ptr, dtype, shape, stride):
     return d
 
 
-def _plan(A, B, C, D, bnz=0, kernel=0, split=0, tile_n=0):
+def _plan(A, B, C, D, bnz=0, kernel=0, split=0, tile_n=0, tile=None, persistent=0):
     o = L.lt_gemm_options()
-    o.kernel, o.split_k, o.tile_n = kernel, split, tile_n
+    o.kernel, o.split_k, o.tile_n, o.persistent = kernel, split, tile_n, persistent
+    if tile:
+        o.tile_m, o.tile_n = tile
     info = L.lt_gemm_plan_info()
     st = L.lib().lt_gemm_plan(ctypes.byref(A), ctypes.byref(B), ctypes.byref(C) if C else None, ctypes.byref(D),
                               bnz, ctypes.byref(o), ctypes.byref(info))
@@ -501,30 +503,60 @@ def test_plan_tile_choice_and_split_remainder():
         st, i = _plan(*_gemm_descs(M, N, K), kernel=L.LT_KERNEL_TILED, split=split)
         assert st == "LT_OK" and i.kernel == L.LT_KERNEL_TILED, (M, N, K, st)
         tn, dp, rem, S = _tile_plan(M, N, K, split)
-        assert (i.tile_n, i.sk_tiles, i.split_k, i.grid) == (tn, rem, S, dp + rem * S), \
-            (M, N, K, i.tile_n, i.sk_tiles, i.split_k, i.grid)
+        # 256x128 tiles run persistent (one workgroup per CU) when whole, K
+        # a multiple of 64 with at least 4 slices, and more than 256 of them
+        pers = tn == 128 and M % 256 == 0 and N % 128 == 0 and K % 64 == 0 and K >= 256 and dp > 256
+        grid = 256 if pers else dp + rem * S
+        assert (i.tile_n, i.sk_tiles, i.split_k, i.grid, i.persistent) == (tn, rem, S, grid, int(pers)), \
+            (M, N, K, i.tile_n, i.sk_tiles, i.split_k, i.grid, i.persistent)
         assert i.tiles == dp + rem
         assert i.sk_workgroups == rem * S
         want_ws = ((rem * 4 + 255) // 256 * 256 + rem * S * 256 * 256 * 4) if rem else 0
         assert i.workspace_bytes == want_ws
     # the 6144x4096x2048 workload: 384 256x256 tiles = 1.5 rounds, and K is
     # too short (32 slices) for the split to pay; 768 256x128 tiles fill
-    # three whole rounds
+    # three whole rounds, walked by 256 persistent workgroups when beta = 0,
+    # one workgroup per tile with beta != 0 (C staged through LDS)
     st, i = _plan(*_gemm_descs(6144, 4096, 2048, a="m", b="n"))
-    assert (i.tile_n, i.sk_tiles, i.tiles, i.grid) == (128, 0, 768, 768)
+    assert (i.tile_n, i.sk_tiles, i.tiles, i.grid, i.persistent) == (128, 0, 768, 256, 1)
+    A, B, C, D = _gemm_descs(6144, 4096, 2048, a="m", b="n")
+    st, i = _plan(A, B, C, D, bnz=1)
+    assert st == "LT_OK" and (i.tile_n, i.tiles, i.grid, i.persistent) == (128, 768, 768, 0)
     # 8192^3: 1,024 256x256 tiles are four whole rounds, one per workgroup
     st, i = _plan(*_gemm_descs(8192, 8192, 8192))
     assert (i.tile_n, i.sk_tiles, i.tiles, i.grid) == (256, 0, 1024, 1024)
     # 49 256x256 tiles of 110 slices: a 5-way split would pay 4 partials'
     # read-back (measured 90.3 us); 98 whole 256x128 tiles win (80.2 us)
     st, i = _plan(*_gemm_descs(1792, 1792, 7040))
-    assert (i.tile_n, i.sk_tiles, i.split_k, i.grid) == (128, 0, 1, 98)
+    assert (i.tile_n, i.sk_tiles, i.split_k, i.grid, i.persistent) == (128, 0, 1, 98, 0)
     # 64 256x256 tiles of 128 slices: 4 segments each (256 workgroups)
     st, i = _plan(*_gemm_descs(2048, 2048, 8192))
     assert (i.tile_n, i.sk_tiles, i.split_k, i.grid) == (256, 64, 4, 256)
     # 1,056 tiles: four whole rounds and 32 tiles split 8 ways (a 4 % saving)
     st, i = _plan(*_gemm_descs(8192, 8448, 8192))
     assert (i.tile_n, i.sk_tiles, i.split_k, i.grid) == (256, 32, 8, 1024 + 256)
+
+
+def test_plan_persistent_option():
+    """persistent = 2 forces the persistent launch of 256x128 tiles (grid
+    min(tiles, 256)), refused (LT_ERR_UNSUPPORTED) for ragged tiles, K not a
+    multiple of 64 or fewer than 4 slices; 1 turns it off; other values are
+    invalid."""
+    def plan(M, N, K, pers, tile_n=128):
+        return _plan(*_gemm_descs(M, N, K), kernel=L.LT_KERNEL_TILED, tile=(256, tile_n), persistent=pers)
+    st, i = plan(2048, 2048, 320, 2)
+    assert st == "LT_OK" and (i.persistent, i.grid, i.tiles) == (1, 128, 128)
+    st, i = plan(4864, 2176, 512, 2)
+    assert st == "LT_OK" and (i.persistent, i.grid, i.tiles) == (1, 256, 323)
+    st, i = plan(6144, 4096, 2048, 1)
+    assert st == "LT_OK" and (i.persistent, i.grid) == (0, 768)
+    st, i = plan(6144, 4096, 2048, 0)
+    assert st == "LT_OK" and (i.persistent, i.grid) == (1, 256)
+    for M, N, K in ((2000, 2048, 256), (2048, 2000, 256), (2048, 2048, 200), (2048, 2048, 192)):
+        assert plan(M, N, K, 2)[0] == "LT_ERR_UNSUPPORTED", (M, N, K)
+        assert plan(M, N, K, 0)[1].persistent == 0
+    assert plan(2048, 2048, 256, 2, tile_n=256)[0] == "LT_ERR_UNSUPPORTED"
+    assert plan(2048, 2048, 256, 3)[0] == "LT_ERR_INVALID_ARGUMENT"
 
 
 def test_plan_m_major_output_is_transposed():

@@ -208,3 +208,23 @@ def test_trace_catches_a_wrong_swizzle_reading(tracer):
         r, c = right[q]
         assert off == 2 * (off0 + ol.evaluate(tile, (8 * c, r, 0)))
     assert mism > 0
+
+
+@pytest.mark.parametrize("cfg,op,kmaj,ld", [(1, "a", 1, 520), (1, "b", 1, 584), (1, "a", 0, 4096), (1, "b", 0, 640),
+                                            (0, "a", 1, 1032), (0, "b", 0, 2048)])
+def test_persistent_offsets_are_row0_offsets_plus_a_tile_base(tracer, cfg, op, kmaj, ld):
+    """The persistent launch copies an interior tile through the offsets of a
+    tile at row 0 plus a uniform tile base: for every copy, the offset the
+    per-tile launch computes for a tile starting at row0 equals the row-0
+    offset plus the element offset of (row0, k = 0) in the operand's
+    layout (oracle evaluate), times two bytes."""
+    ROWSZ = ROWS[(cfg, op)]
+    rows = 16 * ROWSZ
+    (r0,) = tracer([(cfg, op, kmaj, ld, ROWSZ, 0)])
+    L = operand_layout(kmaj, rows, 64, ld)
+    for t in (1, 5, 15):
+        row0 = t * ROWSZ
+        (rt,) = tracer([(cfg, op, kmaj, ld, rows, row0)])
+        base = 2 * ol.evaluate(L, (row0, 0))
+        assert [q for q, _ in rt["copies"]] == [q for q, _ in r0["copies"]]
+        assert all(o1 == base + o0 for (_, o1), (_, o0) in zip(rt["copies"], r0["copies"])), (cfg, op, kmaj, t)
