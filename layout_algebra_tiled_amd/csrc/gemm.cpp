@@ -339,10 +339,12 @@ lt_status make_plan(const lt_tensor* tA, const lt_tensor* tB, const lt_tensor* t
             // persistent with beta = 0.)
             const int want_p = opt ? opt->persistent : 0;
             if (want_p < 0 || want_p > 2) return LT_ERR_INVALID_ARGUMENT;
-            const bool persist_ok =
-                tile_n == 128 && p.M % tsc.bm == 0 && p.N % tsc.bn == 0 && p.K % tsc.bk == 0 && KTt >= 4;
+            // (256x256 tiles: beta = 0 and no split remainder only)
+            const bool persist_ok = (tile_n == 128 || (!beta_nonzero && rem == 0)) && p.M % tsc.bm == 0 &&
+                                    p.N % tsc.bn == 0 && p.K % tsc.bk == 0 && KTt >= 4;
             if (want_p == 2 && !persist_ok) return LT_ERR_UNSUPPORTED;
-            const bool persist = persist_ok && (want_p == 2 || (want_p == 0 && ntiles > kCUs && !beta_nonzero));
+            const bool persist =
+                persist_ok && (want_p == 2 || (want_p == 0 && tile_n == 128 && ntiles > kCUs && !beta_nonzero));
             p.persist_grid = persist ? (int)std::min<int64_t>(ntiles, kCUs) : 0;
             in.persistent = persist ? 1 : 0;
             p.tile_n = tile_n;

@@ -691,20 +691,21 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
     };
     // ---- persistent launch (whole tiles, K a multiple of BK, NS >= 4): the
     // K loop runs over the concatenation of this workgroup's tiles' slices,
-    // so the next tile's first two slices are copied while the current
-    // tile's last slices run, and its third right after the current tile's
-    // epilogue. (The compiler places the epilogue's waits for the C values
-    // counting only the loads it sees, not the copies, so those waits also
-    // cover every copy issued before the epilogue: the third slice's copies
+    // so the next tile's first S-1 slices are copied while the current
+    // tile's last slices run, and its slice S-1 right after the current
+    // tile's epilogue. (The compiler places the epilogue's waits for the C
+    // values counting only the loads it sees, not the copies, so those waits
+    // also cover every copy issued before the epilogue: slice S-1's copies
     // come after it so that the epilogue never waits for them.) ("CUTLASS,
     // in depth", "Kernel schedules": a persistent kernel walks tiles from a
     // tile scheduler and overlaps one tile's epilogue with the next tile's
     // main loop.)
     if constexpr (PERS) {
-        static_assert(Cf::EXPLICIT && S == 3 && KS % 2 == 0, "the persistent launch runs the 3-stage explicit schedule");
         constexpr bool WITH_C = MODE == kPersistentC;
+        static_assert(Cf::EXPLICIT && KS % 2 == 0 && (S == 3 || (S == 2 && !WITH_C)),
+                      "the persistent launch runs the explicit schedule: 3 stages, or 2 without C");
         constexpr int NCL = FM * FN * NG;   // C loads per lane, one group of four outputs each
-        static_assert(Cf::IPW + NCL < 64, "vmcnt range");
+        static_assert(!WITH_C || Cf::IPW + NCL < 64, "vmcnt range");
         u32x2 cvp[FM][FN][NG];
         auto load_c_regs = [&]() {
             for_blocks<FM, FN>([&](auto i, auto j) {
@@ -761,13 +762,13 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
             slice_x(yes, yes, ref_a(1), ref_b(1), ic<0>{}, ic<0>{}, no, ic<W01>{});
             for (int t = 2; t + 1 < NS; ++t) slice_x(yes, yes, ref_a(t), ref_b(t), ic<0>{}, ic<0>{}, no, ic<-1>{});
             // the tile's last slice: the barrier waits for the next tile's
-            // slice 0 while its slice 1 may fly
+            // slice 0 while its slices 1 .. S-2 may fly
             const int st_last = stage;
-            slice_x(yes, no, a_k0, b_k0, ic<0>{}, ic<0>{}, no, ic<Cf::IPW>{});
+            slice_x(yes, no, a_k0, b_k0, ic<0>{}, ic<0>{}, no, ic<Cf::IPW * (S - 2)>{});
             asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");   // MFMA results before VALU reads
             store_tile();
             if (!more) break;
-            issue_at(st_last, na + 2 * a_ks, nb + 2 * b_ks);   // the next tile's slice 2
+            issue_at(st_last, na + (S - 1) * a_ks, nb + (S - 1) * b_ks);   // the next tile's slice S-1
             m0 = m0n;
             n0 = n0n;
             a_k0 = na;
@@ -880,6 +881,8 @@ int launch_variant(const TiledArgs& a, int tile_n, int persist_grid, void* strea
                                   : launch_mode<DT, Dp128<AK, BKM>, kPersistent>(a, persist_grid, s);
         return a.dp_tiles > 0 ? launch_mode<DT, Dp128<AK, BKM>, kDataParallel>(a, a.dp_tiles, s) : 0;
     }
+    if (persist_grid > 0)   // 256x256 tiles, beta = 0, no split remainder
+        return a.beta == 0.0f ? launch_mode<DT, Dp256<AK, BKM>, kPersistent>(a, persist_grid, s) : -1;
     if (a.dp_tiles > 0) {
         const int e = launch_mode<DT, Dp256<AK, BKM>, kDataParallel>(a, a.dp_tiles, s);
         if (e != 0) return e;

@@ -145,6 +145,26 @@ def test_tiled_persistent_all_outputs(M, N, K, dtype, a_major, b_major, alpha, b
     assert plan["persistent"] == 1 and plan["grid"] == min(tiles, 256) and plan["tiles"] == tiles
 
 
+@pytest.mark.parametrize("M,N,K,dtype,a_major,b_major,alpha", [
+    # 320 256x256 tiles (XCD regrouping), 4 slices (the fewest)
+    (5120, 4096, 256, BF16, "row", "col", 1.0),
+    # 135 tiles, one each, no regrouping; M-/N-major, 5 slices
+    (2304, 3840, 320, F16, "col", "row", 2.0),
+    # 528 tiles: 2 or 3 per workgroup, 7 slices
+    (6144, 5632, 448, BF16, "col", "col", 1.0),
+    # 289 tiles without regrouping: 33 workgroups take two
+    (4352, 4352, 576, F16, "row", "row", -1.0),
+])
+def test_tiled_persistent_256_all_outputs(M, N, K, dtype, a_major, b_major, alpha):
+    """The persistent launch of 256x256 tiles (2 LDS stages; beta = 0)."""
+    A, B, C, D = _case(M, N, K, dtype, a_major, b_major, "row", alpha, 0.0, seed=M + N + K)
+    res, plan, _ = run_and_check(A, B, None, D, alpha, 0.0, kernel="tiled", tile=(256, 256), persistent=True,
+                                 split_k=1, expect_kernel="tiled", label="tiled-persistent-256")
+    _ok(res)
+    tiles = (M // 256) * (N // 256)
+    assert plan["persistent"] == 1 and plan["grid"] == min(tiles, 256) and plan["tiles"] == tiles
+
+
 def test_tiled_persistent_matches_one_workgroup_per_tile():
     """The same problem through both launches of the 256x128 kernel: the
     same products summed in the same order, so the outputs agree bit for

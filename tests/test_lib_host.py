@@ -538,10 +538,10 @@ def test_plan_tile_choice_and_split_remainder():
 
 
 def test_plan_persistent_option():
-    """persistent = 2 forces the persistent launch of 256x128 tiles (grid
-    min(tiles, 256)), refused (LT_ERR_UNSUPPORTED) for ragged tiles, K not a
-    multiple of 64 or fewer than 4 slices; 1 turns it off; other values are
-    invalid."""
+    """persistent = 2 forces the persistent launch (grid min(tiles, 256)),
+    refused (LT_ERR_UNSUPPORTED) for ragged tiles, K not a multiple of 64 or
+    fewer than 4 slices, and for 256x256 tiles with beta != 0 or a split
+    remainder; 1 turns it off; other values are invalid."""
     def plan(M, N, K, pers, tile_n=128):
         return _plan(*_gemm_descs(M, N, K), kernel=L.LT_KERNEL_TILED, tile=(256, tile_n), persistent=pers)
     st, i = plan(2048, 2048, 320, 2)
@@ -555,8 +555,15 @@ def test_plan_persistent_option():
     for M, N, K in ((2000, 2048, 256), (2048, 2000, 256), (2048, 2048, 200), (2048, 2048, 192)):
         assert plan(M, N, K, 2)[0] == "LT_ERR_UNSUPPORTED", (M, N, K)
         assert plan(M, N, K, 0)[1].persistent == 0
-    assert plan(2048, 2048, 256, 2, tile_n=256)[0] == "LT_ERR_UNSUPPORTED"
     assert plan(2048, 2048, 256, 3)[0] == "LT_ERR_INVALID_ARGUMENT"
+    # 256x256 tiles: forced only (beta = 0, no split remainder)
+    st, i = plan(2048, 2048, 256, 2, tile_n=256)
+    assert st == "LT_OK" and (i.persistent, i.grid, i.tiles, i.tile_n) == (1, 64, 64, 256)
+    assert plan(8192, 8192, 8192, 0, tile_n=256)[1].persistent == 0
+    A, B, C, D = _gemm_descs(2048, 2048, 256)
+    assert _plan(A, B, C, D, bnz=1, kernel=L.LT_KERNEL_TILED, tile=(256, 256), persistent=2)[0] == "LT_ERR_UNSUPPORTED"
+    # 1,056 tiles leave a split remainder: no persistent launch
+    assert plan(8192, 8448, 8192, 2, tile_n=256)[0] == "LT_ERR_UNSUPPORTED"
 
 
 def test_plan_m_major_output_is_transposed():
