@@ -194,6 +194,7 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
             step = gridDim.x;
             ntl = (p.dp_tiles - (int)blockIdx.x + step - 1) / step;
         }
+        if (ntl <= 0) return;   // (the planner launches at most one workgroup per tile)
         lin = first;
         kt0 = 0;
         kt1 = KT;
@@ -881,8 +882,9 @@ int launch_variant(const TiledArgs& a, int tile_n, int persist_grid, void* strea
                                   : launch_mode<DT, Dp128<AK, BKM>, kPersistent>(a, persist_grid, s);
         return a.dp_tiles > 0 ? launch_mode<DT, Dp128<AK, BKM>, kDataParallel>(a, a.dp_tiles, s) : 0;
     }
-    if (persist_grid > 0)   // 256x256 tiles, beta = 0, no split remainder
-        return a.beta == 0.0f ? launch_mode<DT, Dp256<AK, BKM>, kPersistent>(a, persist_grid, s) : -1;
+    if (persist_grid > 0)   // 256x256 tiles, beta = 0, no split remainder (the planner's rule)
+        return a.beta == 0.0f ? launch_mode<DT, Dp256<AK, BKM>, kPersistent>(a, persist_grid, s)
+                              : static_cast<int>(hipErrorInvalidValue);
     if (a.dp_tiles > 0) {
         const int e = launch_mode<DT, Dp256<AK, BKM>, kDataParallel>(a, a.dp_tiles, s);
         if (e != 0) return e;
