@@ -100,19 +100,86 @@ struct MNTileW {
 };
 using MNTile = MNTileW<32>;
 
-// Thread-value layouts of one mode, as logical products of compact 1-D
-// layouts ("Layouts as Algebra", "The threads are a layout too"): with T
-// threads and V values per thread,
+// ---------------------------------------------------------------------------
+// The algebra at compile time, on the one-leaf layouts the thread-value maps
+// are built from ("Layouts as Algebra", "Complement", "Composition", "Divide
+// is tiling"; "3.5 CUTLASS II", 3.5.6-3.5.8):
+//   complement(s:d, M)   = (d, M/(s*d)) : (1, s*d)   (d*s divides M),
+//   compose(A, n:1)      = A restricted to its first n offsets (n a product
+//                          of A's leading leaves, or a divisor of the first),
+//   logical_product(A, B) = (A, compose(complement(A, size(A)*cosize(B)), B)).
+// Unit leaves (extent 1) are dropped: they add nothing to an offset.
+// ---------------------------------------------------------------------------
+
+template <int N>
+LT_HD constexpr bool operator==(const Flat<N>& a, const Flat<N>& b) {
+    for (int i = 0; i < N; ++i)
+        if (a.s[i] != b.s[i] || a.d[i] != b.d[i]) return false;
+    return true;
+}
+
+LT_HD constexpr Flat<1> leaf(int s, int d) { return Flat<1>{{s}, {d}}; }
+
+LT_HD constexpr Flat<2> complement(const Flat<1>& a, int M) {
+    return Flat<2>{{a.d[0], M / (a.s[0] * a.d[0])}, {1, a.s[0] * a.d[0]}};
+}
+
+// A restricted to its first n offsets (B = n:1).
+template <int N>
+LT_HD constexpr Flat<N> compose(const Flat<N>& a, const Flat<1>& b) {
+    Flat<N> r = a;
+    int left = b.s[0];
+    for (int i = 0; i < N; ++i) {
+        const int take = left >= a.s[i] ? a.s[i] : left;
+        r.s[i] = take < 1 ? 1 : take;
+        left = take >= 1 ? left / r.s[i] : 1;
+    }
+    return r;
+}
+
+template <int N, int M>
+LT_HD constexpr Flat<N + M> concat(const Flat<N>& a, const Flat<M>& b) {
+    Flat<N + M> r{};
+    for (int i = 0; i < N; ++i) r.s[i] = a.s[i], r.d[i] = a.d[i];
+    for (int i = 0; i < M; ++i) r.s[N + i] = b.s[i], r.d[N + i] = b.d[i];
+    return r;
+}
+
+// The leaves of extent > 1, in order, padded with unit leaves to NOUT.
+template <int NOUT, int N>
+LT_HD constexpr Flat<NOUT> drop_unit(const Flat<N>& a) {
+    Flat<NOUT> r{};
+    int k = 0;
+    for (int i = 0; i < N; ++i)
+        if (a.s[i] > 1 && k < NOUT) r.s[k] = a.s[i], r.d[k] = a.d[i], ++k;
+    for (; k < NOUT; ++k) r.s[k] = 1, r.d[k] = 0;
+    return r;
+}
+
+LT_HD constexpr Flat<3> logical_product(const Flat<1>& a, const Flat<1>& b) {
+    const int m = a.s[0] * (b.cosize());
+    return concat(a, compose(complement(a, m), b));
+}
+
+// Thread-value layouts of one mode ("Layouts as Algebra", "The threads are a
+// layout too"): with T threads and V values per thread,
 //   interleaved = logical_product(T:1, V:1) = (T,V):(1,T) -- on one step the
 //                 threads take T consecutive offsets (a coalesced access);
 //   blocked     = logical_product(V:1, T:1), modes swapped, = (T,V):(V,1) --
 //                 each thread owns a run of V.
-// For compact inputs the complement inside the product is the single leaf
-// (V):(T) (resp. (T):(V)), which gives these closed forms; the host library
-// builds the same layouts through its complement and composition
+// Both are built here by the product above; the host library builds the
+// same layouts through its own complement and composition
 // (lt_make_tv_layout), and the tests compare the two.
-LT_HD constexpr Flat<2> tv_interleaved(int T, int V) { return Flat<2>{{T, V}, {1, T}}; }
-LT_HD constexpr Flat<2> tv_blocked(int T, int V) { return Flat<2>{{T, V}, {V, 1}}; }
+LT_HD constexpr Flat<2> tv_interleaved(int T, int V) {
+    return drop_unit<2>(logical_product(leaf(T, 1), leaf(V, 1)));
+}
+LT_HD constexpr Flat<2> tv_blocked(int T, int V) {
+    const Flat<2> vt = drop_unit<2>(logical_product(leaf(V, 1), leaf(T, 1)));
+    return Flat<2>{{vt.s[1], vt.s[0]}, {vt.d[1], vt.d[0]}};
+}
+static_assert(tv_interleaved(64, 1024) == Flat<2>{{64, 1024}, {1, 64}}, "interleaved closed form");
+static_assert(tv_interleaved(16, 4) == Flat<2>{{16, 4}, {1, 16}}, "interleaved closed form");
+static_assert(tv_blocked(64, 8) == Flat<2>{{64, 8}, {8, 1}}, "blocked closed form");
 
 // Direct-to-LDS copy: one instruction of one wave writes 64 consecutive
 // stored chunks (1 KiB); the thread-value layout is lane -> stored chunk, so a

@@ -45,6 +45,15 @@ struct TCfg {
 
 LT_HD constexpr int imin(int a, int b) { return a < b ? a : b; }
 
+// An operand in memory as a (rows, K) layout, A as M x K and B as N x K:
+// (rows, K):(ld, 1) when K-major, (rows, K):(1, ld) when M/N-major. Element
+// (row, k) sits at offset(row, k) elements from the operand's base.
+template <bool KMAJ>
+struct OperandLayout {
+    int64_t ld;
+    LT_HD constexpr int64_t offset(int64_t row, int64_t k) const { return KMAJ ? row * ld + k : row + k * ld; }
+};
+
 // One operand of the block tile: A (ROWS = BM rows of M) or B (ROWS = BN rows
 // of N), K-major or M/N-major.
 //   K-major:   LDS tile KTile<BK>: ROWS rows of BK elements, XOR-swizzled
@@ -78,28 +87,31 @@ struct Operand {
         return KMAJ ? KT::at(q / KT::C, q % KT::C) - KT::C * (q / KT::C) : MT::at(q / W, q % W) - W * (q / W);
     }
     // Byte offset of that source relative to the operand's base, for the K
-    // slice that starts at k = 0 (a later slice adds kslice_bytes). Rows
+    // slice that starts at k = 0 (a later slice adds kslice_bytes): the
+    // operand layout evaluated at the copied chunk's first element, whose
+    // coordinate is the block tile's origin (row0, 0) plus the chunk's place
+    // in the tile -- local_tile of the operand, then the copy's partition of
+    // the tile ("Layouts as Algebra", "The kernel, in three lines"). Rows
     // past the operand's extent `rows` (a ragged edge tile) are clamped to
     // its last row (last 8-element chunk): valid memory whose products land
     // only in outputs that are not stored.
     LT_HD static constexpr uint32_t offset(int64_t ld, int row0, int rows, int wave, int lane, int i) {
         const int r = src_row(wave, lane, i), c = src_chunk(wave, lane, i);
-        if (KMAJ) return (uint32_t)(((int64_t)imin(row0 + r, rows - 1) * ld + 8 * c) * 2);
-        return (uint32_t)(((int64_t)r * ld + imin(row0 + 8 * c, rows - 8)) * 2);
+        const OperandLayout<KMAJ> L{ld};
+        if (KMAJ) return (uint32_t)(L.offset(imin(row0 + r, rows - 1), 8 * c) * 2);
+        return (uint32_t)(L.offset(imin(row0 + 8 * c, rows - 8), r) * 2);
     }
-    // Bytes from the operand's base to the first row of a block tile that
-    // starts at row0: for an interior tile, offset(ld, row0, rows, ...) =
-    // tile_bytes(ld, row0) + offset(ld, 0, ROWS, ...).
+    // Bytes from the operand's base to the origin (row0, 0) of a block tile:
+    // for an interior tile, offset(ld, row0, rows, ...) = tile_bytes(ld,
+    // row0) + offset(ld, 0, ROWS, ...).
     LT_HD static constexpr int64_t tile_bytes(int64_t ld, int row0) {
-        return KMAJ ? (int64_t)row0 * ld * 2 : (int64_t)row0 * 2;
+        return OperandLayout<KMAJ>{ld}.offset(row0, 0) * 2;
     }
     // K offset, within its slice, of what that copy fetches.
     LT_HD static constexpr int kpos(int wave, int lane, int i) {
         return KMAJ ? 8 * src_chunk(wave, lane, i) : src_row(wave, lane, i);
     }
-    LT_HD static constexpr int64_t kslice_bytes(int64_t ld) {
-        return KMAJ ? (int64_t)Cf::BK * 2 : (int64_t)Cf::BK * ld * 2;
-    }
+    LT_HD static constexpr int64_t kslice_bytes(int64_t ld) { return OperandLayout<KMAJ>{ld}.offset(0, Cf::BK) * 2; }
     // Bytes between consecutive K rows of the M/N-major LDS tile.
     static constexpr int KROW_BYTES = W * 16;
 };
