@@ -129,7 +129,7 @@ def run_and_check(A: datagen.Matrix, B: datagen.Matrix, C: Optional[datagen.Matr
 def run_and_check_fused(A: datagen.Matrix, B: datagen.Matrix, C: Optional[datagen.Matrix], D: datagen.Matrix,
                         alpha: float, beta: float, bias: Optional[torch.Tensor], bias_per_row: bool,
                         act: Optional[str], kernel="auto", split_k: int = 0, bias_stride: int = 1,
-                        expect_kernel: Optional[str] = None, label: str = "", tile=None):
+                        expect_kernel: Optional[str] = None, label: str = "", tile=None, persistent=None):
     """The fused epilogue D = act(alpha*A*B + beta*C + bias) through
     lt_gemm_run_ex, every output checked against the oracle; also returns the
     kernel's max |D| and the max over the output it wrote."""
@@ -148,14 +148,14 @@ def run_and_check_fused(A: datagen.Matrix, B: datagen.Matrix, C: Optional[datage
     if C is not None:
         lay["C"] = Layout.make(list(C.shape), list(C.stride))
     plan = g.plan(dA.store, dB.store, dD.store, dC.store if dC is not None else None, beta, kernel=kernel,
-                  tile=tile, split_k=split_k, layouts=lay)
+                  tile=tile, split_k=split_k, layouts=lay, persistent=persistent)
     if expect_kernel:
         assert plan["kernel_name"] == expect_kernel, plan
     amax = torch.full((1,), -1.0, dtype=torch.float32, device=dev)   # the library must clear it
     dbias = bias.to(dev) if bias is not None else None
     g.gemm(dA.store, dB.store, dD.store, dC.store if dC is not None else None, alpha, beta, kernel=kernel,
            tile=tile, split_k=split_k, layouts=lay, bias=dbias, bias_stride=bias_stride, bias_per_row=bias_per_row,
-           activation=act, amax=amax)
+           activation=act, amax=amax, persistent=persistent)
     torch.cuda.synchronize()
     out = datagen.Matrix(dD.store.cpu(), D.shape, D.stride)
     points = all_points(M, N)

@@ -165,6 +165,42 @@ def test_tiled_persistent_256_all_outputs(M, N, K, dtype, a_major, b_major, alph
     assert plan["persistent"] == 1 and plan["grid"] == min(tiles, 256) and plan["tiles"] == tiles
 
 
+@pytest.mark.parametrize("tile_n", [128, 256])
+def test_tiled_persistent_in_place_d_is_c(tile_n):
+    """D == C through the persistent launch (256x128: C loaded at each
+    tile's start, D stored at its end; 256x256 runs only with beta = 0, so
+    there D == C is a plain overwrite with beta = 0)."""
+    from layout_algebra_tiled_amd import gemm as g
+    M, N, K = 2560, 2048, 256
+    beta = 0.5 if tile_n == 128 else 0.0
+    A, B, C, _ = _case(M, N, K, BF16, "row", "col", "row", 1.0, 0.5, seed=77)
+    dA, dB, dC = A.to("cuda"), B.to("cuda"), C.to("cuda")
+    p = g.plan(dA.view(), dB.view(), dC.view(), dC.view(), beta, kernel="tiled", tile=(256, tile_n),
+               persistent=True, split_k=1)
+    assert p["persistent"] == 1
+    g.gemm(dA.view(), dB.view(), dC.view(), dC.view(), 1.0, beta, kernel="tiled", tile=(256, tile_n),
+           persistent=True, split_k=1)
+    torch.cuda.synchronize()
+    pts = all_points(M, N)
+    S, T = og.gemm_points(op(A), op(B), pts)
+    Dref, Cabs = og.epilogue(S, op(C) if beta else None, pts, 1.0, beta)
+    got = og.read_points(og.Operand(dC.store.cpu(), C.shape, C.stride), pts)
+    _ok(og.check(got, Dref, T, Cabs, 1.0, BF16))
+
+
+def test_tiled_persistent_option_with_a_fused_epilogue():
+    """A fused epilogue runs one workgroup per tile even when the persistent
+    launch is asked for: the result is the fused one, every output."""
+    from tests.gemm_cases import run_and_check_fused
+    M, N, K = 2048, 2048, 256
+    A, B, C, D = _case(M, N, K, F16, "row", "col", "row", 1.0, -0.5, seed=78)
+    bias = datagen.matrix(1, N, F16, "row", "uniform", 79).view().reshape(-1).contiguous()
+    res, plan, amax, wmax = run_and_check_fused(A, B, C, D, 1.0, -0.5, bias, False, "gelu", kernel="tiled",
+                                                 tile=(256, 128), persistent=True, label="fused-persistent")
+    _ok(res)
+    assert plan["persistent"] == 1 and amax == wmax
+
+
 def test_tiled_persistent_matches_one_workgroup_per_tile():
     """The same problem through both launches of the 256x128 kernel: the
     same products summed in the same order, so the outputs agree bit for
