@@ -469,6 +469,39 @@ def split_remainder_timing(M: int, N: int, K: int, reps: int = 20):
     return rec
 
 
+def persistent_timing(reps: int = 5, n: int = 20):
+    """The fp16 6144x4096x2048 M-/N-major workload with beta = 0 (where the
+    planner takes the persistent launch of its 256x128 tiles) timed both
+    ways, interleaved: persistent and one workgroup per tile, each as the
+    median over `reps` blocks of n launches queued back to back; plus a
+    sampled check of the persistent result."""
+    import torch
+    ws = {"persistent": Workload(4, beta=0.0, persistent=None), "one_per_tile": Workload(4, beta=0.0, persistent=False)}
+    rec = {"shape": "fp16 6144x4096x2048, M-major A, N-major B, alpha=2, beta=0 (256x128 tiles)"}
+    for w in ws.values():
+        w.run(0)
+    t_end = time.perf_counter() + 0.5
+    while time.perf_counter() < t_end:
+        for w in ws.values():
+            for i in range(4):
+                w.run(i)
+        torch.cuda.synchronize()
+    res = {k: [] for k in ws}
+    for _ in range(reps):
+        for k, w in ws.items():
+            res[k].append(queued_block_time(w.run, n))
+    for k, w in ws.items():
+        p = w.plan()
+        t = sorted(res[k])[reps // 2]
+        rec[k] = {"grid": p["grid"], "persistent": bool(p["persistent"]), "kernel_us_back_to_back": round(t * 1e6, 1),
+                  "TFLOP/s": round(w.c.flops() / t / 1e12, 1)}
+    ws["persistent"].run(0)
+    chk = ws["persistent"].check(256)
+    rec["parity"] = str(chk)
+    rec["parity_ok"] = bool(chk.ok)
+    return rec
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -606,6 +639,8 @@ def main():
             torch.cuda.empty_cache()
         extra["split remainder (2048x2048x8192, 64 tiles)"] = split_remainder_timing(2048, 2048, 8192)
         log(f"[bench] split remainder: {extra['split remainder (2048x2048x8192, 64 tiles)']}")
+        extra["persistent launch (6144x4096x2048, beta 0)"] = persistent_timing()
+        log(f"[bench] persistent launch: {extra['persistent launch (6144x4096x2048, beta 0)']}")
         extra["layout map"] = layout_map_timing()
         log(f"[bench] layout map: {extra['layout map']}")
         line["extra"] = extra
