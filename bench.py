@@ -470,14 +470,14 @@ def split_remainder_timing(M: int, N: int, K: int, reps: int = 20):
 
 
 def persistent_timing(reps: int = 5, n: int = 20):
-    """The fp16 6144x4096x2048 M-/N-major workload with beta = 0 (where the
-    planner takes the persistent launch of its 256x128 tiles) timed both
+    """The fp16 6144x4096x2048 M-/N-major workload (alpha = 2, beta = -1;
+    the planner takes the persistent launch of its 256x128 tiles) timed both
     ways, interleaved: persistent and one workgroup per tile, each as the
     median over `reps` blocks of n launches queued back to back; plus a
     sampled check of the persistent result."""
     import torch
-    ws = {"persistent": Workload(4, beta=0.0, persistent=None), "one_per_tile": Workload(4, beta=0.0, persistent=False)}
-    rec = {"shape": "fp16 6144x4096x2048, M-major A, N-major B, alpha=2, beta=0 (256x128 tiles)"}
+    ws = {"persistent": Workload(4, persistent=None), "one_per_tile": Workload(4, persistent=False)}
+    rec = {"shape": "fp16 6144x4096x2048, M-major A, N-major B, alpha=2, beta=-1 (256x128 tiles)"}
     for w in ws.values():
         w.run(0)
     t_end = time.perf_counter() + 0.5
@@ -639,8 +639,8 @@ def main():
             torch.cuda.empty_cache()
         extra["split remainder (2048x2048x8192, 64 tiles)"] = split_remainder_timing(2048, 2048, 8192)
         log(f"[bench] split remainder: {extra['split remainder (2048x2048x8192, 64 tiles)']}")
-        extra["persistent launch (6144x4096x2048, beta 0)"] = persistent_timing()
-        log(f"[bench] persistent launch: {extra['persistent launch (6144x4096x2048, beta 0)']}")
+        extra["persistent launch (6144x4096x2048)"] = persistent_timing()
+        log(f"[bench] persistent launch: {extra['persistent launch (6144x4096x2048)']}")
         extra["layout map"] = layout_map_timing()
         log(f"[bench] layout map: {extra['layout map']}")
         line["extra"] = extra

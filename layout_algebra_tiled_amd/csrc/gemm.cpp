@@ -330,21 +330,19 @@ lt_status make_plan(const lt_tensor* tA, const lt_tensor* tB, const lt_tensor* t
             // tiles and copies the next tile's first slices while the
             // current one finishes. Whole tiles only, K a multiple of the
             // slice depth, at least 4 slices per tile; chosen when the
-            // tiles take more than one round of the compute units and beta
-            // is 0. (With beta != 0 the one-workgroup-per-tile launch stages
-            // C through the LDS stages its last slices free, which the
-            // persistent launch fills with the next tile's slices; its C
-            // loads into registers measured slower: 6144x4096x2048 fp16
-            // 105-113 us per tile against 107-118 persistent, 95-104 us
-            // persistent with beta = 0.)
+            // 256x128 tiles take more than one round of the compute units
+            // (fp16 6144x4096x2048, beta = -1: 106.3 us against 111.5 us one
+            // workgroup per tile; beta = 0: 101.7-107.3 against 109.3 us).
+            // 256x256 tiles (beta = 0, no split remainder) only when forced:
+            // at 8192^3 the part is at its power cap and the loop gains
+            // nothing there.
             const int want_p = opt ? opt->persistent : 0;
             if (want_p < 0 || want_p > 2) return LT_ERR_INVALID_ARGUMENT;
             // (256x256 tiles: beta = 0 and no split remainder only)
             const bool persist_ok = (tile_n == 128 || (!beta_nonzero && rem == 0)) && p.M % tsc.bm == 0 &&
                                     p.N % tsc.bn == 0 && p.K % tsc.bk == 0 && KTt >= 4;
             if (want_p == 2 && !persist_ok) return LT_ERR_UNSUPPORTED;
-            const bool persist =
-                persist_ok && (want_p == 2 || (want_p == 0 && tile_n == 128 && ntiles > kCUs && !beta_nonzero));
+            const bool persist = persist_ok && (want_p == 2 || (want_p == 0 && tile_n == 128 && ntiles > kCUs));
             p.persist_grid = persist ? (int)std::min<int64_t>(ntiles, kCUs) : 0;
             in.persistent = persist ? 1 : 0;
             p.tile_n = tile_n;

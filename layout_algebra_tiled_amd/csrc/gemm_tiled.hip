@@ -368,14 +368,17 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
     static_assert(!CPF_CFG || (CX_ROWS == 192 && Cf::NW == 4), "C prefetch layout");
     const bool cpf = CPF_CFG && p.beta != 0.0f && !p.epi.fused && m0 + Cf::BM <= p.M && n0 + Cf::BN <= p.N &&
                      NS >= S && (int64_t)p.ldc * 2 * Cf::BM < (int64_t(1) << 32);
-    auto issue_c = [&](int st, auto kc) {   // copy k of the C tile into stage st (k >= 12: rows 192..255)
+    // copy k of the C tile at (mt, nt) into the 48 KiB (k < 12) or 16 KiB
+    // (k >= 12: rows 192..255) region at `base`
+    auto issue_c_of = [&](const char* base, auto kc, int mt, int nt) {
         constexpr int k = decltype(kc)::value;
         constexpr int slot = k < 12 ? k : k - 12;
         const uint32_t cvoff =
             2u * (uint32_t)((wave * 4 + lane / 16) * p.ldc + 8 * ((lane % 16) ^ ((wave * 4 + lane / 16) & 15)));
-        const char* c_tile = reinterpret_cast<const char*>(p.C + (int64_t)(m0 + 16 * k) * p.ldc + n0);
-        copy16<0>(lds_u32(smem + st * Cf::STAGE + (slot * 4 + wave) * 1024), c_tile, cvoff);
+        const char* c_tile = reinterpret_cast<const char*>(p.C + (int64_t)(mt + 16 * k) * p.ldc + nt);
+        copy16<0>(lds_u32(base + (slot * 4 + wave) * 1024), c_tile, cvoff);
     };
+    auto issue_c = [&](const char* base, auto kc) { issue_c_of(base, kc, m0, n0); };
 
     // ---- prologue: slices 0 .. S-1
     if (kbase < 0 && kt0 == 0)
@@ -509,7 +512,7 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
                     if constexpr (copies)
                         issue_one(stage, ga, gb, ic<c>{});
                     else
-                        issue_c(stage, ic<CP == 1 ? c : 12 + c>{});
+                        issue_c(smem + stage * Cf::STAGE, ic<CP == 1 ? c : 12 + c>{});
                 }
                 constexpr int r = read_after(q, NR, NQ);
                 if constexpr (r >= 0) read_one(rstage, rs, nxt, ic<r>{});
@@ -692,29 +695,38 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
     };
     // ---- persistent launch (whole tiles, K a multiple of BK, NS >= 4): the
     // K loop runs over the concatenation of this workgroup's tiles' slices,
-    // so the next tile's first S-1 slices are copied while the current
-    // tile's last slices run, and its slice S-1 right after the current
-    // tile's epilogue. (The compiler places the epilogue's waits for the C
-    // values counting only the loads it sees, not the copies, so those waits
-    // also cover every copy issued before the epilogue: slice S-1's copies
-    // come after it so that the epilogue never waits for them.) ("CUTLASS,
-    // in depth", "Kernel schedules": a persistent kernel walks tiles from a
-    // tile scheduler and overlaps one tile's epilogue with the next tile's
-    // main loop.)
+    // so the next tile's first slices are copied while the current tile's
+    // last slices run, and one more right after the current tile's
+    // epilogue, into the stage that the last slices leave to C or to that
+    // copy. ("CUTLASS, in depth", "Kernel schedules": a persistent kernel
+    // walks tiles from a tile scheduler and overlaps one tile's epilogue
+    // with the next tile's main loop.)
     if constexpr (PERS) {
         constexpr bool WITH_C = MODE == kPersistentC;
         static_assert(Cf::EXPLICIT && KS % 2 == 0 && (S == 3 || (S == 2 && !WITH_C)),
                       "the persistent launch runs the explicit schedule: 3 stages, or 2 without C");
-        constexpr int NCL = FM * FN * NG;   // C loads per lane, one group of four outputs each
-        static_assert(!WITH_C || Cf::IPW + NCL < 64, "vmcnt range");
-        u32x2 cvp[FM][FN][NG];
-        auto load_c_regs = [&]() {
+        // With C (256x128 tiles, 3 stages): the C tile goes through LDS in
+        // row-coalesced 16-byte copies, rows 0..191 (48 KiB, one stage) in
+        // the refill slot of the tile's slice NS-2, rows 192..255 (16 KiB) in
+        // the space beside the three stages at the tile's start; the next
+        // tile's slice 1, whose slot that was, follows the epilogue.
+        static_assert(!WITH_C || (CPF_CFG && CX_ROWS == 192), "C staging layout");
+        const char* c_spare = smem + S * Cf::STAGE;
+        auto issue_c_spare = [&](int mt, int nt) {
+            static_for<12, 16>([&](auto kc) { issue_c_of(c_spare, kc, mt, nt); });
+        };
+        u32x2 cv[FM][FN][NG];
+        // C of this tile, from LDS into the accumulators' layout: rows
+        // below 192 from the stage at st_c, the others from the spare
+        // region (16-byte chunk q of row r stored at q ^ (r mod 16))
+        auto read_c_lds = [&](int st_c) {
             for_blocks<FM, FN>([&](auto i, auto j) {
-                const int m = m0 + arow0 + i * Cf::MF + Mf::out_col(lane);
+                const int r = arow0 + i * Cf::MF + Mf::out_col(lane);
+                const char* crow = r < CX_ROWS ? smem + st_c * Cf::STAGE + r * CROW : c_spare + (r - CX_ROWS) * CROW;
 #pragma unroll
                 for (int g = 0; g < NG; ++g) {
-                    const int n = n0 + brow0 + j * Cf::MF + Mf::out_row(lane, 4 * g);
-                    cvp[i][j][g] = *reinterpret_cast<const u32x2*>(p.C + (int64_t)m * p.ldc + n);
+                    const int c = brow0 + j * Cf::MF + Mf::out_row(lane, 4 * g);
+                    cv[i][j][g] = *(const LDS_AS u32x2*)(crow + 16 * ((c >> 3) ^ (r & 15)) + 2 * (c & 7));
                 }
             });
         };
@@ -727,10 +739,11 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
                     const float v[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
                                         acc[i][j][4 * g + 3]};
                     store4_c<DT>(p.D, (int64_t)m * p.ldd + n, v, p.alpha, p.beta,
-                                 WITH_C ? cvp[i][j][g] : u32x2{0u, 0u});
+                                 WITH_C ? cv[i][j][g] : u32x2{0u, 0u});
                 }
             });
         };
+        if constexpr (WITH_C) issue_c_spare(m0, n0);   // the first tile's C rows 192..255
         // Every tile runs the same slice sequence, so no control flow
         // joins while MFMA results are in flight (at a join the compiler
         // may copy accumulators): the last tile takes itself as its "next"
@@ -753,23 +766,51 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
             // the next tile's slice t+S-NS
             auto ref_a = [&](int t) { return t + S < NS ? a_k0 + (t + S) * a_ks : na + (t + S - NS) * a_ks; };
             auto ref_b = [&](int t) { return t + S < NS ? b_k0 + (t + S) * b_ks : nb + (t + S - NS) * b_ks; };
-            // C for this tile's epilogue is loaded first and flies for the
-            // whole tile: slices 0 and 1 wait for slices 1 and 2, which the C
-            // loads and one more slice follow; from slice 2 on the slice
-            // waited for is newer than the C loads
-            constexpr int W01 = WITH_C ? Cf::IPW + NCL : -1;
-            if constexpr (WITH_C) load_c_regs();
-            slice_x(yes, yes, ref_a(0), ref_b(0), ic<0>{}, ic<0>{}, yes, ic<W01>{});
-            slice_x(yes, yes, ref_a(1), ref_b(1), ic<0>{}, ic<0>{}, no, ic<W01>{});
-            for (int t = 2; t + 1 < NS; ++t) slice_x(yes, yes, ref_a(t), ref_b(t), ic<0>{}, ic<0>{}, no, ic<-1>{});
-            // the tile's last slice: the barrier waits for the next tile's
-            // slice 0 while its slices 1 .. S-2 may fly
-            const int st_last = stage;
-            slice_x(yes, no, a_k0, b_k0, ic<0>{}, ic<0>{}, no, ic<Cf::IPW * (S - 2)>{});
-            asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");   // MFMA results before VALU reads
-            store_tile();
-            if (!more) break;
-            issue_at(st_last, na + (S - 1) * a_ks, nb + (S - 1) * b_ks);   // the next tile's slice S-1
+            if constexpr (!WITH_C) {
+                slice_x(yes, yes, ref_a(0), ref_b(0), ic<0>{}, ic<0>{}, yes, ic<-1>{});
+                for (int t = 1; t + 1 < NS; ++t)
+                    slice_x(yes, yes, ref_a(t), ref_b(t), ic<0>{}, ic<0>{}, no, ic<-1>{});
+                // the tile's last slice: the barrier waits for the next
+                // tile's slice 0 while its slices 1 .. S-2 may fly
+                const int st_last = stage;
+                slice_x(yes, no, a_k0, b_k0, ic<0>{}, ic<0>{}, no, ic<Cf::IPW * (S - 2)>{});
+                asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");   // MFMA results before VALU reads
+                store_tile();
+                if (!more) break;
+                issue_at(st_last, na + (S - 1) * a_ks, nb + (S - 1) * b_ks);   // the next tile's slice S-1
+            } else {
+                // vmcnt waits (loads complete in order; a wait counts the
+                // loads issued after the one it waits for, and the epilogue's
+                // stores can only lengthen it): slice 0 waits for slice 1,
+                // after which only this tile's 4 C copies come (the first
+                // tile: its slice 2 as well); slice 1 for slice 2, after
+                // which 16 or 28 copies come (the next tile's slice 1, the C
+                // copies and slice 3); slice NS-2 for slice NS-1 with the
+                // next tile's slice 0 after it; slice NS-1 for the next
+                // tile's slice 0 with this tile's C rows 0..191 after it; the
+                // epilogue for those rows with the next tile's slice 2 after
+                // them.
+                slice_x(yes, yes, ref_a(0), ref_b(0), ic<0>{}, ic<0>{}, yes, ic<4>{});
+                slice_x(yes, yes, ref_a(1), ref_b(1), ic<0>{}, ic<0>{}, no, ic<16>{});
+                for (int t = 2; t + 2 < NS; ++t)
+                    slice_x(yes, yes, ref_a(t), ref_b(t), ic<0>{}, ic<0>{}, no, ic<-1>{});
+                // slice NS-2: its refill slot takes C rows 0..191
+                const int st_c = stage;
+                slice_x(yes, no, a_k0, b_k0, ic<0>{}, ic<1>{}, no, ic<Cf::IPW>{});
+                // slice NS-1: refilled with the next tile's slice 2
+                slice_x(yes, yes, na + 2 * a_ks, nb + 2 * b_ks, ic<0>{}, ic<0>{}, no, ic<Cf::IPW>{});
+                asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");   // MFMA results before VALU reads
+                LT_WAIT_VM(Cf::IPW);   // C rows 0..191 landed (the next tile's slice 2 may fly)
+                __syncthreads();       // every wave's C copies visible
+                read_c_lds(st_c);
+                __syncthreads();       // every wave has its C values: the stage and the spare are free
+                // the next tile's slice 1 and C rows 192..255 (the last
+                // tile: its own again, unused), then this tile's D
+                issue_at(st_c, na + a_ks, nb + b_ks);
+                issue_c_spare(m0n, n0n);
+                store_tile();
+                if (!more) break;
+            }
             m0 = m0n;
             n0 = n0n;
             a_k0 = na;
@@ -858,12 +899,21 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
 
 namespace {
 
+// LDS of a launch: the stages, plus 16 KiB for C rows 192..255 in the
+// persistent launch with C
+template <class Cf, int MODE>
+constexpr int launch_lds() {
+    return MODE == kPersistentC ? Cf::LDS + 16 * 1024 : Cf::LDS;
+}
+
 template <int DT, class Cf, int MODE>
 int launch_mode(const TiledArgs& a, int grid, hipStream_t s) {
+    constexpr int lds = launch_lds<Cf, MODE>();
+    static_assert(lds <= 160 * 1024, "LDS per workgroup");
     static std::atomic<uint64_t> attr{0};
-    if (const int e = set_lds_limit_once(reinterpret_cast<const void*>(&gemm_tiled<DT, Cf, MODE>), Cf::LDS, attr))
+    if (const int e = set_lds_limit_once(reinterpret_cast<const void*>(&gemm_tiled<DT, Cf, MODE>), lds, attr))
         return e;
-    hipLaunchKernelGGL((gemm_tiled<DT, Cf, MODE>), dim3(grid), dim3(Cf::NT), Cf::LDS, s, a);
+    hipLaunchKernelGGL((gemm_tiled<DT, Cf, MODE>), dim3(grid), dim3(Cf::NT), lds, s, a);
     return static_cast<int>(hipGetLastError());
 }
 

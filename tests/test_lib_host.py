@@ -515,13 +515,13 @@ def test_plan_tile_choice_and_split_remainder():
         assert i.workspace_bytes == want_ws
     # the 6144x4096x2048 workload: 384 256x256 tiles = 1.5 rounds, and K is
     # too short (32 slices) for the split to pay; 768 256x128 tiles fill
-    # three whole rounds, walked by 256 persistent workgroups when beta = 0,
-    # one workgroup per tile with beta != 0 (C staged through LDS)
+    # three whole rounds, walked by 256 persistent workgroups, with or
+    # without C
     st, i = _plan(*_gemm_descs(6144, 4096, 2048, a="m", b="n"))
     assert (i.tile_n, i.sk_tiles, i.tiles, i.grid, i.persistent) == (128, 0, 768, 256, 1)
     A, B, C, D = _gemm_descs(6144, 4096, 2048, a="m", b="n")
     st, i = _plan(A, B, C, D, bnz=1)
-    assert st == "LT_OK" and (i.tile_n, i.tiles, i.grid, i.persistent) == (128, 768, 768, 0)
+    assert st == "LT_OK" and (i.tile_n, i.tiles, i.grid, i.persistent) == (128, 768, 256, 1)
     # 8192^3: 1,024 256x256 tiles are four whole rounds, one per workgroup
     st, i = _plan(*_gemm_descs(8192, 8192, 8192))
     assert (i.tile_n, i.sk_tiles, i.tiles, i.grid) == (256, 0, 1024, 1024)
