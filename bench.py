@@ -637,8 +637,8 @@ def main():
             log(f"[bench] workload {cfg}: {rec}")
             del x
             torch.cuda.empty_cache()
-        extra["split remainder (2048x2048x8192, 64 tiles)"] = split_remainder_timing(2048, 2048, 8192)
-        log(f"[bench] split remainder: {extra['split remainder (2048x2048x8192, 64 tiles)']}")
+        extra["split remainder (8192x8448x8192, 1,056 tiles)"] = split_remainder_timing(8192, 8448, 8192, reps=10)
+        log(f"[bench] split remainder: {extra['split remainder (8192x8448x8192, 1,056 tiles)']}")
         extra["persistent launch (6144x4096x2048)"] = persistent_timing()
         log(f"[bench] persistent launch: {extra['persistent launch (6144x4096x2048)']}")
         extra["layout map"] = layout_map_timing()

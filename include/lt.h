@@ -292,12 +292,12 @@ typedef struct lt_gemm_options {
                            tile past the last whole round of 256 CUs (0: chosen by a
                            cost model; 1: none, all tiles whole; > 1: forced, on all
                            tiles when they fill no whole round) */
-    int32_t persistent; /* TILED: 0 = chosen (persistent for 256x128 tiles when the
-                           tiles are whole, K is a multiple of 64 with at least 4
-                           slices and there are more tiles than compute units);
-                           1 = one workgroup per tile; 2 = persistent, also for
-                           256x256 tiles with beta = 0 and no split remainder
-                           (LT_ERR_UNSUPPORTED where those conditions fail) */
+    int32_t persistent; /* TILED: 0 = chosen (persistent when the tiles are whole, K
+                           is a multiple of 64 with at least 4 slices, there are
+                           more tiles than compute units, and for 256x256 tiles
+                           beta = 0, no split remainder and K <= 4096); 1 = one workgroup per
+                           tile; 2 = persistent (LT_ERR_UNSUPPORTED where the tile,
+                           K, beta or split conditions fail) */
 } lt_gemm_options;
 
 /* What the planner chose, for banners and tests [P1 "Exercise": print the

@@ -329,20 +329,25 @@ lt_status make_plan(const lt_tensor* tA, const lt_tensor* tB, const lt_tensor* t
             // "Kernel schedules"): one workgroup per compute unit walks its
             // tiles and copies the next tile's first slices while the
             // current one finishes. Whole tiles only, K a multiple of the
-            // slice depth, at least 4 slices per tile; chosen when the
-            // 256x128 tiles take more than one round of the compute units
-            // (fp16 6144x4096x2048, beta = -1: 106.3 us against 111.5 us one
-            // workgroup per tile; beta = 0: 101.7-107.3 against 109.3 us).
-            // 256x256 tiles (beta = 0, no split remainder) only when forced:
-            // at 8192^3 the part is at its power cap and the loop gains
-            // nothing there.
+            // slice depth, at least 4 slices per tile, and for 256x256 tiles
+            // beta = 0 and no split remainder; chosen when the tiles take
+            // more than one round of the compute units, for 256x256 tiles up
+            // to 64 slices. Measured against one workgroup per tile (kernel
+            // traces, interleaved): fp16 6144x4096x2048 256x128, beta = -1
+            // 106.3 vs 111.5 us, beta = 0 101.7-107.3 vs 109.3 us; bf16
+            // 256x256 8192^2 x 2048 214.5 vs 223.0 us, 6144x8192x4096 306.3
+            // vs 311.6 us, 8192^2 x 4096 421.1 vs 425.5 us; at 8192^3 (128
+            // slices, the part at its power cap) 752.0 vs 748.6 us with
+            // events around each launch, so longer K stays one workgroup per
+            // tile.
             const int want_p = opt ? opt->persistent : 0;
             if (want_p < 0 || want_p > 2) return LT_ERR_INVALID_ARGUMENT;
             // (256x256 tiles: beta = 0 and no split remainder only)
             const bool persist_ok = (tile_n == 128 || (!beta_nonzero && rem == 0)) && p.M % tsc.bm == 0 &&
                                     p.N % tsc.bn == 0 && p.K % tsc.bk == 0 && KTt >= 4;
             if (want_p == 2 && !persist_ok) return LT_ERR_UNSUPPORTED;
-            const bool persist = persist_ok && (want_p == 2 || (want_p == 0 && tile_n == 128 && ntiles > kCUs));
+            const bool persist =
+                persist_ok && (want_p == 2 || (want_p == 0 && ntiles > kCUs && (tile_n == 128 || KTt <= 64)));
             p.persist_grid = persist ? (int)std::min<int64_t>(ntiles, kCUs) : 0;
             in.persistent = persist ? 1 : 0;
             p.tile_n = tile_n;

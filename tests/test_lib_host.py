@@ -327,7 +327,7 @@ def test_plan_kernel_choice_for_the_workloads():
     st, i = _plan(*_gemm_descs(4096, 4096, 4096, L.LT_F16), bnz=1)
     assert st == "LT_OK" and i.kernel == L.LT_KERNEL_TILED and i.grid == 256
     st, i = _plan(*_gemm_descs(8192, 8192, 8192))
-    assert st == "LT_OK" and i.kernel == L.LT_KERNEL_TILED and (i.tiles, i.grid) == (1024, 1024)
+    assert st == "LT_OK" and i.kernel == L.LT_KERNEL_TILED and (i.tiles, i.grid, i.persistent) == (1024, 1024, 0)
     assert (i.tile_m, i.tile_n) == (256, 256) and i.tile_k in (32, 64) and i.waves in (4, 8)
     assert i.waves * i.wave_m * i.wave_n == 256 * 256 and i.stages >= 2
     st, i = _plan(*_gemm_descs(32, 8192, 8192))
@@ -503,9 +503,11 @@ def test_plan_tile_choice_and_split_remainder():
         st, i = _plan(*_gemm_descs(M, N, K), kernel=L.LT_KERNEL_TILED, split=split)
         assert st == "LT_OK" and i.kernel == L.LT_KERNEL_TILED, (M, N, K, st)
         tn, dp, rem, S = _tile_plan(M, N, K, split)
-        # 256x128 tiles run persistent (one workgroup per CU) when whole, K
-        # a multiple of 64 with at least 4 slices, and more than 256 of them
-        pers = tn == 128 and M % 256 == 0 and N % 128 == 0 and K % 64 == 0 and K >= 256 and dp > 256
+        # tiles run persistent (one workgroup per CU) when whole, K a
+        # multiple of 64 with at least 4 slices, more than 256 of them, and
+        # for 256x256 tiles no split remainder (beta = 0 here)
+        pers = (M % 256 == 0 and N % tn == 0 and K % 64 == 0 and K >= 256 and dp > 256 and rem == 0
+                and (tn == 128 or K <= 4096))
         grid = 256 if pers else dp + rem * S
         assert (i.tile_n, i.sk_tiles, i.split_k, i.grid, i.persistent) == (tn, rem, S, grid, int(pers)), \
             (M, N, K, i.tile_n, i.sk_tiles, i.split_k, i.grid, i.persistent)
@@ -523,8 +525,16 @@ def test_plan_tile_choice_and_split_remainder():
     st, i = _plan(A, B, C, D, bnz=1)
     assert st == "LT_OK" and (i.tile_n, i.tiles, i.grid, i.persistent) == (128, 768, 256, 1)
     # 8192^3: 1,024 256x256 tiles are four whole rounds, one per workgroup
+    # (128 slices: past the persistent launch's range for 256x256 tiles);
+    # at K = 4096 256 persistent workgroups walk them (beta = 0), with
+    # beta != 0 one workgroup per tile
     st, i = _plan(*_gemm_descs(8192, 8192, 8192))
-    assert (i.tile_n, i.sk_tiles, i.tiles, i.grid) == (256, 0, 1024, 1024)
+    assert (i.tile_n, i.sk_tiles, i.tiles, i.grid, i.persistent) == (256, 0, 1024, 1024, 0)
+    st, i = _plan(*_gemm_descs(8192, 8192, 4096))
+    assert (i.tile_n, i.sk_tiles, i.tiles, i.grid, i.persistent) == (256, 0, 1024, 256, 1)
+    A, B, C, D = _gemm_descs(8192, 8192, 4096)
+    st, i = _plan(A, B, C, D, bnz=1)
+    assert (i.tile_n, i.sk_tiles, i.tiles, i.grid, i.persistent) == (256, 0, 1024, 1024, 0)
     # 49 256x256 tiles of 110 slices: a 5-way split would pay 4 partials'
     # read-back (measured 90.3 us); 98 whole 256x128 tiles win (80.2 us)
     st, i = _plan(*_gemm_descs(1792, 1792, 7040))
@@ -556,10 +566,13 @@ def test_plan_persistent_option():
         assert plan(M, N, K, 2)[0] == "LT_ERR_UNSUPPORTED", (M, N, K)
         assert plan(M, N, K, 0)[1].persistent == 0
     assert plan(2048, 2048, 256, 3)[0] == "LT_ERR_INVALID_ARGUMENT"
-    # 256x256 tiles: forced only (beta = 0, no split remainder)
+    # 256x256 tiles (beta = 0, no split remainder): chosen past one round
     st, i = plan(2048, 2048, 256, 2, tile_n=256)
     assert st == "LT_OK" and (i.persistent, i.grid, i.tiles, i.tile_n) == (1, 64, 64, 256)
+    assert plan(2048, 2048, 256, 0, tile_n=256)[1].persistent == 0
+    assert plan(8192, 8192, 4096, 0, tile_n=256)[1].persistent == 1
     assert plan(8192, 8192, 8192, 0, tile_n=256)[1].persistent == 0
+    assert plan(8192, 8192, 8192, 2, tile_n=256)[1].persistent == 1
     A, B, C, D = _gemm_descs(2048, 2048, 256)
     assert _plan(A, B, C, D, bnz=1, kernel=L.LT_KERNEL_TILED, tile=(256, 256), persistent=2)[0] == "LT_ERR_UNSUPPORTED"
     # 1,056 tiles leave a split remainder: no persistent launch
