@@ -275,7 +275,11 @@ lt_status make_plan(const lt_tensor* tA, const lt_tensor* tB, const lt_tensor* t
             //     each): whole rounds, ceil(KT/S), and 12 slices for each of
             //     the S-1 fp32 partials the last segment reads back through
             //     the coherent path (measured: 58 us for 4 partials, 125 us
-            //     for 7), all times 2; taken when it saves 3 %;
+            //     for 7), plus 24 when all 256x128 tiles fit one round (a
+            //     partial costs about the same time, 9-10 us, but slices run
+            //     faster on a part-empty chip: 2048x2048x8192 measured 87-90
+            //     us in 128 whole 256x128 tiles against 91-92 us split 4
+            //     ways), all times 2; taken when it saves 3 %;
             //   256x128: ceil(n128/kCUs) * KT * 23/20 (a 256x128 tile reads
             //     a sixth more LDS bytes per flop and has half the work to
             //     hide its prologue and epilogue behind).
@@ -284,6 +288,7 @@ lt_status make_plan(const lt_tensor* tA, const lt_tensor* tB, const lt_tensor* t
             // round's).
             const int64_t KTt = (p.K + ts.bk - 1) / ts.bk;
             const int64_t n256 = tm_ * tn_;
+            const int64_t n128 = tm_ * ((p.N + 127) / 128);
             int64_t rem = n256 % kCUs;
             int64_t S = 1;
             int64_t c256 = (n256 + kCUs - 1) / kCUs * KTt * 2;
@@ -291,7 +296,8 @@ lt_status make_plan(const lt_tensor* tA, const lt_tensor* tB, const lt_tensor* t
                 if (rem != 0) {
                     S = std::min<int64_t>({kCUs / rem, 8, KTt / 4});
                     if (S >= 2) {
-                        const int64_t t_split = (n256 / kCUs * KTt + (KTt + S - 1) / S + 12 * (S - 1)) * 2;
+                        const int64_t t_split =
+                            (n256 / kCUs * KTt + (KTt + S - 1) / S + 12 * (S - 1) + (n128 <= kCUs ? 24 : 0)) * 2;
                         if (100 * t_split < 97 * c256)
                             c256 = t_split;
                         else
@@ -306,7 +312,6 @@ lt_status make_plan(const lt_tensor* tA, const lt_tensor* tB, const lt_tensor* t
                 S = 1;
                 rem = 0;
             }
-            const int64_t n128 = tm_ * ((p.N + 127) / 128);
             const int64_t c128x20 = (n128 + kCUs - 1) / kCUs * KTt * 23;
             int tile_n = 256;
             if (want_n == 128 || (want_n == 0 && split <= 1 && c128x20 < c256 * 20)) tile_n = 128;

@@ -236,7 +236,8 @@ def test_tiled_ragged_large_auto():
     (512, 512, 640, F16, "row", "col", 0.5, 3),        # forced: segments of 3, 3 and 4 slices
     (300, 520, 200, BF16, "row", "col", -1.0, 2),      # ragged tiles, partial first slice
     (264, 392, 77, F16, "col", "row", 2.0, 2),         # M-/N-major operands
-    (2048, 2048, 8192, BF16, "row", "col", 0.0, 0),    # 64 tiles x 128 slices: 4 segments each
+    (2048, 2048, 8192, BF16, "row", "col", 0.0, 4),    # forced: 64 tiles x 128 slices, 4 segments each
+    (1024, 1024, 16384, BF16, "row", "col", 0.0, 0),   # the planner's split: 16 tiles x 256 slices, 8 segments
     (512, 512, 512, BF16, "row", "col", 1.0, 1),       # forced off: data-parallel only
 ])
 def test_tiled_split_remainder_all_outputs(M, N, K, dtype, a_major, b_major, beta, split):

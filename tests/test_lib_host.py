@@ -467,19 +467,20 @@ def _tile_plan(M, N, K, split=0, want_n=0):
     """The planner's rule, written out, in K-slice times of a 256x128 tile:
     256x256 tiles cost 2 per slice; their whole rounds of 256 tiles stay
     data-parallel and the last round's rem tiles are split into S K segments
-    when that saves 3 % (12 slices per partial the last segment reads back)
-    or when forced;
+    when that saves 3 % (12 slices per partial the last segment reads back,
+    plus 24 when all 256x128 tiles fit one round) or when forced;
     256x128 tiles cost 23/20 per slice and are never split. Returns
     (tile_n, data-parallel tiles, split tiles, S)."""
     kt = -(-K // 64)
     n256 = -(-M // 256) * -(-N // 256)
+    n128 = -(-M // 256) * -(-N // 128)
     rem, S = n256 % 256, 1
     c256 = -(-n256 // 256) * kt * 2
     if split == 0:
         if rem:
             S = min(256 // rem, 8, kt // 4)
             if S >= 2:
-                t_split = (n256 // 256 * kt + -(-kt // S) + 12 * (S - 1)) * 2
+                t_split = (n256 // 256 * kt + -(-kt // S) + 12 * (S - 1) + (24 if n128 <= 256 else 0)) * 2
                 if 100 * t_split < 97 * c256:
                     c256 = t_split
                 else:
@@ -539,9 +540,13 @@ def test_plan_tile_choice_and_split_remainder():
     # read-back (measured 90.3 us); 98 whole 256x128 tiles win (80.2 us)
     st, i = _plan(*_gemm_descs(1792, 1792, 7040))
     assert (i.tile_n, i.sk_tiles, i.split_k, i.grid, i.persistent) == (128, 0, 1, 98, 0)
-    # 64 256x256 tiles of 128 slices: 4 segments each (256 workgroups)
+    # 64 256x256 tiles of 128 slices: one round of 128 whole 256x128 tiles
+    # beats 4 segments each (87-90 vs 91-92 us measured); 16 tiles of 256
+    # slices split 8 ways (128 workgroups)
     st, i = _plan(*_gemm_descs(2048, 2048, 8192))
-    assert (i.tile_n, i.sk_tiles, i.split_k, i.grid) == (256, 64, 4, 256)
+    assert (i.tile_n, i.sk_tiles, i.split_k, i.grid) == (128, 0, 1, 128)
+    st, i = _plan(*_gemm_descs(1024, 1024, 16384))
+    assert (i.tile_n, i.sk_tiles, i.split_k, i.grid) == (256, 16, 8, 128)
     # 1,056 tiles: four whole rounds and 32 tiles split 8 ways (a 4 % saving)
     st, i = _plan(*_gemm_descs(8192, 8448, 8192))
     assert (i.tile_n, i.sk_tiles, i.split_k, i.grid) == (256, 32, 8, 1024 + 256)
