@@ -747,8 +747,9 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
         // Every tile runs the same slice sequence, so no control flow
         // joins while MFMA results are in flight (at a join the compiler
         // may copy accumulators): the last tile takes itself as its "next"
-        // tile, whose first two slices are then copied again into stages
-        // nobody reads, and waited for before the workgroup ends.
+        // tile, whose first slices (and C rows 192..255) are then copied
+        // again into LDS nobody reads, and waited for before the workgroup
+        // ends.
         int m0n = m0, n0n = n0;
         const char* na = a_k0;
         const char* nb = b_k0;
