@@ -230,4 +230,19 @@ struct Mfma {
     LT_HD static constexpr int out_col(int lane) { return lane % MF; }
 };
 
+// Rows of the staged D store in LDS: rows of CPR 16-byte chunks (128 or
+// 256 bytes), row after row; chunk q of row r sits at position q ^ ((r /
+// (16/CPR)) mod CPR) of its row. The 16/CPR rows that share one 256-byte
+// (64-bank) window then place a given chunk q in 16 distinct bank groups
+// over any 16 consecutive rows, and one row's chunks in distinct groups.
+// (chunk_at inverts it: the chunk stored at position pos of row r, which a
+// direct-to-LDS copy, writing position pos, fetches.)
+template <int CPR>
+struct StagedRows {
+    static_assert(CPR == 8 || CPR == 16, "rows of 128 or 256 bytes");
+    LT_HD static constexpr int swz(int r) { return (r / (16 / CPR)) & (CPR - 1); }
+    LT_HD static constexpr int at(int r, int q) { return 16 * (r * CPR + (q ^ swz(r))); }
+    LT_HD static constexpr int chunk_at(int r, int pos) { return pos ^ swz(r); }
+};
+
 }  // namespace lt::dev

@@ -150,6 +150,23 @@ __device__ __forceinline__ void copy16(uint32_t lds, const char* gbase, uint32_t
 }
 #pragma clang diagnostic pop
 
+// The plain epilogue of a whole tile stores D through LDS beside the ring
+// (the persistent launches, with C or without, and the data-parallel launch
+// with K-major A and B and beta = 0: with M/N-major operands the fragment
+// offsets leave the data-parallel kernel no registers for it): 32 KiB when
+// the ring leaves that much of the 160 KiB, else 16 KiB, split evenly over
+// the waves. (The persistent launch with C shares those 16 KiB with the
+// next tile's C rows 192..255, copied after the store.)
+template <class Cf, int MODE>
+constexpr bool staged_d() {
+    return Cf::EXPLICIT &&
+           (MODE == kPersistent || MODE == kPersistentC || (MODE == kDataParallel && Cf::AK && Cf::BKM));
+}
+template <class Cf, int MODE>
+constexpr int staged_d_bytes() {
+    return !staged_d<Cf, MODE>() ? 0 : 160 * 1024 - Cf::LDS >= 32 * 1024 ? 32 * 1024 : 16 * 1024;
+}
+
 }  // namespace
 
 // The kernel's body is compiled in the device pass only: the host pass needs
@@ -550,9 +567,123 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
     // trip per tile, not one per block); the fragment registers are free by
     // now and hold them.
     constexpr int NG = Mf::NACC / 4;   // groups of four outputs per block
+    // ---- staged store of a whole tile with beta = 0. In the accumulators'
+    // layout the 16 lanes of a quarter-wave store 8 bytes to each of 16
+    // rows, so one store instruction reaches 64 cache lines. Staged through
+    // LDS, the 16 lanes store 256 contiguous bytes of one row (two rows of
+    // 128 with 64-column wave tiles): 8 lines per instruction, and half the
+    // instructions. Each wave owns DSW bytes beside the ring and runs
+    // passes of RPP rows of its wave tile: it writes them in the
+    // accumulators' layout (8 bytes per lane), reads them back 16 bytes per
+    // lane along the rows and stores them. The region is the wave's own and
+    // LDS executes one wave's instructions in order, so no barrier is
+    // needed. The rows are swizzled (dev::StagedRows) so that the writes
+    // (16 rows, one column group) and the reads (one or two rows) each
+    // reach every bank once.
+    constexpr bool STAGED_D = staged_d<Cf, MODE>();
+    constexpr int DSW = staged_d_bytes<Cf, MODE>() / Cf::NW;   // bytes per wave
+    constexpr int RB = Cf::TWN * 2;                             // bytes of one wave-tile row
+    constexpr int CPR = RB / 16;                                // its 16-byte chunks
+    constexpr int RPP = STAGED_D ? DSW / RB : Cf::MF;           // rows per pass
+    constexpr int BPP = RPP / Cf::MF;                           // accumulator block rows per pass
+    static_assert(!STAGED_D || (NG == 1 && BPP >= 1 && FM % BPP == 0 && (CPR == 16 || CPR == 8) &&
+                                (RPP * RB) % 1024 == 0 && Cf::LDS + Cf::NW * DSW <= 160 * 1024),
+                  "staged store layout");
+    // cval(i, j): the C values of block (i, j) for epi4 (zero when beta = 0)
+    auto store_staged = [&](auto&& cval) {
+        char* region = smem + Cf::LDS + wave * DSW;
+        auto at = [&](int r, int q) { return region + dev::StagedRows<CPR>::at(r, q); };
+        static_for<0, FM / BPP>([&](auto pc) {
+            constexpr int ps = decltype(pc)::value;
+            for_blocks<BPP, FN>([&](auto bi, auto j) {
+                constexpr int i = ps * BPP + decltype(bi)::value;
+                const int r = decltype(bi)::value * Cf::MF + Mf::out_col(lane);
+                const int cb = 2 * (j * Cf::MF + Mf::out_row(lane, 0));   // byte of the wave-tile row
+                const float v[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
+                *(LDS_AS u32x2*)(at(r, cb >> 4) + (cb & 15)) = epi4<DT>(v, p.alpha, p.beta, cval(i, j));
+            });
+            // all the pass's reads, then its stores (each store waits only
+            // for its own read)
+            constexpr int NRD16 = RPP * RB / 1024;
+            u32x4 w[NRD16];
+            static_for<0, NRD16>([&](auto kc) {
+                const int lin16 = decltype(kc)::value * 64 + lane;   // 16-byte unit of the pass
+                w[decltype(kc)::value] = *(const LDS_AS u32x4*)at(lin16 / CPR, lin16 % CPR);
+            });
+            static_for<0, NRD16>([&](auto kc) {
+                const int lin16 = decltype(kc)::value * 64 + lane;
+                const int r = lin16 / CPR, q = lin16 % CPR;
+                *reinterpret_cast<u32x4*>(p.D + (int64_t)(m0 + arow0 + ps * RPP + r) * p.ldd + n0 + brow0 + 8 * q) =
+                    w[decltype(kc)::value];
+            });
+            // one pass at a time: the next pass's conversions are not hoisted
+            // above this one's stores (they would hold more registers)
+            __builtin_amdgcn_sched_barrier(0);
+        });
+    };
+    // ---- staged store with C (a whole 256x256 tile of the data-parallel
+    // launch, beta != 0). After a barrier the ring is free, a quarter per
+    // wave, which holds the wave's C tile in the rows of dev::StagedRows:
+    // the wave copies it in row-coalesced 16-byte copies (each lane fetching
+    // the chunk that the rows store at its position), reads C in the
+    // accumulators' layout, writes D over it, and reads D back along the
+    // rows for the stores. A wave reads all of its C before it stores any D
+    // and no other wave reads those elements, so D may be C.
+    constexpr bool STAGED_C = STAGED_D && MODE == kDataParallel && Cf::BN == 256;
+    constexpr int CWB = Cf::TWM * RB;   // bytes of a wave's C tile
+    static_assert(!STAGED_C || (Cf::NW * CWB <= Cf::LDS && CWB % 8192 == 0), "the C tiles fit the ring");
+    auto store_staged_c = [&]() {
+        using SR = dev::StagedRows<CPR>;
+        char* region = smem + wave * CWB;
+        auto at = [&](int r, int q) { return region + SR::at(r, q); };
+        const char* cbase = reinterpret_cast<const char*>(p.C + (int64_t)(m0 + arow0) * p.ldc + n0 + brow0);
+        __syncthreads();   // every wave is done with the ring
+        static_for<0, CWB / 1024>([&](auto kc) {
+            constexpr int k = decltype(kc)::value;
+            const int lin16 = 64 * k + lane, r = lin16 / CPR;
+            copy16<0>(lds_u32(region + 1024 * k), cbase,
+                      2u * (uint32_t)(r * p.ldc + 8 * SR::chunk_at(r, lin16 % CPR)));
+        });
+        LT_WAIT_VM(0);   // the wave's own C copies have landed
+        // C read and D written in the accumulators' layout, a block row at a time
+        static_for<0, FM>([&](auto ic_) {
+            constexpr int i = decltype(ic_)::value;
+            u32x2 cvr[FN];
+            static_for<0, FN>([&](auto jc) {
+                const int r = i * Cf::MF + Mf::out_col(lane), cb = 2 * (jc * Cf::MF + Mf::out_row(lane, 0));
+                cvr[jc] = *(const LDS_AS u32x2*)(at(r, cb >> 4) + (cb & 15));
+            });
+            static_for<0, FN>([&](auto jc) {
+                constexpr int j = decltype(jc)::value;
+                const int r = i * Cf::MF + Mf::out_col(lane), cb = 2 * (j * Cf::MF + Mf::out_row(lane, 0));
+                const float v[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
+                *(LDS_AS u32x2*)(at(r, cb >> 4) + (cb & 15)) = epi4<DT>(v, p.alpha, p.beta, cvr[j]);
+            });
+            __builtin_amdgcn_sched_barrier(0);
+        });
+        // D along the rows: eight reads, then their stores
+        static_for<0, CWB / 8192>([&](auto bc) {
+            u32x4 w[8];
+            static_for<0, 8>([&](auto kc) {
+                const int lin16 = 64 * (8 * bc + kc) + lane;
+                w[kc] = *(const LDS_AS u32x4*)at(lin16 / CPR, lin16 % CPR);
+            });
+            static_for<0, 8>([&](auto kc) {
+                const int lin16 = 64 * (8 * bc + kc) + lane, r = lin16 / CPR, q = lin16 % CPR;
+                *reinterpret_cast<u32x4*>(p.D + (int64_t)(m0 + arow0 + r) * p.ldd + n0 + brow0 + 8 * q) = w[kc];
+            });
+            __builtin_amdgcn_sched_barrier(0);
+        });
+    };
     auto epilogue = [&](auto edge) {
         constexpr bool EDGE = decltype(edge)::value;
         const bool use_c = p.beta != 0.0f;
+        if constexpr (STAGED_D && !EDGE) {
+            if (!use_c) {
+                store_staged([](int, int) { return u32x2{0u, 0u}; });
+                return;
+            }
+        }
         u32x2 cv[FM][FN][NG];
         auto load_c = [&](auto guarded) {
             for_blocks<FM, FN>([&](auto i, auto j) {
@@ -730,19 +861,6 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
                 }
             });
         };
-        auto store_tile = [&]() {
-            for_blocks<FM, FN>([&](auto i, auto j) {
-                const int m = m0 + arow0 + i * Cf::MF + Mf::out_col(lane);
-#pragma unroll
-                for (int g = 0; g < NG; ++g) {
-                    const int n = n0 + brow0 + j * Cf::MF + Mf::out_row(lane, 4 * g);
-                    const float v[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
-                                        acc[i][j][4 * g + 3]};
-                    store4_c<DT>(p.D, (int64_t)m * p.ldd + n, v, p.alpha, p.beta,
-                                 WITH_C ? cv[i][j][g] : u32x2{0u, 0u});
-                }
-            });
-        };
         if constexpr (WITH_C) issue_c_spare(m0, n0);   // the first tile's C rows 192..255
         // Every tile runs the same slice sequence, so no control flow
         // joins while MFMA results are in flight (at a join the compiler
@@ -776,7 +894,7 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
                 const int st_last = stage;
                 slice_x(yes, no, a_k0, b_k0, ic<0>{}, ic<0>{}, no, ic<Cf::IPW * (S - 2)>{});
                 asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");   // MFMA results before VALU reads
-                store_tile();
+                store_staged([](int, int) { return u32x2{0u, 0u}; });
                 if (!more) break;
                 issue_at(st_last, na + (S - 1) * a_ks, nb + (S - 1) * b_ks);   // the next tile's slice S-1
             } else {
@@ -805,11 +923,14 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
                 __syncthreads();       // every wave's C copies visible
                 read_c_lds(st_c);
                 __syncthreads();       // every wave has its C values: the stage and the spare are free
-                // the next tile's slice 1 and C rows 192..255 (the last
-                // tile: its own again, unused), then this tile's D
+                // the next tile's slice 1, this tile's D through the spare,
+                // then (once every wave has read its rows back) the next
+                // tile's C rows 192..255 into the spare (the last tile: its
+                // own again, unused)
                 issue_at(st_c, na + a_ks, nb + b_ks);
+                store_staged([&](int i, int j) { return cv[i][j][0]; });
+                __syncthreads();
                 issue_c_spare(m0n, n0n);
-                store_tile();
                 if (!more) break;
             }
             m0 = m0n;
@@ -842,8 +963,21 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
     }
     for (; t + 1 < NS; ++t) slice(yes, no, t, ic<0>{});   // slices already in flight
     slice(no, no, t, ic<0>{});                            // the last slice
-    // MFMA results before any VALU or memory instruction reads them
-    if constexpr (Cf::EXPLICIT) asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+    // MFMA results before any VALU or memory instruction reads them (the
+    // scheduling barrier keeps the epilogue's accumulator reads from being
+    // hoisted into the last slice, where they would also hold registers
+    // beside the accumulators)
+    if constexpr (Cf::EXPLICIT) {
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        // each accumulator block redefined here, in its AGPRs, by an empty
+        // statement: a register the epilogues need moved or spilled is then
+        // moved or spilled after the wait states, never between MFMAs
+        for_blocks<FM, FN>([&](auto i, auto j) {
+            auto& c = acc[i][j];
+            asm volatile("" : "+a"(c));
+        });
+    }
 
     // ---- split-K segment: publish the fp32 partial; the segment that
     // arrives last adds the others' and goes on to the epilogue. No waiting:
@@ -887,12 +1021,23 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
         if (threadIdx.x == 0) __hip_atomic_store(&p.counters[skt], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 
-    if (p.epi.fused)
+    const bool whole = m0 + Cf::BM <= p.M && n0 + Cf::BN <= p.N;
+    if (p.epi.fused) {
         epilogue_fused();
-    else if (m0 + Cf::BM > p.M || n0 + Cf::BN > p.N)
+    } else if constexpr (STAGED_C) {
+        // whole tiles through LDS; the predicated path takes the rest (and
+        // a C whose rows lie too far apart for the 32-bit copy offsets)
+        if (whole && p.beta == 0.0f)
+            store_staged([](int, int) { return u32x2{0u, 0u}; });
+        else if (whole && (int64_t)p.ldc * 2 * Cf::TWM < (int64_t(1) << 32))
+            store_staged_c();
+        else
+            epilogue(std::true_type{});
+    } else if (!whole) {
         epilogue(std::true_type{});
-    else
+    } else {
         epilogue(std::false_type{});
+    }
 #else
     (void)p;
 #endif
@@ -901,10 +1046,12 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
 namespace {
 
 // LDS of a launch: the stages, plus 16 KiB for C rows 192..255 in the
-// persistent launch with C
+// persistent launch with C, or the staged store's regions
 template <class Cf, int MODE>
 constexpr int launch_lds() {
-    return MODE == kPersistentC ? Cf::LDS + 16 * 1024 : Cf::LDS;
+    constexpr int c_rows = MODE == kPersistentC ? 16 * 1024 : 0;
+    constexpr int staged = staged_d_bytes<Cf, MODE>();
+    return Cf::LDS + (c_rows > staged ? c_rows : staged);
 }
 
 template <int DT, class Cf, int MODE>

@@ -102,11 +102,12 @@ __device__ __forceinline__ void store4(uint16_t* D, const uint16_t* C, int64_t d
     *reinterpret_cast<u32x2*>(D + dof) = o;
 }
 
-// store4 with the four C values already loaded (c = 0 when beta == 0), so a
-// caller can issue all its C loads before the first one is waited on.
+// alpha*acc + beta*c of four consecutive N outputs with the four C values
+// already loaded (c = 0 when beta == 0), rounded to the output format and
+// packed: the one arithmetic of the plain epilogue, whichever way the
+// result is then stored.
 template <int DT>
-__device__ __forceinline__ void store4_c(uint16_t* D, int64_t dof, const float* a, float alpha, float beta,
-                                         u32x2 c) {
+__device__ __forceinline__ u32x2 epi4(const float* a, float alpha, float beta, u32x2 c) {
     const float v0 = alpha * a[0] + beta * Tr<DT>::to_f32(static_cast<uint16_t>(c.x & 0xffff));
     const float v1 = alpha * a[1] + beta * Tr<DT>::to_f32(static_cast<uint16_t>(c.x >> 16));
     const float v2 = alpha * a[2] + beta * Tr<DT>::to_f32(static_cast<uint16_t>(c.y & 0xffff));
@@ -114,7 +115,15 @@ __device__ __forceinline__ void store4_c(uint16_t* D, int64_t dof, const float* 
     u32x2 o;
     o.x = pack2<DT>(v0, v1);
     o.y = pack2<DT>(v2, v3);
-    *reinterpret_cast<u32x2*>(D + dof) = o;
+    return o;
+}
+
+// epi4 stored as one 8-byte write, so a caller can issue all its C loads
+// before the first one is waited on.
+template <int DT>
+__device__ __forceinline__ void store4_c(uint16_t* D, int64_t dof, const float* a, float alpha, float beta,
+                                         u32x2 c) {
+    *reinterpret_cast<u32x2*>(D + dof) = epi4<DT>(a, alpha, beta, c);
 }
 
 // The activation of the fused epilogue, in fp32.

@@ -1,6 +1,7 @@
 // Host build of the kernels' compile-time layouts: prints every map the
 // tiled kernel evaluates so the tests can check it against the layout algebra.
 #include <cstdio>
+#include <initializer_list>
 
 #include "device_layout.hpp"
 
@@ -52,5 +53,16 @@ int main() {
     std::printf("\n");
     dump_mfma<32>();
     dump_mfma<16>();
+    for (int cpr : {8, 16}) {   // staged D rows: 128 rows of either width, then chunk_at
+        std::printf("staged %d 128\n", cpr);
+        for (int r = 0; r < 128; ++r)
+            for (int q = 0; q < cpr; ++q)
+                std::printf("%d ", cpr == 8 ? StagedRows<8>::at(r, q) : StagedRows<16>::at(r, q));
+        std::printf("\nstaged_inv %d 128\n", cpr);
+        for (int r = 0; r < 128; ++r)
+            for (int q = 0; q < cpr; ++q)
+                std::printf("%d ", cpr == 8 ? StagedRows<8>::chunk_at(r, q) : StagedRows<16>::chunk_at(r, q));
+        std::printf("\n");
+    }
     return 0;
 }

@@ -166,6 +166,57 @@ def test_mfma_operand_and_output_maps(maps, mf):
     assert cells == {(r, c) for r in range(mf) for c in range(mf)}
 
 
+@pytest.mark.parametrize("cpr", [8, 16])
+def test_staged_store_round_trip_and_banks(maps, cpr):
+    """The staged D store: rows of a wave tile 8*cpr columns wide (64 or
+    128) in the layout of dev::StagedRows, 128 rows (a whole wave tile,
+    the store with C) or 32 (one pass, beta = 0; checked here). The accumulators' 8-byte
+    writes (row = lane % 16 of the 16x16 block, four consecutive columns)
+    cover the region once, each 32-lane half of a write instruction hits 64
+    distinct banks, each 16-lane quarter of a 16-byte read hits 16 distinct
+    bank groups, and the lane that reads chunk q of row r gets exactly the
+    values of row r, columns 8q .. 8q+7, which it stores there."""
+    flat = maps[("staged", str(cpr), "128")]
+    at = lambda r, q: flat[r * cpr + q]
+    RB = 16 * cpr
+    assert sorted(flat) == [16 * i for i in range(128 * cpr)]
+    # the copy's inverse: the chunk a direct-to-LDS copy writing position
+    # pos of row r fetches is the one the map stores there
+    inv = maps[("staged_inv", str(cpr), "128")]
+    for r in range(128):
+        for pos in range(cpr):
+            assert at(r, inv[r * cpr + pos]) == RB * r + 16 * pos
+    out = maps[("mout", "16")]
+    orow = lambda l, v: out[2 * (4 * l + v)]   # the block's N index (four consecutive columns)
+    ocol = lambda l: out[2 * (4 * l) + 1]      # the block's M index
+    byte_of = {}
+    for bi in range(2):
+        for j in range(cpr // 2):
+            banks = []
+            for l in range(64):
+                r, n0 = 16 * bi + ocol(l), orow(l, 0)
+                assert [orow(l, v) for v in range(4)] == [n0 + v for v in range(4)]
+                cb = 2 * (16 * j + n0)
+                a = at(r, cb >> 4) + (cb & 15)
+                assert a % 8 == 0
+                for v in range(4):
+                    assert a + 2 * v not in byte_of
+                    byte_of[a + 2 * v] = (r, 16 * j + n0 + v)
+                banks += [(a // 4) % 64, (a // 4 + 1) % 64]
+            for h in range(2):
+                assert len(set(banks[64 * h:64 * h + 64])) == 64
+    assert len(byte_of) == 32 * RB // 2
+    for k in range(32 * RB // 1024):
+        groups = []
+        for l in range(64):
+            r, q = (64 * k + l) // cpr, (64 * k + l) % cpr
+            a = at(r, q)
+            assert [byte_of[a + 2 * e] for e in range(8)] == [(r, 8 * q + e) for e in range(8)]
+            groups.append((a // 16) % 16)
+        for h in range(4):
+            assert len(set(groups[16 * h:16 * h + 16])) == 16
+
+
 def test_fragment_and_accumulator_maps(maps):
     frag = maps[("frag",)]
     assert frag == [(l % 32) + 32 * (l // 32) for l in range(64)]
