@@ -230,19 +230,37 @@ struct Mfma {
     LT_HD static constexpr int out_col(int lane) { return lane % MF; }
 };
 
-// Rows of the staged D store in LDS: rows of CPR 16-byte chunks (128 or
-// 256 bytes), row after row; chunk q of row r sits at position q ^ ((r /
-// (16/CPR)) mod CPR) of its row. The 16/CPR rows that share one 256-byte
-// (64-bank) window then place a given chunk q in 16 distinct bank groups
-// over any 16 consecutive rows, and one row's chunks in distinct groups.
-// (chunk_at inverts it: the chunk stored at position pos of row r, which a
-// direct-to-LDS copy, writing position pos, fetches.)
+// Rows of the staged D store in LDS: rows of CPR 16-byte chunks (RB = 16 *
+// CPR bytes), row after row. The accumulators write 8 bytes per lane, one
+// 8-byte unit u (of 2*CPR) of each of 16 consecutive rows per quarter-wave;
+// unit u of row r sits at unit u ^ g(r) of its row, with g(r) = r mod 16
+// for 128-byte rows and 2 (r mod 16) + ((r / 8) mod 2) for 256-byte rows.
+// Then the 16 rows' copies of a unit fall in 16 distinct 8-byte bank pairs
+// of a 128-byte (32-bank) window, and a half-wave's 32 writes (two units
+// each in 16 rows) in 32 distinct pairs of a 256-byte window, whichever of
+// the two the LDS serves per cycle. A 16-byte read of chunk q finds units
+// 2q and 2q+1 together in slot q ^ (g(r) / 2), in swapped order when g(r)
+// is odd; the 16 (or 8) lanes reading one row (two 128-byte rows) reach
+// distinct slots.
 template <int CPR>
 struct StagedRows {
     static_assert(CPR == 8 || CPR == 16, "rows of 128 or 256 bytes");
-    LT_HD static constexpr int swz(int r) { return (r / (16 / CPR)) & (CPR - 1); }
-    LT_HD static constexpr int at(int r, int q) { return 16 * (r * CPR + (q ^ swz(r))); }
-    LT_HD static constexpr int chunk_at(int r, int pos) { return pos ^ swz(r); }
+    LT_HD static constexpr int g(int r) { return CPR == 8 ? (r & 15) : 2 * (r & 15) + ((r >> 3) & 1); }
+    // byte offset of 8-byte unit u of row r
+    LT_HD static constexpr int unit(int r, int u) { return 8 * (2 * CPR * r + (u ^ g(r))); }
+    // byte offset of the 16-byte slot holding chunk q of row r
+    LT_HD static constexpr int slot(int r, int q) { return 16 * (CPR * r + (q ^ (g(r) >> 1))); }
+    LT_HD static constexpr bool swapped(int r) { return (g(r) & 1) != 0; }
+};
+
+// The C tile of the staged store with C, 256-byte rows copied in whole
+// 16-byte chunks by direct-to-LDS copies: chunk q of row r at slot q ^ (r
+// mod 16). chunk_at inverts it: the chunk a copy writing slot pos of row r
+// fetches. The accumulators' 8-byte reads of a half-wave (two units of 16
+// rows) reach 32 distinct bank pairs of a 256-byte window.
+struct StagedC {
+    LT_HD static constexpr int at(int r, int q) { return 16 * (16 * r + (q ^ (r & 15))); }
+    LT_HD static constexpr int chunk_at(int r, int pos) { return pos ^ (r & 15); }
 };
 
 }  // namespace lt::dev

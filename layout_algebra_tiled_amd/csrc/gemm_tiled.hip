@@ -577,9 +577,10 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
     // accumulators' layout (8 bytes per lane), reads them back 16 bytes per
     // lane along the rows and stores them. The region is the wave's own and
     // LDS executes one wave's instructions in order, so no barrier is
-    // needed. The rows are swizzled (dev::StagedRows) so that the writes
-    // (16 rows, one column group) and the reads (one or two rows) each
-    // reach every bank once.
+    // needed. The rows are swizzled in 8-byte units (dev::StagedRows) so
+    // that the writes (16 rows, one column group) and the reads (one or two
+    // rows) each reach every bank once; a read whose two halves the swizzle
+    // swapped swaps them back in registers.
     constexpr bool STAGED_D = staged_d<Cf, MODE>();
     constexpr int DSW = staged_d_bytes<Cf, MODE>() / Cf::NW;   // bytes per wave
     constexpr int RB = Cf::TWN * 2;                             // bytes of one wave-tile row
@@ -589,10 +590,15 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
     static_assert(!STAGED_D || (NG == 1 && BPP >= 1 && FM % BPP == 0 && (CPR == 16 || CPR == 8) &&
                                 (RPP * RB) % 1024 == 0 && Cf::LDS + Cf::NW * DSW <= 160 * 1024),
                   "staged store layout");
+    using SR = dev::StagedRows<CPR>;
+    // 8 accumulator values (16 bytes) of row r, chunk q, from a staged region
+    auto read_row16 = [&](const char* region, int r, int q) {
+        const u32x4 x = *(const LDS_AS u32x4*)(region + SR::slot(r, q));
+        return SR::swapped(r) ? u32x4{x.z, x.w, x.x, x.y} : x;
+    };
     // cval(i, j): the C values of block (i, j) for epi4 (zero when beta = 0)
     auto store_staged = [&](auto&& cval) {
         char* region = smem + Cf::LDS + wave * DSW;
-        auto at = [&](int r, int q) { return region + dev::StagedRows<CPR>::at(r, q); };
         static_for<0, FM / BPP>([&](auto pc) {
             constexpr int ps = decltype(pc)::value;
             for_blocks<BPP, FN>([&](auto bi, auto j) {
@@ -600,7 +606,7 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
                 const int r = decltype(bi)::value * Cf::MF + Mf::out_col(lane);
                 const int cb = 2 * (j * Cf::MF + Mf::out_row(lane, 0));   // byte of the wave-tile row
                 const float v[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
-                *(LDS_AS u32x2*)(at(r, cb >> 4) + (cb & 15)) = epi4<DT>(v, p.alpha, p.beta, cval(i, j));
+                *(LDS_AS u32x2*)(region + SR::unit(r, cb >> 3)) = epi4<DT>(v, p.alpha, p.beta, cval(i, j));
             });
             // all the pass's reads, then its stores (each store waits only
             // for its own read)
@@ -608,7 +614,7 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
             u32x4 w[NRD16];
             static_for<0, NRD16>([&](auto kc) {
                 const int lin16 = decltype(kc)::value * 64 + lane;   // 16-byte unit of the pass
-                w[decltype(kc)::value] = *(const LDS_AS u32x4*)at(lin16 / CPR, lin16 % CPR);
+                w[decltype(kc)::value] = read_row16(region, lin16 / CPR, lin16 % CPR);
             });
             static_for<0, NRD16>([&](auto kc) {
                 const int lin16 = decltype(kc)::value * 64 + lane;
@@ -623,26 +629,28 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
     };
     // ---- staged store with C (a whole 256x256 tile of the data-parallel
     // launch, beta != 0). After a barrier the ring is free, a quarter per
-    // wave, which holds the wave's C tile in the rows of dev::StagedRows:
-    // the wave copies it in row-coalesced 16-byte copies (each lane fetching
-    // the chunk that the rows store at its position), reads C in the
-    // accumulators' layout, writes D over it, and reads D back along the
-    // rows for the stores. A wave reads all of its C before it stores any D
-    // and no other wave reads those elements, so D may be C.
+    // wave, which holds the wave's C tile (dev::StagedC): the wave copies
+    // it in row-coalesced 16-byte copies (each lane fetching the chunk that
+    // the map stores at its position) and reads it in the accumulators'
+    // layout. It then writes D into the same rows in the layout of the
+    // store without C (a block row's D goes in only after all of its C has
+    // been read: the two layouts place a row's units differently) and reads
+    // D back along the rows for the stores. A wave reads all of its C before
+    // it stores any D and no other wave reads those elements, so D may be
+    // C.
     constexpr bool STAGED_C = STAGED_D && MODE == kDataParallel && Cf::BN == 256;
     constexpr int CWB = Cf::TWM * RB;   // bytes of a wave's C tile
     static_assert(!STAGED_C || (Cf::NW * CWB <= Cf::LDS && CWB % 8192 == 0), "the C tiles fit the ring");
     auto store_staged_c = [&]() {
-        using SR = dev::StagedRows<CPR>;
+        static_assert(!STAGED_C || CPR == 16, "256-byte rows");
         char* region = smem + wave * CWB;
-        auto at = [&](int r, int q) { return region + SR::at(r, q); };
         const char* cbase = reinterpret_cast<const char*>(p.C + (int64_t)(m0 + arow0) * p.ldc + n0 + brow0);
         __syncthreads();   // every wave is done with the ring
         static_for<0, CWB / 1024>([&](auto kc) {
             constexpr int k = decltype(kc)::value;
             const int lin16 = 64 * k + lane, r = lin16 / CPR;
             copy16<0>(lds_u32(region + 1024 * k), cbase,
-                      2u * (uint32_t)(r * p.ldc + 8 * SR::chunk_at(r, lin16 % CPR)));
+                      2u * (uint32_t)(r * p.ldc + 8 * dev::StagedC::chunk_at(r, lin16 % CPR)));
         });
         LT_WAIT_VM(0);   // the wave's own C copies have landed
         // C read and D written in the accumulators' layout, a block row at a time
@@ -651,13 +659,13 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
             u32x2 cvr[FN];
             static_for<0, FN>([&](auto jc) {
                 const int r = i * Cf::MF + Mf::out_col(lane), cb = 2 * (jc * Cf::MF + Mf::out_row(lane, 0));
-                cvr[jc] = *(const LDS_AS u32x2*)(at(r, cb >> 4) + (cb & 15));
+                cvr[jc] = *(const LDS_AS u32x2*)(region + dev::StagedC::at(r, cb >> 4) + (cb & 15));
             });
             static_for<0, FN>([&](auto jc) {
                 constexpr int j = decltype(jc)::value;
                 const int r = i * Cf::MF + Mf::out_col(lane), cb = 2 * (j * Cf::MF + Mf::out_row(lane, 0));
                 const float v[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
-                *(LDS_AS u32x2*)(at(r, cb >> 4) + (cb & 15)) = epi4<DT>(v, p.alpha, p.beta, cvr[j]);
+                *(LDS_AS u32x2*)(region + SR::unit(r, cb >> 3)) = epi4<DT>(v, p.alpha, p.beta, cvr[j]);
             });
             __builtin_amdgcn_sched_barrier(0);
         });
@@ -666,7 +674,7 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
             u32x4 w[8];
             static_for<0, 8>([&](auto kc) {
                 const int lin16 = 64 * (8 * bc + kc) + lane;
-                w[kc] = *(const LDS_AS u32x4*)at(lin16 / CPR, lin16 % CPR);
+                w[kc] = read_row16(region, lin16 / CPR, lin16 % CPR);
             });
             static_for<0, 8>([&](auto kc) {
                 const int lin16 = 64 * (8 * bc + kc) + lane, r = lin16 / CPR, q = lin16 % CPR;

@@ -53,16 +53,22 @@ int main() {
     std::printf("\n");
     dump_mfma<32>();
     dump_mfma<16>();
-    for (int cpr : {8, 16}) {   // staged D rows: 128 rows of either width, then chunk_at
-        std::printf("staged %d 128\n", cpr);
+    // staged D rows (128 rows of either width): unit, slot, swapped; the C tile
+    for (int cpr : {8, 16}) {
+        std::printf("staged_unit %d 128\n", cpr);
+        for (int r = 0; r < 128; ++r)
+            for (int u = 0; u < 2 * cpr; ++u)
+                std::printf("%d ", cpr == 8 ? StagedRows<8>::unit(r, u) : StagedRows<16>::unit(r, u));
+        std::printf("\nstaged_slot %d 128\n", cpr);
         for (int r = 0; r < 128; ++r)
             for (int q = 0; q < cpr; ++q)
-                std::printf("%d ", cpr == 8 ? StagedRows<8>::at(r, q) : StagedRows<16>::at(r, q));
-        std::printf("\nstaged_inv %d 128\n", cpr);
-        for (int r = 0; r < 128; ++r)
-            for (int q = 0; q < cpr; ++q)
-                std::printf("%d ", cpr == 8 ? StagedRows<8>::chunk_at(r, q) : StagedRows<16>::chunk_at(r, q));
+                std::printf("%d %d ", cpr == 8 ? StagedRows<8>::slot(r, q) : StagedRows<16>::slot(r, q),
+                            (int)(cpr == 8 ? StagedRows<8>::swapped(r) : StagedRows<16>::swapped(r)));
         std::printf("\n");
     }
+    std::printf("staged_c 16 128\n");
+    for (int r = 0; r < 128; ++r)
+        for (int q = 0; q < 16; ++q) std::printf("%d %d ", StagedC::at(r, q), StagedC::chunk_at(r, q));
+    std::printf("\n");
     return 0;
 }

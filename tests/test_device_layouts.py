@@ -166,55 +166,99 @@ def test_mfma_operand_and_output_maps(maps, mf):
     assert cells == {(r, c) for r in range(mf) for c in range(mf)}
 
 
+def _staged(maps, cpr):
+    unit = maps[("staged_unit", str(cpr), "128")]
+    sl = maps[("staged_slot", str(cpr), "128")]
+    return (lambda r, u: unit[r * 2 * cpr + u]), (lambda r, q: sl[2 * (r * cpr + q)]), \
+        (lambda r, q: sl[2 * (r * cpr + q) + 1])
+
+
+def _distinct_banks(addrs, nbytes, window):
+    """LDS accesses of nbytes each, served together: no two touch the same
+    4-byte bank of a window-byte (window/4-bank) LDS."""
+    banks = [(a % window) // 4 + k for a in addrs for k in range(nbytes // 4)]
+    return len(set(banks)) == len(banks)
+
+
 @pytest.mark.parametrize("cpr", [8, 16])
 def test_staged_store_round_trip_and_banks(maps, cpr):
-    """The staged D store: rows of a wave tile 8*cpr columns wide (64 or
-    128) in the layout of dev::StagedRows, 128 rows (a whole wave tile,
-    the store with C) or 32 (one pass, beta = 0; checked here). The accumulators' 8-byte
-    writes (row = lane % 16 of the 16x16 block, four consecutive columns)
-    cover the region once, each 32-lane half of a write instruction hits 64
-    distinct banks, each 16-lane quarter of a 16-byte read hits 16 distinct
-    bank groups, and the lane that reads chunk q of row r gets exactly the
-    values of row r, columns 8q .. 8q+7, which it stores there."""
-    flat = maps[("staged", str(cpr), "128")]
-    at = lambda r, q: flat[r * cpr + q]
+    """The staged D store, rows of a wave tile 8*cpr columns wide (64 or 128)
+    in the layout of dev::StagedRows. The map covers 128 rows once in 8-byte
+    units; slot(r, q) holds units 2q and 2q+1 of row r (swapped when the map
+    says so). One pass (32 rows): the accumulators' 8-byte writes (row =
+    lane % 16 of the 16x16 block, four consecutive columns) are bank-free
+    whether the LDS serves 16 lanes (128 bytes) or 32 (256 bytes) per cycle,
+    the 16-byte reads whether it serves 8 lanes or 16, and the lane that
+    reads chunk q of row r gets exactly row r, columns 8q .. 8q+7, which it
+    stores there."""
+    unit, slot, swapped = _staged(maps, cpr)
     RB = 16 * cpr
-    assert sorted(flat) == [16 * i for i in range(128 * cpr)]
-    # the copy's inverse: the chunk a direct-to-LDS copy writing position
-    # pos of row r fetches is the one the map stores there
-    inv = maps[("staged_inv", str(cpr), "128")]
+    allu = [unit(r, u) for r in range(128) for u in range(2 * cpr)]
+    assert sorted(allu) == [8 * i for i in range(128 * 2 * cpr)]
     for r in range(128):
-        for pos in range(cpr):
-            assert at(r, inv[r * cpr + pos]) == RB * r + 16 * pos
+        for q in range(cpr):
+            lo, hi = (unit(r, 2 * q + 1), unit(r, 2 * q)) if swapped(r, q) else (unit(r, 2 * q), unit(r, 2 * q + 1))
+            assert (lo, hi) == (slot(r, q), slot(r, q) + 8)
     out = maps[("mout", "16")]
     orow = lambda l, v: out[2 * (4 * l + v)]   # the block's N index (four consecutive columns)
     ocol = lambda l: out[2 * (4 * l) + 1]      # the block's M index
     byte_of = {}
     for bi in range(2):
         for j in range(cpr // 2):
-            banks = []
+            addrs = []
             for l in range(64):
                 r, n0 = 16 * bi + ocol(l), orow(l, 0)
                 assert [orow(l, v) for v in range(4)] == [n0 + v for v in range(4)]
-                cb = 2 * (16 * j + n0)
-                a = at(r, cb >> 4) + (cb & 15)
-                assert a % 8 == 0
+                a = unit(r, (2 * (16 * j + n0)) >> 3)
                 for v in range(4):
                     assert a + 2 * v not in byte_of
                     byte_of[a + 2 * v] = (r, 16 * j + n0 + v)
-                banks += [(a // 4) % 64, (a // 4 + 1) % 64]
+                addrs.append(a)
+            for g in range(4):
+                assert _distinct_banks(addrs[16 * g:16 * g + 16], 8, 128)
             for h in range(2):
-                assert len(set(banks[64 * h:64 * h + 64])) == 64
+                assert _distinct_banks(addrs[32 * h:32 * h + 32], 8, 256)
     assert len(byte_of) == 32 * RB // 2
     for k in range(32 * RB // 1024):
-        groups = []
+        addrs = []
         for l in range(64):
             r, q = (64 * k + l) // cpr, (64 * k + l) % cpr
-            a = at(r, q)
-            assert [byte_of[a + 2 * e] for e in range(8)] == [(r, 8 * q + e) for e in range(8)]
-            groups.append((a // 16) % 16)
-        for h in range(4):
-            assert len(set(groups[16 * h:16 * h + 16])) == 16
+            a = slot(r, q)
+            got = [byte_of[a + 2 * e] for e in range(8)]
+            if swapped(r, q):   # the reader swaps the two 8-byte halves back
+                got = got[4:] + got[:4]
+            assert got == [(r, 8 * q + e) for e in range(8)]
+            addrs.append(a)
+        for g in range(8):
+            assert _distinct_banks(addrs[8 * g:8 * g + 8], 16, 128)
+        for g in range(4):
+            assert _distinct_banks(addrs[16 * g:16 * g + 16], 16, 256)
+
+
+def test_staged_c_tile_copy_and_reads(maps):
+    """The C tile of the staged store with C (256-byte rows, dev::StagedC):
+    the direct-to-LDS copy writing slot pos of row r fetches the chunk the
+    map stores there, the map covers the tile once, and the accumulators'
+    8-byte C reads of a half-wave (two units of 16 rows) reach 64 distinct
+    banks of a 256-byte window."""
+    c = maps[("staged_c", "16", "128")]
+    at = lambda r, q: c[2 * (r * 16 + q)]
+    chunk_at = lambda r, pos: c[2 * (r * 16 + pos) + 1]
+    assert sorted(at(r, q) for r in range(128) for q in range(16)) == [16 * i for i in range(128 * 16)]
+    for r in range(128):
+        for pos in range(16):
+            assert at(r, chunk_at(r, pos)) == 256 * r + 16 * pos
+    out = maps[("mout", "16")]
+    orow = lambda l: out[2 * (4 * l)]
+    ocol = lambda l: out[2 * (4 * l) + 1]
+    for i in range(8):
+        for j in range(8):
+            addrs = []
+            for l in range(64):
+                r, cb = 16 * i + ocol(l), 2 * (16 * j + orow(l))
+                addrs.append(at(r, cb >> 4) + (cb & 15))
+            for h in range(2):
+                assert _distinct_banks(addrs[32 * h:32 * h + 32], 8, 256)
 
 
 def test_fragment_and_accumulator_maps(maps):
