@@ -312,7 +312,8 @@ typedef struct lt_gemm_plan_info {
     int32_t split_k;
     int32_t a_kmajor, b_kmajor, d_nmajor;
     int64_t grid;            /* workgroups launched (all launches) */
-    int64_t lds_bytes;       /* per workgroup */
+    int64_t lds_bytes;       /* per workgroup (TILED: of the persistent or data-parallel launch, its
+                                staging region for D beside the LDS ring included) */
     int64_t workspace_bytes; /* caller-provided scratch the run needs */
     int64_t mfma_per_wave_kstep; /* MFMA instructions per wave per K step (tile_k) */
     int32_t mfma_m, mfma_n, mfma_k; /* shape of the MFMA instruction the kernel issues */

@@ -19,6 +19,7 @@
 #include "gemm_kernels.hpp"
 #include "layout_host.hpp"
 #include "lt.h"
+#include "tiled_config.hpp"
 
 // Scratch of the allocation-free entry point (lt_gemm_run_noalloc): the
 // split-K partials and arrival counters live here instead of in a caller's
@@ -366,6 +367,13 @@ lt_status make_plan(const lt_tensor* tA, const lt_tensor* tB, const lt_tensor* t
             in.sk_tiles = rem;
             in.sk_workgroups = static_cast<int32_t>(rem * S);
             in.workspace_bytes = rem > 0 ? p.sk_counter_bytes + rem * S * (int64_t)ts.bm * ts.bn * 4 : 0;
+            // LDS per workgroup of the first launch (the persistent or the
+            // data-parallel one; the split launch when every tile is split):
+            // the ring plus the staged store's region, by the kernel's rule
+            in.lds_bytes = launch_lds_bytes((int)tsc.lds_bytes,
+                                            staged_d_launch(persist, !persist && p.dp_tiles > 0, p.a_k, p.b_k),
+                                            persist && beta_nonzero);
+            if (in.lds_bytes > 160 * 1024) return LT_ERR_LDS_OVERFLOW;
             // (wave_m/mf) * (wave_n/mf) * (bk/mfma_k): the analogue of counting mma
             // per warp per K slice ("CUTLASS and CuTe layouts", "The arch tag
             // is not one instruction")

@@ -150,21 +150,16 @@ __device__ __forceinline__ void copy16(uint32_t lds, const char* gbase, uint32_t
 }
 #pragma clang diagnostic pop
 
-// The plain epilogue of a whole tile stores D through LDS beside the ring
-// (the persistent launches, with C or without, and the data-parallel launch
-// with K-major A and B and beta = 0: with M/N-major operands the fragment
-// offsets leave the data-parallel kernel no registers for it): 32 KiB when
-// the ring leaves that much of the 160 KiB, else 16 KiB, split evenly over
-// the waves. (The persistent launch with C shares those 16 KiB with the
-// next tile's C rows 192..255, copied after the store.)
+// Which launches stage D through LDS, and how much LDS they hold: the rule
+// in tiled_config.hpp, which the planner reports from.
 template <class Cf, int MODE>
 constexpr bool staged_d() {
-    return Cf::EXPLICIT &&
-           (MODE == kPersistent || MODE == kPersistentC || (MODE == kDataParallel && Cf::AK && Cf::BKM));
+    return Cf::EXPLICIT && staged_d_launch(MODE == kPersistent || MODE == kPersistentC, MODE == kDataParallel,
+                                           Cf::AK, Cf::BKM);
 }
 template <class Cf, int MODE>
 constexpr int staged_d_bytes() {
-    return !staged_d<Cf, MODE>() ? 0 : 160 * 1024 - Cf::LDS >= 32 * 1024 ? 32 * 1024 : 16 * 1024;
+    return staged_d<Cf, MODE>() ? staged_d_region(Cf::LDS) : 0;
 }
 
 }  // namespace
@@ -727,6 +722,10 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
                     cv[i][j][g] = *(const LDS_AS u32x2*)(row + 16 * ((c >> 3) ^ (r & 15)) + 2 * (c & 7));
                 }
             });
+            if constexpr (STAGED_D) {   // D through the region beside the stages
+                store_staged([&](int i, int j) { return cv[i][j][0]; });
+                return;
+            }
         } else {
             load_c(std::integral_constant<bool, EDGE>{});   // a whole tile loads with no branch per block
         }
@@ -1053,15 +1052,12 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
 
 namespace {
 
-// LDS of a launch: the stages, plus 16 KiB for C rows 192..255 in the
-// persistent launch with C, or the staged store's regions
+// LDS of a launch: the stages, then the staged store's region or (the
+// persistent launch with C) the 16 KiB of C rows 192..255
 template <class Cf, int MODE>
 constexpr int launch_lds() {
-    constexpr int c_rows = MODE == kPersistentC ? 16 * 1024 : 0;
-    constexpr int staged = staged_d_bytes<Cf, MODE>();
-    return Cf::LDS + (c_rows > staged ? c_rows : staged);
+    return launch_lds_bytes(Cf::LDS, staged_d<Cf, MODE>(), MODE == kPersistentC);
 }
-
 template <int DT, class Cf, int MODE>
 int launch_mode(const TiledArgs& a, int grid, hipStream_t s) {
     constexpr int lds = launch_lds<Cf, MODE>();

@@ -116,6 +116,26 @@ struct Operand {
     static constexpr int KROW_BYTES = W * 16;
 };
 
+// The staged D store of the plain epilogue (D, and C for a 256x256
+// data-parallel tile, through LDS for 16-byte row stores) runs in the
+// persistent launches and in the data-parallel launch with K-major A and B
+// (with M-/N-major operands the fragment offsets leave the data-parallel
+// kernel no registers for it), never in the split launch. Its region lies
+// beside a ring of ring_lds bytes: 32 KiB when the ring leaves that much of
+// the 160 KiB a workgroup may hold, else 16 KiB. The persistent launch with
+// C shares those 16 KiB with the next tile's C rows 192..255. The planner
+// reports the launch's LDS from the same rule.
+LT_HD constexpr bool staged_d_launch(bool persistent, bool data_parallel, bool a_kmajor, bool b_kmajor) {
+    return persistent || (data_parallel && a_kmajor && b_kmajor);
+}
+LT_HD constexpr int staged_d_region(int ring_lds) { return 160 * 1024 - ring_lds >= 32 * 1024 ? 32 * 1024 : 16 * 1024; }
+// LDS of one workgroup: the ring, then the larger of the staged region and
+// (persistent with C) the 16 KiB of C rows 192..255
+LT_HD constexpr int launch_lds_bytes(int ring_lds, bool staged, bool persistent_c) {
+    const int extra = staged ? staged_d_region(ring_lds) : 0;
+    return ring_lds + (persistent_c && extra < 16 * 1024 ? 16 * 1024 : extra);
+}
+
 // The configurations the planner launches.
 //   Dp256:   256x256 block tile, 4 waves of 128x128 (one per SIMD), 2 stages
 //            of 64 KiB; every operand major-ness.

@@ -384,7 +384,8 @@ def test_plan_closed_forms_reproduce_page_arithmetic():
     assert (4096 // 128) ** 2 == w["tiles_128x128"] and round(w["tiles_128x128"] / w["sms"], 2) == w["waves_128x128"]
     assert round(w["tiles_128x256"] / w["sms"], 2) == w["waves_128x256"]
     _, i = _plan(*_gemm_descs(8192, 8192, 8192))
-    assert i.lds_bytes == i.stages * stage_bytes(i.tile_m, i.tile_n, i.tile_k, 2)
+    # the stages, plus 32 KiB beside them where the epilogue stages D
+    assert i.lds_bytes == i.stages * stage_bytes(i.tile_m, i.tile_n, i.tile_k, 2) + 32 * 1024
     assert (i.mfma_m, i.mfma_n, i.mfma_k) in ((32, 32, 16), (16, 16, 32))
     assert i.mfma_per_wave_kstep == instr_per_wave(i.wave_m, i.wave_n, i.tile_k, i.mfma_m, i.mfma_n, i.mfma_k)
     assert i.tiles / 256 == 4.0   # 1,024 tiles on 256 CUs: whole waves
@@ -633,19 +634,42 @@ def test_plan_reports_the_wave_layout_of_the_data_parallel_launch():
     """The data-parallel launch runs 4 waves (one per SIMD) for every operand
     major-ness: 256x256 tiles as 128x128 wave tiles (8 x 8 MFMA blocks x 2 K
     steps per wave per 64-deep K slice, 2 stages of 64 KiB), 256x128 tiles as
-    128x64 wave tiles (8 x 4 blocks, 3 stages of 48 KiB)."""
+    128x64 wave tiles (8 x 4 blocks, 3 stages of 48 KiB). With K-major A and
+    B the epilogue stages D beside the stages (32 KiB of the 160 beside 128,
+    16 beside 144), which the LDS figure includes."""
     for a, b in (("k", "k"), ("m", "k"), ("k", "n"), ("m", "n")):
-        st, i = _plan(*_gemm_descs(2048, 2048, 1024, a=a, b=b), kernel=L.LT_KERNEL_TILED, tile_n=256)
+        staged = a == "k" and b == "k"
+        st, i = _plan(*_gemm_descs(2048, 2048, 1024, a=a, b=b), kernel=L.LT_KERNEL_TILED, tile_n=256, split=1)
         assert st == "LT_OK" and i.kernel == L.LT_KERNEL_TILED, (a, b, st)
         assert (i.waves, i.wave_m, i.wave_n) == (4, 128, 128), (a, b)
         assert (i.tile_m, i.tile_n, i.tile_k, i.stages) == (256, 256, 64, 2)
         assert i.mfma_per_wave_kstep == 8 * 8 * 2 and (i.mfma_m, i.mfma_n, i.mfma_k) == (16, 16, 32)
-        assert i.lds_bytes == 2 * 2 * 256 * 64 * 2
+        assert i.lds_bytes == 2 * 2 * 256 * 64 * 2 + (32 * 1024 if staged else 0), (a, b)
         st, i = _plan(*_gemm_descs(2048, 2048, 1024, a=a, b=b), kernel=L.LT_KERNEL_TILED, tile_n=128)
         assert st == "LT_OK" and (i.waves, i.wave_m, i.wave_n) == (4, 128, 64), (a, b)
         assert (i.tile_m, i.tile_n, i.tile_k, i.stages, i.grid) == (256, 128, 64, 3, 128)
         assert i.mfma_per_wave_kstep == 8 * 4 * 2
-        assert i.lds_bytes == 3 * (256 + 128) * 64 * 2
+        assert i.lds_bytes == 3 * (256 + 128) * 64 * 2 + (16 * 1024 if staged else 0), (a, b)
+
+
+def test_plan_lds_of_persistent_and_split_launches():
+    """The persistent launches stage D for every major-ness (256x256 beside
+    128 KiB: +32 KiB; 256x128 with or without C: +16 KiB, which the launch
+    with C shares with C rows 192..255), and a launch of split segments only
+    holds just its stages."""
+    for a, b in (("k", "k"), ("m", "n")):
+        st, i = _plan(*_gemm_descs(6144, 4096, 2048, a=a, b=b), kernel=L.LT_KERNEL_TILED, tile_n=128,
+                      persistent=2)
+        assert st == "LT_OK" and i.persistent == 1 and i.lds_bytes == 160 * 1024, (a, b, st)
+        st, i = _plan(*_gemm_descs(6144, 4096, 2048, a=a, b=b), bnz=1, kernel=L.LT_KERNEL_TILED,
+                      tile_n=128, persistent=2)
+        assert st == "LT_OK" and i.persistent == 1 and i.lds_bytes == 160 * 1024, (a, b, st)
+        st, i = _plan(*_gemm_descs(8192, 8192, 2048, a=a, b=b), kernel=L.LT_KERNEL_TILED, tile_n=256,
+                      persistent=2)
+        assert st == "LT_OK" and i.persistent == 1 and i.lds_bytes == 160 * 1024, (a, b, st)
+    st, i = _plan(*_gemm_descs(1024, 1024, 16384), kernel=L.LT_KERNEL_TILED, tile_n=256)
+    assert st == "LT_OK" and i.grid == i.sk_workgroups > 0, i.as_dict()   # every tile split
+    assert i.lds_bytes == 2 * 2 * 256 * 64 * 2
 
 
 def test_noalloc_refuses_oversized_plans_before_the_device():
