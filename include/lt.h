@@ -295,9 +295,10 @@ typedef struct lt_gemm_options {
     int32_t persistent; /* TILED: 0 = chosen (persistent when the tiles are whole, K
                            is a multiple of 64 with at least 4 slices, there are
                            more tiles than compute units, and for 256x256 tiles
-                           beta = 0, no split remainder and K <= 4096); 1 = one workgroup per
-                           tile; 2 = persistent (LT_ERR_UNSUPPORTED where the tile,
-                           K, beta or split conditions fail) */
+                           beta = 0, no split remainder and K <= 4096; with beta != 0
+                           also C's row stride below 2^27 elements); 1 = one workgroup
+                           per tile; 2 = persistent (LT_ERR_UNSUPPORTED where the tile,
+                           K, beta, C stride or split conditions fail) */
 } lt_gemm_options;
 
 /* What the planner chose, for banners and tests [P1 "Exercise": print the

@@ -349,8 +349,11 @@ lt_status make_plan(const lt_tensor* tA, const lt_tensor* tB, const lt_tensor* t
             const int want_p = opt ? opt->persistent : 0;
             if (want_p < 0 || want_p > 2) return LT_ERR_INVALID_ARGUMENT;
             // (256x256 tiles: beta = 0 and no split remainder only)
+            // (with C, a copy of C rows reaches 16 rows of C through a 32-bit
+            // byte offset)
+            const bool c_rows_fit = !beta_nonzero || p.C.s0 * 2 * 16 < (int64_t(1) << 32);
             const bool persist_ok = (tile_n == 128 || (!beta_nonzero && rem == 0)) && p.M % tsc.bm == 0 &&
-                                    p.N % tsc.bn == 0 && p.K % tsc.bk == 0 && KTt >= 4;
+                                    p.N % tsc.bn == 0 && p.K % tsc.bk == 0 && KTt >= 4 && c_rows_fit;
             if (want_p == 2 && !persist_ok) return LT_ERR_UNSUPPORTED;
             const bool persist =
                 persist_ok && (want_p == 2 || (want_p == 0 && ntiles > kCUs && (tile_n == 128 || KTt <= 64)));

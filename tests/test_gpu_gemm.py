@@ -9,7 +9,8 @@ import pytest
 import torch
 
 import datagen
-from tests.gemm_cases import all_points, check_all_rows, op, run_and_check, run_gemm, sample_points, say
+from tests.gemm_cases import (all_points, check_all_rows, check_points, op, run_and_check, run_gemm,
+                              sample_points, say)
 from oracle import gemm as og
 
 pytestmark = pytest.mark.gpu
@@ -315,6 +316,42 @@ def test_in_place_d_is_c():
     Dref, Cabs = og.epilogue(S, op(C), pts, 1.0, 0.5)
     got = og.read_points(og.Operand(dC.store.cpu(), C.shape, C.stride), pts)
     _ok(og.check(got, Dref, T, Cabs, 1.0, F16))
+
+
+def test_tiled_c_rows_at_the_staged_copy_offset_limit():
+    """A whole 256x256 tile with C: the staged store copies the wave's 128 C
+    rows through 32-bit byte offsets, so a C row stride of 2^24 - 64 elements
+    takes that path and 2^24 + 64 the predicated one. Both check every
+    output. C lives in one 8.6 GB device buffer of which only the 256 rows
+    are written."""
+    from layout_algebra_tiled_amd import gemm as g
+    from layout_algebra_tiled_amd.layout import Layout
+    M = N = 256
+    K = 128
+    A, B, C, D = _case(M, N, K, F16, "row", "col", "row", 1.0, 0.5, seed=77)
+    dev = torch.device("cuda:0")
+    dA, dB, dD = A.to(dev), B.to(dev), D.to(dev)
+    big = torch.empty((M - 1) * ((1 << 24) + 64) + N, dtype=torch.float16, device=dev)
+    try:
+        for ldc in ((1 << 24) - 64, (1 << 24) + 64):
+            say(f"[gemm] C row stride {ldc}")
+            big.as_strided((M, N), (ldc, 1)).copy_(C.view().to(dev))
+            dD.store.fill_(float("nan"))
+            lay = {"A": Layout.make([M, K], list(A.stride)), "B": Layout.make([K, N], list(B.stride)),
+                   "D": Layout.make([M, N], list(D.stride)), "C": Layout.make([M, N], [ldc, 1])}
+            plan = g.plan(dA.store, dB.store, dD.store, big, 0.5, kernel="tiled", tile=(256, 256), split_k=1,
+                          layouts=lay)
+            assert (plan["tile_n"], plan["grid"], plan["persistent"]) == (256, 1, 0), plan
+            g.gemm(dA.store, dB.store, dD.store, big, 1.0, 0.5, kernel="tiled", tile=(256, 256), split_k=1,
+                   layouts=lay)
+            torch.cuda.synchronize()
+            out = datagen.Matrix(dD.store.cpu(), D.shape, D.stride)
+            res = check_points(A, B, C, out, 1.0, 0.5, all_points(M, N))
+            say(f"[gemm] C row stride {ldc}: {res}")
+            _ok(res)
+    finally:
+        del big
+        torch.cuda.empty_cache()
 
 
 def test_k_zero_gives_beta_c_and_m_zero_is_noop():

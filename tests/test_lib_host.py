@@ -652,6 +652,20 @@ def test_plan_reports_the_wave_layout_of_the_data_parallel_launch():
         assert i.lds_bytes == 3 * (256 + 128) * 64 * 2 + (16 * 1024 if staged else 0), (a, b)
 
 
+def test_plan_persistent_with_c_needs_c_rows_within_32_bit_copy_offsets():
+    """The persistent launch with C copies 16 rows of C per copy instruction
+    through a 32-bit byte offset: a C row stride of 2^27 elements or more
+    leaves the planner's choice on one workgroup per tile and refuses the
+    forced persistent launch; 2^27 - 8 is still taken."""
+    for ldc, ok in ((2 ** 27 - 8, True), (2 ** 27, False)):
+        A, B, C, D = _gemm_descs(6144, 4096, 2048)
+        C = _desc(BASE + (1 << 44), L.LT_BF16, [6144, 4096], [ldc, 1])
+        st, i = _plan(A, B, C, D, bnz=1, kernel=L.LT_KERNEL_TILED, tile_n=128)
+        assert st == "LT_OK" and i.persistent == (1 if ok else 0), (ldc, st)
+        st, i = _plan(A, B, C, D, bnz=1, kernel=L.LT_KERNEL_TILED, tile_n=128, persistent=2)
+        assert st == ("LT_OK" if ok else "LT_ERR_UNSUPPORTED"), (ldc, st)
+
+
 def test_plan_lds_of_persistent_and_split_launches():
     """The persistent launches stage D for every major-ness (256x256 beside
     128 KiB: +32 KiB; 256x128 with or without C: +16 KiB, which the launch
