@@ -26,6 +26,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -389,6 +390,61 @@ def torch_matmul_timing(w: Workload, steps: int):
             "TFLOP/s": round(w.c.flops() / mean / 1e12, 1)}
 
 
+# bf16, K-major A and B, N-major D, alpha = 1, beta = 0 (the headline's
+# layouts): squares, then shapes of the kind a transformer's linear layers
+# run (hidden 4096 with an 11008 or 14336 MLP width, 8192 with 28672), and a
+# short-K and a long-K one
+SWEEP_SHAPES = [(n, n, n) for n in (1024, 2048, 3072, 4096, 6144, 8192, 12288, 16384)] + [
+    (4096, 11008, 4096), (4096, 4096, 11008), (8192, 14336, 4096), (8192, 28672, 8192), (16384, 16384, 1024),
+    (2048, 2048, 32768)]
+
+
+def sweep(reps: int = 8, launches: int = 10):
+    """Ours against torch.matmul (the vendor GEMM library) on the same
+    operands over SWEEP_SHAPES: launches queued back to back behind a stream
+    hold, one event pair per block, the two libraries alternating block by
+    block; the median block of each. Operands are drawn on the device from a
+    seeded generator (N(0,1)/sqrt(K), rounded to bf16). One JSON line per
+    shape on stdout. Timing only: the parity tests check these kernels."""
+    import torch
+    from layout_algebra_tiled_amd import gemm as g
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(20261202)
+    for M, N, K in SWEEP_SHAPES:
+        A = (torch.randn(M, K, device=dev, generator=gen) / math.sqrt(K)).to(torch.bfloat16)
+        Bt = (torch.randn(N, K, device=dev, generator=gen) / math.sqrt(K)).to(torch.bfloat16)
+        B = Bt.t()   # K x N, K-major
+        D, D2 = (torch.empty(M, N, dtype=torch.bfloat16, device=dev) for _ in range(2))
+        plan = g.plan(A, B, D)
+        need = plan["workspace_bytes"]
+        ws = torch.empty(need, dtype=torch.uint8, device=dev) if need else None
+        runs = {"ours": lambda i: g.gemm(A, B, D, workspace=ws),
+                "torch.matmul": lambda i: torch.matmul(A, B, out=D2)}
+        t_end = time.perf_counter() + 0.5
+        while time.perf_counter() < t_end:
+            for r in runs.values():
+                r(0)
+            torch.cuda.synchronize()
+        t = {k: [] for k in runs}
+        names = list(runs)
+        for rep in range(reps):
+            for k in (names if rep % 2 == 0 else names[::-1]):
+                t[k].append(queued_block_time(runs[k], launches))
+        flops = 2.0 * M * N * K
+        rec = {"M": M, "N": N, "K": K, "plan": {k: plan[k] for k in ("kernel_name", "tile_m", "tile_n", "grid",
+                                                                     "persistent", "tile_order", "split_k",
+                                                                     "sk_tiles")}}
+        for k, v in t.items():
+            med = sorted(v)[len(v) // 2]
+            rec[k] = {"us": round(med * 1e6, 1), "TFLOP/s": round(flops / med / 1e12, 1),
+                      "frac": round(flops / med / 1e12 / PEAK_TFLOPS, 4)}
+        rec["ours_vs_torch"] = round(rec["torch.matmul"]["us"] / rec["ours"]["us"], 3)
+        print(json.dumps(rec), flush=True)
+        del A, Bt, B, D, D2, ws
+        torch.cuda.empty_cache()
+
+
 def copy_probe(nbytes: int = 1 << 30, reps: int = 5):
     """A plain device copy of known size through the library's layout gather
     with the identity layout (n):(1): it reads and writes exactly nbytes per
@@ -523,6 +579,8 @@ def main():
     ap.add_argument("--persistent", choices=("auto", "on", "off"), default="auto",
                     help="the persistent launch of 256x128 tiles: the planner's choice, forced on or off "
                          "(profiling runs)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="only time ours against torch.matmul over a list of bf16 shapes (one JSON line each)")
     ap.add_argument("--also-torch-matmul", action="store_true",
                     help="also time torch.matmul (the vendor GEMM library) on the same operands, for scale")
     args = ap.parse_args()
@@ -543,6 +601,9 @@ def main():
 
     if args.copy_probe:
         copy_probe()
+        return
+    if args.sweep:
+        sweep()
         return
 
     # the skinny workload's B (128 MiB) would sit in the 256 MB last-level
@@ -585,6 +646,7 @@ def main():
                                f"fp32 accumulate", "M": w.c.M, "N": w.c.N, "K": w.c.K,
                    "kernel": plan["kernel_name"], "tile": [plan["tile_m"], plan["tile_n"], plan["tile_k"]],
                    "grid": plan["grid"], "persistent": bool(plan["persistent"]),
+                   "tile_order": {0: None, 1: "raster", 2: "superblock"}[plan["tile_order"]],
                    "pct_of_peak": round(100 * value / PEAK_TFLOPS, 2),
                    "kernel_us": {"mean": round(kern * 1e6, 1),
                                  "median": round(w.kernel_times[len(w.kernel_times) // 2] * 1e6, 1),

@@ -299,6 +299,15 @@ typedef struct lt_gemm_options {
                            also C's row stride below 2^27 elements); 1 = one workgroup
                            per tile; 2 = persistent (LT_ERR_UNSUPPORTED where the tile,
                            K, beta, C stride or split conditions fail) */
+    int32_t tile_order; /* TILED, the data-parallel launch of 256x256 tiles: 0 = chosen
+                           (super-blocks when a last-level-cache model of the two
+                           orders, walked round by round, fetches at most 85 % as
+                           many operand panels with them and a round's 32 panels fit
+                           192 MiB); 1 = raster (groups of 8 tile rows, a stretch per
+                           XCD); 2 = super-blocks: each round of 256 tiles a 16 x 16
+                           block, each XCD an 8 x 4 part of it (LT_ERR_UNSUPPORTED
+                           unless both tile counts are multiples of 16 and every tile
+                           is whole, unsplit and not persistent) */
 } lt_gemm_options;
 
 /* What the planner chose, for banners and tests [P1 "Exercise": print the
@@ -326,6 +335,8 @@ typedef struct lt_gemm_plan_info {
                                 tiles ["CUTLASS, in depth", "Kernel schedules"]; grid is
                                 then the workgroup count. A fused epilogue (lt_gemm_run_ex)
                                 runs one workgroup per tile instead. */
+    int32_t tile_order;      /* TILED data-parallel launch: 1 raster, 2 super-blocks; 0 for
+                                the other kernels and the persistent launch */
 } lt_gemm_plan_info;
 
 /* Validate and plan without launching: the can_implement half of the

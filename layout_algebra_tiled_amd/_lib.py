@@ -39,7 +39,7 @@ class lt_tensor(ctypes.Structure):
 
 class lt_gemm_options(ctypes.Structure):
     _fields_ = [("kernel", ctypes.c_int32), ("tile_m", ctypes.c_int32), ("tile_n", ctypes.c_int32),
-                ("split_k", ctypes.c_int32), ("persistent", ctypes.c_int32)]
+                ("split_k", ctypes.c_int32), ("persistent", ctypes.c_int32), ("tile_order", ctypes.c_int32)]
 
 
 class lt_epilogue(ctypes.Structure):
@@ -58,7 +58,7 @@ class lt_gemm_plan_info(ctypes.Structure):
                 ("grid", ctypes.c_int64), ("lds_bytes", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64),
                 ("mfma_per_wave_kstep", ctypes.c_int64), ("mfma_m", ctypes.c_int32), ("mfma_n", ctypes.c_int32),
                 ("mfma_k", ctypes.c_int32), ("sk_tiles", ctypes.c_int64), ("sk_workgroups", ctypes.c_int32),
-                ("tiles", ctypes.c_int64), ("persistent", ctypes.c_int32)]
+                ("tiles", ctypes.c_int64), ("persistent", ctypes.c_int32), ("tile_order", ctypes.c_int32)]
 
     def as_dict(self):
         return {name: getattr(self, name) for name, _ in self._fields_}

@@ -217,6 +217,17 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
     const int NS = kt1 - kt0;   // K slices this workgroup runs (>= 1)
     int tm, tn;
     tile_coords(lin, p, &tm, &tn);
+    if constexpr (!PERS && !SPLIT) {
+        // super-blocks (the planner sets this only for whole, unsplit tiles
+        // in multiples of 16 each way): the j-th workgroup of XCD x takes
+        // tile (8 (x mod 2) + j mod 8, 4 (x / 2) + (j mod 32) / 8) of 16x16
+        // block j / 32, blocks in row order
+        if (p.superblock) {
+            const int x = blockIdx.x & 7, j = blockIdx.x >> 3, sb = j >> 5, r = j & 31, sbn = p.tiles_n >> 4;
+            tm = 16 * (sb / sbn) + 8 * (x & 1) + (r & 7);
+            tn = 16 * (sb % sbn) + 4 * (x >> 1) + (r >> 3);
+        }
+    }
     int m0 = tm * Cf::BM, n0 = tn * Cf::BN;   // (the persistent launch moves them tile by tile)
 
     // ---- copy: S-stage ring, stage s at s*STAGE (A slice, then B slice).

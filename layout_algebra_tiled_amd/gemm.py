@@ -43,12 +43,19 @@ def tensor_desc(t: torch.Tensor, layout: Optional[Layout] = None) -> L.lt_tensor
     return d
 
 
-def _opts(kernel: Union[str, int], tile=None, split_k: int = 0, persistent=None) -> L.lt_gemm_options:
+TILE_ORDERS = {None: 0, "raster": 1, "superblock": 2}
+
+
+def _opts(kernel: Union[str, int], tile=None, split_k: int = 0, persistent=None,
+          tile_order=None) -> L.lt_gemm_options:
     o = L.lt_gemm_options()
     o.kernel = KERNELS[kernel] if isinstance(kernel, str) else int(kernel)
     o.tile_m, o.tile_n = tile if tile else (0, 0)
     o.split_k = split_k
     o.persistent = 0 if persistent is None else (2 if persistent else 1)
+    if tile_order not in TILE_ORDERS:
+        raise ValueError(f"unknown tile order {tile_order!r}")
+    o.tile_order = TILE_ORDERS[tile_order]
     return o
 
 
@@ -61,12 +68,12 @@ def _stream(stream) -> int:
 
 
 def plan(A, B, D, C=None, beta: float = 0.0, kernel="auto", tile=None, split_k=0, layouts=None,
-         persistent=None) -> dict:
+         persistent=None, tile_order=None) -> dict:
     la = layouts or {}
     dA, dB, dD = tensor_desc(A, la.get("A")), tensor_desc(B, la.get("B")), tensor_desc(D, la.get("D"))
     dC = tensor_desc(C, la.get("C")) if C is not None else None
     info = L.lt_gemm_plan_info()
-    o = _opts(kernel, tile, split_k, persistent)
+    o = _opts(kernel, tile, split_k, persistent, tile_order)
     L.check(L.lib().lt_gemm_plan(ctypes.byref(dA), ctypes.byref(dB), ctypes.byref(dC) if dC else None,
                                  ctypes.byref(dD), int(beta != 0.0), ctypes.byref(o), ctypes.byref(info)),
             "gemm_plan")
@@ -92,7 +99,7 @@ def _epilogue(bias, bias_stride, bias_per_row, activation, amax) -> Optional[L.l
 
 def gemm(A: torch.Tensor, B: torch.Tensor, D: torch.Tensor, C: Optional[torch.Tensor] = None,
          alpha: float = 1.0, beta: float = 0.0, *, kernel="auto", tile=None, split_k: int = 0,
-         persistent: Optional[bool] = None, layouts: Optional[dict] = None,
+         persistent: Optional[bool] = None, tile_order: Optional[str] = None, layouts: Optional[dict] = None,
          workspace: Optional[torch.Tensor] = None, stream=None,
          bias: Optional[torch.Tensor] = None, bias_stride: int = 1, bias_per_row: bool = False,
          activation: Optional[str] = None, amax: Optional[torch.Tensor] = None) -> None:
@@ -100,12 +107,13 @@ def gemm(A: torch.Tensor, B: torch.Tensor, D: torch.Tensor, C: Optional[torch.Te
     ``bias`` (D's dtype, one value per column, or per row with
     ``bias_per_row``), ``activation`` ("relu", "gelu") and ``amax`` (a float32
     device scalar receiving max |D|) select the fused epilogue. ``persistent``
-    (None: the planner's choice) forces the persistent launch of 256x128
-    tiles on or off."""
+    (None: the planner's choice) forces the persistent launch on or off;
+    ``tile_order`` ("raster", "superblock"; None: the planner's choice) sets
+    the order of the data-parallel launch's tiles."""
     la = layouts or {}
     dA, dB, dD = tensor_desc(A, la.get("A")), tensor_desc(B, la.get("B")), tensor_desc(D, la.get("D"))
     dC = tensor_desc(C, la.get("C")) if C is not None else None
-    o = _opts(kernel, tile, split_k, persistent)
+    o = _opts(kernel, tile, split_k, persistent, tile_order)
     ws_ptr, ws_bytes = None, 0
     sid = _stream(stream)
     if workspace is None:
@@ -133,7 +141,8 @@ def gemm(A: torch.Tensor, B: torch.Tensor, D: torch.Tensor, C: Optional[torch.Te
 
 def gemm_noalloc(A: torch.Tensor, B: torch.Tensor, D: torch.Tensor, C: Optional[torch.Tensor] = None,
                  alpha: float = 1.0, beta: float = 0.0, *, kernel="auto", tile=None, split_k: int = 0,
-                 persistent: Optional[bool] = None, layouts: Optional[dict] = None, stream=None,
+                 persistent: Optional[bool] = None, tile_order: Optional[str] = None,
+                 layouts: Optional[dict] = None, stream=None,
                  bias: Optional[torch.Tensor] = None,
                  bias_stride: int = 1, bias_per_row: bool = False, activation: Optional[str] = None,
                  amax: Optional[torch.Tensor] = None) -> None:
@@ -143,7 +152,7 @@ def gemm_noalloc(A: torch.Tensor, B: torch.Tensor, D: torch.Tensor, C: Optional[
     la = layouts or {}
     dA, dB, dD = tensor_desc(A, la.get("A")), tensor_desc(B, la.get("B")), tensor_desc(D, la.get("D"))
     dC = tensor_desc(C, la.get("C")) if C is not None else None
-    o = _opts(kernel, tile, split_k, persistent)
+    o = _opts(kernel, tile, split_k, persistent, tile_order)
     epi = _epilogue(bias, bias_stride, bias_per_row, activation, amax)
     L.check(L.lib().lt_gemm_run_noalloc(ctypes.byref(dA), ctypes.byref(dB), ctypes.byref(dC) if dC else None,
                                         ctypes.byref(dD), float(alpha), float(beta), ctypes.byref(o),

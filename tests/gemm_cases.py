@@ -39,7 +39,7 @@ def all_points(M: int, N: int) -> np.ndarray:
 
 def run_gemm(A: datagen.Matrix, B: datagen.Matrix, C: Optional[datagen.Matrix], D: datagen.Matrix,
              alpha: float, beta: float, kernel="auto", split_k: int = 0, tile=None,
-             expect_kernel: Optional[str] = None, label: str = "", persistent=None):
+             expect_kernel: Optional[str] = None, label: str = "", persistent=None, tile_order=None):
     """Run D = alpha*A*B + beta*C on cuda:0 through the library, D pre-filled
     with NaN (an output the kernel never writes fails any check). Returns
     (plan dict, output matrix on the CPU)."""
@@ -48,7 +48,8 @@ def run_gemm(A: datagen.Matrix, B: datagen.Matrix, C: Optional[datagen.Matrix], 
 
     M, N = D.shape
     say(f"[gemm] {label} M={M} N={N} K={A.shape[1]} {A.dtype} A{A.stride} B{B.stride} D{D.stride} "
-        f"alpha={alpha} beta={beta} kernel={kernel} tile={tile} split_k={split_k} persistent={persistent}")
+        f"alpha={alpha} beta={beta} kernel={kernel} tile={tile} split_k={split_k} persistent={persistent} "
+        f"tile_order={tile_order}")
     dev = torch.device("cuda:0")
     dA, dB, dD = A.to(dev), B.to(dev), D.to(dev)
     dC = C.to(dev) if C is not None else None
@@ -58,11 +59,11 @@ def run_gemm(A: datagen.Matrix, B: datagen.Matrix, C: Optional[datagen.Matrix], 
     if C is not None:
         lay["C"] = Layout.make(list(C.shape), list(C.stride))
     plan = g.plan(dA.store, dB.store, dD.store, dC.store if dC is not None else None, beta, kernel=kernel,
-                  tile=tile, split_k=split_k, layouts=lay, persistent=persistent)
+                  tile=tile, split_k=split_k, layouts=lay, persistent=persistent, tile_order=tile_order)
     if expect_kernel:
         assert plan["kernel_name"] == expect_kernel, plan
     g.gemm(dA.store, dB.store, dD.store, dC.store if dC is not None else None, alpha, beta, kernel=kernel,
-           tile=tile, split_k=split_k, layouts=lay, persistent=persistent)
+           tile=tile, split_k=split_k, layouts=lay, persistent=persistent, tile_order=tile_order)
     torch.cuda.synchronize()
     out = datagen.Matrix(dD.store.cpu(), D.shape, D.stride)
     say(f"[gemm] {label} ran {plan['kernel_name']} tile {plan['tile_m']}x{plan['tile_n']} grid={plan['grid']} "

@@ -318,6 +318,23 @@ def test_in_place_d_is_c():
     _ok(og.check(got, Dref, T, Cabs, 1.0, F16))
 
 
+def test_tiled_superblock_order_matches_the_raster():
+    """The data-parallel launch in 16x16-tile super-blocks (forced; 16 x 32
+    tiles: two blocks) computes every tile exactly as the raster order does:
+    the outputs are bit-equal, and every one is within the oracle's bound."""
+    M, N, K = 4096, 8192, 512
+    A, B, C, D = _case(M, N, K, BF16, "row", "col", "row", 1.0, 0.0, dist="normal_over_sqrtk", seed=91)
+    outs = {}
+    for order in ("superblock", "raster"):
+        plan, out = run_gemm(A, B, None, D, 1.0, 0.0, kernel="tiled", tile=(256, 256), split_k=1,
+                             persistent=False, tile_order=order, label=f"order {order}")
+        assert plan["tile_order"] == (2 if order == "superblock" else 1), plan
+        outs[order] = out.view().clone()
+    assert torch.equal(outs["superblock"].view(torch.int16), outs["raster"].view(torch.int16))
+    res = check_all_rows(A, B, None, datagen.Matrix(outs["superblock"].reshape(-1), (M, N), (N, 1)), 1.0, 0.0)
+    _ok(res)
+
+
 def test_tiled_c_rows_at_the_staged_copy_offset_limit():
     """A whole 256x256 tile with C: the staged store copies the wave's 128 C
     rows through 32-bit byte offsets, so a C row stride of 2^24 - 64 elements

@@ -666,6 +666,39 @@ def test_plan_persistent_with_c_needs_c_rows_within_32_bit_copy_offsets():
         assert st == ("LT_OK" if ok else "LT_ERR_UNSUPPORTED"), (ldc, st)
 
 
+def test_plan_tile_order():
+    """The data-parallel launch's tile order: super-blocks where the
+    last-level-cache model says they pay (measured faster on these shapes),
+    the raster where they do not (measured slower or even), 0 for the
+    persistent launch; forcing super-blocks needs tile counts in multiples of
+    16 and whole, unsplit tiles."""
+    for (M, N, K), want in (((16384, 16384, 8192), 2), ((12288, 12288, 12288), 2), ((16384, 8192, 8192), 2),
+                            ((16384, 16384, 12288), 2), ((8192, 8192, 8192), 1), ((8192, 28672, 8192), 1),
+                            ((16384, 16384, 16384), 1), ((12288, 12288, 16384), 1), ((8192, 8192, 4096), 0)):
+        st, i = _plan(*_gemm_descs(M, N, K))
+        assert st == "LT_OK" and i.tile_order == want, (M, N, K, i.tile_order)
+        assert (i.persistent == 1) == (want == 0)
+    descs = _gemm_descs(4096, 8192, 512)
+    for order in (1, 2):
+        o = L.lt_gemm_options()
+        o.kernel, o.tile_n, o.persistent, o.tile_order = L.LT_KERNEL_TILED, 256, 1, order
+        info = L.lt_gemm_plan_info()
+        st = L.lib().lt_gemm_plan(*(ctypes.byref(d) for d in descs[:2]), None, ctypes.byref(descs[3]), 0,
+                                  ctypes.byref(o), ctypes.byref(info))
+        assert L.STATUS_NAMES[st] == "LT_OK" and info.tile_order == order
+    o = L.lt_gemm_options()
+    o.kernel, o.tile_n, o.persistent, o.tile_order = L.LT_KERNEL_TILED, 256, 1, 2
+    for M, N, K in ((4096, 4096 + 256, 512), (1024, 1024, 16384)):   # 17 tile columns; a split plan
+        d = _gemm_descs(M, N, K)
+        st = L.lib().lt_gemm_plan(ctypes.byref(d[0]), ctypes.byref(d[1]), None, ctypes.byref(d[3]), 0,
+                                  ctypes.byref(o), ctypes.byref(L.lt_gemm_plan_info()))
+        assert L.STATUS_NAMES[st] == "LT_ERR_UNSUPPORTED", (M, N, K)
+    o.tile_order = 3
+    st = L.lib().lt_gemm_plan(*(ctypes.byref(d) for d in descs[:2]), None, ctypes.byref(descs[3]), 0,
+                              ctypes.byref(o), ctypes.byref(L.lt_gemm_plan_info()))
+    assert L.STATUS_NAMES[st] == "LT_ERR_INVALID_ARGUMENT"
+
+
 def test_plan_lds_of_persistent_and_split_launches():
     """The persistent launches stage D for every major-ness (256x256 beside
     128 KiB: +32 KiB; 256x128 with or without C: +16 KiB, which the launch
