@@ -193,7 +193,7 @@ struct Plan {
     int64_t dp_tiles = 0, sk_tiles = 0;
     int sk_splits = 1;
     int64_t sk_counter_bytes = 0;   // workspace: counters first, then partials
-    int tile_n = 256;               // tiled kernel: block tile 256 x tile_n
+    int tile_m = 256, tile_n = 256; // tiled kernel: block tile tile_m x tile_n
     int persist_grid = 0;           // > 0: persistent launch of this many workgroups
     bool superblock = false;        // the data-parallel launch walks 16x16-tile super-blocks
 };
@@ -266,7 +266,7 @@ lt_status make_plan(const lt_tensor* tA, const lt_tensor* tB, const lt_tensor* t
     const bool c_n = !beta_nonzero || p.C.e1 == 1 || p.C.s1 == 1;
 
     int kernel = opt ? opt->kernel : LT_KERNEL_AUTO;
-    const TiledShape ts = tiled_shape(p.a_k, p.b_k, 256);
+    const TiledShape ts = tiled_shape(p.a_k, p.b_k, 256, 256);
     // M-major A and N-major B stream through the same kernel (transposed
     // fragment reads); any stride-1 mode of A and B works.
     // The tiled kernel addresses a K slice as a uniform base plus a per-lane
@@ -336,9 +336,12 @@ lt_status make_plan(const lt_tensor* tA, const lt_tensor* tB, const lt_tensor* t
         case LT_KERNEL_TILED: {
             if (!tiled_ok) return d_n && c_n ? LT_ERR_NOT_DIVISIBLE : LT_ERR_UNSUPPORTED;
             const int want_n = opt ? opt->tile_n : 0;
-            if (opt && opt->tile_m && opt->tile_m != 256) return LT_ERR_UNSUPPORTED;
+            const int want_m = opt ? opt->tile_m : 0;
+            if (want_m != 0 && want_m != 256 && want_m != 128) return LT_ERR_UNSUPPORTED;
             if (want_n != 0 && want_n != 256 && want_n != 128) return LT_ERR_UNSUPPORTED;
-            if (want_n == 128 && split > 1) return LT_ERR_UNSUPPORTED;   // 256x128 tiles are never split
+            if (want_m == 128 && want_n == 256) return LT_ERR_UNSUPPORTED;   // no 128x256 tile
+            // 256x128 and 128x128 tiles are never split
+            if ((want_n == 128 || want_m == 128) && split > 1) return LT_ERR_UNSUPPORTED;
             // Block tile and wave quantisation ("CUTLASS, in depth", "Worked
             // example: tile choice and wave quantisation"): ntiles whole
             // tiles on kCUs compute units leave the last round part empty.
@@ -388,13 +391,31 @@ lt_status make_plan(const lt_tensor* tA, const lt_tensor* tB, const lt_tensor* t
                 rem = 0;
             }
             const int64_t c128x20 = (n128 + kCUs - 1) / kCUs * KTt * 23;
-            int tile_n = 256;
+            // 128x128: a quarter of a 256x256 tile's work per slice at a
+            // lower rate (more LDS bytes per MFMA, shorter K steps to hide
+            // the reads behind): 16 in the units in which a 256x128 slice
+            // costs 23 (measured 14.5-16.2: bf16 1024^3 10.6 us against 16.8
+            // for 256x128, 2048^3 20.7 against 29.4, 2048^2 x 8192 63.0
+            // against 91.2; the larger tiles win from 3072^3: 72.9 against
+            // 65.7 for 256x256); only for a fully automatic tile choice, and
+            // against a split of 256x256 tiles only when they fill at least
+            // half the CUs (1024^2 x 16384: 64 128x128 tiles 92.4 us, 16
+            // tiles split 8 ways 83.7; 1536^2 x 12288: 144 tiles 77.1, the
+            // split 96.1; 2048^2 x 16384: 256 tiles 117.3, the split 135.7)
+            const int64_t n64 = ((p.M + 127) / 128) * ((p.N + 127) / 128);
+            const int64_t c64x20 = (n64 + kCUs - 1) / kCUs * KTt * 16;
+            int tile_m = 256, tile_n = 256;
             if (want_n == 128 || (want_n == 0 && split <= 1 && c128x20 < c256 * 20)) tile_n = 128;
+            if (want_m == 128 || (want_m == 0 && want_n == 0 && split <= 1 && (S < 2 || 2 * n64 >= kCUs) &&
+                                  c64x20 < std::min(c128x20, c256 * 20))) {
+                tile_m = 128;
+                tile_n = 128;
+            }
             if (tile_n == 128) {
                 S = 1;
                 rem = 0;
             }
-            const TiledShape tsc = tiled_shape(p.a_k, p.b_k, tile_n);
+            const TiledShape tsc = tiled_shape(p.a_k, p.b_k, tile_m, tile_n);
             in.tile_m = tsc.bm;
             in.tile_n = tsc.bn;
             in.tile_k = tsc.bk;
@@ -404,7 +425,7 @@ lt_status make_plan(const lt_tensor* tA, const lt_tensor* tB, const lt_tensor* t
             in.stages = tsc.stages;
             in.lds_bytes = tsc.lds_bytes;
             if (in.lds_bytes > 160 * 1024) return LT_ERR_LDS_OVERFLOW;
-            const int64_t ntiles = tile_n == 128 ? n128 : n256;
+            const int64_t ntiles = tile_m == 128 ? n64 : tile_n == 128 ? n128 : n256;
             // Persistent launch of 256x128 tiles ("CUTLASS, in depth",
             // "Kernel schedules"): one workgroup per compute unit walks its
             // tiles and copies the next tile's first slices while the
@@ -426,7 +447,8 @@ lt_status make_plan(const lt_tensor* tA, const lt_tensor* tB, const lt_tensor* t
             // (with C, a copy of C rows reaches 16 rows of C through a 32-bit
             // byte offset)
             const bool c_rows_fit = !beta_nonzero || p.C.s0 * 2 * 16 < (int64_t(1) << 32);
-            const bool persist_ok = (tile_n == 128 || (!beta_nonzero && rem == 0)) && p.M % tsc.bm == 0 &&
+            const bool persist_ok = tile_m == 256 && (tile_n == 128 || (!beta_nonzero && rem == 0)) &&
+                                    p.M % tsc.bm == 0 &&
                                     p.N % tsc.bn == 0 && p.K % tsc.bk == 0 && KTt >= 4 && c_rows_fit;
             if (want_p == 2 && !persist_ok) return LT_ERR_UNSUPPORTED;
             const bool persist =
@@ -441,6 +463,7 @@ lt_status make_plan(const lt_tensor* tA, const lt_tensor* tB, const lt_tensor* t
             if (want_o == 2 && !sb_ok) return LT_ERR_UNSUPPORTED;
             p.superblock = sb_ok && (want_o == 2 || (want_o == 0 && superblock_pays(tm_, tn_, p.K)));
             in.tile_order = persist ? 0 : (p.superblock ? 2 : 1);
+            p.tile_m = tile_m;
             p.tile_n = tile_n;
             p.dp_tiles = ntiles - rem;
             p.sk_tiles = rem;
@@ -672,7 +695,7 @@ lt_status lt_gemm_run_ex(const lt_tensor* A, const lt_tensor* B, const lt_tensor
             // The tile grid: mode 1 of zipped_divide(D', (256,256)), where D'
             // is D's layout with M and N rounded up to whole tiles (the
             // outputs past (M, N) are predicated off in the epilogue).
-            const lt::TiledShape ts = lt::tiled_shape(p.a_k, p.b_k, p.tile_n);
+            const lt::TiledShape ts = lt::tiled_shape(p.a_k, p.b_k, p.tile_m, p.tile_n);
             const int64_t mp = (p.M + ts.bm - 1) / ts.bm * ts.bm, np = (p.N + ts.bn - 1) / ts.bn * ts.bn;
             lt::Tree dl = lt::Tree::tuple({lt::Tree::leaf(mp, p.D.s0), lt::Tree::leaf(np, 1)});
             const int64_t tiler[2] = {ts.bm, ts.bn};
@@ -701,7 +724,7 @@ lt_status lt_gemm_run_ex(const lt_tensor* A, const lt_tensor* B, const lt_tensor
             }
             a.epi = ea;
             // the fused epilogue runs in the one-workgroup-per-tile launch
-            err = lt::launch_tiled(dt, p.a_k, p.b_k, p.tile_n, ea.fused ? 0 : p.persist_grid, a, stream);
+            err = lt::launch_tiled(dt, p.a_k, p.b_k, p.tile_m, p.tile_n, ea.fused ? 0 : p.persist_grid, a, stream);
             break;
         }
         case LT_KERNEL_SKINNY: {

@@ -344,27 +344,28 @@ TiledShape shape_of() {
 }
 
 template <bool AK, bool BKM>
-TiledShape shape_for(int tile_n) {
+TiledShape shape_for(int tile_m, int tile_n) {
+    if (tile_m == 128) return shape_of<Dp128x128<AK, BKM>>();
     return tile_n == 128 ? shape_of<Dp128<AK, BKM>>() : shape_of<Dp256<AK, BKM>>();
 }
 
-TiledShape tiled_shape(bool a_kmajor, bool b_kmajor, int tile_n) {
-    if (a_kmajor && b_kmajor) return shape_for<true, true>(tile_n);
-    if (a_kmajor) return shape_for<true, false>(tile_n);
-    if (b_kmajor) return shape_for<false, true>(tile_n);
-    return shape_for<false, false>(tile_n);
+TiledShape tiled_shape(bool a_kmajor, bool b_kmajor, int tile_m, int tile_n) {
+    if (a_kmajor && b_kmajor) return shape_for<true, true>(tile_m, tile_n);
+    if (a_kmajor) return shape_for<true, false>(tile_m, tile_n);
+    if (b_kmajor) return shape_for<false, true>(tile_m, tile_n);
+    return shape_for<false, false>(tile_m, tile_n);
 }
 
-int launch_tiled(int dtype, bool a_kmajor, bool b_kmajor, int tile_n, int persist_grid, const TiledArgs& a,
-                 void* stream) {
+int launch_tiled(int dtype, bool a_kmajor, bool b_kmajor, int tile_m, int tile_n, int persist_grid,
+                 const TiledArgs& a, void* stream) {
     static_assert(LT_F16 == 1 && LT_BF16 == 2, "variant names carry the dtype code");
-    const int pg = persist_grid;
+    const int pg = persist_grid, tm = tile_m, tn = tile_n;
     if (dtype == LT_F16) {
-        if (a_kmajor) return b_kmajor ? launch_tiled_11_1(a, tile_n, pg, stream) : launch_tiled_11_0(a, tile_n, pg, stream);
-        return b_kmajor ? launch_tiled_10_1(a, tile_n, pg, stream) : launch_tiled_10_0(a, tile_n, pg, stream);
+        if (a_kmajor) return b_kmajor ? launch_tiled_11_1(a, tm, tn, pg, stream) : launch_tiled_11_0(a, tm, tn, pg, stream);
+        return b_kmajor ? launch_tiled_10_1(a, tm, tn, pg, stream) : launch_tiled_10_0(a, tm, tn, pg, stream);
     }
-    if (a_kmajor) return b_kmajor ? launch_tiled_21_1(a, tile_n, pg, stream) : launch_tiled_21_0(a, tile_n, pg, stream);
-    return b_kmajor ? launch_tiled_20_1(a, tile_n, pg, stream) : launch_tiled_20_0(a, tile_n, pg, stream);
+    if (a_kmajor) return b_kmajor ? launch_tiled_21_1(a, tm, tn, pg, stream) : launch_tiled_21_0(a, tm, tn, pg, stream);
+    return b_kmajor ? launch_tiled_20_1(a, tm, tn, pg, stream) : launch_tiled_20_0(a, tm, tn, pg, stream);
 }
 
 template <int DT>

@@ -117,24 +117,24 @@ struct TiledShape {
     int mfma_mn, mfma_k;     // MFMA instruction: mfma_mn x mfma_mn outputs, K depth
 };
 // The block shape of the data-parallel launch of the tiled kernel for a
-// block tile 256 x tile_n (tile_n 256 or 128).
-TiledShape tiled_shape(bool a_kmajor, bool b_kmajor, int tile_n);
+// block tile tile_m x tile_n (256x256, 256x128 or 128x128).
+TiledShape tiled_shape(bool a_kmajor, bool b_kmajor, int tile_m, int tile_n);
 
 // Each returns 0 on success or the hipError_t of the launch.
 int launch_wave16(int dtype, const Wave16Args& a, void* stream);
-int launch_tiled(int dtype, bool a_kmajor, bool b_kmajor, int tile_n, int persist_grid, const TiledArgs& a,
-                 void* stream);
+int launch_tiled(int dtype, bool a_kmajor, bool b_kmajor, int tile_m, int tile_n, int persist_grid,
+                 const TiledArgs& a, void* stream);
 // The variants of the tiled kernel, launch_tiled_<dtype><A K-major>_<B
 // K-major>; each is compiled in a translation unit of its own
 // (gemm_tiled.hip built with LT_TILED_DT / LT_TILED_AK / LT_TILED_BK).
-int launch_tiled_11_1(const TiledArgs& a, int tile_n, int persist_grid, void* stream);
-int launch_tiled_11_0(const TiledArgs& a, int tile_n, int persist_grid, void* stream);
-int launch_tiled_10_1(const TiledArgs& a, int tile_n, int persist_grid, void* stream);
-int launch_tiled_10_0(const TiledArgs& a, int tile_n, int persist_grid, void* stream);
-int launch_tiled_21_1(const TiledArgs& a, int tile_n, int persist_grid, void* stream);
-int launch_tiled_21_0(const TiledArgs& a, int tile_n, int persist_grid, void* stream);
-int launch_tiled_20_1(const TiledArgs& a, int tile_n, int persist_grid, void* stream);
-int launch_tiled_20_0(const TiledArgs& a, int tile_n, int persist_grid, void* stream);
+int launch_tiled_11_1(const TiledArgs& a, int tile_m, int tile_n, int persist_grid, void* stream);
+int launch_tiled_11_0(const TiledArgs& a, int tile_m, int tile_n, int persist_grid, void* stream);
+int launch_tiled_10_1(const TiledArgs& a, int tile_m, int tile_n, int persist_grid, void* stream);
+int launch_tiled_10_0(const TiledArgs& a, int tile_m, int tile_n, int persist_grid, void* stream);
+int launch_tiled_21_1(const TiledArgs& a, int tile_m, int tile_n, int persist_grid, void* stream);
+int launch_tiled_21_0(const TiledArgs& a, int tile_m, int tile_n, int persist_grid, void* stream);
+int launch_tiled_20_1(const TiledArgs& a, int tile_m, int tile_n, int persist_grid, void* stream);
+int launch_tiled_20_0(const TiledArgs& a, int tile_m, int tile_n, int persist_grid, void* stream);
 int launch_skinny(int dtype, const SkinnyArgs& a, void* stream);
 // *p = 0.0f on the stream (a one-thread kernel: no memset node in a captured graph)
 int launch_zero_f32(float* p, void* stream);

@@ -1082,13 +1082,16 @@ int launch_mode(const TiledArgs& a, int grid, hipStream_t s) {
 
 }  // namespace
 
-// 256x128 tiles: one workgroup per tile, or (persist_grid > 0) a
+// 128x128 tiles: one workgroup per tile. 256x128 tiles: one workgroup per
+// tile, or (persist_grid > 0) a
 // persistent launch of persist_grid workgroups walking the tiles; the
 // planner never splits them. 256x256 tiles: the data-parallel tiles, then
 // (same stream, so after them) the split remainder.
 template <int DT, bool AK, bool BKM>
-int launch_variant(const TiledArgs& a, int tile_n, int persist_grid, void* stream) {
+int launch_variant(const TiledArgs& a, int tile_m, int tile_n, int persist_grid, void* stream) {
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (tile_m == 128)   // 128x128 tiles: one workgroup per tile, never split or persistent
+        return a.dp_tiles > 0 ? launch_mode<DT, Dp128x128<AK, BKM>, kDataParallel>(a, a.dp_tiles, s) : 0;
     if (tile_n == 128) {
         if (persist_grid > 0)
             return a.beta != 0.0f ? launch_mode<DT, Dp128<AK, BKM>, kPersistentC>(a, persist_grid, s)
@@ -1112,8 +1115,9 @@ int launch_variant(const TiledArgs& a, int tile_n, int persist_grid, void* strea
 #if defined(LT_TILED_DT) && defined(LT_TILED_AK) && defined(LT_TILED_BK)
 #define LT_CAT(dt, ak, bk) launch_tiled_##dt##ak##_##bk
 #define LT_NAME(dt, ak, bk) LT_CAT(dt, ak, bk)
-int LT_NAME(LT_TILED_DT, LT_TILED_AK, LT_TILED_BK)(const TiledArgs& a, int tile_n, int persist_grid, void* stream) {
-    return launch_variant<LT_TILED_DT, LT_TILED_AK != 0, LT_TILED_BK != 0>(a, tile_n, persist_grid, stream);
+int LT_NAME(LT_TILED_DT, LT_TILED_AK, LT_TILED_BK)(const TiledArgs& a, int tile_m, int tile_n, int persist_grid,
+                                                    void* stream) {
+    return launch_variant<LT_TILED_DT, LT_TILED_AK != 0, LT_TILED_BK != 0>(a, tile_m, tile_n, persist_grid, stream);
 }
 #endif
 

@@ -142,6 +142,9 @@ LT_HD constexpr int launch_lds_bytes(int ring_lds, bool staged, bool persistent_
 //   Dp128:   256x128 block tile, 4 waves of 128x64, 3 stages of 48 KiB: twice
 //            the tiles, for shapes whose 256x256 tiles leave a round of the
 //            CUs part empty.
+//   Dp128x128: 128x128 block tile, 4 waves of 64x64, 4 stages of 32 KiB:
+//            four times the tiles of 256x256, for problems whose larger
+//            tiles would leave most of the CUs idle (data-parallel only).
 //   Split256: the split-remainder launch, 8 waves (4 x 2) of 64x128: its
 //            fix-up adds the other segments' fp32 partials in registers, and
 //            with 256 accumulators per lane that step spills.
@@ -149,6 +152,8 @@ template <bool AK, bool BKM>
 using Dp256 = TCfg<256, 256, 2, 2, 64, 2, 16, AK, BKM>;
 template <bool AK, bool BKM>
 using Dp128 = TCfg<256, 128, 2, 2, 64, 3, 16, AK, BKM>;
+template <bool AK, bool BKM>
+using Dp128x128 = TCfg<128, 128, 2, 2, 64, 4, 16, AK, BKM>;
 template <bool AK, bool BKM>
 using Split256 = TCfg<256, 256, 4, 2, 64, 2, 16, AK, BKM>;
 

@@ -43,6 +43,7 @@ CASES = [
     ("tiled-mn", 264, 392, 96, BF16, "col", "row", "row", 1.0, "tiled", 0, "tiled", None),
     ("tiled-mn-256", 264, 392, 96, F16, "col", "row", "row", 0.0, "tiled", 0, "tiled", (256, 256)),
     ("tiled-split", 512, 768, 512, BF16, "row", "col", "row", 0.5, "tiled", 2, "tiled", None),
+    ("tiled-128", 392, 648, 192, F16, "col", "col", "row", 0.5, "tiled", 1, "tiled", (128, 128)),
     ("skinny", 32, 1024, 4096, BF16, "row", "col", "row", 0.0, "auto", 0, "skinny", None),
     ("skinny-split", 17, 512, 4096, F16, "row", "col", "row", 0.5, "auto", 2, "skinny", None),
 ]
@@ -58,7 +59,7 @@ def test_fused_epilogue_all_kernels(case, per_row, act):
     res, plan, amax, wmax = run_and_check_fused(A, B, C, D, 1.5, beta, bias, per_row, act, kernel=kernel,
                                                 split_k=split, expect_kernel=expect, label=label, tile=tile)
     if tile:
-        assert plan["tile_n"] == tile[1]
+        assert (plan["tile_m"], plan["tile_n"]) == tile
     assert res.ok, str(res)
     assert amax == wmax
 

@@ -318,6 +318,35 @@ def test_in_place_d_is_c():
     _ok(og.check(got, Dref, T, Cabs, 1.0, F16))
 
 
+@pytest.mark.parametrize("M,N,K,dtype,a_major,b_major,alpha,beta,tile", [
+    (1024, 1024, 1024, BF16, "row", "col", 1.0, 0.0, None),            # the planner's: 64 tiles, staged D
+    (640, 384, 320, F16, "col", "row", 2.0, -1.0, (128, 128)),         # M-/N-major, C
+    (300, 520, 200, F16, "row", "row", 1.0, 0.5, (128, 128)),          # ragged tiles, partial first slice
+    (512, 768, 448, BF16, "col", "col", 1.0, 1.0, (128, 128)),
+    (1536, 1536, 1536, F16, "row", "col", 1.0, 0.5, None),             # the planner's: 144 tiles, C
+])
+def test_tiled_128x128_all_outputs(M, N, K, dtype, a_major, b_major, alpha, beta, tile):
+    """128x128 block tiles (4 waves of 64x64, 4 stages of 32 KiB), forced or
+    the planner's choice for problems whose larger tiles leave CUs idle;
+    every output checked."""
+    A, B, C, D = _case(M, N, K, dtype, a_major, b_major, "row", alpha, beta, seed=M + 7 * K)
+    res, plan, _ = run_and_check(A, B, C, D, alpha, beta, kernel="tiled" if tile else "auto", tile=tile,
+                                 split_k=1 if tile else 0, expect_kernel="tiled", label="128x128")
+    assert (plan["tile_m"], plan["tile_n"], plan["persistent"]) == (128, 128, 0), plan
+    _ok(res)
+
+
+def test_tiled_128x128_planned_long_k_sampled():
+    """The planner's 128x128 tiles on bf16 2048^2 x 8192 (256 tiles, one
+    round, 128 slices each), sampled outputs."""
+    M, N, K = 2048, 2048, 8192
+    A, B, C, D = _case(M, N, K, BF16, "row", "col", "row", 1.0, 0.0, dist="normal_over_sqrtk", seed=5)
+    res, plan, _ = run_and_check(A, B, C, D, 1.0, 0.0, points=sample_points(M, N, 20000, seed=3),
+                                 expect_kernel="tiled", label="128x128 planned")
+    assert (plan["tile_m"], plan["tile_n"], plan["grid"]) == (128, 128, 256), plan
+    _ok(res)
+
+
 def test_tiled_superblock_order_matches_the_raster():
     """The data-parallel launch in 16x16-tile super-blocks (forced; 16 x 32
     tiles: two blocks) computes every tile exactly as the raster order does:

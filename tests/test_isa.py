@@ -116,11 +116,13 @@ def test_every_tiled_variant_has_device_code_and_a_stub(disasm):
                 # (last template argument: the launch mode)
                 t256 = f"_ZN2lt10gemm_tiledILi{dt}ENS_4TCfgILi256ELi256ELi2ELi2ELi64ELi2ELi16EL{a}EL{b}EEE"
                 t128 = f"_ZN2lt10gemm_tiledILi{dt}ENS_4TCfgILi256ELi128ELi2ELi2ELi64ELi3ELi16EL{a}EL{b}EEE"
+                tsq = f"_ZN2lt10gemm_tiledILi{dt}ENS_4TCfgILi128ELi128ELi2ELi2ELi64ELi4ELi16EL{a}EL{b}EEE"
                 tspl = f"_ZN2lt10gemm_tiledILi{dt}ENS_4TCfgILi256ELi256ELi4ELi2ELi64ELi2ELi16EL{a}EL{b}EEE"
                 for mode in (0, 2):
                     want.add(t256 + f"Li{mode}EEEvNS_9TiledArgsE")
                 for mode in (0, 2, 3):
                     want.add(t128 + f"Li{mode}EEEvNS_9TiledArgsE")
+                want.add(tsq + "Li0EEEvNS_9TiledArgsE")   # 128x128: one workgroup per tile
                 want.add(tspl + "Li1EEEvNS_9TiledArgsE")
     assert want <= names, sorted(want - names)
 
@@ -174,7 +176,7 @@ def test_no_instruction_reads_an_mfma_result_too_early(disasm):
         bad = mfma_result_hazards(insts)
         assert not bad, f"{key[1]}: {bad[:3]}"
         checked += 1
-    assert checked == 48
+    assert checked == 56
 
 
 def test_mfma_hazard_checker_catches_an_early_read():
@@ -265,7 +267,7 @@ def test_tiled_kernels_keep_scratch_out_of_the_k_loop(disasm):
     funcs, addrs, _ = disasm
     meta = disasm_meta()
     tiled = [k for k in funcs if "gemm_tiled" in k[1]]
-    assert len(tiled) == 48
+    assert len(tiled) == 56
     skinny = [k for k in funcs if "gemm_skinny" in k[1]]
     assert len(skinny) == 2
     for key in skinny:

@@ -415,8 +415,8 @@ def test_plan_validation_statuses():
     # predicated); the automatic choice keeps a problem smaller than one tile
     # on the 16x16 kernel
     A, B, C, D = _gemm_descs(250, 256, 64)
-    st, i = _plan(A, B, C, D, kernel=L.LT_KERNEL_TILED)   # one 256x256 tile = two 256x128 ones
-    assert st == "LT_OK" and i.kernel == L.LT_KERNEL_TILED and (i.tile_n, i.grid) == (128, 2)
+    st, i = _plan(A, B, C, D, kernel=L.LT_KERNEL_TILED)   # one 256x256 tile = four 128x128 ones
+    assert st == "LT_OK" and i.kernel == L.LT_KERNEL_TILED and (i.tile_m, i.tile_n, i.grid) == (128, 128, 4)
     st, i = _plan(A, B, C, D, kernel=L.LT_KERNEL_TILED, tile_n=256)
     assert st == "LT_OK" and (i.tile_n, i.grid) == (256, 1)
     # block tiles other than 256x256 and 256x128 are refused, and so is a
@@ -460,7 +460,7 @@ def test_plan_ragged_shapes_on_the_tiled_kernel():
         st, i = _plan(*_gemm_descs(M, N, K))
         assert st == "LT_OK" and i.kernel == expect, (M, N, K, st, i.kernel)
         if expect == L.LT_KERNEL_TILED:
-            tiles = -(-M // 256) * -(-N // i.tile_n)
+            tiles = -(-M // i.tile_m) * -(-N // i.tile_n)
             assert i.tiles == tiles and i.grid == tiles - i.sk_tiles + i.sk_workgroups
 
 
@@ -470,8 +470,10 @@ def _tile_plan(M, N, K, split=0, want_n=0):
     data-parallel and the last round's rem tiles are split into S K segments
     when that saves 3 % (12 slices per partial the last segment reads back,
     plus 24 when all 256x128 tiles fit one round) or when forced;
-    256x128 tiles cost 23/20 per slice and are never split. Returns
-    (tile_n, data-parallel tiles, split tiles, S)."""
+    256x128 tiles cost 23/20 per slice and are never split; 128x128 tiles
+    cost 16/20 per slice, never split, taken only by a fully automatic tile
+    choice. Returns (tile code: 256, 128 for 256x128, 64 for 128x128,
+    data-parallel tiles, split tiles, S)."""
     kt = -(-K // 64)
     n256 = -(-M // 256) * -(-N // 256)
     n128 = -(-M // 256) * -(-N // 128)
@@ -492,7 +494,11 @@ def _tile_plan(M, N, K, split=0, want_n=0):
     if S < 2:
         S, rem = 1, 0
     n128 = -(-M // 256) * -(-N // 128)
-    if want_n == 128 or (want_n == 0 and split <= 1 and -(-n128 // 256) * kt * 23 < c256 * 20):
+    c128 = -(-n128 // 256) * kt * 23
+    n64 = -(-M // 128) * -(-N // 128)
+    if want_n == 0 and split <= 1 and (S < 2 or 2 * n64 >= 256) and -(-n64 // 256) * kt * 16 < min(c128, c256 * 20):
+        return 64, n64, 0, 1   # 128x128 tiles (tile_n 128, tile_m 128)
+    if want_n == 128 or (want_n == 0 and split <= 1 and c128 < c256 * 20):
         return 128, n128, 0, 1
     return 256, n256 - rem, rem, S
 
@@ -505,14 +511,16 @@ def test_plan_tile_choice_and_split_remainder():
         st, i = _plan(*_gemm_descs(M, N, K), kernel=L.LT_KERNEL_TILED, split=split)
         assert st == "LT_OK" and i.kernel == L.LT_KERNEL_TILED, (M, N, K, st)
         tn, dp, rem, S = _tile_plan(M, N, K, split)
-        # tiles run persistent (one workgroup per CU) when whole, K a
-        # multiple of 64 with at least 4 slices, more than 256 of them, and
-        # for 256x256 tiles no split remainder (beta = 0 here)
-        pers = (M % 256 == 0 and N % tn == 0 and K % 64 == 0 and K >= 256 and dp > 256 and rem == 0
+        sq = tn == 64   # 128x128 tiles
+        # tiles run persistent (one workgroup per CU) when 256 rows high and
+        # whole, K a multiple of 64 with at least 4 slices, more than 256 of
+        # them, and for 256x256 tiles no split remainder (beta = 0 here)
+        pers = (not sq and M % 256 == 0 and N % tn == 0 and K % 64 == 0 and K >= 256 and dp > 256 and rem == 0
                 and (tn == 128 or K <= 4096))
         grid = 256 if pers else dp + rem * S
-        assert (i.tile_n, i.sk_tiles, i.split_k, i.grid, i.persistent) == (tn, rem, S, grid, int(pers)), \
-            (M, N, K, i.tile_n, i.sk_tiles, i.split_k, i.grid, i.persistent)
+        want = (128 if sq else 256, 128 if sq else tn, rem, S, grid, int(pers))
+        assert (i.tile_m, i.tile_n, i.sk_tiles, i.split_k, i.grid, i.persistent) == want, \
+            (M, N, K, i.tile_m, i.tile_n, i.sk_tiles, i.split_k, i.grid, i.persistent, want)
         assert i.tiles == dp + rem
         assert i.sk_workgroups == rem * S
         want_ws = ((rem * 4 + 255) // 256 * 256 + rem * S * 256 * 256 * 4) if rem else 0
@@ -538,14 +546,20 @@ def test_plan_tile_choice_and_split_remainder():
     st, i = _plan(A, B, C, D, bnz=1)
     assert (i.tile_n, i.sk_tiles, i.tiles, i.grid, i.persistent) == (256, 0, 1024, 1024, 0)
     # 49 256x256 tiles of 110 slices: a 5-way split would pay 4 partials'
-    # read-back (measured 90.3 us); 98 whole 256x128 tiles win (80.2 us)
+    # read-back (measured 84.9 us), 98 whole 256x128 tiles half the CUs
+    # (78.3 us); 196 128x128 tiles take 49.5 us
     st, i = _plan(*_gemm_descs(1792, 1792, 7040))
-    assert (i.tile_n, i.sk_tiles, i.split_k, i.grid, i.persistent) == (128, 0, 1, 98, 0)
-    # 64 256x256 tiles of 128 slices: one round of 128 whole 256x128 tiles
-    # beats 4 segments each (87-90 vs 91-92 us measured); 16 tiles of 256
-    # slices split 8 ways (128 workgroups)
+    assert (i.tile_m, i.tile_n, i.sk_tiles, i.split_k, i.grid, i.persistent) == (128, 128, 0, 1, 196, 0)
+    # 2560^3: 400 128x128 tiles need two rounds; 200 256x128 tiles one (38.6
+    # us against 43.4)
+    st, i = _plan(*_gemm_descs(2560, 2560, 2560))
+    assert (i.tile_m, i.tile_n, i.grid) == (256, 128, 200)
+    # 64 256x256 tiles of 128 slices: 256 128x128 tiles (63.0 us) beat 128
+    # whole 256x128 tiles (87-91 us) and 4 segments each (91-92 us); 16
+    # tiles of 256 slices split 8 ways (128 workgroups, 83.7 us) beat 64
+    # 128x128 tiles (92.4 us)
     st, i = _plan(*_gemm_descs(2048, 2048, 8192))
-    assert (i.tile_n, i.sk_tiles, i.split_k, i.grid) == (128, 0, 1, 128)
+    assert (i.tile_m, i.tile_n, i.sk_tiles, i.split_k, i.grid) == (128, 128, 0, 1, 256)   # 63.0 us
     st, i = _plan(*_gemm_descs(1024, 1024, 16384))
     assert (i.tile_n, i.sk_tiles, i.split_k, i.grid) == (256, 16, 8, 128)
     # 1,056 tiles: four whole rounds and 32 tiles split 8 ways (a 4 % saving)
