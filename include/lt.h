@@ -286,7 +286,8 @@ typedef enum lt_kernel {
 /* Optional planner overrides; zero fields mean "choose". */
 typedef struct lt_gemm_options {
     int32_t kernel;     /* lt_kernel */
-    int32_t tile_m;     /* block tile (kernel-specific allowed values) */
+    int32_t tile_m;     /* block tile (kernel-specific allowed values; TILED: 256x256,
+                           256x128 or 128x128, the last never split nor persistent) */
     int32_t tile_n;
     int32_t split_k;    /* SKINNY: number of K slices (>= 1). TILED: K segments of each
                            tile past the last whole round of 256 CUs (0: chosen by a
