@@ -646,7 +646,7 @@ def main():
                                f"fp32 accumulate", "M": w.c.M, "N": w.c.N, "K": w.c.K,
                    "kernel": plan["kernel_name"], "tile": [plan["tile_m"], plan["tile_n"], plan["tile_k"]],
                    "grid": plan["grid"], "persistent": bool(plan["persistent"]),
-                   "tile_order": {0: None, 1: "raster", 2: "superblock"}[plan["tile_order"]],
+                   "tile_order": {0: None, 1: "raster", 2: "superblock", 3: "raster_krev"}[plan["tile_order"]],
                    "pct_of_peak": round(100 * value / PEAK_TFLOPS, 2),
                    "kernel_us": {"mean": round(kern * 1e6, 1),
                                  "median": round(w.kernel_times[len(w.kernel_times) // 2] * 1e6, 1),

@@ -308,7 +308,11 @@ typedef struct lt_gemm_options {
                            XCD); 2 = super-blocks: each round of 256 tiles a 16 x 16
                            block, each XCD an 8 x 4 part of it (LT_ERR_UNSUPPORTED
                            unless both tile counts are multiples of 16 and every tile
-                           is whole, unsplit and not persistent) */
+                           is whole, unsplit and not persistent); 3 = raster with the
+                           odd rounds walking K downward (chosen where a round's 32
+                           panels exceed 192 MiB; LT_ERR_UNSUPPORTED unless K is a
+                           multiple of 64, the tiles unsplit, not persistent and more
+                           than one round) */
 } lt_gemm_options;
 
 /* What the planner chose, for banners and tests [P1 "Exercise": print the
@@ -336,8 +340,9 @@ typedef struct lt_gemm_plan_info {
                                 tiles ["CUTLASS, in depth", "Kernel schedules"]; grid is
                                 then the workgroup count. A fused epilogue (lt_gemm_run_ex)
                                 runs one workgroup per tile instead. */
-    int32_t tile_order;      /* TILED data-parallel launch: 1 raster, 2 super-blocks; 0 for
-                                the other kernels and the persistent launch */
+    int32_t tile_order;      /* TILED data-parallel launch: 1 raster, 2 super-blocks, 3 raster
+                                with odd rounds K-reversed; 0 for the other kernels and the
+                                persistent launch */
 } lt_gemm_plan_info;
 
 /* Validate and plan without launching: the can_implement half of the

@@ -50,6 +50,7 @@ struct TiledArgs {
     int group_m;                  // tile rows per raster group
     int xcd_remap;                // 1: spread consecutive tiles over one XCD
     int superblock;               // 1: the data-parallel launch walks 16x16-tile super-blocks
+    int krev;                     // 1: its odd rounds of 256 workgroups walk K downward
     // A and B moved to the start of K slice 0, k = kbase = K - ceil(K/BK)*BK
     // (<= 0): a pointer offset only, never dereferenced below k = 0
     const void* A0;

@@ -276,8 +276,14 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
         static_for<0, Cf::IPW>([&](auto cc) { issue_one(stage, ga, gb, cc); });
     };
     // slice kt of this workgroup's K range
-    auto src_a = [&](int kt) { return a_k0 + (kt0 + kt) * a_ks; };
-    auto src_b = [&](int kt) { return b_k0 + (kt0 + kt) * b_ks; };
+    // (the planner's K-reversed raster: the workgroups of odd rounds, 256
+    // at a time, walk their K slices downward, so a round starts on the
+    // slices the round before touched last, still in the last-level cache
+    // for the tile rows the two share; whole slices only)
+    const int krev = (!PERS && !SPLIT && p.krev && kbase == 0) ? (blockIdx.x >> 8) & 1 : 0;
+    auto kslice = [&](int kt) { return kt0 + (krev ? NS - 1 - kt : kt); };
+    auto src_a = [&](int kt) { return a_k0 + kslice(kt) * a_ks; };
+    auto src_b = [&](int kt) { return b_k0 + kslice(kt) * b_ks; };
     auto issue = [&](int stage, int kt) { issue_at(stage, src_a(kt), src_b(kt)); };
 
     // Slice 0 when it is partial: a lane whose chunk lies below K = 0 writes

@@ -43,7 +43,7 @@ def tensor_desc(t: torch.Tensor, layout: Optional[Layout] = None) -> L.lt_tensor
     return d
 
 
-TILE_ORDERS = {None: 0, "raster": 1, "superblock": 2}
+TILE_ORDERS = {None: 0, "raster": 1, "superblock": 2, "raster_krev": 3}
 
 
 def _opts(kernel: Union[str, int], tile=None, split_k: int = 0, persistent=None,
@@ -108,8 +108,8 @@ def gemm(A: torch.Tensor, B: torch.Tensor, D: torch.Tensor, C: Optional[torch.Te
     ``bias_per_row``), ``activation`` ("relu", "gelu") and ``amax`` (a float32
     device scalar receiving max |D|) select the fused epilogue. ``persistent``
     (None: the planner's choice) forces the persistent launch on or off;
-    ``tile_order`` ("raster", "superblock"; None: the planner's choice) sets
-    the order of the data-parallel launch's tiles."""
+    ``tile_order`` ("raster", "superblock", "raster_krev"; None: the
+    planner's choice) sets the order of the data-parallel launch's tiles."""
     la = layouts or {}
     dA, dB, dD = tensor_desc(A, la.get("A")), tensor_desc(B, la.get("B")), tensor_desc(D, la.get("D"))
     dC = tensor_desc(C, la.get("C")) if C is not None else None

@@ -364,6 +364,37 @@ def test_tiled_superblock_order_matches_the_raster():
     _ok(res)
 
 
+def test_tiled_k_reversed_rounds():
+    """The raster with odd rounds walking K downward (forced; 512 tiles, two
+    rounds): every output within the oracle's bound, and only the second
+    round's tiles may differ from the plain raster's (their sums run in the
+    other order), the first round's bit-equal."""
+    M, N, K = 4096, 8192, 512
+    A, B, C, D = _case(M, N, K, BF16, "row", "col", "row", 1.0, 0.0, dist="normal_over_sqrtk", seed=93)
+    outs = {}
+    for order in ("raster_krev", "raster"):
+        plan, out = run_gemm(A, B, None, D, 1.0, 0.0, kernel="tiled", tile=(256, 256), split_k=1,
+                             persistent=False, tile_order=order, label=f"order {order}")
+        assert plan["tile_order"] == (3 if order == "raster_krev" else 1), plan
+        outs[order] = out.view().clone()
+    res = check_all_rows(A, B, None, datagen.Matrix(outs["raster_krev"].reshape(-1), (M, N), (N, 1)), 1.0, 0.0)
+    _ok(res)
+    # workgroup w of the raster takes tile lin = (w % 8) * (512 / 8) + w / 8,
+    # groups of 8 tile rows walked down, then right; w >= 256 is round 1
+    tm, tn, gsz = M // 256, N // 256, 8 * (N // 256)
+    round1 = set()
+    for w in range(256, tm * tn):
+        lin = (w % 8) * (tm * tn // 8) + w // 8
+        grp, i = divmod(lin, gsz)
+        round1.add((8 * grp + i % 8, i // 8))
+    same = (outs["raster_krev"].view(torch.int16) == outs["raster"].view(torch.int16))
+    for r in range(tm):
+        for c in range(tn):
+            tile_same = bool(same[256 * r:256 * (r + 1), 256 * c:256 * (c + 1)].all())
+            assert tile_same or (r, c) in round1, (r, c)
+    assert not bool(same.all())   # the second round did run reversed
+
+
 def test_tiled_c_rows_at_the_staged_copy_offset_limit():
     """A whole 256x256 tile with C: the staged store copies the wave's 128 C
     rows through 32-bit byte offsets, so a C row stride of 2^24 - 64 elements

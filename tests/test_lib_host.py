@@ -683,17 +683,19 @@ def test_plan_persistent_with_c_needs_c_rows_within_32_bit_copy_offsets():
 def test_plan_tile_order():
     """The data-parallel launch's tile order: super-blocks where the
     last-level-cache model says they pay (measured faster on these shapes),
-    the raster where they do not (measured slower or even), 0 for the
-    persistent launch; forcing super-blocks needs tile counts in multiples of
-    16 and whole, unsplit tiles."""
+    the raster where they do not (measured slower or even), the raster with
+    odd rounds walking K downward where a round's 32 panels exceed 192 MiB
+    (K above 12288), 0 for the persistent launch; forcing super-blocks needs
+    tile counts in multiples of 16 and whole, unsplit tiles, forcing the
+    K-reversed raster K a multiple of 64 and more than one round."""
     for (M, N, K), want in (((16384, 16384, 8192), 2), ((12288, 12288, 12288), 2), ((16384, 8192, 8192), 2),
                             ((16384, 16384, 12288), 2), ((8192, 8192, 8192), 1), ((8192, 28672, 8192), 1),
-                            ((16384, 16384, 16384), 1), ((12288, 12288, 16384), 1), ((8192, 8192, 4096), 0)):
+                            ((16384, 16384, 16384), 3), ((12288, 12288, 16384), 3), ((8192, 8192, 4096), 0)):
         st, i = _plan(*_gemm_descs(M, N, K))
         assert st == "LT_OK" and i.tile_order == want, (M, N, K, i.tile_order)
         assert (i.persistent == 1) == (want == 0)
     descs = _gemm_descs(4096, 8192, 512)
-    for order in (1, 2):
+    for order in (1, 2, 3):
         o = L.lt_gemm_options()
         o.kernel, o.tile_n, o.persistent, o.tile_order = L.LT_KERNEL_TILED, 256, 1, order
         info = L.lt_gemm_plan_info()
@@ -708,6 +710,12 @@ def test_plan_tile_order():
                                   ctypes.byref(o), ctypes.byref(L.lt_gemm_plan_info()))
         assert L.STATUS_NAMES[st] == "LT_ERR_UNSUPPORTED", (M, N, K)
     o.tile_order = 3
+    for M, N, K in ((4096, 4096, 512), (4096, 8192, 520)):   # one round; a partial K slice
+        d = _gemm_descs(M, N, K)
+        st = L.lib().lt_gemm_plan(ctypes.byref(d[0]), ctypes.byref(d[1]), None, ctypes.byref(d[3]), 0,
+                                  ctypes.byref(o), ctypes.byref(L.lt_gemm_plan_info()))
+        assert L.STATUS_NAMES[st] == "LT_ERR_UNSUPPORTED", (M, N, K)
+    o.tile_order = 4
     st = L.lib().lt_gemm_plan(*(ctypes.byref(d) for d in descs[:2]), None, ctypes.byref(descs[3]), 0,
                               ctypes.byref(o), ctypes.byref(L.lt_gemm_plan_info()))
     assert L.STATUS_NAMES[st] == "LT_ERR_INVALID_ARGUMENT"
