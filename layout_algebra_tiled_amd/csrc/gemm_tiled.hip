@@ -608,8 +608,12 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
         const u32x4 x = *(const LDS_AS u32x4*)(region + SR::slot(r, q));
         return SR::swapped(r) ? u32x4{x.z, x.w, x.x, x.y} : x;
     };
-    // cval(i, j): the C values of block (i, j) for epi4 (zero when beta = 0)
-    auto store_staged = [&](auto&& cval) {
+    // cval(i, j): the C values of block (i, j) for epi4 (zero when beta = 0).
+    // A tile on a ragged edge (edge = true) stores the rows below M only, and
+    // of a 16-byte chunk that N cuts, its first elements one at a time (D's
+    // rows start 16-byte aligned, so every chunk left of N is whole).
+    auto store_staged = [&](auto&& cval, auto edge) {
+        constexpr bool EDGE = decltype(edge)::value;
         char* region = smem + Cf::LDS + wave * DSW;
         static_for<0, FM / BPP>([&](auto pc) {
             constexpr int ps = decltype(pc)::value;
@@ -631,8 +635,21 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
             static_for<0, NRD16>([&](auto kc) {
                 const int lin16 = decltype(kc)::value * 64 + lane;
                 const int r = lin16 / CPR, q = lin16 % CPR;
-                *reinterpret_cast<u32x4*>(p.D + (int64_t)(m0 + arow0 + ps * RPP + r) * p.ldd + n0 + brow0 + 8 * q) =
-                    w[decltype(kc)::value];
+                const int m = m0 + arow0 + ps * RPP + r, n = n0 + brow0 + 8 * q;
+                uint16_t* dst = p.D + (int64_t)m * p.ldd + n;
+                const u32x4 x = w[decltype(kc)::value];
+                if constexpr (EDGE) {
+                    if (m < p.M) {
+                        if (n + 8 <= p.N) {
+                            *reinterpret_cast<u32x4*>(dst) = x;
+                        } else if (n < p.N) {
+                            const uint32_t u[4] = {x.x, x.y, x.z, x.w};
+                            for (int e = 0; e < p.N - n; ++e) dst[e] = uint16_t(u[e >> 1] >> (16 * (e & 1)));
+                        }
+                    }
+                } else {
+                    *reinterpret_cast<u32x4*>(dst) = x;
+                }
             });
             // one pass at a time: the next pass's conversions are not hoisted
             // above this one's stores (they would hold more registers)
@@ -698,9 +715,9 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
     auto epilogue = [&](auto edge) {
         constexpr bool EDGE = decltype(edge)::value;
         const bool use_c = p.beta != 0.0f;
-        if constexpr (STAGED_D && !EDGE) {
+        if constexpr (STAGED_D) {
             if (!use_c) {
-                store_staged([](int, int) { return u32x2{0u, 0u}; });
+                store_staged([](int, int) { return u32x2{0u, 0u}; }, edge);
                 return;
             }
         }
@@ -712,9 +729,20 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
                 for (int g = 0; g < NG; ++g) {
                     const int n = n0 + brow0 + j * Cf::MF + Mf::out_row(lane, 4 * g);
                     const u32x2* src = reinterpret_cast<const u32x2*>(p.C + (int64_t)m * p.ldc + n);
-                    if constexpr (decltype(guarded)::value)
+                    if constexpr (decltype(guarded)::value) {
                         cv[i][j][g] = (m < p.M && n + 4 <= p.N) ? *src : u32x2{0u, 0u};
-                    else
+                        // the staged store takes C from here, also of the
+                        // group that N cuts (the direct store reads that
+                        // group's C itself)
+                        if constexpr (STAGED_D) {
+                            if (m < p.M && n < p.N && n + 4 > p.N) {
+                                const uint16_t* c = p.C + (int64_t)m * p.ldc + n;
+                                uint32_t h[4] = {0u, 0u, 0u, 0u};
+                                for (int e = 0; e < p.N - n; ++e) h[e] = c[e];
+                                cv[i][j][g] = u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+                            }
+                        }
+                    } else
                         cv[i][j][g] = *src;
                 }
             });
@@ -740,11 +768,15 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
                 }
             });
             if constexpr (STAGED_D) {   // D through the region beside the stages
-                store_staged([&](int i, int j) { return cv[i][j][0]; });
+                store_staged([&](int i, int j) { return cv[i][j][0]; }, std::false_type{});
                 return;
             }
         } else {
             load_c(std::integral_constant<bool, EDGE>{});   // a whole tile loads with no branch per block
+            if constexpr (STAGED_D) {
+                store_staged([&](int i, int j) { return cv[i][j][0]; }, edge);
+                return;
+            }
         }
         for_blocks<FM, FN>([&](auto i, auto j) {
             const int m = m0 + arow0 + i * Cf::MF + Mf::out_col(lane);
@@ -918,7 +950,7 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
                 const int st_last = stage;
                 slice_x(yes, no, a_k0, b_k0, ic<0>{}, ic<0>{}, no, ic<Cf::IPW * (S - 2)>{});
                 asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");   // MFMA results before VALU reads
-                store_staged([](int, int) { return u32x2{0u, 0u}; });
+                store_staged([](int, int) { return u32x2{0u, 0u}; }, std::false_type{});
                 if (!more) break;
                 issue_at(st_last, na + (S - 1) * a_ks, nb + (S - 1) * b_ks);   // the next tile's slice S-1
             } else {
@@ -952,7 +984,7 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
                 // tile's C rows 192..255 into the spare (the last tile: its
                 // own again, unused)
                 issue_at(st_c, na + a_ks, nb + b_ks);
-                store_staged([&](int i, int j) { return cv[i][j][0]; });
+                store_staged([&](int i, int j) { return cv[i][j][0]; }, std::false_type{});
                 __syncthreads();
                 issue_c_spare(m0n, n0n);
                 if (!more) break;
@@ -1052,7 +1084,7 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
         // whole tiles through LDS; the predicated path takes the rest (and
         // a C whose rows lie too far apart for the 32-bit copy offsets)
         if (whole && p.beta == 0.0f)
-            store_staged([](int, int) { return u32x2{0u, 0u}; });
+            store_staged([](int, int) { return u32x2{0u, 0u}; }, std::false_type{});
         else if (whole && (int64_t)p.ldc * 2 * Cf::TWM < (int64_t(1) << 32))
             store_staged_c();
         else

@@ -336,6 +336,20 @@ def test_tiled_128x128_all_outputs(M, N, K, dtype, a_major, b_major, alpha, beta
     _ok(res)
 
 
+@pytest.mark.parametrize("tile", [(128, 128), (256, 128), (256, 256)])
+@pytest.mark.parametrize("beta", [0.0, 0.5])
+def test_tiled_staged_edge_tiles_partial_chunks(tile, beta):
+    """K-major operands: edge tiles store D through LDS too. N % 8 = 2 (D's
+    rows padded to 16-byte multiples) leaves a 16-byte chunk that N cuts in
+    every row; M cuts the last tile row. Every output checked."""
+    M, N, K = 300, 522, 200
+    A, B, C, D = _case(M, N, K, BF16, "row", "col", "row", 1.0, beta, seed=N + int(8 * beta), lds=(K, K, 528))
+    res, plan, _ = run_and_check(A, B, C, D, 1.0, beta, kernel="tiled", tile=tile, split_k=1,
+                                 expect_kernel="tiled", label="staged-edge")
+    assert (plan["tile_m"], plan["tile_n"], plan["persistent"]) == (tile[0], tile[1], 0), plan
+    _ok(res)
+
+
 def test_tiled_128x128_planned_long_k_sampled():
     """The planner's 128x128 tiles on bf16 2048^2 x 8192 (256 tiles, one
     round, 128 slices each), sampled outputs."""
@@ -505,6 +519,9 @@ def test_skinny_with_beta():
     (4608, 3584, 192, F16, "row", "col", 1.0, 0.5, 128),     # 504 tiles, 3 slices
     (4608, 3584, 200, BF16, "col", "row", -1.5, 2.0, 128),   # 4 slices, the first partial
     (4100, 4104, 320, F16, "row", "row", 1.0, -1.0, 128),    # ragged: edge tiles read C directly
+    # K-major: edge tiles store D through LDS, whole tiles copy C through it
+    (4100, 4104, 256, BF16, "row", "col", 1.0, 0.5, 256),    # 289 tiles
+    (4100, 4104, 256, F16, "row", "col", 1.0, -1.0, 128),    # 561 tiles, C in the accumulators' layout
 ])
 def test_many_rounds_tiled_all_outputs(M, N, K, dtype, a_major, b_major, alpha, beta, tile_n):
     A, B, C, D = _case(M, N, K, dtype, a_major, b_major, "row", alpha, beta, seed=M + K + tile_n)
