@@ -1,6 +1,6 @@
-// Block-tiled GEMM for gfx950: D = alpha * A*B + beta * C with a 256x256 or
-// 256x128 block tile, fp16/bf16 operands, fp32 accumulation in 16x16x32
-// MFMAs. M, N and K need not be multiples of the tile: edge tiles clamp their
+// Block-tiled GEMM for gfx950: D = alpha * A*B + beta * C with a 256x256,
+// 256x128 or 128x128 block tile, fp16/bf16 operands, fp32 accumulation in
+// 16x16x32 MFMAs. M, N and K need not be multiples of the tile: edge tiles clamp their
 // copy rows and store only the outputs inside (M, N); a partial K slice is
 // zero-filled in LDS.
 //
@@ -579,8 +579,10 @@ __global__ __launch_bounds__(Cf::NT, 1) void gemm_tiled(TiledArgs p) {
     // trip per tile, not one per block); the fragment registers are free by
     // now and hold them.
     constexpr int NG = Mf::NACC / 4;   // groups of four outputs per block
-    // ---- staged store of a whole tile with beta = 0. In the accumulators'
-    // layout the 16 lanes of a quarter-wave store 8 bytes to each of 16
+    // ---- staged store (K-major data-parallel and persistent launches:
+    // whole tiles with beta = 0, edge tiles, and tiles whose C values are
+    // already in registers). In the accumulators' layout the 16 lanes of a
+    // quarter-wave store 8 bytes to each of 16
     // rows, so one store instruction reaches 64 cache lines. Staged through
     // LDS, the 16 lanes store 256 contiguous bytes of one row (two rows of
     // 128 with 64-column wave tiles): 8 lines per instruction, and half the
