@@ -394,7 +394,8 @@ def test_tiled_k_reversed_rounds():
     res = check_all_rows(A, B, None, datagen.Matrix(outs["raster_krev"].reshape(-1), (M, N), (N, 1)), 1.0, 0.0)
     _ok(res)
     # workgroup w of the raster takes tile lin = (w % 8) * (512 / 8) + w / 8,
-    # groups of 8 tile rows walked down, then right; w >= 256 is round 1
+    # groups of 8 tile rows walked down, then right; workgroups w >= 256 form
+    # the second round of 256 tiles (K walked downward there)
     tm, tn, gsz = M // 256, N // 256, 8 * (N // 256)
     round1 = set()
     for w in range(256, tm * tn):
